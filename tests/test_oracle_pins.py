@@ -1,0 +1,453 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties one oracle function to a value printed on the pages, a closed form, an
+invariant the pages fix, or an independent library routine (torch float64 CPU ops), so that a
+plausible slip (a dropped term, a wrong sign or index, a transposed operand) fails here.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import dit_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "token_counts.json")
+
+TINY = O.Dims(hidden=256, heads=2, head_dim=128, mlp_hidden=192, in_channels=64,
+              time_dim=32)
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def rand_set(r, dims, scale=0.05):
+    d, f = dims.hidden, dims.mlp_hidden
+    return O.WeightSet(w1=r.normal(0, scale, (3 * d + 2 * f, d)),
+                       w2=r.normal(0, scale, (d, d + f)),
+                       qn=r.uniform(0.5, 1.5, dims.head_dim),
+                       kn=r.uniform(0.5, 1.5, dims.head_dim))
+
+
+def rand_mods(r, dims, n=3, gate_zero=False):
+    d = dims.hidden
+    out = []
+    for _ in range(n):
+        m = r.normal(0, 0.5, 3 * d)
+        if gate_zero:
+            m[2 * d:] = 0.0
+        out.append(m)
+    return out
+
+
+# ------------------------------------------------------------------ token accounting
+
+def test_token_counts_match_printed_values():
+    g = json.load(open(GOLDEN))
+    for case in g["image_tokens"]:
+        assert O.image_token_grid(*case["hw"]) == tuple(case["grid"])
+        assert O.image_tokens(*case["hw"]) == case["tokens"]
+    for case in g["tokens_per_call"]:
+        img = O.image_tokens(*case["out_hw"]) + sum(O.image_tokens(*hw) for hw in case["ref_hws"])
+        # the printed total must be reachable with a padded prompt: some prompt length
+        # gives exactly the printed count, and the text part is a positive multiple of 80
+        txt = case["tokens"] - img
+        assert txt > 0 and txt % g["text_pad_multiple"]["value"] == 0, case
+        ok = [L for L in range(1, 1000)
+              if O.tokens_per_call(L, tuple(case["out_hw"]),
+                                   tuple(tuple(h) for h in case["ref_hws"])) == case["tokens"]]
+        assert ok and ok == list(range(txt - 79, txt + 1)), case
+
+
+def test_config_token_counts():
+    # the benchmark configurations: 64x64 px -> 16 tokens, 256^2 -> 256, 512^2 -> 1024
+    assert O.image_tokens(64, 64) == 16
+    assert O.image_token_grid(256, 256) == (16, 16)
+    assert O.image_tokens(512, 512) == 1024
+    assert O.padded_text_tokens(0) == 0 and O.padded_text_tokens(1) == 80
+    assert O.padded_text_tokens(80) == 80 and O.padded_text_tokens(81) == 160
+    with pytest.raises(ValueError):
+        O.image_token_grid(100, 64)
+
+
+# ------------------------------------------------------------------ positions and RoPE
+
+def test_positions_structure():
+    pos = O.positions(5, (3, 4), ((3, 4), (2, 2)))
+    assert pos.shape == (5 + 12 + 12 + 4, 4)
+    assert np.all(pos[:, 0] == 0)                             # t is 0 for every token
+    assert np.all(pos[:5, 1:3] == 0) and np.all(pos[:5, 3] == np.arange(5))
+    img = pos[5:17]
+    ref0 = pos[17:29]
+    ref1 = pos[29:]
+    assert np.all(img[:, 3] == 0) and np.all(ref0[:, 3] == -1) and np.all(ref1[:, 3] == -2)
+    # reference tokens share the image's (h, w) grid (same place -> same coordinates)
+    assert np.array_equal(img[:, 1:3], ref0[:, 1:3])
+    assert img[:, 1].max() == 2 and img[:, 2].max() == 3
+    # row-major inside an image
+    assert tuple(img[5, 1:3]) == (1, 1)
+
+
+def rope_complex(x, pos, theta):
+    """Independent formulation: each adjacent pair is a complex number multiplied by
+    exp(i * pos_axis * theta^(-j/16))."""
+    n, h, d = x.shape
+    xc = torch.view_as_complex(torch.tensor(x).reshape(n, h, d // 2, 2).contiguous())
+    p = torch.arange(d // 2, dtype=torch.float64)
+    axis = (p // 16).long()
+    j = p % 16
+    ang = torch.tensor(pos)[:, axis] * theta ** (-j / 16.0)
+    rot = torch.polar(torch.ones_like(ang), ang)
+    return torch.view_as_real(xc * rot[:, None, :]).reshape(n, h, d).numpy()
+
+
+def test_rope_matches_complex_rotation():
+    r = rng(1)
+    pos = O.positions(7, (3, 3), ((2, 3),))
+    x = r.normal(size=(pos.shape[0], 2, 128))
+    got = O.apply_rope(x, O.rope_angles(pos, 10000.0))
+    np.testing.assert_allclose(got, rope_complex(x, pos, 10000.0), rtol=0, atol=1e-12)
+
+
+def test_rope_invariants():
+    r = rng(2)
+    pos = O.positions(6, (4, 5), ((4, 5),))
+    n = pos.shape[0]
+    x = r.normal(size=(n, 3, 128))
+    y = O.apply_rope(x, O.rope_angles(pos))
+    # rotations preserve norms (per pair, hence per head)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+    # t slice untouched for all tokens; l slice untouched for image tokens;
+    # h and w slices untouched for text tokens
+    np.testing.assert_array_equal(y[:, :, 0:32], x[:, :, 0:32])
+    np.testing.assert_array_equal(y[6:26, :, 96:128], x[6:26, :, 96:128])
+    np.testing.assert_array_equal(y[:6, :, 32:96], x[:6, :, 32:96])
+    # pos = 0 is the identity
+    np.testing.assert_array_equal(O.apply_rope(x, O.rope_angles(np.zeros((n, 4)))), x)
+    # the first pair of each axis turns by exactly pos radians (frequency theta^0 = 1)
+    e = np.zeros((1, 1, 128))
+    e[0, 0, 96] = 1.0
+    out = O.apply_rope(e, O.rope_angles(np.array([[0.0, 0.0, 0.0, 1.0]])))
+    assert abs(out[0, 0, 96] - math.cos(1.0)) < 1e-15 and abs(out[0, 0, 97] - math.sin(1.0)) < 1e-15
+
+
+def test_rope_relative_position():
+    # scores between rotated q and k depend only on the position difference
+    r = rng(3)
+    q = r.normal(size=(1, 1, 128))
+    k = r.normal(size=(1, 1, 128))
+    p1 = np.array([[0.0, 3.0, 5.0, 7.0]])
+    k1 = np.array([[0.0, 1.0, 2.0, 4.0]])
+    shift = np.array([[0.0, 11.0, -4.0, 9.0]])
+
+    def score(pq, pk):
+        return float((O.apply_rope(q, O.rope_angles(pq)) * O.apply_rope(k, O.rope_angles(pk))).sum())
+
+    assert abs(score(p1, k1) - score(p1 + shift, k1 + shift)) < 1e-10
+    assert abs(score(p1, k1) - score(p1 + 1.0, k1)) > 1e-3
+
+
+# ------------------------------------------------------------------ norms, activations
+
+def test_layer_norm_matches_library():
+    x = rng(4).normal(3.0, 2.0, (9, 256))
+    ref = F.layer_norm(torch.tensor(x), (256,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, 1e-6), ref, rtol=0, atol=1e-12)
+    y = O.layer_norm(x, 0.0)
+    np.testing.assert_allclose(y.mean(-1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(-1), 1, atol=1e-12)
+
+
+def test_rms_norm_matches_library():
+    r = rng(5)
+    x = r.normal(size=(7, 3, 128))
+    w = r.uniform(0.5, 1.5, 128)
+    ref = F.rms_norm(torch.tensor(x), (128,), torch.tensor(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, w, 1e-6), ref, rtol=0, atol=1e-12)
+    y = O.rms_norm(x, np.ones(128), 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(-1)), 1, atol=1e-12)
+
+
+def test_silu_matches_library():
+    z = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(O.silu(z), F.silu(torch.tensor(z)).numpy(), rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------------------ attention
+
+def test_attention_matches_library():
+    r = rng(6)
+    n, h, d = 13, 2, 128
+    q, k, v = (r.normal(size=(n, h, d)) for _ in range(3))
+    seg = O.segment_ids(4, 6, 3)
+    for mask in (O.MASK_FULL, O.MASK_SEGMENT):
+        got = O.attention(q, k, v, seg, mask)
+        am = None if mask == O.MASK_FULL else torch.tensor(seg[:, None] == seg[None, :])
+        ref = F.scaled_dot_product_attention(
+            torch.tensor(q).transpose(0, 1), torch.tensor(k).transpose(0, 1),
+            torch.tensor(v).transpose(0, 1), attn_mask=am).transpose(0, 1).numpy()
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_invariants():
+    r = rng(7)
+    n, h, d = 11, 2, 128
+    q, k = r.normal(size=(n, h, d)), r.normal(size=(n, h, d))
+    seg = O.segment_ids(3, 5, 3)
+    # constant values -> constant output
+    v = np.full((n, h, d), 0.37)
+    np.testing.assert_allclose(O.attention(q, k, v, seg, O.MASK_FULL), 0.37, atol=1e-14)
+    # q = 0 -> uniform weights: output is the mean of the allowed values
+    v = r.normal(size=(n, h, d))
+    z = np.zeros_like(q)
+    np.testing.assert_allclose(O.attention(z, k, v, seg, O.MASK_FULL),
+                               np.broadcast_to(v.mean(0), (n, h, d)), atol=1e-13)
+    o = O.attention(z, k, v, seg, O.MASK_SEGMENT)
+    for s in range(3):
+        sel = seg == s
+        np.testing.assert_allclose(o[sel], np.broadcast_to(v[sel].mean(0), o[sel].shape), atol=1e-13)
+
+
+# ------------------------------------------------------------------ one block
+
+def torch_block(x, segs, sets, sos, mods, pos, mask, dims):
+    """Independent composition of torch float64 library routines for one block."""
+    d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
+    seg = torch.tensor(O.segment_ids(*segs))
+    n = x.shape[0]
+    X = torch.tensor(x)
+    M = torch.stack([torch.tensor(mods[int(s)]) for s in seg])          # [n, 3D]
+    shift, scale, gate = M[:, :d], M[:, d:2 * d], M[:, 2 * d:]
+    xm = F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + scale) + shift
+    W1 = torch.stack([torch.tensor(sets[sos[int(s)]].w1) for s in seg])  # [n, 3D+2F, D]
+    h = torch.einsum("nk,nok->no", xm, W1)
+    q, k, v = h[:, :d].reshape(n, nh, hd), h[:, d:2 * d].reshape(n, nh, hd), h[:, 2 * d:3 * d].reshape(n, nh, hd)
+    qw = torch.stack([torch.tensor(sets[sos[int(s)]].qn) for s in seg])[:, None, :]
+    kw = torch.stack([torch.tensor(sets[sos[int(s)]].kn) for s in seg])[:, None, :]
+    q = F.rms_norm(q, (hd,), eps=dims.rms_eps) * qw
+    k = F.rms_norm(k, (hd,), eps=dims.rms_eps) * kw
+    q = torch.tensor(rope_complex(q.numpy(), pos, dims.rope_theta))
+    k = torch.tensor(rope_complex(k.numpy(), pos, dims.rope_theta))
+    am = None if mask == O.MASK_FULL else (seg[:, None] == seg[None, :])
+    o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                       attn_mask=am).transpose(0, 1).reshape(n, d)
+    g, u = h[:, 3 * d:3 * d + f], h[:, 3 * d + f:]
+    cat = torch.cat([o, F.silu(g) * u], dim=1)
+    W2 = torch.stack([torch.tensor(sets[sos[int(s)]].w2) for s in seg])
+    return (X + gate * torch.einsum("nk,nok->no", cat, W2)).numpy()
+
+
+@pytest.mark.parametrize("mask,sos,segs", [
+    (O.MASK_FULL, (0, 0, 0), (4, 6, 0)),
+    (O.MASK_FULL, (0, 1, 1), (5, 4, 3)),
+    (O.MASK_SEGMENT, (0, 1, 2), (3, 6, 4)),
+])
+def test_block_matches_library_composition(mask, sos, segs):
+    r = rng(8)
+    dims = TINY
+    n = sum(segs)
+    sets = [rand_set(r, dims) for _ in range(3)]
+    mods = rand_mods(r, dims)
+    x = r.normal(size=(n, dims.hidden))
+    pos = O.positions(segs[0], (2, segs[1] // 2), ((segs[2], 1),) if segs[2] else ())
+    got = O.block_forward(x, segs, sets, sos, mods, pos, mask, dims)
+    ref = torch_block(x, segs, sets, sos, mods, pos, mask, dims)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    # computing a subset of rows gives the same rows
+    rows = np.array([0, n // 2, n - 1])
+    np.testing.assert_allclose(O.block_forward(x, segs, sets, sos, mods, pos, mask, dims, rows=rows),
+                               got[rows], rtol=0, atol=1e-12)
+
+
+def test_block_gate_zero_is_identity():
+    r = rng(9)
+    x = r.normal(size=(10, TINY.hidden))
+    sets = [rand_set(r, TINY)]
+    mods = rand_mods(r, TINY, gate_zero=True)
+    pos = O.positions(4, (2, 3))
+    out = O.block_forward(x, (4, 6, 0), sets, (0, 0, 0), mods, pos, O.MASK_FULL, TINY)
+    np.testing.assert_array_equal(out, x)
+
+
+def test_double_block_with_equal_sets_is_single_block():
+    r = rng(10)
+    s = rand_set(r, TINY)
+    m = rand_mods(r, TINY, n=1)[0]
+    x = r.normal(size=(9, TINY.hidden))
+    pos = O.positions(3, (2, 3))
+    a = O.block_forward(x, (3, 6, 0), [s, s], (0, 1, 1), [m, m, m], pos, O.MASK_FULL, TINY)
+    b = O.block_forward(x, (3, 6, 0), [s], (0, 0, 0), [m, m, m], pos, O.MASK_FULL, TINY)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_per_mode_block_equals_separate_streams():
+    """Per-mode blocks = each stream run on its own with its own weights (the stream sees
+    only itself)."""
+    r = rng(11)
+    segs = (4, 6, 6)
+    n = sum(segs)
+    sets = [rand_set(r, TINY) for _ in range(3)]
+    mods = rand_mods(r, TINY)
+    x = r.normal(size=(n, TINY.hidden))
+    pos = O.positions(4, (2, 3), ((2, 3),))
+    joint = O.block_forward(x, segs, sets, (0, 1, 2), mods, pos, O.MASK_SEGMENT, TINY)
+    start = 0
+    for s in range(3):
+        sl = slice(start, start + segs[s])
+        alone = O.block_forward(x[sl], (segs[s], 0, 0), [sets[s]], (0, 0, 0),
+                                [mods[s]] * 3, pos[sl], O.MASK_FULL, TINY)
+        np.testing.assert_allclose(joint[sl], alone, rtol=0, atol=1e-12)
+        start += segs[s]
+
+
+def test_joint_block_with_equal_mods_is_single_block():
+    r = rng(12)
+    s = rand_set(r, TINY)
+    m = rand_mods(r, TINY, n=1)[0]
+    x = r.normal(size=(10, TINY.hidden))
+    pos = O.positions(2, (2, 2), ((2, 2),))
+    a = O.block_forward(x, (2, 4, 4), [s], (0, 0, 0), [m, m, m], pos, O.MASK_FULL, TINY)
+    b = O.block_forward(x, (10, 0, 0), [s], (0, 0, 0), [m, m, m], pos, O.MASK_FULL, TINY)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------ conditioning, head, Euler
+
+def test_timestep_embedding_closed_forms():
+    e0 = O.timestep_embedding(0.0, 256)
+    np.testing.assert_array_equal(e0, np.concatenate([np.ones(128), np.zeros(128)]))
+    e = O.timestep_embedding(0.37, 256)
+    np.testing.assert_allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, atol=1e-15)
+    assert abs(e[0] - math.cos(370.0)) < 1e-12          # f_0 = 1: angle 1000 t
+    assert abs(e[128 + 64] - math.sin(370.0 * 10000 ** -0.5)) < 1e-12
+
+
+def test_modulation_and_cond_match_library():
+    r = rng(13)
+    d = 64
+    w_mod = r.normal(size=(3 * d, d))
+    c = r.normal(size=d)
+    ref = F.linear(F.silu(torch.tensor(c)), torch.tensor(w_mod)).numpy()
+    np.testing.assert_allclose(O.modulation(w_mod, c), ref, atol=1e-12)
+    w1, w2 = r.normal(size=(d, 32)), r.normal(size=(d, d))
+    e = torch.tensor(O.timestep_embedding(0.5, 32))
+    ref = F.linear(F.silu(F.linear(e, torch.tensor(w1))), torch.tensor(w2)).numpy()
+    np.testing.assert_allclose(O.cond_vector(0.5, w1, w2), ref, atol=1e-12)
+
+
+def test_cond_rows_per_token_type():
+    r = rng(14)
+    w1, w2 = r.normal(size=(16, 32)), r.normal(size=(16, 16))
+    c2 = O.cond_rows(O.ARCH_FLUX2, 0.7, w1, w2)
+    assert np.array_equal(c2[0], c2[1]) and np.array_equal(c2[1], c2[2])
+    c3 = O.cond_rows(O.ARCH_FLUX3, 0.7, w1, w2)
+    assert np.array_equal(c3[0], O.cond_vector(0.0, w1, w2))
+    assert np.array_equal(c3[2], c3[0]) and not np.allclose(c3[1], c3[0])
+
+
+def test_final_layer_matches_library():
+    r = rng(15)
+    d, c = 64, 16
+    x = r.normal(size=(5, d))
+    cond = r.normal(size=d)
+    w_fmod, w_out = r.normal(size=(2 * d, d)), r.normal(size=(c, d))
+    fm = F.linear(F.silu(torch.tensor(cond)), torch.tensor(w_fmod))
+    y = F.layer_norm(torch.tensor(x), (d,), eps=1e-6) * (1 + fm[d:]) + fm[:d]
+    ref = F.linear(y, torch.tensor(w_out)).numpy()
+    np.testing.assert_allclose(O.final_layer(x, cond, w_fmod, w_out, 1e-6), ref, atol=1e-12)
+
+
+def test_euler_closed_forms():
+    ts = O.euler_schedule(4)
+    assert ts[0] == 1.0 and ts[-1] == 0.0 and np.all(np.diff(ts) < 0)
+    lat = rng(16).normal(size=(6, 4))
+    c = 0.25
+    out = lat.copy()
+    for i in range(4):
+        out = O.euler_step(out, np.full_like(lat, c), ts[i], ts[i + 1])
+    np.testing.assert_allclose(out, lat + c, atol=1e-15)     # sum of steps = 1
+    np.testing.assert_array_equal(O.euler_step(lat, np.zeros_like(lat), 1.0, 0.5), lat)
+
+
+def tiny_model(arch, r, n_stream=1, n_shared=1, zero_out=False):
+    dims = TINY
+    d, c = dims.hidden, dims.in_channels
+    nsets = 2 if arch == O.ARCH_FLUX2 else 3
+    m = O.Model(arch=arch, dims=dims, n_stream=n_stream, n_shared=n_shared,
+                img_in=r.normal(0, 0.1, (d, c)), temb_l1=r.normal(0, 0.1, (d, dims.time_dim)),
+                temb_l2=r.normal(0, 0.1, (d, d)), final_mod=r.normal(0, 0.05, (2 * d, d)),
+                final_out=np.zeros((c, d)) if zero_out else r.normal(0, 0.05, (c, d)))
+    m.mods = [[r.normal(0, 0.05, (3 * d, d)) for _ in range(nsets)], [r.normal(0, 0.05, (3 * d, d))]]
+    m.blocks = [[rand_set(r, dims) for _ in range(nsets)] for _ in range(n_stream)] + \
+               [[rand_set(r, dims)] for _ in range(n_shared)]
+    return m
+
+
+def test_denoise_zero_head_keeps_noise():
+    r = rng(17)
+    m = tiny_model(O.ARCH_FLUX2, r, zero_out=True)
+    noise = r.normal(size=(4, TINY.in_channels))
+    txt = r.normal(size=(3, TINY.hidden))
+    np.testing.assert_array_equal(O.denoise(m, noise, txt, (2, 2), 3), noise)
+
+
+def test_forward_stack_is_block_composition():
+    """forward() = img_in, the planned blocks, then the output head on image rows."""
+    r = rng(18)
+    for arch in (O.ARCH_FLUX2, O.ARCH_FLUX3):
+        m = tiny_model(arch, r)
+        lat = r.normal(size=(4, TINY.in_channels))
+        ref_lat = r.normal(size=(4, TINY.in_channels))
+        txt = r.normal(size=(3, TINY.hidden))
+        seen = []
+        v = O.forward(m, lat, txt, (2, 2), 0.6, ref_lat, (2, 2), block_hook=lambda b, x: seen.append(x.copy()))
+        assert len(seen) == 2
+        np.testing.assert_allclose(seen[0][3:7], lat @ m.img_in.T, atol=1e-14)
+        np.testing.assert_allclose(seen[0][7:], ref_lat @ m.img_in.T, atol=1e-14)
+        assert v.shape == (4, TINY.in_channels)
+        # the per-mode block of FLUX.3 keeps streams apart: changing the reference latents
+        # does not change the image rows after the first (per-mode) block
+        if arch == O.ARCH_FLUX3:
+            seen2 = []
+            O.forward(m, lat, txt, (2, 2), 0.6, ref_lat * 2.0, (2, 2),
+                      block_hook=lambda b, x: seen2.append(x.copy()))
+            np.testing.assert_allclose(seen2[1][:7], seen[1][:7], atol=1e-13)
+            assert not np.allclose(seen2[1][7:], seen[1][7:])
+
+
+# ------------------------------------------------------------------ the pins catch planted slips
+
+def _wrong_rope(x, angles):
+    n, h, d = x.shape
+    xr = x.reshape(n, h, 4, 16, 2)
+    c, s = np.cos(angles)[:, None], np.sin(angles)[:, None]
+    out = np.empty_like(xr)
+    out[..., 0] = xr[..., 0] * c + xr[..., 1] * s      # sign slip
+    out[..., 1] = -xr[..., 0] * s + xr[..., 1] * c
+    return out.reshape(n, h, d)
+
+
+def _wrong_layer_norm(x, eps):
+    return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + eps + 1e-3)
+
+
+def test_pins_catch_planted_slips(monkeypatch):
+    monkeypatch.setattr(O, "apply_rope", _wrong_rope)
+    with pytest.raises(AssertionError):
+        test_rope_matches_complex_rotation()
+    with pytest.raises(AssertionError):
+        test_block_matches_library_composition(O.MASK_FULL, (0, 0, 0), (4, 6, 0))
+    monkeypatch.undo()
+    monkeypatch.setattr(O, "layer_norm", _wrong_layer_norm)
+    with pytest.raises(AssertionError):
+        test_layer_norm_matches_library()
+    monkeypatch.undo()
+    # a slightly wrong activation
+    orig = O.silu
+    monkeypatch.setattr(O, "silu", lambda z: orig(z) * 1.0001)
+    with pytest.raises(AssertionError):
+        test_silu_matches_library()
