@@ -1,0 +1,181 @@
+/*
+ * dit.h - C ABI of the MI355X (gfx950) denoising-transformer library.
+ *
+ * The library computes the forward pass of the FLUX.2-klein / FLUX.3-Klein latent
+ * flow-matching image transformer and its few-step Euler sampling loop on one GPU.
+ * Its shape follows the small C library described for FLUX.2-klein: load a context,
+ * generate, free it, read a thread-local error string, NULL / negative on failure
+ * ("Flux 2 Klein: Reine C-basierte Inferenz", section "C-Bibliotheks-API"; hakusoku
+ * FLUX.2-klein-4B article, sections "CライブラリAPI" and "エラーハンドリング").  It is narrowed
+ * to the transformer: text embeddings come in precomputed (cf. the embeddings option,
+ * hakusoku article, "コマンドラインオプション") and latents go out unpacked by any VAE.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "dev" are device memory owned by the caller (for example torch
+ *     tensors).  They must stay valid until the work queued on `stream` has finished.
+ *     Pointers marked "host" are read before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is queued
+ *     asynchronously on it; nothing synchronises unless DIT_DEBUG_SYNC=1 is set in the
+ *     environment, which synchronises and checks after every kernel.
+ *   - One context serves one stream at a time: calls that overlap on one context race on
+ *     its workspace.
+ *   - Row-major everywhere.  "D" = hidden, "C" = in_channels, N = n_txt + n_img + n_ref.
+ *   - Return values: 0 on success, or DIT_EINVAL / DIT_ENOMEM / DIT_EHIP / DIT_EUNSUPPORTED;
+ *     dit_ctx_create returns NULL on failure.  dit_get_error() then describes the failure.
+ *     Faults of queued kernels surface at a later call or synchronisation.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dit_ctx dit_ctx;
+
+/* element types.  Host weight data: DIT_F32 or DIT_BF16.  Compute types:
+ *   DIT_F32   fp32 throughout (no MFMA)
+ *   DIT_BF16  bf16 MFMA operands and activations, fp32 accumulation, fp32 residual
+ *   DIT_F16   fp16 MFMA operands and activations (bf16 weights are held exactly, up to the
+ *             fp16 subnormal grid below 2^-14), fp32 accumulation, fp32 residual; same MFMA
+ *             rate as bf16 on gfx950 with 8x finer operand rounding; activations saturate at
+ *             +-65504 */
+enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2 };
+
+/* model families.
+ * DIT_FLUX2: n_stream_blocks double-stream blocks (separate text / image weights, joint
+ *   attention from the first block), then n_shared_blocks single-stream blocks
+ *   ("Flux 2 Klein: Reine C-basierte Inferenz", "Modellarchitektur und Leistung": 5 double,
+ *   20 single, hidden 3072, 24 heads).
+ * DIT_FLUX3: n_stream_blocks per-mode blocks (text, image and reference streams each with
+ *   their own weights, attending only within their stream), then n_shared_blocks joint
+ *   blocks sharing one weight set, every token attending every token; image tokens are
+ *   modulated with t, text and reference tokens with t = 0 ("FLUX.3 Image Klein in
+ *   Diffusers", sections "Entkoppelte Vorverarbeitung und gemeinsame Attention-Blöcke" and
+ *   "Modulation pro Token-Typ, Flow-Map-Destillation und 4D-RoPE"). */
+enum { DIT_FLUX2 = 0, DIT_FLUX3 = 1 };
+
+/* attention masks: DEFAULT = the block kind's own (per-mode: SEGMENT, others: FULL) */
+enum { DIT_MASK_DEFAULT = -1, DIT_MASK_FULL = 0, DIT_MASK_SEGMENT = 1 };
+
+/* error codes */
+enum { DIT_OK = 0, DIT_EINVAL = -1, DIT_ENOMEM = -2, DIT_EHIP = -3, DIT_EUNSUPPORTED = -4 };
+
+typedef struct {
+  int arch;             /* DIT_FLUX2 or DIT_FLUX3 */
+  int hidden;           /* D; multiple of 256, <= 4096, = heads * head_dim  (3072) */
+  int heads;            /*                                                  (24)   */
+  int head_dim;         /* must be 128: four 32-dim RoPE axes (t, h, w, l)  (128)  */
+  int mlp_hidden;       /* F, SwiGLU width; multiple of 128                 (9216) */
+  int in_channels;      /* C, latent channels per token; multiple of 64     (128)  */
+  int time_dim;         /* sinusoidal timestep embedding width; mult. of 16 (256)  */
+  int n_stream_blocks;  /* double (FLUX2) or per-mode (FLUX3) blocks        (5)    */
+  int n_shared_blocks;  /* single (FLUX2) or joint (FLUX3) blocks           (20/28) */
+  int max_tokens;       /* largest N any call will use (sizes the workspace)       */
+  int compute;          /* DIT_F16, DIT_BF16 or DIT_F32 (see above)                 */
+  float rope_theta;     /* RoPE base (10000)      */
+  float ln_eps;         /* LayerNorm epsilon (1e-6) */
+  float rms_eps;        /* QK RMSNorm epsilon (1e-6) */
+} dit_config;
+
+/* One named weight tensor in host memory, row-major [out, in].  dtype DIT_F32: float
+ * values; DIT_BF16: uint16 bf16 bit patterns.  Values are converted to the compute type
+ * (round-to-nearest-even) and copied during dit_ctx_create; the caller keeps ownership.
+ * Names and shapes (b = block index, s = weight set):
+ *   img_in      [D, C]       input projection of image and reference latents
+ *   temb.l1     [D, time_dim], temb.l2 [D, D]   timestep MLP
+ *   final.mod   [2D, D]      output-head modulation (shift || scale)
+ *   final.out   [C, D]       output projection to the velocity
+ *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) of stream blocks, per set
+ *   mod.1.s0    [3D, D]      modulation of shared (single / joint) blocks
+ *   blk{b}.s{s}.w1 [3D+2F, D]  rows Q | K | V | gate | up (head-major Q, K, V)
+ *   blk{b}.s{s}.w2 [D, D+F]    output projection of [attention || SwiGLU]
+ *   blk{b}.s{s}.qn, .kn [128]  query / key RMSNorm scales
+ * Sets: stream blocks have 2 (FLUX2: text, image; references use the image set) or 3
+ * (FLUX3: text, image, reference); shared blocks have 1. */
+typedef struct {
+  const char *name;
+  const void *data;     /* host */
+  int64_t numel;
+  int dtype;            /* DIT_F32 or DIT_BF16 */
+} dit_tensor;
+
+/* Validate cfg, upload and repack all weights, allocate the workspace for max_tokens.
+ * Every tensor listed above must be present exactly once with the right numel; unknown
+ * names are an error.  Returns NULL on failure (no device, bad config, missing or
+ * misshaped tensor, out of device memory). */
+dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *weights, int n_weights);
+
+/* Release all device memory of ctx (synchronises the device first).  NULL is a no-op. */
+void dit_ctx_free(dit_ctx *ctx);
+
+/* One transformer block in place on the residual stream.
+ *   x     dev fp32 [N, D], in/out; rows ordered text || image || reference
+ *   pos   dev fp32 [N, 4] RoPE coordinates (t, h, w, l) per token
+ *   cond  dev fp32 [3, D] conditioning vector per segment (text, image, reference);
+ *         rows of empty segments are ignored but must be readable
+ *   mask  DIT_MASK_DEFAULT / FULL / SEGMENT
+ * Computes x <- x + gate_s * ([attention || SwiGLU](LN(x) * (1 + scale_s) + shift_s) W2^T)
+ * with (shift, scale, gate)_s = mod.{kind}.s{set(s)} . SiLU(cond[s])
+ * ("FLUX.3 Image Klein in Diffusers": parallel attention and SwiGLU MLP on one normalised
+ * input, QK RMSNorm, adaLN from the timestep embedding, 4D RoPE).
+ * Requires 0 <= block < n_stream_blocks + n_shared_blocks, 1 <= N <= max_tokens. */
+int dit_block_forward(dit_ctx *ctx, int block, float *x, int n_txt, int n_img, int n_ref,
+                      const float *pos, const float *cond, int mask, void *stream);
+
+/* One full transformer call at time t: v = velocity of the image tokens.
+ *   lat      dev fp32 [gh*gw, C]      packed image latents (16x16 px per token)
+ *   ref_lat  dev fp32 [rgh*rgw, C]    reference latents, or NULL with rgh = rgw = 0
+ *   txt      dev fp32 [n_txt, D]      text embeddings (enter the residual as they are)
+ *   v        dev fp32 [gh*gw, C]      output
+ * Positions: text i -> (0,0,0,i), image (r,c) -> (0,r,c,0), reference (r,c) -> (0,r,c,-1)
+ * ("FLUX.3 Image Klein in Diffusers", "Modulation pro Token-Typ, Flow-Map-Destillation und
+ * 4D-RoPE"). */
+int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt,
+                int n_txt, int gh, int gw, int rgh, int rgw, float t, float *v, void *stream);
+
+/* Few-step Euler sampling from t = 1 (noise) to t = 0 (clean) on the uniform schedule
+ * t_i = 1 - i/n_steps: lat <- lat + (t_i - t_{i+1}) * v(lat, t_i).
+ *   lat   dev fp32 [gh*gw, C], in/out.  seed >= 0: first filled with N(0,1) noise from
+ *         Philox4x32-10 (counter = element index / 4, key = seed) and Box-Muller;
+ *         seed < 0: lat is used as given.
+ * Other arguments as in dit_forward.  n_steps >= 1. */
+int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, int gw,
+                const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed,
+                void *stream);
+
+/* Fill dst (dev fp32, n elements) with the N(0,1) noise dit_denoise draws for seed. */
+int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
+
+/* Workspace buffer of the last call, for inspection after the stream has finished:
+ * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
+ * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32
+ * [2][3][3][3D]: kind, set, segment, shift || scale || gate), "x" (fp32 [N, D], the
+ * residual stream of dit_forward / dit_denoise after the last block).  *dtype receives
+ * the element type (compute type for xm, qkv, cat; DIT_F32 for mod and x); *row_stride the
+ * elements per row.  NULL for an unknown name. */
+const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t *row_stride);
+
+/* Per-kernel timing, for benchmarks.  dit_profile_start makes the following calls record a
+ * hipEvent on their stream before and after each kernel launch (up to max_launches launches;
+ * later ones are not timed).  dit_profile_stop ends recording and waits for the last event.
+ * dit_profile_get sums, over the recorded launches of one kernel class, the elapsed time (ms),
+ * the launch count, and the algorithmic work the library attributes to them: FLOPs (GEMMs,
+ * attention: 4 * D per attended query-key pair) and HBM bytes (memory-bound kernels).
+ * Kernel classes: "ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2",
+ * "conditioning", "embed", "final". */
+int dit_profile_start(dit_ctx *ctx, int max_launches);
+int dit_profile_stop(dit_ctx *ctx);
+int dit_profile_get(dit_ctx *ctx, const char *kernel, double *ms, int64_t *launches,
+                    double *flops, double *bytes);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *dit_get_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

@@ -1,0 +1,231 @@
+// MFMA GEMM (16-bit operands: bf16 or fp16, fp32 accumulation) for the block's two fused
+// projections on gfx950.
+//
+//   out[token][n] = sum_k X[token][k] * W[n][k]       (X = activations, W = [N, K] weights)
+//
+// Both operands are K-contiguous, which is the per-lane layout of v_mfma_f32_32x32x16_{bf16,f16}
+// (lane l holds 8 consecutive k of row l%32, k-half l/32).  The weight tile is the MFMA A
+// operand and the token tile the B operand, so each lane's accumulator holds one token and
+// four consecutive output features: stores are 8-byte (bf16) or 16-byte (fp32) vectors.
+//
+// Workgroup tile 256 features x BM tokens x 64 k, 8 waves (WN x WM), LDS double-buffered
+// with one barrier per k-tile: global loads for tile k+1 are in flight while the MFMAs of
+// tile k run.  LDS rows are 128 B (64 bf16) with the 16-byte chunk index XOR-swizzled by
+// (row & 7), so the 32 rows one ds_read_b128 touches spread over all banks.
+//
+// Epilogues (the fusions of the block):
+//   EPI_QKV_SWIGLU  linear1: columns [0, split) are Q|K|V and go to the qkv buffer; the
+//                   rest holds gate and up rows interleaved in 32-row chunks, so one lane
+//                   owns gate and up of the same feature and writes SiLU(gate) * up
+//                   ("FLUX.3 Image Klein in Diffusers", "Entkoppelte Vorverarbeitung ...":
+//                   the MLP is a SwiGLU MLP run in parallel with attention).
+//   EPI_RESID       linear2: x[token] += gate_seg(token) * acc (gated residual, fp32).
+//   EPI_STORE_F32   plain fp32 store or out += alpha * acc.
+//
+// Workgroups are remapped so that each of the 8 XCDs receives a contiguous range of tiles
+// (tokens fastest), keeping a weight tile's readers on one L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+constexpr int BN = 256;  // output features per workgroup
+constexpr int BK = 64;   // k per LDS stage
+
+__device__ __forceinline__ int swz(int row, int chunk) {  // byte offset inside a tile
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+template <typename T, int BM, int WN, int WM, int EPI>
+__global__ __launch_bounds__(64 * WN *WM) void k_gemm_mfma(GemmArgs a, int m_tiles_total,
+                                                            int t_before1, int t_before2,
+                                                            int total_tiles) {
+  constexpr int NT = 64 * WN * WM;
+  constexpr int WTN = BN / WN, WTM = BM / WM;  // wave tile
+  constexpr int FS = WTN / 32, TS = WTM / 32;  // 32x32 sub-tiles per wave
+  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 16-byte loads per thread per stage
+  constexpr int STAGE = (BN + BM) * BK * 2;
+  static_assert(LA * NT == BN * 8 && LB * NT == BM * 8, "tile/threads mismatch");
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  // XCD-contiguous tile id: hardware places workgroup b on XCD b % 8
+  const int per = gridDim.x >> 3;
+  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lid >= total_tiles) return;
+  const int tile_n = lid / m_tiles_total;
+  const int mt = lid - tile_n * m_tiles_total;
+  const int gi = (mt >= t_before1) + (mt >= t_before2);
+  const int lmt = mt - (gi == 0 ? 0 : (gi == 1 ? t_before1 : t_before2));
+  const GemmGroup grp = a.g[gi];
+  const int n0 = tile_n * BN;
+  const int m0 = lmt * BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WN, wm = wave / WN;
+  const int K = a.k;
+  typedef typename Mfma<T>::v8 V8;
+  const T *W = reinterpret_cast<const T *>(grp.w) + (size_t)n0 * K;
+  const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
+  const int lchunk = tid & 7, lrow = tid >> 3;
+
+  u32x4 ra[LA], rb[LB];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK + lchunk * 8;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      ra[i] = *reinterpret_cast<const u32x4 *>(W + (size_t)(lrow + i * (NT / 8)) * K + k0);
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      rb[i] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + i * (NT / 8)) * a.ldx + k0);
+  };
+  auto sstore = [&](int buf) {
+    char *As = smem + buf * STAGE;
+    char *Bs = As + BN * 128;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      *reinterpret_cast<u32x4 *>(As + swz(lrow + i * (NT / 8), lchunk)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      *reinterpret_cast<u32x4 *>(Bs + swz(lrow + i * (NT / 8), lchunk)) = rb[i];
+  };
+
+  f32x16 acc[FS][TS];
+#pragma unroll
+  for (int i = 0; i < FS; ++i)
+#pragma unroll
+    for (int j = 0; j < TS; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int KT = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int r32 = lane & 31, hk = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const char *As = smem + buf * STAGE;
+    const char *Bs = As + BN * 128;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + hk;
+      V8 af[FS], bfr[TS];
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+        af[i] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + i * 32 + r32, ch));
+#pragma unroll
+      for (int j = 0; j < TS; ++j)
+        bfr[j] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + j * 32 + r32, ch));
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+#pragma unroll
+        for (int j = 0; j < TS; ++j)
+          acc[i][j] = Mfma<T>::mma(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue: lane owns token (r32) and features 8g + 4hk + {0..3}
+  const int fbase = n0 + wn * WTN + 4 * hk;
+#pragma unroll
+  for (int j = 0; j < TS; ++j) {
+    const int m = m0 + wm * WTM + j * 32 + r32;  // row inside the group
+    if (m >= grp.rows) continue;
+    const int tok = grp.out_row0 + m;
+    if constexpr (EPI == EPI_RESID) {
+      const int seg = segment_of(tok, a.b1, a.b2);
+      const float *gate = a.gate[seg];
+      float *xr = a.x + (size_t)tok * a.ldres;
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = fbase + i * 32 + 8 * g;
+          f32x4 gv = *reinterpret_cast<const f32x4 *>(gate + n);
+          f32x4 xv = *reinterpret_cast<const f32x4 *>(xr + n);
+          xv.x += gv.x * acc[i][j][4 * g + 0];
+          xv.y += gv.y * acc[i][j][4 * g + 1];
+          xv.z += gv.z * acc[i][j][4 * g + 2];
+          xv.w += gv.w * acc[i][j][4 * g + 3];
+          *reinterpret_cast<f32x4 *>(xr + n) = xv;
+        }
+    } else if constexpr (EPI == EPI_QKV_SWIGLU) {
+      if (n0 < a.split) {
+        T *qr = reinterpret_cast<T *>(a.qkv) + (size_t)tok * a.ldq;
+#pragma unroll
+        for (int i = 0; i < FS; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4(qr + fbase + i * 32 + 8 * g, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+      } else {
+        // sub-tiles (2p, 2p+1) = gate / up rows of SwiGLU features [32c, 32c + 32)
+        T *cr = reinterpret_cast<T *>(a.cat) + (size_t)tok * a.ldc + a.cat_off;
+        const int jb = (n0 - a.split + wn * WTN) / 2;  // first SwiGLU feature of the wave
+#pragma unroll
+        for (int p = 0; p < FS / 2; ++p)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              o[r] = silu(acc[2 * p][j][4 * g + r]) * acc[2 * p + 1][j][4 * g + r];
+            store4(cr + jb + p * 32 + 8 * g + 4 * hk, o[0], o[1], o[2], o[3]);
+          }
+      }
+    } else {
+      float *orow = a.out + (size_t)tok * a.ldo;
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = fbase + i * 32 + 8 * g;
+          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                     acc[i][j][4 * g + 3]};
+          if (a.accumulate) {
+            f32x4 o = *reinterpret_cast<const f32x4 *>(orow + n);
+            v = o + a.alpha * v;
+          }
+          *reinterpret_cast<f32x4 *>(orow + n) = v;
+        }
+    }
+  }
+}
+
+template <typename T, int BM, int WN, int WM, int EPI>
+hipError_t launch(const GemmArgs &a, hipStream_t s) {
+  int tb[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 3; ++i) tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
+  const int m_tiles = tb[3];
+  if (m_tiles == 0) return hipSuccess;
+  const int total = m_tiles * (a.n / BN);
+  const int grid = (total + 7) / 8 * 8;
+  k_gemm_mfma<T, BM, WN, WM, EPI><<<grid, 64 * WN * WM, 0, s>>>(a, m_tiles, tb[1], tb[2], total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t dispatch(const GemmArgs &a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_QKV_SWIGLU: return launch<T, 256, 2, 4, EPI_QKV_SWIGLU>(a, s);
+    case EPI_RESID: return launch<T, 256, 2, 4, EPI_RESID>(a, s);
+    case EPI_STORE_F32: return launch<T, 256, 2, 4, EPI_STORE_F32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s) {
+  if (a.n % BN || a.k % BK || a.ng < 1 || a.ng > 3) return hipErrorInvalidValue;
+  if (op == OP_BF16) return dispatch<bf16>(a, epi, s);
+  if (op == OP_F16) return dispatch<f16>(a, epi, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dit

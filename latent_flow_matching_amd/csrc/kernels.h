@@ -1,0 +1,86 @@
+// Launchers of the gfx950 kernels (internal to the library; the C ABI is include/dit.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// Element types of activations / weights (same codes as the C ABI's compute types).
+enum ElemType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
+
+// Token rows are ordered text [0, b1) | image [b1, b2) | reference [b2, n).
+struct Segs {
+  int b1, b2, n;
+};
+
+// --- GEMM row groups: up to three row ranges, each with its own input rows and weights.
+struct GemmGroup {
+  const void *x;   // first input row of the group (row stride ldx elements)
+  const void *w;   // weights [N, K] row-major
+  int rows;        // rows in the group
+  int out_row0;    // token index of the first row (output row; segment lookup)
+};
+
+enum Epilogue {
+  EPI_STORE_F32 = 0,   // out[r][n] = acc  or  out[r][n] += alpha * acc
+  EPI_QKV_SWIGLU = 1,  // cols < split -> qkv; cols >= split (gate/up interleaved by 32) -> SiLU(g)*u
+  EPI_RESID = 2,       // x[r][n] += gate_seg(r)[n] * acc
+};
+
+struct GemmArgs {
+  GemmGroup g[3];
+  int ng;
+  int n, k;            // output columns, reduction length
+  int ldx;             // input row stride (elements)
+  // EPI_STORE_F32
+  float *out; int ldo; int accumulate; float alpha;
+  // EPI_QKV_SWIGLU
+  void *qkv; int ldq; int split; void *cat; int ldc; int cat_off;
+  // EPI_RESID
+  float *x; int ldres; const float *gate[3]; int b1, b2;
+};
+
+// MFMA GEMM: input and weights of 16-bit type op (OP_BF16 / OP_F16), fp32 accumulation.
+// n % 256 == 0, k % 64 == 0, input rows readable up to 256 past each group's end.
+hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s);
+// fp32-accumulating general GEMM with fp32 inputs and weights of type w_type.
+// n % 64 == 0, k % 16 == 0; any rows; input rows are not read past a group's end.
+hipError_t gemm_simple(const GemmArgs &a, int epi, int w_type, hipStream_t s);
+
+// --- attention
+struct AttnGroup {
+  int q0, q1, k0, k1;  // query rows [q0, q1) attend keys [k0, k1)
+};
+struct AttnArgs {
+  const void *qkv; int ldqkv; int d_model;  // q at column h*128, k at d_model + h*128
+  const void *vt; int ldv;                  // MFMA path: V transposed [heads][128][ldv]
+  void *out; int ldo;                       // out[q][h*128 + d]
+  AttnGroup g[3]; int ng;
+  int heads;
+  float scale;                              // 1/sqrt(head_dim)
+};
+hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s);
+hipError_t attention_f32(const AttnArgs &a, hipStream_t s);  // V read from qkv at 2*d_model
+
+// --- norms, RoPE, small ops
+hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, int rgh, int rgw, hipStream_t s);
+hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream_t s);
+// out[r] = LN(x[r]) * (1 + scale_seg) + shift_seg, mod_seg[s] = [shift | scale | ...]
+hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
+                       int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
+                       hipStream_t s);
+// q, k of every (token, head): RMSNorm with the segment's scale, then RoPE, in place;
+// 16-bit paths also write V transposed into vt (and zeros for columns [n, n+64)).
+hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, void *vt, int ldv,
+                        const float *cs, int n, const float *const qn[3],
+                        const float *const kn[3], Segs segs, float eps, hipStream_t s);
+// y[v][i] = sum_k W[i][k] * act(x[v][k]) for v < nvec (x, y contiguous [nvec][k|rows])
+hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
+                int silu_in, hipStream_t s);
+// e[v] = [cos(1000 t_v f_j), sin(1000 t_v f_j)], f_j = 10000^(-j/(dim/2))
+hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s);
+hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,
+                         hipStream_t s);
+hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s);
+
+}  // namespace dit

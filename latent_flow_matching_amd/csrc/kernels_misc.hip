@@ -1,0 +1,411 @@
+// Memory-bound kernels of the block and the conditioning path (gfx950):
+//   positions + RoPE tables, LayerNorm + adaLN modulation, QK RMSNorm + RoPE (+ V transpose),
+//   GEMV for timestep MLP and modulation, timestep embedding, Philox noise.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+// ------------------------------------------------------------------------------------------
+// 4D RoPE coordinates: text i -> (0,0,0,i), image (r,c) -> (0,r,c,0), reference (r,c) ->
+// (0,r,c,-1), tokens ordered text | image | reference, row-major inside an image
+// ("FLUX.3 Image Klein in Diffusers", section "Modulation pro Token-Typ, Flow-Map-Destillation
+// und 4D-RoPE").  The page's row/2, col/2 counts VAE-latent cells, two per token side.
+// ------------------------------------------------------------------------------------------
+__global__ void k_positions(float *pos, int n_txt, int gw, int n_img, int rgw, int n_ref) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  int n = n_txt + n_img + n_ref;
+  if (i >= n) return;
+  float h = 0.f, w = 0.f, l = 0.f;
+  if (i < n_txt) {
+    l = (float)i;
+  } else if (i < n_txt + n_img) {
+    int j = i - n_txt;
+    h = (float)(j / gw);
+    w = (float)(j % gw);
+  } else {
+    int j = i - n_txt - n_img;
+    h = (float)(j / rgw);
+    w = (float)(j % rgw);
+    l = -1.f;
+  }
+  f32x4 v = {0.f, h, w, l};
+  *reinterpret_cast<f32x4 *>(pos + 4 * (size_t)i) = v;
+}
+
+hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, int rgh, int rgw,
+                          hipStream_t s) {
+  int n = n_txt + gh * gw + rgh * rgw;
+  if (n <= 0) return hipSuccess;
+  k_positions<<<(n + 255) / 256, 256, 0, s>>>(pos, n_txt, gw > 0 ? gw : 1, gh * gw,
+                                               rgw > 0 ? rgw : 1, rgh * rgw);
+  return hipGetLastError();
+}
+
+// cs[i][p] = (cos, sin) of pos[i][p/16] * theta^(-2 (p%16) / 32), p = 0..63: one rotation
+// angle per adjacent pair of the four 32-dim axis slices (t, h, w, l).  Angles in fp64.
+__global__ void k_rope_table(float *cs, const float *pos, int n, double log_theta) {
+  int i = blockIdx.x;
+  int p = threadIdx.x;  // 64 threads
+  if (i >= n) return;
+  int axis = p >> 4, j = p & 15;
+  double freq = exp(-log_theta * (2.0 * j) / 32.0);
+  double ang = (double)pos[4 * (size_t)i + axis] * freq;
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  cs[(size_t)i * 128 + 2 * p] = (float)cn;
+  cs[(size_t)i * 128 + 2 * p + 1] = (float)sn;
+}
+
+hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_rope_table<<<n, 64, 0, s>>>(cs, pos, n, log((double)theta));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// LayerNorm without affine parameters, then y * (1 + scale_s) + shift_s with the segment's
+// modulation ("FLUX.3 Image Klein in Diffusers", "Modulation pro Token-Typ ...": each block
+// starts with a parameter-free LayerNorm whose scale and shift come from the timestep
+// embedding).  One wave per row; the row stays in registers (D <= 4096, D % 256 == 0).
+// ------------------------------------------------------------------------------------------
+constexpr int kLnMaxVec = 16;  // float4 per lane -> D <= 64 * 4 * 16 = 4096
+
+template <typename TO>
+__global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const float *x, int ldx,
+                                                      int rows, int row0, int d, float eps,
+                                                      const float *m0, const float *m1,
+                                                      const float *m2, int b1, int b2) {
+  int lane = threadIdx.x & 63;
+  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  int tok = row0 + r;
+  const float *xr = x + (size_t)tok * ldx;
+  int nv = d >> 8;
+  f32x4 v[kLnMaxVec];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      v[i] = *reinterpret_cast<const f32x4 *>(xr + (i * 64 + lane) * 4);
+      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  float mean = wave_sum(sum) / (float)d;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+      sq += (a * a + b * b) + (c * c + e * e);
+    }
+  }
+  float var = wave_sum(sq) / (float)d;
+  float rstd = 1.0f / sqrtf(var + eps);
+  int seg = segment_of(tok, b1, b2);
+  const float *mod = seg == 0 ? m0 : (seg == 1 ? m1 : m2);
+  const float *shift = mod, *scale = mod + d;
+  TO *orow = out + (size_t)r * ldo;
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      int c = (i * 64 + lane) * 4;
+      f32x4 sh = *reinterpret_cast<const f32x4 *>(shift + c);
+      f32x4 sc = *reinterpret_cast<const f32x4 *>(scale + c);
+      float y0 = (v[i].x - mean) * rstd * (1.f + sc.x) + sh.x;
+      float y1 = (v[i].y - mean) * rstd * (1.f + sc.y) + sh.y;
+      float y2 = (v[i].z - mean) * rstd * (1.f + sc.z) + sh.z;
+      float y3 = (v[i].w - mean) * rstd * (1.f + sc.w) + sh.w;
+      store4(orow + c, y0, y1, y2, y3);
+    }
+  }
+}
+
+template <typename TO>
+void launch_ln(void *out, int ldo, const float *x, int ldx, int rows, int row0, int d, float eps,
+               const float *const m[3], Segs sg, hipStream_t s) {
+  k_ln_modulate<TO><<<(rows + 3) / 4, 256, 0, s>>>((TO *)out, ldo, x, ldx, rows, row0, d, eps,
+                                                   m[0], m[1], m[2], sg.b1, sg.b2);
+}
+
+hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
+                       int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
+                       hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 256 || d > 64 * 4 * kLnMaxVec) return hipErrorInvalidValue;
+  switch (out_type) {
+    case OP_F32: launch_ln<float>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
+    case OP_BF16: launch_ln<bf16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
+    case OP_F16: launch_ln<f16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Queries and keys: RMSNorm over the 128 dims of each head with the weight set's learned
+// scale ("FLUX.3 Image Klein in Diffusers", "Entkoppelte Vorverarbeitung ...": queries and
+// keys are RMS-normalised before attention), then the 4D rotary embedding: lane p rotates
+// the adjacent pair (2p, 2p+1) by the angle of axis p/16, frequency index p%16.
+// The bf16 path also writes V transposed, vt[h][d][token], the layout the attention
+// kernel's P.V product reads (keys contiguous), with zeros for the 64 columns past n.
+// Grid: (ceil(n/64) + 1 token tiles, heads); 4 waves, each 16 tokens of the tile.
+// ------------------------------------------------------------------------------------------
+template <typename T> struct Pair;
+template <> struct Pair<float> {
+  typedef float2 type;
+  static __device__ float lo(float2 v) { return v.x; }
+  static __device__ float hi(float2 v) { return v.y; }
+  static __device__ float2 make(float a, float b) { return make_float2(a, b); }
+};
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <> struct Pair<bf16> {
+  typedef bf16x2 type;
+  static __device__ float lo(bf16x2 v) { return to_f32(v.x); }
+  static __device__ float hi(bf16x2 v) { return to_f32(v.y); }
+  static __device__ bf16x2 make(float a, float b) { return bf16x2{to_bf16(a), to_bf16(b)}; }
+};
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <> struct Pair<f16> {
+  typedef f16x2 type;
+  static __device__ float lo(f16x2 v) { return to_f32(v.x); }
+  static __device__ float hi(f16x2 v) { return to_f32(v.y); }
+  static __device__ f16x2 make(float a, float b) { return f16x2{to_f16(a), to_f16(b)}; }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_model, T *vt,
+                                                       int ldv, const float *cs, int n,
+                                                       const float *qn0, const float *qn1,
+                                                       const float *qn2, const float *kn0,
+                                                       const float *kn1, const float *kn2,
+                                                       int b1, int b2, float eps) {
+  typedef typename Pair<T>::type P2;
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int h = blockIdx.y;
+  int t0 = blockIdx.x * 64;
+  for (int i = 0; i < 16; ++i) {
+    int tok = t0 + wave * 16 + i;
+    if (tok >= n) break;
+    int seg = segment_of(tok, b1, b2);
+    const float *qn = seg == 0 ? qn0 : (seg == 1 ? qn1 : qn2);
+    const float *kn = seg == 0 ? kn0 : (seg == 1 ? kn1 : kn2);
+    T *qp = qkv + (size_t)tok * ldq + h * 128 + 2 * lane;
+    T *kp = qp + d_model;
+    P2 qv = *reinterpret_cast<const P2 *>(qp);
+    P2 kv = *reinterpret_cast<const P2 *>(kp);
+    float q0 = Pair<T>::lo(qv), q1 = Pair<T>::hi(qv);
+    float k0 = Pair<T>::lo(kv), k1 = Pair<T>::hi(kv);
+    float qs = wave_sum(q0 * q0 + q1 * q1);
+    float ks = wave_sum(k0 * k0 + k1 * k1);
+    float rq = 1.0f / sqrtf(qs * (1.0f / 128.f) + eps);
+    float rk = 1.0f / sqrtf(ks * (1.0f / 128.f) + eps);
+    float2 wq = *reinterpret_cast<const float2 *>(qn + 2 * lane);
+    float2 wk = *reinterpret_cast<const float2 *>(kn + 2 * lane);
+    q0 *= rq * wq.x;
+    q1 *= rq * wq.y;
+    k0 *= rk * wk.x;
+    k1 *= rk * wk.y;
+    float2 c = *reinterpret_cast<const float2 *>(cs + (size_t)tok * 128 + 2 * lane);
+    *reinterpret_cast<P2 *>(qp) = Pair<T>::make(q0 * c.x - q1 * c.y, q0 * c.y + q1 * c.x);
+    *reinterpret_cast<P2 *>(kp) = Pair<T>::make(k0 * c.x - k1 * c.y, k0 * c.y + k1 * c.x);
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (vt == nullptr) return;
+    // V transpose through LDS: tile [64 tokens][128 dims]
+    __shared__ __attribute__((aligned(16))) T tile[64][128 + 8];
+    const T *vsrc = qkv;
+    for (int c = threadIdx.x; c < 64 * 16; c += 256) {
+      int r = c >> 4, ch = c & 15;
+      int tok = t0 + r;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (tok < n)
+        val = *reinterpret_cast<const u32x4 *>(vsrc + (size_t)tok * ldq + 2 * d_model + h * 128 + ch * 8);
+      // 16-byte LDS writes into a padded row (row stride 272 B keeps them 16-byte aligned)
+      *reinterpret_cast<u32x4 *>(&tile[r][ch * 8]) = val;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 128 * 8; c += 256) {
+      int d = c & 127, ch = c >> 7;  // consecutive lanes take consecutive dims
+      typename Mfma<T>::v8 o;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = tile[ch * 8 + e][d];
+      *reinterpret_cast<typename Mfma<T>::v8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
+    }
+  }
+}
+
+hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, void *vt, int ldv,
+                        const float *cs, int n, const float *const qn[3],
+                        const float *const kn[3], Segs segs, float eps, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid(n / 64 + 2, heads);  // covers [0, n + 64) for the V transpose
+  switch (type) {
+    case OP_BF16:
+      k_qk_norm_rope<bf16><<<grid, 256, 0, s>>>((bf16 *)qkv, ldq, d_model, (bf16 *)vt, ldv, cs, n,
+                                                qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
+                                                segs.b2, eps);
+      break;
+    case OP_F16:
+      k_qk_norm_rope<f16><<<grid, 256, 0, s>>>((f16 *)qkv, ldq, d_model, (f16 *)vt, ldv, cs, n,
+                                               qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
+                                               segs.b2, eps);
+      break;
+    case OP_F32:
+      k_qk_norm_rope<float><<<dim3((n + 63) / 64, heads), 256, 0, s>>>(
+          (float *)qkv, ldq, d_model, nullptr, 0, cs, n, qn[0], qn[1], qn[2], kn[0], kn[1], kn[2],
+          segs.b1, segs.b2, eps);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMV for the conditioning path: y[v][i] = sum_k W[i][k] * act(x[v][k]), act = SiLU or
+// identity.  Used for the timestep MLP and for mod = W_mod . SiLU(cond) ("FLUX.3 Image Klein
+// in Diffusers", "Modulation pro Token-Typ ...": scale, shift and gate come from the
+// timestep embedding).  4 waves x 4 rows per workgroup; the input vectors sit in LDS.
+// ------------------------------------------------------------------------------------------
+template <typename TW>
+__global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, int k,
+                                               const float *x, int nvec, int silu_in) {
+  extern __shared__ float xs[];  // [nvec][k]
+  for (int i = threadIdx.x; i < nvec * k; i += 256) {
+    float z = x[i];
+    xs[i] = silu_in ? silu(z) : z;
+  }
+  __syncthreads();
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rr = 0; rr < 4; ++rr) {
+    int row = blockIdx.x * 16 + wave * 4 + rr;
+    if (row >= rows) break;
+    const TW *wr = w + (size_t)row * k;
+    float acc[3] = {0.f, 0.f, 0.f};
+    for (int c = lane * 8; c < k; c += 512) {
+      float wv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = to_f32(wr[c + e]);
+#pragma unroll
+      for (int v = 0; v < 3; ++v) {
+        if (v < nvec) {
+          const float *xv = xs + v * k + c;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[v] += wv[e] * xv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      if (v < nvec) {
+        float t = wave_sum(acc[v]);
+        if (lane == 0) y[(size_t)v * rows + row] = t;
+      }
+    }
+  }
+}
+
+hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
+                int silu_in, hipStream_t s) {
+  if (nvec < 1 || nvec > 3 || k % 8) return hipErrorInvalidValue;
+  size_t lds = sizeof(float) * nvec * k;
+  dim3 grid((rows + 15) / 16);
+  switch (w_type) {
+    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec, silu_in); break;
+    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec, silu_in); break;
+    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec, silu_in); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Sinusoidal timestep embedding (reading: the Transformer / DiT sinusoid with time factor
+// 1000 and max period 10000), in fp64: e = [cos(1000 t f_j) | sin(1000 t f_j)].
+struct TVals {
+  double t[3];
+};
+__global__ void k_timestep_embed(float *e, TVals tv, int nvec, int dim) {
+  int j = blockIdx.x * blockDim.x + threadIdx.x;
+  int half = dim / 2;
+  if (j >= nvec * dim) return;
+  int v = j / dim, c = j % dim;
+  int idx = c < half ? c : c - half;
+  double f = exp(-log(10000.0) * (double)idx / (double)half);
+  double arg = 1000.0 * tv.t[v] * f;
+  e[j] = (float)(c < half ? cos(arg) : sin(arg));
+}
+
+hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s) {
+  TVals tv = {{0.0, 0.0, 0.0}};
+  for (int i = 0; i < nvec && i < 3; ++i) tv.t[i] = t_host[i];
+  int tot = nvec * dim;
+  k_timestep_embed<<<(tot + 255) / 256, 256, 0, s>>>(e, tv, nvec, dim);
+  return hipGetLastError();
+}
+
+__global__ void k_copy_rows(float *dst, int ldd, const float *src, int lds, int rows, int cols) {
+  int r = blockIdx.y;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x)
+    dst[(size_t)r * ldd + c] = src[(size_t)r * lds + c];
+}
+
+hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,
+                         hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  k_copy_rows<<<dim3(4, rows), 256, 0, s>>>(dst, ldd, src, lds, rows, cols);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Seeded N(0,1) noise: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with counter
+// (element / 4, 0, 0) and key (seed low, seed high) words, then Box-Muller on the pairs
+// (x0, x1) and (x2, x3); uniforms u = (x + 0.5) / 2^32.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void philox_round(uint32_t c[4], const uint32_t k[2]) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+  uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k[0];
+  uint32_t n1 = (uint32_t)p1;
+  uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k[1];
+  uint32_t n3 = (uint32_t)p0;
+  c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+}
+
+__global__ void k_philox_normal(float *dst, int64_t n, uint64_t seed) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of 4 elements
+  if (g * 4 >= n) return;
+  uint32_t c[4] = {(uint32_t)g, (uint32_t)((uint64_t)g >> 32), 0u, 0u};
+  uint32_t k[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k[0] += 0x9E3779B9u;
+      k[1] += 0xBB67AE85u;
+    }
+    philox_round(c, k);
+  }
+  const double inv = 1.0 / 4294967296.0;
+  double out[4];
+  for (int p = 0; p < 2; ++p) {
+    double u0 = ((double)c[2 * p] + 0.5) * inv;
+    double u1 = ((double)c[2 * p + 1] + 0.5) * inv;
+    double rad = sqrt(-2.0 * log(u0));
+    double sn, cn;
+    sincospi(2.0 * u1, &sn, &cn);
+    out[2 * p] = rad * cn;
+    out[2 * p + 1] = rad * sn;
+  }
+  for (int e = 0; e < 4; ++e)
+    if (g * 4 + e < n) dst[g * 4 + e] = (float)out[e];
+}
+
+hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t groups = (n + 3) / 4;
+  k_philox_normal<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(dst, n, seed);
+  return hipGetLastError();
+}
+
+}  // namespace dit

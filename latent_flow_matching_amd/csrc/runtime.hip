@@ -1,0 +1,748 @@
+// Runtime of the denoising-transformer library: context, weight upload and repack,
+// workspace, the per-block launch sequence and the C ABI declared in include/dit.h.
+//
+// Launch sequence of one block (all on the caller's stream):
+//   ln_modulate      x (fp32) -> xm                 LayerNorm + adaLN (shift, scale)
+//   linear1          xm . W1^T -> qkv, cat[:, D:]   fused QKV + SwiGLU epilogue
+//   qk_norm_rope     qkv in place (+ V^T)           QK RMSNorm + 4D RoPE
+//   attention        qkv, V^T -> cat[:, :D]         softmax attention (full or per stream)
+//   linear2          cat . W2^T -> x += gate * .    gated residual
+// Stream blocks (double / per-mode) run the two projections as row groups with one weight
+// set per stream; shared blocks (single / joint) use one set for all rows.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "dit.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+}  // namespace
+
+struct dit_ctx {
+  dit_config cfg;
+  int device = 0;
+  int op = OP_BF16;          // element type of MFMA operands, activations and weights
+  bool debug_sync = false;
+  std::vector<void *> allocs;
+
+  struct Set {
+    void *w1 = nullptr, *w2 = nullptr;
+    float *qn = nullptr, *kn = nullptr;
+  };
+  std::vector<std::vector<Set>> blk;
+  void *mod[2][3] = {{nullptr}};
+  void *img_in = nullptr, *temb1 = nullptr, *temb2 = nullptr, *fmod = nullptr, *fout = nullptr;
+
+  int rows_alloc = 0, ldv = 0;
+  float *x = nullptr;        // [rows_alloc][D] residual of dit_forward / dit_denoise
+  void *xm = nullptr;        // [rows_alloc][D]
+  void *qkv = nullptr;       // [rows_alloc][3D]
+  void *cat = nullptr;       // [rows_alloc][D+F]
+  void *vt = nullptr;        // [H][128][ldv] (16-bit paths)
+  float *pos = nullptr;      // [rows_alloc][4]
+  float *cs = nullptr;       // [rows_alloc][128]
+  float *modbuf = nullptr;   // [2][3][3][3D]
+  float *cond = nullptr;     // [3][D]
+  float *temb_e = nullptr;   // [3][time_dim]
+  float *temb_h = nullptr;   // [3][D]
+  float *fmodv = nullptr;    // [3][2D]
+  float *xf = nullptr;       // [max_tokens][D]
+
+  // per-kernel timing: hipEvents recorded on the call's stream around each launch
+  struct ProfRec {
+    int cls;
+    double flops, bytes;
+    int e0, e1;
+  };
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<ProfRec> prof_rec;
+  int prof_next = 0;
+
+  int D() const { return cfg.hidden; }
+  int F() const { return cfg.mlp_hidden; }
+  size_t esz() const { return op == OP_F32 ? 4 : 2; }
+  int nblocks() const { return cfg.n_stream_blocks + cfg.n_shared_blocks; }
+  int kind(int b) const { return b < cfg.n_stream_blocks ? 0 : 1; }
+  int nsets_kind(int k) const { return k == 0 ? (cfg.arch == DIT_FLUX2 ? 2 : 3) : 1; }
+  void set_of_seg(int k, int out[3]) const {
+    if (k == 1) {
+      out[0] = out[1] = out[2] = 0;
+    } else if (cfg.arch == DIT_FLUX2) {
+      out[0] = 0; out[1] = 1; out[2] = 1;   // references travel with the image stream
+    } else {
+      out[0] = 0; out[1] = 1; out[2] = 2;
+    }
+  }
+  float *mod_vec(int k, int set, int seg) const {
+    return modbuf + ((size_t)(k * 3 + set) * 3 + seg) * 3 * D();
+  }
+};
+
+namespace {
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DIT_CHECK(call, what)                                   \
+  do {                                                          \
+    hipError_t e_ = (call);                                     \
+    if (e_ != hipSuccess) return hip_fail(e_, what);            \
+    if (ctx->debug_sync) {                                      \
+      e_ = hipStreamSynchronize(stream);                        \
+      if (e_ != hipSuccess) return hip_fail(e_, what);          \
+    }                                                           \
+  } while (0)
+
+enum ProfClass { P_LN, P_LINEAR1, P_QKNORM, P_ATTN, P_LINEAR2, P_COND, P_EMBED, P_FINAL, P_NCLASS };
+const char *const kProfNames[P_NCLASS] = {"ln_modulate", "linear1", "qk_norm_rope", "attention",
+                                          "linear2", "conditioning", "embed", "final"};
+
+// Start / end markers around one launch when timing is on (no-op otherwise).
+int prof_begin(dit_ctx *ctx, hipStream_t stream) {
+  if (!ctx->prof_on || ctx->prof_next + 2 > (int)ctx->prof_ev.size()) return -1;
+  const int e = ctx->prof_next;
+  ctx->prof_next += 2;
+  (void)hipEventRecord(ctx->prof_ev[e], stream);
+  return e;
+}
+void prof_end(dit_ctx *ctx, int e, int cls, double flops, double bytes, hipStream_t stream) {
+  if (e < 0) return;
+  (void)hipEventRecord(ctx->prof_ev[e + 1], stream);
+  ctx->prof_rec.push_back(dit_ctx::ProfRec{cls, flops, bytes, e, e + 1});
+}
+
+#define DIT_TIMED(cls, flops, bytes, call, what)               \
+  do {                                                          \
+    const int pe_ = prof_begin(ctx, stream);                    \
+    DIT_CHECK(call, what);                                      \
+    prof_end(ctx, pe_, cls, flops, bytes, stream);              \
+  } while (0)
+
+int dalloc(dit_ctx *ctx, void **p, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(DIT_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  ctx->allocs.push_back(*p);
+  e = hipMemset(*p, 0, bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipMemset");
+  return 0;
+}
+
+int validate_config(const dit_config *c) {
+  if (!c) return fail(DIT_EINVAL, "config is NULL");
+  if (c->arch != DIT_FLUX2 && c->arch != DIT_FLUX3) return fail(DIT_EINVAL, "unknown arch %d", c->arch);
+  if (c->head_dim != 128)
+    return fail(DIT_EUNSUPPORTED, "head_dim must be 128 (four 32-dim RoPE axes), got %d", c->head_dim);
+  if (c->heads < 1 || c->hidden != c->heads * c->head_dim)
+    return fail(DIT_EINVAL, "hidden (%d) must equal heads (%d) * head_dim", c->hidden, c->heads);
+  if (c->hidden % 256 || c->hidden > 4096)
+    return fail(DIT_EUNSUPPORTED, "hidden must be a multiple of 256 and at most 4096, got %d", c->hidden);
+  if (c->mlp_hidden < 128 || c->mlp_hidden % 128)
+    return fail(DIT_EUNSUPPORTED, "mlp_hidden must be a positive multiple of 128, got %d", c->mlp_hidden);
+  if (c->in_channels < 16 || c->in_channels % 64)
+    return fail(DIT_EUNSUPPORTED, "in_channels must be a positive multiple of 64, got %d", c->in_channels);
+  if (c->time_dim < 8 || c->time_dim % 16)
+    return fail(DIT_EUNSUPPORTED, "time_dim must be a positive multiple of 16, got %d", c->time_dim);
+  if (c->n_stream_blocks < 0 || c->n_shared_blocks < 0 || c->n_stream_blocks + c->n_shared_blocks < 1)
+    return fail(DIT_EINVAL, "need at least one block");
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
+    return fail(DIT_EINVAL, "max_tokens out of range: %d", c->max_tokens);
+  if (c->compute != DIT_F32 && c->compute != DIT_BF16 && c->compute != DIT_F16)
+    return fail(DIT_EINVAL, "unknown compute type %d", c->compute);
+  if (!(c->rope_theta > 0.f) || !(c->ln_eps > 0.f) || !(c->rms_eps > 0.f))
+    return fail(DIT_EINVAL, "rope_theta, ln_eps and rms_eps must be positive");
+  return 0;
+}
+
+// Convert host data to the compute type (optionally as fp32 regardless) and upload.
+// perm (optional): destination row r takes source row perm[r]; rows of `cols` elements.
+// bf16 -> fp16 is exact for magnitudes >= 2^-14; smaller ones round to the fp16 subnormal grid.
+int upload(dit_ctx *ctx, void **dst, const dit_tensor &t, bool as_f32,
+           const std::vector<int> *perm = nullptr, int cols = 0) {
+  const int64_t n = t.numel;
+  const int out = as_f32 ? OP_F32 : ctx->op;
+  const size_t es = out == OP_F32 ? 4 : 2;
+  if (int rc = dalloc(ctx, dst, (size_t)n * es)) return rc;
+  const bool same = (t.dtype == DIT_BF16 && out == OP_BF16) || (t.dtype == DIT_F32 && out == OP_F32);
+  if (same && !perm) {  // no conversion, no reordering: copy straight from the caller
+    hipError_t e = hipMemcpy(*dst, t.data, (size_t)n * es, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "upload");
+    return 0;
+  }
+  std::vector<uint8_t> stage((size_t)n * es);
+  if (same) {  // reorder rows only
+    const int64_t rows = n / cols;
+    for (int64_t r = 0; r < rows; ++r)
+      memcpy(stage.data() + (size_t)r * cols * es,
+             (const uint8_t *)t.data + (size_t)(*perm)[r] * cols * es, (size_t)cols * es);
+  } else {
+    auto src_at = [&](int64_t i) -> float {
+      return t.dtype == DIT_BF16 ? bf16_to_f32(((const uint16_t *)t.data)[i]) : ((const float *)t.data)[i];
+    };
+    for (int64_t i = 0; i < n; ++i) {
+      int64_t si = i;
+      if (perm) si = (int64_t)(*perm)[i / cols] * cols + i % cols;
+      const float v = src_at(si);
+      if (out == OP_BF16)
+        ((uint16_t *)stage.data())[i] = f32_to_bf16_rne(v);
+      else if (out == OP_F16)
+        ((_Float16 *)stage.data())[i] = (_Float16)v;
+      else
+        ((float *)stage.data())[i] = v;
+    }
+  }
+  hipError_t e = hipMemcpy(*dst, stage.data(), stage.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "upload");
+  return 0;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+extern "C" const char *dit_get_error(void) { return g_err.c_str(); }
+
+extern "C" void dit_ctx_free(dit_ctx *ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  for (void *p : ctx->allocs) (void)hipFree(p);
+  for (hipEvent_t e : ctx->prof_ev) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, int n_w) {
+  g_err.clear();
+  if (validate_config(cfg)) return nullptr;
+  if (n_w < 0 || (n_w > 0 && !w)) {
+    fail(DIT_EINVAL, "weight table is NULL");
+    return nullptr;
+  }
+  const dit_config &c = *cfg;
+  const int D = c.hidden, F = c.mlp_hidden, C = c.in_channels, T = c.time_dim;
+  // expected tensors
+  std::unordered_map<std::string, int64_t> want;
+  want["img_in"] = (int64_t)D * C;
+  want["temb.l1"] = (int64_t)D * T;
+  want["temb.l2"] = (int64_t)D * D;
+  want["final.mod"] = (int64_t)2 * D * D;
+  want["final.out"] = (int64_t)C * D;
+  const int nsets0 = c.arch == DIT_FLUX2 ? 2 : 3;
+  if (c.n_stream_blocks > 0)
+    for (int s = 0; s < nsets0; ++s) want["mod.0.s" + std::to_string(s)] = (int64_t)3 * D * D;
+  if (c.n_shared_blocks > 0) want["mod.1.s0"] = (int64_t)3 * D * D;
+  const int nb = c.n_stream_blocks + c.n_shared_blocks;
+  for (int b = 0; b < nb; ++b) {
+    const int ns = b < c.n_stream_blocks ? nsets0 : 1;
+    for (int s = 0; s < ns; ++s) {
+      std::string p = "blk" + std::to_string(b) + ".s" + std::to_string(s);
+      want[p + ".w1"] = (int64_t)(3 * D + 2 * F) * D;
+      want[p + ".w2"] = (int64_t)D * (D + F);
+      want[p + ".qn"] = 128;
+      want[p + ".kn"] = 128;
+    }
+  }
+  std::unordered_map<std::string, const dit_tensor *> have;
+  for (int i = 0; i < n_w; ++i) {
+    if (!w[i].name || !w[i].data) {
+      fail(DIT_EINVAL, "weight %d has a NULL name or data pointer", i);
+      return nullptr;
+    }
+    auto it = want.find(w[i].name);
+    if (it == want.end()) {
+      fail(DIT_EINVAL, "unknown weight '%s'", w[i].name);
+      return nullptr;
+    }
+    if (have.count(w[i].name)) {
+      fail(DIT_EINVAL, "weight '%s' given twice", w[i].name);
+      return nullptr;
+    }
+    if (w[i].numel != it->second) {
+      fail(DIT_EINVAL, "weight '%s' has %lld elements, expected %lld", w[i].name,
+           (long long)w[i].numel, (long long)it->second);
+      return nullptr;
+    }
+    if (w[i].dtype != DIT_F32 && w[i].dtype != DIT_BF16) {
+      fail(DIT_EINVAL, "weight '%s' has unknown dtype %d", w[i].name, w[i].dtype);
+      return nullptr;
+    }
+    have[w[i].name] = &w[i];
+  }
+  for (auto &kv : want)
+    if (!have.count(kv.first)) {
+      fail(DIT_EINVAL, "missing weight '%s'", kv.first.c_str());
+      return nullptr;
+    }
+
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    fail(DIT_EHIP, "no HIP device available (%s)", e == hipSuccess ? "0 devices" : hipGetErrorString(e));
+    return nullptr;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    fail(DIT_EHIP, "hipGetDevice failed");
+    return nullptr;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    fail(DIT_EHIP, "hipGetDeviceProperties failed");
+    return nullptr;
+  }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    fail(DIT_EUNSUPPORTED, "this library is built for gfx950 (MI355X); device is %s", prop.gcnArchName);
+    return nullptr;
+  }
+
+  dit_ctx *ctx = new dit_ctx();
+  ctx->cfg = c;
+  ctx->device = dev;
+  ctx->op = c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
+  const char *ds = getenv("DIT_DEBUG_SYNC");
+  ctx->debug_sync = ds && ds[0] == '1';
+
+  // linear1 row order: Q | K | V unchanged, then gate / up rows interleaved in chunks of 32
+  // (chunk c: gate rows of features [32c, 32c+32), then the up rows of the same features)
+  std::vector<int> perm1(3 * D + 2 * F);
+  for (int r = 0; r < 3 * D; ++r) perm1[r] = r;
+  for (int j = 0; j < 2 * F; ++j) {
+    const int chunk = j / 64, within = j % 64;
+    const int feat = chunk * 32 + (within % 32);
+    perm1[3 * D + j] = 3 * D + (within < 32 ? 0 : F) + feat;
+  }
+
+  auto up = [&](void **dst, const char *name, bool as_f32, const std::vector<int> *perm = nullptr,
+                int cols = 0) { return upload(ctx, dst, *have[name], as_f32, perm, cols); };
+  int rc = 0;
+  // small projections run through the fp32 GEMM; keep their weights in the compute type
+  rc = rc ? rc : up(&ctx->img_in, "img_in", false);
+  rc = rc ? rc : up(&ctx->temb1, "temb.l1", false);
+  rc = rc ? rc : up(&ctx->temb2, "temb.l2", false);
+  rc = rc ? rc : up(&ctx->fmod, "final.mod", false);
+  rc = rc ? rc : up(&ctx->fout, "final.out", false);
+  for (int k = 0; k < 2 && !rc; ++k) {
+    if ((k == 0 && c.n_stream_blocks == 0) || (k == 1 && c.n_shared_blocks == 0)) continue;
+    for (int s = 0; s < ctx->nsets_kind(k) && !rc; ++s) {
+      std::string n = "mod." + std::to_string(k) + ".s" + std::to_string(s);
+      rc = up(&ctx->mod[k][s], n.c_str(), false);
+    }
+  }
+  ctx->blk.resize(nb);
+  for (int b = 0; b < nb && !rc; ++b) {
+    const int ns = b < c.n_stream_blocks ? nsets0 : 1;
+    ctx->blk[b].resize(ns);
+    for (int s = 0; s < ns && !rc; ++s) {
+      std::string p = "blk" + std::to_string(b) + ".s" + std::to_string(s);
+      dit_ctx::Set &st = ctx->blk[b][s];
+      rc = rc ? rc : up(&st.w1, (p + ".w1").c_str(), false, &perm1, D);
+      rc = rc ? rc : up(&st.w2, (p + ".w2").c_str(), false);
+      rc = rc ? rc : up((void **)&st.qn, (p + ".qn").c_str(), true);
+      rc = rc ? rc : up((void **)&st.kn, (p + ".kn").c_str(), true);
+    }
+  }
+  // workspace
+  const size_t es = ctx->esz();
+  ctx->rows_alloc = c.max_tokens + 256;
+  ctx->ldv = (c.max_tokens / 64 + 2) * 64;
+  const size_t R = ctx->rows_alloc;
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->x, R * D * 4);
+  rc = rc ? rc : dalloc(ctx, &ctx->xm, R * D * es);
+  rc = rc ? rc : dalloc(ctx, &ctx->qkv, R * 3 * D * es);
+  rc = rc ? rc : dalloc(ctx, &ctx->cat, R * (D + F) * es);
+  if (ctx->op != OP_F32) rc = rc ? rc : dalloc(ctx, &ctx->vt, (size_t)c.heads * 128 * ctx->ldv * es);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->pos, R * 4 * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs, R * 128 * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (size_t)2 * 3 * 3 * 3 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->cond, (size_t)3 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)3 * T * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)3 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
+  if (rc) {
+    std::string msg = g_err;
+    dit_ctx_free(ctx);
+    g_err = msg;
+    return nullptr;
+  }
+  return ctx;
+}
+
+// ------------------------------------------------------------------------------------------
+namespace {
+
+Segs make_segs(int n_txt, int n_img, int n_ref) { return Segs{n_txt, n_txt + n_img, n_txt + n_img + n_ref}; }
+
+// mod[kind][set][seg] = W_mod[kind][set] . SiLU(cond[seg]) for every set of the kind
+int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) {
+  const int D = ctx->D();
+  for (int s = 0; s < ctx->nsets_kind(kind); ++s)
+    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, 3 * D, D, cond, 3, 1, stream),
+              "modulation gemv");
+  return 0;
+}
+
+int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stream) {
+  const dit_config &c = ctx->cfg;
+  const int D = ctx->D(), F = ctx->F();
+  const int kind = ctx->kind(b);
+  int sos[3];
+  ctx->set_of_seg(kind, sos);
+  const float *mseg[3], *gate[3], *qn[3], *kn[3];
+  for (int s = 0; s < 3; ++s) {
+    mseg[s] = ctx->mod_vec(kind, sos[s], s);
+    gate[s] = mseg[s] + 2 * D;
+    qn[s] = ctx->blk[b][sos[s]].qn;
+    kn[s] = ctx->blk[b][sos[s]].kn;
+  }
+  if (mask == DIT_MASK_DEFAULT) mask = (kind == 0 && c.arch == DIT_FLUX3) ? DIT_MASK_SEGMENT : DIT_MASK_FULL;
+  const int N = sg.n;
+  const size_t es = ctx->esz();
+
+  const double es_d = (double)es;
+  DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
+            ln_modulate(ctx->xm, ctx->op, D, x, D, N, 0, D, c.ln_eps, mseg, sg, stream), "ln_modulate");
+
+  // row groups: one per distinct weight set over contiguous rows
+  const int bounds[4] = {0, sg.b1, sg.b2, sg.n};
+  GemmGroup g1[3], g2[3];
+  int ng = 0;
+  for (int s = 0; s < 3; ++s) {
+    if (bounds[s + 1] == bounds[s]) continue;
+    const int set = sos[s];
+    if (ng > 0 && (const void *)g1[ng - 1].w == ctx->blk[b][set].w1) {  // extend
+      g1[ng - 1].rows += bounds[s + 1] - bounds[s];
+      g2[ng - 1].rows += bounds[s + 1] - bounds[s];
+      continue;
+    }
+    g1[ng] = GemmGroup{(const char *)ctx->xm + (size_t)bounds[s] * D * es, ctx->blk[b][set].w1,
+                       bounds[s + 1] - bounds[s], bounds[s]};
+    g2[ng] = GemmGroup{(const char *)ctx->cat + (size_t)bounds[s] * (D + F) * es, ctx->blk[b][set].w2,
+                       bounds[s + 1] - bounds[s], bounds[s]};
+    ++ng;
+  }
+  GemmArgs a1 = {};
+  for (int i = 0; i < ng; ++i) a1.g[i] = g1[i];
+  a1.ng = ng;
+  a1.n = 3 * D + 2 * F;
+  a1.k = D;
+  a1.ldx = D;
+  a1.qkv = ctx->qkv;
+  a1.ldq = 3 * D;
+  a1.split = 3 * D;
+  a1.cat = ctx->cat;
+  a1.ldc = D + F;
+  a1.cat_off = D;
+  const double fl1 = 2.0 * N * D * (3.0 * D + 2.0 * F);
+  if (ctx->op != OP_F32)
+    DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_mfma(a1, EPI_QKV_SWIGLU, ctx->op, stream), "linear1");
+  else
+    DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_simple(a1, EPI_QKV_SWIGLU, OP_F32, stream), "linear1");
+
+  // bytes: q, k read + written, V read + V^T written, one cos/sin row per token
+  DIT_TIMED(P_QKNORM, 0.0, (double)N * (6.0 * D * es_d + 512.0),
+            qk_norm_rope(ctx->qkv, ctx->op, 3 * D, D, c.heads, ctx->vt, ctx->ldv, ctx->cs, N, qn,
+                         kn, sg, c.rms_eps, stream),
+            "qk_norm_rope");
+
+  AttnArgs at = {};
+  at.qkv = ctx->qkv;
+  at.ldqkv = 3 * D;
+  at.d_model = D;
+  at.vt = ctx->vt;
+  at.ldv = ctx->ldv;
+  at.out = ctx->cat;
+  at.ldo = D + F;
+  at.heads = c.heads;
+  at.scale = 1.0f / sqrtf(128.0f);
+  if (mask == DIT_MASK_SEGMENT) {
+    for (int s = 0; s < 3; ++s)
+      if (bounds[s + 1] > bounds[s])
+        at.g[at.ng++] = AttnGroup{bounds[s], bounds[s + 1], bounds[s], bounds[s + 1]};
+  } else {
+    at.g[0] = AttnGroup{0, N, 0, N};
+    at.ng = 1;
+  }
+  double pairs = 0.0;
+  for (int i = 0; i < at.ng; ++i)
+    pairs += (double)(at.g[i].q1 - at.g[i].q0) * (at.g[i].k1 - at.g[i].k0);
+  const double fla = 4.0 * D * pairs;
+  if (ctx->op != OP_F32)
+    DIT_TIMED(P_ATTN, fla, 0.0, attention_mfma(at, ctx->op, stream), "attention");
+  else
+    DIT_TIMED(P_ATTN, fla, 0.0, attention_f32(at, stream), "attention");
+
+  GemmArgs a2 = {};
+  for (int i = 0; i < ng; ++i) a2.g[i] = g2[i];
+  a2.ng = ng;
+  a2.n = D;
+  a2.k = D + F;
+  a2.ldx = D + F;
+  a2.x = x;
+  a2.ldres = D;
+  for (int s = 0; s < 3; ++s) a2.gate[s] = gate[s];
+  a2.b1 = sg.b1;
+  a2.b2 = sg.b2;
+  const double fl2 = 2.0 * N * (double)(D + F) * D;
+  if (ctx->op != OP_F32)
+    DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
+  else
+    DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_simple(a2, EPI_RESID, OP_F32, stream), "linear2");
+  return 0;
+}
+
+int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref) {
+  if (n_txt < 0 || n_img < 0 || n_ref < 0) return fail(DIT_EINVAL, "negative token count");
+  const long long n = (long long)n_txt + n_img + n_ref;
+  if (n < 1) return fail(DIT_EINVAL, "empty sequence");
+  if (n > ctx->cfg.max_tokens)
+    return fail(DIT_EINVAL, "%lld tokens exceed max_tokens %d", n, ctx->cfg.max_tokens);
+  return 0;
+}
+
+// Conditioning for one transformer call at time t: cond rows per segment, modulation of
+// every block kind, output-head modulation.  FLUX.2: one timestep for all tokens; FLUX.3:
+// image tokens at t, text and reference tokens at t = 0.
+int prepare_conditioning(dit_ctx *ctx, double t, hipStream_t stream) {
+  const dit_config &c = ctx->cfg;
+  const int D = c.hidden;
+  double tv[3] = {t, t, t};
+  if (c.arch == DIT_FLUX3) tv[0] = tv[2] = 0.0;
+  DIT_CHECK(timestep_embed(ctx->temb_e, tv, 3, c.time_dim, stream), "timestep_embed");
+  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, c.time_dim, ctx->temb_e, 3, 0, stream), "temb l1");
+  DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, stream), "temb l2");
+  if (c.n_stream_blocks > 0)
+    if (int rc = compute_mods(ctx, 0, ctx->cond, stream)) return rc;
+  if (c.n_shared_blocks > 0)
+    if (int rc = compute_mods(ctx, 1, ctx->cond, stream)) return rc;
+  DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, stream), "final modulation");
+  return 0;
+}
+
+// Embed, run every block, output head.  out = v (accumulate 0) or out += alpha * v.
+int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt, int n_txt,
+                int gh, int gw, int rgh, int rgw, double t, float *out, int accumulate, float alpha,
+                hipStream_t stream) {
+  const dit_config &c = ctx->cfg;
+  const int D = c.hidden, C = c.in_channels;
+  const int n_img = gh * gw, n_ref = rgh * rgw;
+  const Segs sg = make_segs(n_txt, n_img, n_ref);
+  {
+    const int pe = prof_begin(ctx, stream);
+    if (int rc = prepare_conditioning(ctx, t, stream)) return rc;
+    prof_end(ctx, pe, P_COND, 0.0, 0.0, stream);
+  }
+  DIT_CHECK(fill_positions(ctx->pos, n_txt, gh, gw, rgh, rgw, stream), "positions");
+  DIT_CHECK(rope_table(ctx->cs, ctx->pos, sg.n, c.rope_theta, stream), "rope_table");
+  // sequence: text embeddings as they are, latents through the input projection
+  DIT_CHECK(copy_rows_f32(ctx->x, D, txt, D, n_txt, D, stream), "copy text");
+  GemmArgs ae = {};
+  ae.g[0] = GemmGroup{lat, ctx->img_in, n_img, n_txt};
+  ae.ng = 1;
+  if (n_ref > 0) ae.g[ae.ng++] = GemmGroup{ref_lat, ctx->img_in, n_ref, n_txt + n_img};
+  ae.n = D;
+  ae.k = C;
+  ae.ldx = C;
+  ae.out = ctx->x;
+  ae.ldo = D;
+  DIT_TIMED(P_EMBED, 2.0 * (n_img + n_ref) * (double)C * D, 0.0,
+            gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  for (int b = 0; b < ctx->nblocks(); ++b)
+    if (int rc = run_block(ctx, b, ctx->x, sg, DIT_MASK_DEFAULT, stream)) return rc;
+  // output head on the image rows
+  const float *fm = ctx->fmodv + 2 * D;  // image segment's (shift, scale)
+  const float *fms[3] = {fm, fm, fm};
+  DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
+  GemmArgs af = {};
+  af.g[0] = GemmGroup{ctx->xf, ctx->fout, n_img, 0};
+  af.ng = 1;
+  af.n = C;
+  af.k = D;
+  af.ldx = D;
+  af.out = out;
+  af.ldo = C;
+  af.accumulate = accumulate;
+  af.alpha = alpha;
+  DIT_TIMED(P_FINAL, 2.0 * n_img * (double)C * D, 0.0,
+            gemm_simple(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+  return 0;
+}
+
+int check_grid(dit_ctx *ctx, const float *lat, const float *txt, int n_txt, int gh, int gw,
+               const float *ref_lat, int rgh, int rgw) {
+  if (gh < 1 || gw < 1) return fail(DIT_EINVAL, "image grid must be at least 1x1");
+  if (rgh < 0 || rgw < 0 || (rgh == 0) != (rgw == 0)) return fail(DIT_EINVAL, "bad reference grid");
+  if (!lat) return fail(DIT_EINVAL, "lat is NULL");
+  if (n_txt > 0 && !txt) return fail(DIT_EINVAL, "txt is NULL");
+  if (rgh > 0 && !ref_lat) return fail(DIT_EINVAL, "ref_lat is NULL");
+  return check_tokens(ctx, n_txt, gh * gw, rgh * rgw);
+}
+
+}  // namespace
+
+extern "C" int dit_block_forward(dit_ctx *ctx, int block, float *x, int n_txt, int n_img, int n_ref,
+                                 const float *pos, const float *cond, int mask, void *stream_) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (block < 0 || block >= ctx->nblocks())
+    return fail(DIT_EINVAL, "block %d out of range [0, %d)", block, ctx->nblocks());
+  if (!x || !pos || !cond) return fail(DIT_EINVAL, "x, pos and cond must be device pointers");
+  if (mask != DIT_MASK_DEFAULT && mask != DIT_MASK_FULL && mask != DIT_MASK_SEGMENT)
+    return fail(DIT_EINVAL, "unknown mask %d", mask);
+  if (int rc = check_tokens(ctx, n_txt, n_img, n_ref)) return rc;
+  hipStream_t stream = (hipStream_t)stream_;
+  const Segs sg = make_segs(n_txt, n_img, n_ref);
+  DIT_CHECK(rope_table(ctx->cs, pos, sg.n, ctx->cfg.rope_theta, stream), "rope_table");
+  if (int rc = compute_mods(ctx, ctx->kind(block), cond, stream)) return rc;
+  return run_block(ctx, block, x, sg, mask, stream);
+}
+
+extern "C" int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt,
+                           int n_txt, int gh, int gw, int rgh, int rgw, float t, float *v, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
+  if (!v) return fail(DIT_EINVAL, "v is NULL");
+  return run_forward(ctx, lat, ref_lat, txt, n_txt, gh, gw, rgh, rgw, (double)t, v, 0, 0.f,
+                     (hipStream_t)stream);
+}
+
+extern "C" int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, int gw,
+                           const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed, void *stream_) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
+  if (n_steps < 1) return fail(DIT_EINVAL, "n_steps must be >= 1, got %d", n_steps);
+  hipStream_t stream = (hipStream_t)stream_;
+  if (seed >= 0)
+    DIT_CHECK(philox_normal(lat, (int64_t)gh * gw * ctx->cfg.in_channels, (uint64_t)seed, stream), "noise");
+  for (int i = 0; i < n_steps; ++i) {
+    const double t_cur = 1.0 - (double)i / n_steps;
+    const double t_next = 1.0 - (double)(i + 1) / n_steps;
+    // Euler: lat += (t_i - t_{i+1}) * v, fused into the output projection's epilogue
+    if (int rc = run_forward(ctx, lat, ref_lat, txt, n_txt, gh, gw, rgh, rgw, t_cur, lat, 1,
+                             (float)(t_cur - t_next), stream))
+      return rc;
+  }
+  return 0;
+}
+
+extern "C" int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream) {
+  g_err.clear();
+  if (!dst || n < 0 || seed < 0) return fail(DIT_EINVAL, "bad arguments");
+  hipError_t e = philox_normal(dst, n, (uint64_t)seed, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "noise");
+  return 0;
+}
+
+extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t *row_stride) {
+  if (!ctx || !name) return nullptr;
+  const int D = ctx->D(), F = ctx->F();
+  const int dt = ctx->op;
+  auto ret = [&](const void *p, int t, int64_t rs) -> const void * {
+    if (dtype) *dtype = t;
+    if (row_stride) *row_stride = rs;
+    return p;
+  };
+  if (!strcmp(name, "xm")) return ret(ctx->xm, dt, D);
+  if (!strcmp(name, "qkv")) return ret(ctx->qkv, dt, 3 * D);
+  if (!strcmp(name, "cat")) return ret(ctx->cat, dt, D + F);
+  if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, 3 * D);
+  if (!strcmp(name, "x")) return ret(ctx->x, DIT_F32, D);
+  return nullptr;
+}
+
+extern "C" int dit_profile_start(dit_ctx *ctx, int max_launches) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(DIT_EINVAL, "max_launches out of range");
+  while ((int)ctx->prof_ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    ctx->prof_ev.push_back(e);
+  }
+  ctx->prof_rec.clear();
+  ctx->prof_next = 0;
+  ctx->prof_on = true;
+  return 0;
+}
+
+extern "C" int dit_profile_stop(dit_ctx *ctx) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  ctx->prof_on = false;
+  if (!ctx->prof_rec.empty()) {
+    hipError_t err = hipEventSynchronize(ctx->prof_ev[ctx->prof_rec.back().e1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+  }
+  return 0;
+}
+
+extern "C" int dit_profile_get(dit_ctx *ctx, const char *kernel, double *ms, int64_t *launches,
+                               double *flops, double *bytes) {
+  g_err.clear();
+  if (!ctx || !kernel) return fail(DIT_EINVAL, "ctx or kernel is NULL");
+  int cls = -1;
+  for (int i = 0; i < P_NCLASS; ++i)
+    if (!strcmp(kernel, kProfNames[i])) cls = i;
+  if (cls < 0) return fail(DIT_EINVAL, "unknown kernel class '%s'", kernel);
+  double t = 0.0, f = 0.0, b = 0.0;
+  int64_t n = 0;
+  for (const auto &r : ctx->prof_rec) {
+    if (r.cls != cls) continue;
+    float e = 0.f;
+    hipError_t err = hipEventElapsedTime(&e, ctx->prof_ev[r.e0], ctx->prof_ev[r.e1]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+    t += e;
+    f += r.flops;
+    b += r.bytes;
+    ++n;
+  }
+  if (ms) *ms = t;
+  if (launches) *launches = n;
+  if (flops) *flops = f;
+  if (bytes) *bytes = b;
+  return 0;
+}

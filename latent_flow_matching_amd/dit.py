@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libdit.so (include/dit.h).  Argument marshalling only: every step of
+the forward pass runs in the library's HIP kernels.  torch tensors provide device memory and
+streams.  There is no CPU fallback: without the built library on a gfx950 GPU every call
+raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+from .synth import ModelConfig
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdit.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "dit.h")
+
+DIT_F32, DIT_BF16, DIT_F16 = 0, 1, 2
+COMPUTE = {"f32": DIT_F32, "bf16": DIT_BF16, "f16": DIT_F16}
+DIT_FLUX2, DIT_FLUX3 = 0, 1
+DIT_MASK_DEFAULT, DIT_MASK_FULL, DIT_MASK_SEGMENT = -1, 0, 1
+DIT_OK, DIT_EINVAL, DIT_ENOMEM, DIT_EHIP, DIT_EUNSUPPORTED = 0, -1, -2, -3, -4
+
+
+class DitConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "arch", "hidden", "heads", "head_dim", "mlp_hidden", "in_channels", "time_dim",
+        "n_stream_blocks", "n_shared_blocks", "max_tokens", "compute")] + \
+        [(n, ctypes.c_float) for n in ("rope_theta", "ln_eps", "rms_eps")]
+
+
+class DitTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("numel", ctypes.c_int64),
+                ("dtype", ctypes.c_int)]
+
+
+class DitError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"dit error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdit.so and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build() or "
+                           "python -m latent_flow_matching_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I, F, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    lib.dit_ctx_create.restype = P
+    lib.dit_ctx_create.argtypes = [ctypes.POINTER(DitConfig), ctypes.POINTER(DitTensor), I]
+    lib.dit_ctx_free.restype = None
+    lib.dit_ctx_free.argtypes = [P]
+    lib.dit_block_forward.restype = I
+    lib.dit_block_forward.argtypes = [P, I, P, I, I, I, P, P, I, P]
+    lib.dit_forward.restype = I
+    lib.dit_forward.argtypes = [P, P, P, P, I, I, I, I, I, F, P, P]
+    lib.dit_denoise.restype = I
+    lib.dit_denoise.argtypes = [P, P, P, I, I, I, P, I, I, I, I64, P]
+    lib.dit_fill_noise.restype = I
+    lib.dit_fill_noise.argtypes = [P, I64, I64, P]
+    lib.dit_debug_buffer.restype = P
+    lib.dit_debug_buffer.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(I), ctypes.POINTER(I64)]
+    lib.dit_profile_start.restype = I
+    lib.dit_profile_start.argtypes = [P, I]
+    lib.dit_profile_stop.restype = I
+    lib.dit_profile_stop.argtypes = [P]
+    D = ctypes.POINTER(ctypes.c_double)
+    lib.dit_profile_get.restype = I
+    lib.dit_profile_get.argtypes = [P, ctypes.c_char_p, D, ctypes.POINTER(I64), D, D]
+    lib.dit_get_error.restype = ctypes.c_char_p
+    lib.dit_get_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/dit.h declares."""
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z_0-9]+)\s*\(", txt)))
+
+
+def last_error() -> str:
+    return load_library().dit_get_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DitError(rc, last_error())
+
+
+def make_config(cfg: ModelConfig, max_tokens: int) -> DitConfig:
+    return DitConfig(cfg.arch, cfg.hidden, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
+                     cfg.in_channels, cfg.time_dim, cfg.n_stream_blocks, cfg.n_shared_blocks,
+                     max_tokens, COMPUTE[cfg.compute], cfg.rope_theta, cfg.ln_eps,
+                     cfg.rms_eps)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype_name, what):
+    import torch
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != getattr(torch, dtype_name) or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype_name} CUDA tensor")
+
+
+class DiT:
+    """One library context (weights uploaded, workspace allocated)."""
+
+    def __init__(self, cfg: ModelConfig, weights: dict, max_tokens: int):
+        lib = load_library()
+        self.cfg = cfg
+        self.max_tokens = max_tokens
+        names, keep = [], []
+        arr = (DitTensor * len(weights))()
+        for i, (name, a) in enumerate(weights.items()):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                dt = DIT_BF16
+            elif a.dtype == np.float32:
+                dt = DIT_F32
+            else:
+                raise ValueError(f"weight {name}: dtype {a.dtype} (want float32 or uint16 bf16 bits)")
+            keep.append(a)
+            names.append(name.encode())
+            arr[i] = DitTensor(names[-1], a.ctypes.data, a.size, dt)
+        c = make_config(cfg, max_tokens)
+        h = lib.dit_ctx_create(ctypes.byref(c), arr, len(weights))
+        if not h:
+            raise DitError(-1, last_error())
+        self._h = ctypes.c_void_p(h)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load_library().dit_ctx_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def block_forward(self, block, x, n_txt, n_img, n_ref, pos, cond, mask=DIT_MASK_DEFAULT,
+                      stream=None):
+        for t, w in ((x, "x"), (pos, "pos"), (cond, "cond")):
+            _need(t, "float32", w)
+        _check(load_library().dit_block_forward(self._h, block, _ptr(x), n_txt, n_img, n_ref,
+                                                _ptr(pos), _ptr(cond), mask, _stream(stream)))
+
+    def forward(self, lat, txt, grid, t, v, ref_lat=None, ref_grid=(0, 0), stream=None):
+        for a, w in ((lat, "lat"), (txt, "txt"), (v, "v"), (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        _check(load_library().dit_forward(self._h, _ptr(lat), _ptr(ref_lat), _ptr(txt),
+                                          txt.shape[0], grid[0], grid[1], ref_grid[0],
+                                          ref_grid[1], float(t), _ptr(v), _stream(stream)))
+
+    def denoise(self, lat, txt, grid, n_steps, seed=-1, ref_lat=None, ref_grid=(0, 0),
+                stream=None):
+        for a, w in ((lat, "lat"), (txt, "txt"), (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        _check(load_library().dit_denoise(self._h, _ptr(lat), _ptr(txt), txt.shape[0], grid[0],
+                                          grid[1], _ptr(ref_lat), ref_grid[0], ref_grid[1],
+                                          n_steps, seed, _stream(stream)))
+
+    KERNELS = ("ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2", "conditioning",
+               "embed", "final")
+
+    def profile_start(self, max_launches: int = 100000):
+        _check(load_library().dit_profile_start(self._h, max_launches))
+
+    def profile_stop(self) -> dict:
+        """Stop timing; {kernel: (ms, launches, flops, bytes)} over the recorded launches."""
+        lib = load_library()
+        _check(lib.dit_profile_stop(self._h))
+        out = {}
+        for k in self.KERNELS:
+            ms, n, fl, by = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+            _check(lib.dit_profile_get(self._h, k.encode(), ctypes.byref(ms), ctypes.byref(n),
+                                       ctypes.byref(fl), ctypes.byref(by)))
+            out[k] = (ms.value, n.value, fl.value, by.value)
+        return out
+
+    def debug_buffer(self, name: str, rows: int, cols: int | None = None):
+        """Copy a workspace buffer (see dit_debug_buffer) into a new float32 CUDA tensor."""
+        import torch
+        lib = load_library()
+        dt, rs = ctypes.c_int(), ctypes.c_int64()
+        p = lib.dit_debug_buffer(self._h, name.encode(), ctypes.byref(dt), ctypes.byref(rs))
+        if not p:
+            raise KeyError(name)
+        cols = rs.value if cols is None else cols
+        tdt = {DIT_BF16: torch.bfloat16, DIT_F16: torch.float16}.get(dt.value, torch.float32)
+        out = torch.empty((rows, rs.value), dtype=tdt, device="cuda")
+        torch.cuda.synchronize()
+        _hip_memcpy_dtod(out.data_ptr(), p, out.numel() * out.element_size())
+        return out[:, :cols].float()
+
+
+def fill_noise(dst, seed: int, stream=None):
+    _need(dst, "float32", "dst")
+    _check(load_library().dit_fill_noise(_ptr(dst), dst.numel(), seed, _stream(stream)))
+
+
+_hip = None
+
+
+def _hip_memcpy_dtod(dst: int, src: int, nbytes: int):
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.restype = ctypes.c_int
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    rc = _hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, 3)  # device to device
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed: {rc}")

@@ -40,7 +40,8 @@ class ModelConfig:
     time_dim: int = 256
     n_stream_blocks: int = 5
     n_shared_blocks: int = 20
-    bf16: bool = True
+    bf16: bool = True            # weights are bf16 values (the checkpoint format)
+    compute: str = "f16"         # MFMA operand type of the library: "f16", "bf16" or "f32"
     rope_theta: float = 10000.0
     ln_eps: float = 1e-6
     rms_eps: float = 1e-6
@@ -91,7 +92,7 @@ class Workload:
 WORKLOADS = {
     "single_block_fp32_32txt_16img": Workload(
         "single_block_fp32_32txt_16img",
-        replace(FLUX2_KLEIN, n_stream_blocks=0, n_shared_blocks=1, bf16=False),
+        replace(FLUX2_KLEIN, n_stream_blocks=0, n_shared_blocks=1, bf16=False, compute="f32"),
         32, (4, 4), None, 0, "one",
         "one single-stream block, 32 text + 16 image tokens (64x64 px), fp32"),
     "double_block_bf16_128txt_256img": Workload(

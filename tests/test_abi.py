@@ -1,0 +1,106 @@
+"""The C-ABI library builds, loads and exports every symbol include/dit.h declares; host-side
+validation and error paths work without a GPU (no compute calls here)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from latent_flow_matching_amd import dit, synth as S
+from tests.helpers import TINY2, lib_built
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not lib_built():
+        from latent_flow_matching_amd import build
+        build.build()
+    return dit.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = dit.header_functions()
+    assert {"dit_ctx_create", "dit_ctx_free", "dit_block_forward", "dit_forward", "dit_denoise",
+            "dit_get_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    c = dit.make_config(TINY2, 512)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _table(cfg=TINY2, drop=None, extra=None, bad_numel=None):
+    w = S.gen_weights(cfg, bits=True)
+    if drop:
+        w.pop(drop)
+    if extra:
+        w[extra] = np.zeros(4, np.uint16)
+    if bad_numel:
+        w[bad_numel] = w[bad_numel][:-1]
+    names = [k.encode() for k in w]
+    arr = (dit.DitTensor * len(w))()
+    keep = list(w.values())
+    for i, (n, a) in enumerate(zip(names, keep)):
+        arr[i] = dit.DitTensor(n, a.ctypes.data, a.size, dit.DIT_BF16)
+    return arr, len(w), (names, keep)
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("head_dim", 64, "head_dim must be 128"),
+    ("hidden", 300, "hidden"),
+    ("mlp_hidden", 100, "mlp_hidden"),
+    ("in_channels", 100, "in_channels"),
+    ("arch", 7, "unknown arch"),
+    ("compute", 9, "unknown compute"),
+    ("max_tokens", 0, "max_tokens"),
+    ("n_stream_blocks", -1, "block"),
+    ("rope_theta", 0.0, "positive"),
+])
+def test_bad_config_rejected(lib, field, value, msg):
+    arr, n, keep = _table()
+    h = lib.dit_ctx_create(ctypes.byref(_cfg(**{field: value})), arr, n)
+    assert not h
+    assert msg in dit.last_error()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    ({"drop": "blk0.s1.w2"}, "missing weight 'blk0.s1.w2'"),
+    ({"extra": "blk9.s0.w1"}, "unknown weight 'blk9.s0.w1'"),
+    ({"bad_numel": "final.out"}, "'final.out' has"),
+])
+def test_bad_weight_table_rejected(lib, kw, msg):
+    arr, n, keep = _table(**kw)
+    assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+    assert msg in dit.last_error()
+
+
+def test_no_device_is_an_error_not_a_fallback(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    arr, n, keep = _table()
+    assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+    assert "no HIP device" in dit.last_error()
+
+
+def test_null_context_calls_fail(lib):
+    assert lib.dit_block_forward(None, 0, None, 1, 1, 0, None, None, -1, None) == dit.DIT_EINVAL
+    assert "ctx is NULL" in dit.last_error()
+    assert lib.dit_forward(None, None, None, None, 1, 1, 1, 0, 0, 0.5, None, None) == dit.DIT_EINVAL
+    assert lib.dit_denoise(None, None, None, 1, 1, 1, None, 0, 0, 4, -1, None) == dit.DIT_EINVAL
+    assert lib.dit_fill_noise(None, 4, 1, None) == dit.DIT_EINVAL
+    assert lib.dit_debug_buffer(None, b"xm", None, None) is None
+    lib.dit_ctx_free(None)   # no-op
+
+
+def test_binding_refuses_to_run_without_library(tmp_path):
+    saved = dit._lib
+    try:
+        dit._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            dit.load_library(str(tmp_path / "missing.so"))
+    finally:
+        dit._lib = saved

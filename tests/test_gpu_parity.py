@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Bars: max|gpu - oracle| <= 2e-2 * RMS(oracle) for bf16 paths, <= 1e-4 * RMS(oracle) for the
+fp32 path.  Small shapes compare every element; the full benchmark shapes compare sampled
+rows (the oracle computes those rows one by one over all keys).
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from latent_flow_matching_amd import synth as S
+from oracle import dit_oracle as O
+from tests.helpers import (BF16_TOL, F32_TOL, TINY2, TINY3, dims_of, f64, gpu_weights,
+                           oracle_block, oracle_mod_sets, oracle_model, oracle_sets, rel_err, tol)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from latent_flow_matching_amd import dit
+    dit.load_library()
+
+
+def dev(a):
+    return torch.tensor(np.ascontiguousarray(a, dtype=np.float32), device="cuda")
+
+
+_CTX = {}
+
+
+def context(cfg, max_tokens):
+    """One library context per (config, max_tokens), reused across tests."""
+    from latent_flow_matching_amd import dit
+    key = (cfg, max_tokens)
+    if key not in _CTX:
+        w32 = S.gen_weights(cfg)
+        _CTX.clear()
+        _CTX[key] = (dit.DiT(cfg, gpu_weights(cfg, w32), max_tokens), w32)
+    return _CTX[key]
+
+
+def oracle_stages(cfg, w, b, x, segs, pos, cond):
+    """Intermediate tensors of the oracle block, from the synthetic inputs only."""
+    dims = dims_of(cfg)
+    d, f, nh = cfg.hidden, cfg.mlp_hidden, cfg.heads
+    kind, sos, mask = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
+    mods = O.segment_mods(oracle_mod_sets(cfg, w, kind), sos, [f64(c) for c in cond])
+    sets = oracle_sets(cfg, w, b)
+    seg = O.segment_ids(*segs)
+    n = seg.shape[0]
+    y = O.layer_norm(f64(x), cfg.ln_eps)
+    xm = np.empty_like(y)
+    h = np.empty((n, 3 * d + 2 * f))
+    qn = np.empty((n, nh, 128))
+    kn = np.empty((n, nh, 128))
+    for s in range(3):
+        sel = seg == s
+        if not sel.any():
+            continue
+        sh, sc, _ = O.split_modulation(mods[s], d)
+        xm[sel] = y[sel] * (1 + sc) + sh
+        h[sel] = xm[sel] @ sets[sos[s]].w1.T
+        qn[sel] = O.rms_norm(h[sel, :d].reshape(-1, nh, 128), sets[sos[s]].qn, cfg.rms_eps)
+        kn[sel] = O.rms_norm(h[sel, d:2 * d].reshape(-1, nh, 128), sets[sos[s]].kn, cfg.rms_eps)
+    ang = O.rope_angles(f64(pos), cfg.rope_theta)
+    q = O.apply_rope(qn, ang).reshape(n, d)
+    k = O.apply_rope(kn, ang).reshape(n, d)
+    v = h[:, 2 * d:3 * d]
+    o = O.attention(q.reshape(n, nh, 128), k.reshape(n, nh, 128), v.reshape(n, nh, 128), seg,
+                    mask).reshape(n, d)
+    m = O.silu(h[:, 3 * d:3 * d + f]) * h[:, 3 * d + f:]
+    return dict(xm=xm, q=q, k=k, v=v, o=o, m=m, mods=mods)
+
+
+def stage_report(ctx, cfg, w, b, x, segs, pos, cond):
+    n = sum(segs)
+    d = cfg.hidden
+    st = oracle_stages(cfg, w, b, x, segs, pos, cond)
+    qkv = ctx.debug_buffer("qkv", n).cpu().numpy()
+    cat = ctx.debug_buffer("cat", n).cpu().numpy()
+    xm = ctx.debug_buffer("xm", n).cpu().numpy()
+    rep = {"xm": rel_err(xm, st["xm"]), "q": rel_err(qkv[:, :d], st["q"]),
+           "k": rel_err(qkv[:, d:2 * d], st["k"]), "v": rel_err(qkv[:, 2 * d:], st["v"]),
+           "attn": rel_err(cat[:, :d], st["o"]), "swiglu": rel_err(cat[:, d:], st["m"])}
+    return rep
+
+
+def run_block(cfg, b, n_txt, grid, ref_grid=None, mask=None, rows=None, seed=0, stages=True,
+              max_tokens=None, distinct_cond=True):
+    from latent_flow_matching_amd import dit
+    n_img = grid[0] * grid[1]
+    n_ref = 0 if ref_grid is None else ref_grid[0] * ref_grid[1]
+    segs = (n_txt, n_img, n_ref)
+    n = sum(segs)
+    ctx, w = context(cfg, max_tokens or n)
+    x = S.gen_tokens(n, cfg.hidden, key=(seed,))
+    cond = S.gen_cond(3, cfg.hidden)
+    if not distinct_cond:
+        cond = np.repeat(cond[:1], 3, axis=0)
+    pos = O.positions(n_txt, grid, (ref_grid,) if ref_grid else ())
+    xt = dev(x)
+    print(f"[block] arch={cfg.arch} b={b} segs={segs} compute={cfg.compute} D={cfg.hidden}", flush=True)
+    ctx.block_forward(b, xt, n_txt, n_img, n_ref, dev(pos), dev(cond),
+                      dit.DIT_MASK_DEFAULT if mask is None else mask)
+    torch.cuda.synchronize()
+    got = xt.cpu().numpy()
+    ref = oracle_block(cfg, w, b, x, segs, pos, cond, mask=mask, rows=rows)
+    if rows is not None:
+        got = got[rows]
+    err = rel_err(got, ref)
+    derr = rel_err(got - x[rows if rows is not None else slice(None)],
+                   ref - f64(x[rows if rows is not None else slice(None)]))
+    print(f"    out err {err:.3e}  delta err {derr:.3e}", flush=True)
+    if stages and rows is None and err > tol(cfg) / 4:
+        print("    stages:", {k: f"{v:.2e}" for k, v in stage_report(ctx, cfg, w, b, x, segs, pos, cond).items()},
+              flush=True)
+    return err, derr
+
+
+C16 = [replace(TINY2, compute="bf16"), replace(TINY3, compute="bf16")]
+F32 = [replace(TINY2, bf16=False, compute="f32"), replace(TINY3, bf16=False, compute="f32")]
+
+
+# ----------------------------------------------------------------- small shapes, every element
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3] + C16 + F32,
+                         ids=["flux2_f16", "flux3_f16", "flux2_bf16", "flux3_bf16", "flux2_f32",
+                              "flux3_f32"])
+@pytest.mark.parametrize("b", [0, 1], ids=["stream_block", "shared_block"])
+def test_block_tiny_ragged(cfg, b):
+    """Ragged segments spanning several GEMM / attention tiles, all three streams."""
+    err, _ = run_block(cfg, b, 77, (13, 11), (9, 10))
+    assert err <= tol(cfg, full_width=False)
+
+
+@pytest.mark.parametrize("segs", [(1, (1, 1), None), (0, (3, 5), None), (300, (2, 2), None),
+                                  (64, (16, 16), (8, 8))])
+def test_block_tiny_edge_shapes(segs):
+    n_txt, grid, ref = segs
+    for cfg in (TINY2, TINY3):
+        for b in (0, 1):
+            err, _ = run_block(cfg, b, n_txt, grid, ref, max_tokens=600, stages=False)
+            assert err <= BF16_TOL
+
+
+def test_single_block_fp32_32txt_16img():
+    """One single-stream block, 32 text + 16 image tokens, fp32, full model width."""
+    wl = S.WORKLOADS["single_block_fp32_32txt_16img"]
+    err, derr = run_block(wl.model, 0, wl.n_txt, wl.grid)
+    assert err <= F32_TOL and derr <= 10 * F32_TOL
+
+
+@pytest.mark.parametrize("compute", ["f16", "bf16"])
+def test_double_block_bf16_128txt_256img(compute):
+    """One double-stream block, 128 text + 256 image tokens, bf16 weights, full model width."""
+    wl = S.WORKLOADS["double_block_bf16_128txt_256img"]
+    cfg = replace(wl.model, compute=compute)
+    err, derr = run_block(cfg, 0, wl.n_txt, wl.grid)
+    assert err <= tol(cfg)
+
+
+def test_mask_override_segment_equals_separate_streams():
+    """A shared block run with the block-diagonal mask equals the oracle's masked block."""
+    from latent_flow_matching_amd import dit
+    err, _ = run_block(TINY3, 1, 40, (6, 7), (5, 5), mask=dit.DIT_MASK_SEGMENT)
+    assert err <= BF16_TOL
+
+
+# ----------------------------------------------------------------- whole forward / denoise
+
+def _forward_case(cfg, n_txt, grid, ref_grid, t):
+    ctx, w = context(cfg, 600)
+    lat = S.gen_latents(grid[0] * grid[1], cfg.in_channels)
+    ref = S.gen_latents(ref_grid[0] * ref_grid[1], cfg.in_channels, key=(1,)) if ref_grid else None
+    txt = S.gen_text(n_txt, cfg.hidden)
+    v = torch.empty((grid[0] * grid[1], cfg.in_channels), device="cuda")
+    ctx.forward(dev(lat), dev(txt), grid, t, v, None if ref is None else dev(ref), ref_grid or (0, 0))
+    torch.cuda.synchronize()
+    want = O.forward(oracle_model(cfg, w), f64(lat), f64(txt), grid, float(np.float32(t)),
+                     None if ref is None else f64(ref), ref_grid)
+    return rel_err(v.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3, C16[0], F32[0]], ids=["flux2", "flux3", "flux2_bf16", "flux2_f32"])
+def test_forward_tiny(cfg):
+    err = _forward_case(cfg, 50, (9, 7), (6, 5) if cfg.arch == S.ARCH_FLUX3 else None, 0.75)
+    print(f"forward err {err:.3e}")
+    assert err <= tol(cfg, full_width=False)
+
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3], ids=["flux2", "flux3"])
+def test_denoise_tiny(cfg):
+    ctx, w = context(cfg, 600)
+    grid = (8, 6)
+    ref_grid = (4, 4) if cfg.arch == S.ARCH_FLUX3 else None
+    noise = S.gen_latents(48, cfg.in_channels, key=(2,))
+    ref = S.gen_latents(16, cfg.in_channels, key=(3,)) if ref_grid else None
+    txt = S.gen_text(20, cfg.hidden)
+    lat = dev(noise)
+    ctx.denoise(lat, dev(txt), grid, 3, -1, None if ref is None else dev(ref), ref_grid or (0, 0))
+    torch.cuda.synchronize()
+    want = O.denoise(oracle_model(cfg, w), f64(noise), f64(txt), grid, 3,
+                     None if ref is None else f64(ref), ref_grid)
+    err = rel_err(lat.cpu().numpy(), want)
+    print(f"denoise err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_block_is_deterministic():
+    cfg = TINY3
+    ctx, w = context(cfg, 600)
+    x = S.gen_tokens(300, cfg.hidden)
+    cond = S.gen_cond(3, cfg.hidden)
+    pos = O.positions(100, (10, 10), ((10, 10),))
+    outs = []
+    for _ in range(2):
+        xt = dev(x)
+        for b in (0, 1):
+            ctx.block_forward(b, xt, 100, 100, 100, dev(pos), dev(cond))
+        torch.cuda.synchronize()
+        outs.append(xt.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ----------------------------------------------------------------- full benchmark shapes, sampled rows
+
+def _rows(n, k=24, seed=0):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], r.choice(n, k, replace=False)]))
+
+
+@pytest.mark.parametrize("b", [0, 1], ids=["double", "single"])
+def test_flux2_block_1024px_sampled_rows(b):
+    """FLUX.2 double / single block at 512 text + 4096 image tokens (1024x1024 px)."""
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
+    n = 512 + 4096
+    err, _ = run_block(cfg, b, 512, (64, 64), rows=_rows(n), max_tokens=n)
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("b", [0, 1], ids=["per_mode", "joint"])
+def test_flux3_block_1024px_ref_sampled_rows(b):
+    """FLUX.3 per-mode / joint block at 512 text + 4096 image + 4096 reference tokens."""
+    cfg = replace(S.FLUX3_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
+    n = 512 + 4096 + 4096
+    err, _ = run_block(cfg, b, 512, (64, 64), (64, 64), rows=_rows(n), max_tokens=n)
+    assert err <= BF16_TOL
