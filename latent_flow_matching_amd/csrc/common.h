@@ -34,6 +34,11 @@ template <> __device__ __forceinline__ float from_f32<float>(float f) { return f
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { return to_bf16(f); }
 template <> __device__ __forceinline__ f16 from_f32<f16>(float f) { return to_f16(f); }
 
+// Conversion of values known to lie inside the fp16 range (no saturation step).
+template <typename T> __device__ __forceinline__ T from_f32_inrange(float f) {
+  return static_cast<T>(f);
+}
+
 // MFMA operand traits: 16-bit operand type -> 8-element vector and the 32x32x16 MFMA.
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {

@@ -285,16 +285,17 @@ __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, i
     if (row >= rows) break;
     const TW *wr = w + (size_t)row * k;
     float acc[3] = {0.f, 0.f, 0.f};
-    for (int c = lane * 8; c < k; c += 512) {
-      float wv[8];
+    // lane takes 4 consecutive k per step: float4 LDS reads of consecutive lanes are
+    // contiguous (no bank conflicts)
+    for (int c = lane * 4; c < k; c += 256) {
+      float wv[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wv[e] = to_f32(wr[c + e]);
+      for (int e = 0; e < 4; ++e) wv[e] = to_f32(wr[c + e]);
 #pragma unroll
       for (int v = 0; v < 3; ++v) {
         if (v < nvec) {
-          const float *xv = xs + v * k + c;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[v] += wv[e] * xv[e];
+          const f32x4 xv = *reinterpret_cast<const f32x4 *>(xs + v * k + c);
+          acc[v] += (wv[0] * xv.x + wv[1] * xv.y) + (wv[2] * xv.z + wv[3] * xv.w);
         }
       }
     }
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, i
 
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
                 int silu_in, hipStream_t s) {
-  if (nvec < 1 || nvec > 3 || k % 8) return hipErrorInvalidValue;
+  if (nvec < 1 || nvec > 3 || k % 4) return hipErrorInvalidValue;
   size_t lds = sizeof(float) * nvec * k;
   dim3 grid((rows + 15) / 16);
   switch (w_type) {
