@@ -7,18 +7,21 @@
 // Attention-Blöcke").  Padded prompt tokens are attended like any other token ("...",
 // section "Verarbeitung einzelner Prompts und Batching-Architektur in der Praxis").
 //
-// Work split: a workgroup takes 256 queries of one head, 8 waves x 32 queries, two waves per
-// SIMD: while one wave exponentiates its scores on the VALU the other's MFMAs run.  The
-// workgroup walks the allowed keys in tiles of 64 staged through LDS (K and V^T tiles,
-// double-buffered, one barrier per tile; the global loads of tile t+1 are in flight while
-// tile t is computed).
+// Work split: a workgroup takes 128 queries of one head, 4 waves x 32 queries, and two
+// workgroups share a CU (one wave of each per SIMD).  The two workgroups synchronise
+// independently, so their phases drift apart and one wave's softmax (VALU) overlaps the
+// other's MFMAs.  A workgroup walks the allowed keys in tiles of 64 staged through LDS (K and
+// V^T tiles, double-buffered, one barrier per tile; the global loads of tile t+1 are in
+// flight while tile t is computed).
 //   S^T = K Q^T   (A = K tile from LDS, B = the wave's queries held in registers): each lane
 //                 owns one query and 32 of the tile's keys, so the row max needs one exchange
 //                 with the partner lane l^32.
 //   O^T += V^T P^T (A = V^T tile from LDS, B = P straight from the S registers).
 // The running max is raised lazily: P is formed against the stored max unless some row's
 // max grew by more than 2^8, so O is rescaled only when that happens (P <= 256 fits fp16).
-// V is read in the transposed layout vt[h][d][token] written by the QK-norm kernel.  Scores
+// V is read in the transposed layout written by the QK-norm kernel, vt[h][d][token'] with the
+// middle two quads of every 16 tokens swapped, so that the eight keys a lane multiplies in
+// one P.V MFMA form a single 16-byte chunk.  Scores
 // are kept in the log2 domain (scale * log2(e) folded into one FMA before exp2).
 // Groups: each (q0, q1, k0, k1) range gets its own query tiles; key tiles start at k0
 // rounded down to 64 and keys outside [k0, k1) are masked to -inf.
@@ -31,7 +34,7 @@ namespace dit {
 
 namespace {
 
-constexpr int BQ = 256, BKV = 64, HD = 128;
+constexpr int BQ = 128, BKV = 64, HD = 128;
 constexpr int KT_BYTES = BKV * HD * 2;   // K tile [64 keys][128 d]   (row 256 B)
 constexpr int VT_BYTES = HD * BKV * 2;   // V^T tile [128 d][64 keys] (row 128 B)
 constexpr float kLazy = 8.0f;            // log2 headroom before O is rescaled
@@ -42,14 +45,14 @@ constexpr float kLazy = 8.0f;            // log2 headroom before O is rescaled
 __device__ __forceinline__ int k_off(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
-// V^T tile: 16 units of 8 B per 128-B row, unit index XOR ((row >> 1) & 15), so the 32 rows
-// of a half-wave ds_read_b64 (two rows per 256 B) hit 32 distinct slots.
-__device__ __forceinline__ int v_off_unit(int row, int unit) {
-  return row * 128 + ((unit ^ ((row >> 1) & 15)) << 3);
+// V^T tile: 8 chunks of 16 B per 128-B row, chunk index XOR ((row >> 1) & 7), so the 16 rows
+// of a quarter-wave ds_read_b128 (two rows per 256 B) hit 16 distinct slots.
+__device__ __forceinline__ int v_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 template <typename T>
-__global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnArgs a, int qt_before1, int qt_before2,
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int qt_before1, int qt_before2,
                                                        int q_tiles, int total) {
   typedef typename Mfma<T>::v8 V8;
   __shared__ __attribute__((aligned(16))) char smem[2 * (KT_BYTES + VT_BYTES)];
@@ -80,31 +83,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnArgs a, int qt_before1
   const int kv_begin = (grp.k0 / BKV) * BKV;
   const int n_tiles = (grp.k1 - kv_begin + BKV - 1) / BKV;
 
-  // global -> register staging: 2 K chunks and 2 V^T chunks of 16 B per thread
-  u32x4 rk[2], rv[2];
-  const int k_row = tid >> 4, k_ch = tid & 15;   // K: rows k_row + 32 i
-  const int v_row = tid >> 3, v_ch = tid & 7;    // V^T: rows v_row + 64 i
+  // global -> register staging: 4 K chunks and 4 V^T chunks of 16 B per thread
+  u32x4 rk[4], rv[4];
+  const int k_row = tid >> 4, k_ch = tid & 15;   // K: rows k_row + 16 i
+  const int v_row = tid >> 3, v_ch = tid & 7;    // V^T: rows v_row + 32 i
   auto gload = [&](int t) {
     const int kv0 = kv_begin + t * BKV;
     const T *kp = qkv + (size_t)(kv0 + k_row) * a.ldqkv + a.d_model + head * HD + k_ch * 8;
     const T *vp = vt + (size_t)v_row * a.ldv + kv0 + v_ch * 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rk[i] = *reinterpret_cast<const u32x4 *>(kp + (size_t)(32 * i) * a.ldqkv);
-      rv[i] = *reinterpret_cast<const u32x4 *>(vp + (size_t)(64 * i) * a.ldv);
+    for (int i = 0; i < 4; ++i) {
+      rk[i] = *reinterpret_cast<const u32x4 *>(kp + (size_t)(16 * i) * a.ldqkv);
+      rv[i] = *reinterpret_cast<const u32x4 *>(vp + (size_t)(32 * i) * a.ldv);
     }
   };
   auto sstore = [&](int buf) {
     char *ks = smem + buf * (KT_BYTES + VT_BYTES);
     char *vs = ks + KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4 *>(ks + k_off(k_row + 32 * i, k_ch)) = rk[i];
-      const int row = v_row + 64 * i;
-      const int x = (row >> 1) & 15;
-      u32x4 val = rv[i];
-      if (x & 1) val = u32x4{val.z, val.w, val.x, val.y};  // unit-level swizzle
-      *reinterpret_cast<u32x4 *>(vs + row * 128 + ((v_ch ^ (x >> 1)) << 4)) = val;
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4 *>(ks + k_off(k_row + 16 * i, k_ch)) = rk[i];
+      *reinterpret_cast<u32x4 *>(vs + v_off(v_row + 32 * i, v_ch)) = rv[i];
     }
   };
 
@@ -184,10 +183,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnArgs a, int qt_before1
       const int row = ds * 32 + r32;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        u32x2 lo = *reinterpret_cast<const u32x2 *>(vs + v_off_unit(row, 4 * kc + hk));
-        u32x2 hi = *reinterpret_cast<const u32x2 *>(vs + v_off_unit(row, 4 * kc + 2 + hk));
-        u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-        V8 vf = __builtin_bit_cast(V8, w);
+        // keys 16 kc + {4 hk .. 4 hk + 3, 8 + 4 hk .. 8 + 4 hk + 3}: one chunk of the
+        // quad-permuted V^T row
+        V8 vf = *reinterpret_cast<const V8 *>(vs + v_off(row, 2 * kc + hk));
         o[ds] = Mfma<T>::mma(vf, pf[kc], o[ds]);
       }
     }
@@ -219,9 +217,9 @@ hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
   const int total = q_tiles * a.heads;
   const int grid = (total + 7) / 8 * 8;
   if (op == OP_BF16)
-    k_attn_mfma<bf16><<<grid, 512, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
+    k_attn_mfma<bf16><<<grid, 256, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
   else if (op == OP_F16)
-    k_attn_mfma<f16><<<grid, 512, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
+    k_attn_mfma<f16><<<grid, 256, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -149,8 +149,9 @@ hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx
 // scale ("FLUX.3 Image Klein in Diffusers", "Entkoppelte Vorverarbeitung ...": queries and
 // keys are RMS-normalised before attention), then the 4D rotary embedding: lane p rotates
 // the adjacent pair (2p, 2p+1) by the angle of axis p/16, frequency index p%16.
-// The bf16 path also writes V transposed, vt[h][d][token], the layout the attention
-// kernel's P.V product reads (keys contiguous), with zeros for the 64 columns past n.
+// The 16-bit paths also write V transposed, vt[h][d][token'], the layout the attention
+// kernel's P.V product reads (keys contiguous; token' swaps the middle two quads of every
+// 16 tokens), with zeros for the 64 columns past n.
 // Grid: (ceil(n/64) + 1 token tiles, heads); 4 waves, each 16 tokens of the tile.
 // ------------------------------------------------------------------------------------------
 template <typename T> struct Pair;
@@ -230,8 +231,11 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
     for (int c = threadIdx.x; c < 128 * 8; c += 256) {
       int d = c & 127, ch = c >> 7;  // consecutive lanes take consecutive dims
       typename Mfma<T>::v8 o;
+      // within every 16 tokens the middle two quads are swapped (column order 0-3, 8-11,
+      // 4-7, 12-15), so the eight keys one attention lane multiplies are contiguous
+      const int base = (ch >> 1) * 16 + ((ch & 1) ? 4 : 0);
   #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = tile[ch * 8 + e][d];
+      for (int e = 0; e < 8; ++e) o[e] = tile[base + (e < 4 ? e : e + 4)][d];
       *reinterpret_cast<typename Mfma<T>::v8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
     }
   }
