@@ -8,10 +8,16 @@ output head.  Inputs (weights, text embeddings) are resident in HBM before timin
 Prints ONE JSON line on stdout; details go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute f16|bf16]
+    python bench.py --mode copy-calibration      # elementwise copy of 1 GiB, for PMC scaling
+    python bench.py --summarize-rocprof DIR ...  # rocprofv3 CSVs -> profiles/*.md (CPU only)
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -20,6 +26,16 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (AMD spec)
 PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SOURCE = os.path.join(ROOT, "latent_flow_matching_amd", "csrc", "gemm_mfma.hip")
+COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
+# rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
+# (patterns match the mangled names rocprofv3 prints: the epilogue is the last template argument)
+KERNEL_CLASSES = [("linear1", r"k_gemm_(?:v3|mfma)I.*Li1EEEv"),
+                  ("linear2", r"k_gemm_(?:v3|mfma)I.*Li2EEEv"),
+                  ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
+                  ("ln_modulate", r"k_ln_modulate"), ("final/embed", r"k_gemm_simple"),
+                  ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
 
 
 def log(*a):
@@ -59,6 +75,137 @@ def cpu_baseline(wl, cfg):
                       f"NumPy/OpenBLAS, {dt:.2f} s"}
 
 
+def source_sha256(path=GEMM_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary, or None when
+    there is none or the kernel source has changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"^traffic_json: (\{.*\})$", f.read(), re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256") != source_sha256():
+        return None
+    return d
+
+
+def copy_calibration():
+    """One elementwise kernel that reads COPY_BYTES and writes COPY_BYTES, three launches; its
+    FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calibration", "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _csv_rows(d, suffix):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _kernel_class(name):
+    for cls, pat in KERNEL_CLASSES:
+        if re.search(pat, name):
+            return cls
+    return None
+
+
+def summarize_rocprof(args):
+    """Write profiles/*.md from rocprofv3 output folders (runs on the CPU, reads CSV only)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    wl = args.workload
+    if args.trace_dir:
+        rows = _csv_rows(args.trace_dir, "kernel_stats.csv")
+        total = sum(float(r["TotalDurationNs"]) for r in rows)
+        lines = [f"# Kernel trace: {wl}, {args.compute}", "",
+                 "Command (from the repository root on an MI355X, after `cd /tmp && export "
+                 "TMPDIR=/tmp`):", "", "```", args.trace_cmd, "```", "",
+                 "| kernel class | kernel | calls | avg us | total ms | share |",
+                 "|---|---|---|---|---|---|"]
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"]
+            cls = _kernel_class(name) or "other"
+            short = name.replace("_ZN3dit12_GLOBAL__N_1", "")
+            lines.append(f"| {cls} | `{short[:70]}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                         f"{float(r['TotalDurationNs']) / total:.3f} |")
+        out = os.path.join(PROFILES, f"kernel_trace_{wl}.md")
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote {out}")
+    if args.fetch_dir and args.write_dir and args.copy_fetch_dir and args.copy_write_dir:
+        def per_kernel(d, counter):
+            acc = {}
+            for r in _csv_rows(d, "counter_collection.csv"):
+                if r.get("Counter_Name") != counter:
+                    continue
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            return acc
+
+        def copy_kib(d, counter):
+            vals = [v for k, vs in per_kernel(d, counter).items() if "mul" in k.lower()
+                    for v in vs]
+            if not vals:
+                raise SystemExit(f"no multiply kernel with {counter} in {d}")
+            return sorted(vals)[len(vals) // 2]
+
+        f_scale = COPY_BYTES / copy_kib(args.copy_fetch_dir, "FETCH_SIZE")
+        w_scale = COPY_BYTES / copy_kib(args.copy_write_dir, "WRITE_SIZE")
+        fetch = per_kernel(args.fetch_dir, "FETCH_SIZE")
+        write = per_kernel(args.write_dir, "WRITE_SIZE")
+        lines = [f"# HBM traffic per launch: {wl}, {args.compute}", "",
+                 "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 pass each, "
+                 "scaled by what the same counter reads for an elementwise kernel that reads and "
+                 f"writes exactly {COPY_BYTES} bytes (bytes per counter unit: fetch "
+                 f"{f_scale:.1f}, write {w_scale:.1f}).", "", "Commands (from /tmp, "
+                 "TMPDIR=/tmp):", "", "```", *args.pmc_cmd, "```", "",
+                 "| kernel class | launches | fetch MB / launch | write MB / launch |",
+                 "|---|---|---|---|"]
+        per_class = {}
+        for k, vs in fetch.items():
+            cls = _kernel_class(k)
+            if cls is None:
+                continue
+            ws = write.get(k, [])
+            c = per_class.setdefault(cls, [0, 0.0, 0.0, 0])
+            c[0] += len(vs)
+            c[1] += sum(vs) * f_scale
+            c[2] += sum(ws) * w_scale
+            c[3] += len(ws)
+        out_json = None
+        for cls, (n, fb, wb, nw) in sorted(per_class.items()):
+            lines.append(f"| {cls} | {n} | {fb / n / 1e6:.1f} | {wb / max(nw, 1) / 1e6:.1f} |")
+            if cls == args.traffic_kernel:
+                out_json = {"kernel": cls, "workload": wl, "compute": args.compute,
+                            "fetch_bytes_per_launch": fb / n,
+                            "write_bytes_per_launch": wb / max(nw, 1),
+                            "bytes_per_launch": fb / n + wb / max(nw, 1),
+                            "source_sha256": source_sha256()}
+        if out_json:
+            lines += ["", "Used by bench.py for `roofline.traffic` while the GEMM source hash "
+                      "matches:", "", "traffic_json: " + json.dumps(out_json)]
+        out = os.path.join(PROFILES, f"traffic_{args.traffic_kernel}_{wl}.md")
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,9 +214,22 @@ def main():
     ap.add_argument("--workload", default="flux2_stack_512txt_4096img_4step")
     ap.add_argument("--compute", default="f16", choices=["f16", "bf16"])
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration"])
+    ap.add_argument("--summarize-rocprof", action="store_true")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--trace-cmd", default="")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--pmc-cmd", action="append", default=[])
+    ap.add_argument("--traffic-kernel", default="linear1")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
@@ -77,6 +237,11 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.mode == "copy-calibration":
+        torch.cuda.set_device(0)
+        copy_calibration()
+        return
 
     from latent_flow_matching_amd import dit, synth as S
 
@@ -120,7 +285,9 @@ def main():
     per_step_ms = ms / args.steps
     blocks = cfg.n_blocks
     block_tokens = n * blocks * wl.steps * args.steps
-    total_flops = sum(v[2] for v in prof.values())
+    # headline: GEMM + attention flops over the whole timed wall time (norms, RoPE, conditioning,
+    # output head and Euler update included in the time)
+    total_flops = sum(prof[k][2] for k in ("linear1", "linear2", "attention"))
     tflops = total_flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.compute]
     kernels = {}
@@ -138,9 +305,13 @@ def main():
     dom = max((k for k in prof if prof[k][2] > 0), key=lambda k: prof[k][0])
     dms, dcnt, dfl, _ = prof[dom]
     achieved = dfl / dcnt / (dms / dcnt * 1e-3) / 1e12
+    tr = load_traffic(dom, wl.name)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "flops_per_launch": dfl / dcnt}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": round(tr["bytes_per_launch"]) if tr else None,
+                "flops_per_launch": dfl / dcnt, "avg_launch_us": round(dms / dcnt * 1e3, 2)}
+    if tr:
+        roofline["traffic_source"] = f"profiles/traffic_{dom}_{wl.name}.md"
 
     result = {
         "metric": "DiT block tokens/sec and attention+GEMM TFLOP/s (% bf16 MFMA peak)",
