@@ -463,3 +463,60 @@ def denoise(model: Model, noise: np.ndarray, txt: np.ndarray, grid, n_steps: int
         v = forward(model, lat, txt, grid, ts[i], ref_lat, ref_grid)
         lat = euler_step(lat, v, ts[i], ts[i + 1])
     return lat
+
+
+# ----------------------------------------------------------------------------------------
+# Seeded starting noise.  The C tool makes generation reproducible from a seed ([HK]
+# 再現性・シード管理); the noise here is a counter-based generator written from its
+# published definition: Philox-4x32 with 10 rounds (J. K. Salmon, M. A. Moraes, R. O. Dror,
+# D. E. Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), then the Box-Muller
+# transform (G. E. P. Box, M. E. Muller, 1958).
+# ----------------------------------------------------------------------------------------
+
+PHILOX_MUL = (0xD2511F53, 0xCD9E8D57)     # round multipliers of Philox-4x32
+PHILOX_BUMP = (0x9E3779B9, 0xBB67AE85)    # Weyl key increments (golden ratio, sqrt(3) - 1)
+_U32 = 0xFFFFFFFF
+
+
+def philox4x32(counter, key, rounds: int = 10) -> np.ndarray:
+    """Philox-4x32 bijection of 128-bit counters under a 64-bit key.
+
+    counter: integer array [..., 4] of 32-bit words; key: (k0, k1).  One round multiplies
+    words 0 and 2 by the two constants (64-bit products split into high and low halves) and
+    forms (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)); the key words
+    advance by the Weyl increments between rounds."""
+    c = np.asarray(counter, dtype=np.uint64)
+    x0, x1, x2, x3 = (c[..., i] & _U32 for i in range(4))
+    k0, k1 = int(key[0]) & _U32, int(key[1]) & _U32
+    m0, m1 = np.uint64(PHILOX_MUL[0]), np.uint64(PHILOX_MUL[1])
+    for _ in range(rounds):
+        p0, p1 = x0 * m0, x2 * m1           # < 2^64: exact in uint64
+        x0, x1, x2, x3 = ((p1 >> np.uint64(32)) ^ x1 ^ np.uint64(k0), p1 & np.uint64(_U32),
+                          (p0 >> np.uint64(32)) ^ x3 ^ np.uint64(k1), p0 & np.uint64(_U32))
+        k0, k1 = (k0 + PHILOX_BUMP[0]) & _U32, (k1 + PHILOX_BUMP[1]) & _U32
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
+def box_muller(u0: np.ndarray, u1: np.ndarray):
+    """Two independent N(0,1) values from two uniforms in (0, 1)."""
+    r = np.sqrt(-2.0 * np.log(u0))
+    return r * np.cos(2.0 * np.pi * u1), r * np.sin(2.0 * np.pi * u1)
+
+
+def noise(n: int, seed: int) -> np.ndarray:
+    """n values of N(0,1) noise for a seed (the library's seeded latents, row-major).
+
+    Element e comes from the Philox block of counter (e // 4 as two 32-bit words, 0, 0) and
+    key (seed low word, seed high word), output word e % 4; words 0,1 and 2,3 form two
+    Box-Muller pairs with uniforms u = (word + 1/2) / 2^32 (never 0 or 1)."""
+    if n < 0:
+        raise ValueError("negative length")
+    groups = (n + 3) // 4
+    g = np.arange(groups, dtype=np.uint64)
+    ctr = np.stack([g & np.uint64(_U32), g >> np.uint64(32), np.zeros_like(g), np.zeros_like(g)], -1)
+    seed = int(seed)
+    words = philox4x32(ctr, (seed & _U32, (seed >> 32) & _U32)).astype(np.float64)
+    u = (words + 0.5) / 4294967296.0
+    z0, z1 = box_muller(u[:, 0], u[:, 1])
+    z2, z3 = box_muller(u[:, 2], u[:, 3])
+    return np.stack([z0, z1, z2, z3], axis=-1).reshape(-1)[:n]

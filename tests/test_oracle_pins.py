@@ -16,6 +16,7 @@ import torch.nn.functional as F
 from oracle import dit_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "token_counts.json")
+PHILOX_KAT = os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")
 
 TINY = O.Dims(hidden=256, heads=2, head_dim=128, mlp_hidden=192, in_channels=64,
               time_dim=32)
@@ -431,6 +432,50 @@ def _wrong_rope(x, angles):
     return out.reshape(n, h, d)
 
 
+# ------------------------------------------------------------------ seeded noise
+
+def test_philox_known_answers():
+    """The generator reproduces the published known-answer vectors bit for bit."""
+    with open(PHILOX_KAT) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        ctr = np.array([int(w, 16) for w in v["counter"]], dtype=np.uint64)
+        key = [int(w, 16) for w in v["key"]]
+        got = O.philox4x32(ctr, key, rounds=kat["rounds"])
+        assert [f"{int(w):08x}" for w in got] == v["output"]
+
+
+def test_noise_inverts_to_its_uniforms():
+    """Box-Muller closed form: z0^2 + z1^2 = -2 ln u0 and atan2(z1, z0) = 2 pi u1 (mod 2 pi),
+    with u the Philox words of the element's counter, (w + 1/2) / 2^32."""
+    n, seed = 4 * 257 + 3, (7 << 32) | 12345
+    z = O.noise(n, seed)
+    assert z.shape == (n,)
+    g = np.arange((n + 3) // 4, dtype=np.uint64)
+    ctr = np.stack([g, np.zeros_like(g), np.zeros_like(g), np.zeros_like(g)], -1)
+    u = (O.philox4x32(ctr, (12345, 7)).astype(np.float64) + 0.5) / 2.0 ** 32
+    zz = np.concatenate([z, np.zeros(4 * len(g) - n)]).reshape(-1, 4)
+    for a in (0, 2):
+        r2 = zz[:-1, a] ** 2 + zz[:-1, a + 1] ** 2
+        np.testing.assert_allclose(np.exp(-0.5 * r2), u[:-1, a], rtol=1e-12)
+        ang = np.mod(np.arctan2(zz[:-1, a + 1], zz[:-1, a]) / (2 * np.pi), 1.0)
+        d = np.abs(ang - u[:-1, a + 1])
+        assert np.all(np.minimum(d, 1 - d) < 1e-12)
+
+
+def test_noise_distribution_and_prefix():
+    """N(0,1) in distribution (Kolmogorov-Smirnov), pairs uncorrelated, counter-based (a
+    shorter draw is a prefix of a longer one), and the seed's high word matters."""
+    from scipy import stats
+    z = O.noise(200_003, 42)
+    assert stats.kstest(z, "norm").pvalue > 1e-4
+    assert abs(z.mean()) < 5 / math.sqrt(len(z))
+    assert abs(z.var() - 1) < 5 * math.sqrt(2 / len(z))
+    assert abs(np.corrcoef(z[0:-3:4], z[1:-2:4])[0, 1]) < 5 / math.sqrt(len(z) / 4)
+    np.testing.assert_array_equal(O.noise(1001, 42), z[:1001])
+    assert not np.array_equal(O.noise(64, 42), O.noise(64, 42 + (1 << 32)))
+
+
 def _wrong_layer_norm(x, eps):
     return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + eps + 1e-3)
 
@@ -445,6 +490,11 @@ def test_pins_catch_planted_slips(monkeypatch):
     monkeypatch.setattr(O, "layer_norm", _wrong_layer_norm)
     with pytest.raises(AssertionError):
         test_layer_norm_matches_library()
+    monkeypatch.undo()
+    # Philox with the two round multipliers swapped
+    monkeypatch.setattr(O, "PHILOX_MUL", (O.PHILOX_MUL[1], O.PHILOX_MUL[0]))
+    with pytest.raises(AssertionError):
+        test_philox_known_answers()
     monkeypatch.undo()
     # a slightly wrong activation
     orig = O.silu
