@@ -31,8 +31,8 @@ GEMM_SOURCE = os.path.join(ROOT, "latent_flow_matching_amd", "csrc", "gemm_mfma.
 COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
 # rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
 # (patterns match the mangled names rocprofv3 prints: the epilogue is the last template argument)
-KERNEL_CLASSES = [("linear1", r"k_gemm_(?:v3|mfma)I.*Li1EEEv"),
-                  ("linear2", r"k_gemm_(?:v3|mfma)I.*Li2EEEv"),
+KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma)?I.*Li1EEEv"),
+                  ("linear2", r"k_gemm(?:_v3|_mfma)?I.*Li2EEEv"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
                   ("ln_modulate", r"k_ln_modulate"), ("final/embed", r"k_gemm_simple"),
                   ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
@@ -132,6 +132,8 @@ def summarize_rocprof(args):
     wl = args.workload
     if args.trace_dir:
         rows = _csv_rows(args.trace_dir, "kernel_stats.csv")
+        if not rows:
+            raise SystemExit(f"no kernel_stats.csv under {args.trace_dir}")
         total = sum(float(r["TotalDurationNs"]) for r in rows)
         lines = [f"# Kernel trace: {wl}, {args.compute}", "",
                  "Command (from the repository root on an MI355X, after `cd /tmp && export "

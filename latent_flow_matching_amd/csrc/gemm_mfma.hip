@@ -8,10 +8,11 @@
 // operand and the token tile the B operand, so each lane's accumulator holds one token and
 // four consecutive output features: stores are 8-byte (bf16) or 16-byte (fp32) vectors.
 //
-// Workgroup tile 256 features x BM tokens x 64 k, 8 waves (WN x WM), LDS double-buffered
-// with one barrier per k-tile: global loads for tile k+1 are in flight while the MFMAs of
-// tile k run.  LDS rows are 128 B (64 values) with the 16-byte chunk index XOR-swizzled by
-// ((row >> 1) & 7): gfx950's LDS serves 256 B (64 banks) per cycle, i.e. two consecutive
+// Workgroup tile 256 features x 256 tokens, 4 waves (2 x 2) each owning 128 x 128 (16
+// accumulators of 32x32 in AGPRs, one wave per SIMD).  k advances in tiles of 64 through two
+// LDS stages (128 KB) with one barrier per k-tile; global loads are staged through registers
+// one k-tile ahead.  LDS rows are 128 B (64 values) with the 16-byte chunk index XOR-swizzled
+// by ((row >> 1) & 7): gfx950's LDS serves 256 B (64 banks) per cycle, i.e. two consecutive
 // rows, so the 16 rows of one quarter-wave ds_read_b128 land on 16 distinct 16-byte slots.
 //
 // Epilogues (the fusions of the block):
@@ -26,8 +27,6 @@
 // Workgroups are remapped so that each of the 8 XCDs receives a contiguous range of tile ids,
 // and ids are ordered in groups of 4 feature tiles (feature fastest, then tokens): the 32
 // workgroups one XCD runs at a time then share 4 weight tiles and 8 token tiles in its L2.
-#include <stdlib.h>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -44,7 +43,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // byte offset inside 
 
 constexpr int kGroupN = 4;  // feature tiles per ordering group (4 x 8 tiles per XCD round)
 
-// Epilogue shared by both kernels: lane owns token (lane & 31) and features
+// Epilogue: lane owns token (lane & 31) and features
 // 8 g + 4 (lane >> 5) + {0..3} of every 32x32 sub-tile.
 template <typename T, int BM, int WN, int WM, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp, int n0, int m0,
@@ -119,136 +118,32 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
   }
 }
 
-template <typename T, int BM, int WN, int WM, int EPI>
-__global__ __launch_bounds__(64 * WN *WM) void k_gemm_mfma(GemmArgs a, int m_tiles_total,
-                                                            int t_before1, int t_before2,
-                                                            int total_tiles) {
-  constexpr int NT = 64 * WN * WM;
-  constexpr int WTN = BN / WN, WTM = BM / WM;  // wave tile
-  constexpr int FS = WTN / 32, TS = WTM / 32;  // 32x32 sub-tiles per wave
-  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 16-byte loads per thread per stage
-  constexpr int STAGE = (BN + BM) * BK * 2;
-  static_assert(LA * NT == BN * 8 && LB * NT == BM * 8, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-  // XCD-contiguous tile id: hardware places workgroup b on XCD b % 8
-  const int per = gridDim.x >> 3;
-  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lid >= total_tiles) return;
-  const int n_tiles = a.n / BN;
-  const int in_group = kGroupN * m_tiles_total;
-  const int group = lid / in_group;
-  const int first_n = group * kGroupN;
-  const int gsize = min(n_tiles - first_n, kGroupN);
-  const int rem = lid - group * in_group;
-  const int tile_n = first_n + rem % gsize;
-  const int mt = rem / gsize;
-  const int gi = (mt >= t_before1) + (mt >= t_before2);
-  const int lmt = mt - (gi == 0 ? 0 : (gi == 1 ? t_before1 : t_before2));
-  const GemmGroup grp = a.g[gi];
-  const int n0 = tile_n * BN;
-  const int m0 = lmt * BM;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WN, wm = wave / WN;
-  const int K = a.k;
-  typedef typename Mfma<T>::v8 V8;
-  const T *W = reinterpret_cast<const T *>(grp.w) + (size_t)n0 * K;
-  const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
-  const int lchunk = tid & 7, lrow = tid >> 3;
-
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK + lchunk * 8;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      ra[i] = *reinterpret_cast<const u32x4 *>(W + (size_t)(lrow + i * (NT / 8)) * K + k0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      rb[i] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + i * (NT / 8)) * a.ldx + k0);
-  };
-  auto sstore = [&](int buf) {
-    char *As = smem + buf * STAGE;
-    char *Bs = As + BN * 128;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      *reinterpret_cast<u32x4 *>(As + swz(lrow + i * (NT / 8), lchunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      *reinterpret_cast<u32x4 *>(Bs + swz(lrow + i * (NT / 8), lchunk)) = rb[i];
-  };
-
-  f32x16 acc[FS][TS];
-#pragma unroll
-  for (int i = 0; i < FS; ++i)
-#pragma unroll
-    for (int j = 0; j < TS; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int r32 = lane & 31, hk = lane >> 5;
-  // fragment double-buffering: the ds_reads of k-step s+1 are in flight while the MFMAs of
-  // k-step s run
-  V8 af[2][FS], bfr[2][TS];
-  auto load_frags = [&](const char *As, const char *Bs, int ks, V8 (&fa)[FS], V8 (&fb)[TS]) {
-    const int ch = ks * 2 + hk;
-#pragma unroll
-    for (int i = 0; i < FS; ++i)
-      fa[i] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + i * 32 + r32, ch));
-#pragma unroll
-    for (int j = 0; j < TS; ++j)
-      fb[j] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + j * 32 + r32, ch));
-  };
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const char *As = smem + buf * STAGE;
-    const char *Bs = As + BN * 128;
-    load_frags(As, Bs, 0, af[0], bfr[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) load_frags(As, Bs, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next reads ahead of these MFMAs
-#pragma unroll
-      for (int i = 0; i < FS; ++i)
-#pragma unroll
-        for (int j = 0; j < TS; ++j)
-          acc[i][j] = Mfma<T>::mma(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
-}
-
-// ------------------------------------------------------------------------------------------
-// Register-resident variant: 4 waves (2 x 2), each a 128 x 128 tile (16 accumulators of
-// 32x32, held in AGPRs), one wave per SIMD.  A k-tile (BK = 64) of fragments stays in
-// registers while its 64 MFMAs run; interleaved with those MFMAs (sched_group_barrier) the
-// wave writes the next k-tile from its staging registers into LDS, issues the global loads
-// of the one after, and, past the second barrier, reads the next k-tile's fragments.  The
-// MFMAs only touch registers, so they are free to sit on either side of the barriers.
+// Barrier for LDS hand-over only: global loads stay in flight across it (a workgroup fence
+// would also drain them).
 __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS traffic is done
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
+// Main loop.  Entering k-tile kt a wave holds the fragments of its k-steps 0 and 1.  Before
+// the barrier it runs the MFMAs of k-steps 0..2 while it reads k-steps 2 and 3 of tile kt,
+// writes tile kt+1 into the other stage and issues the global loads of tile kt+2; after the
+// barrier the MFMAs of k-step 3 overlap the reads of k-steps 0 and 1 of tile kt+1.  A stage is
+// rewritten only after the barrier that follows the last reads of its previous tile.  The
+// order of every MFMA and memory operation is pinned (sched_barrier), one memory operation
+// after each MFMA, so the LDS and global latencies sit under MFMAs.
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_v3(GemmArgs a, int m_tiles_total, int t_before1,
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int t_before1,
                                                   int t_before2, int total_tiles) {
   constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
   constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
   constexpr int FS = WTN / 32, TS = WTM / 32;  // 4 x 4
   constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 16-byte loads per thread
   constexpr int KS = BK / 16;                  // 4 k-steps per k-tile
-  __shared__ __attribute__((aligned(16))) char smem[(BN + BM) * BK * 2];
+  constexpr int STAGE = (BN + BM) * BK * 2;    // 64 KB
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   typedef typename Mfma<T>::v8 V8;
 
   const int per = gridDim.x >> 3;
@@ -274,8 +169,6 @@ __global__ __launch_bounds__(256) void k_gemm_v3(GemmArgs a, int m_tiles_total, 
   const T *W = reinterpret_cast<const T *>(grp.w) + (size_t)n0 * K;
   const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
   const int lchunk = tid & 7, lrow = tid >> 3;
-  char *As = smem;
-  char *Bs = smem + BN * 128;
 
   u32x4 ra[LA], rb[LB];
   auto gload = [&](int kt) {
@@ -287,7 +180,9 @@ __global__ __launch_bounds__(256) void k_gemm_v3(GemmArgs a, int m_tiles_total, 
     for (int i = 0; i < LB; ++i)
       rb[i] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + i * (NT / 8)) * a.ldx + k0);
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int stage) {
+    char *As = smem + stage * STAGE;
+    char *Bs = As + BN * 128;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       *reinterpret_cast<u32x4 *>(As + swz(lrow + i * (NT / 8), lchunk)) = ra[i];
@@ -297,7 +192,9 @@ __global__ __launch_bounds__(256) void k_gemm_v3(GemmArgs a, int m_tiles_total, 
   };
   const int r32 = lane & 31, hk = lane >> 5;
   V8 fr[KS][FS + TS];
-  auto lread = [&](int ks) {
+  auto lread = [&](int stage, int ks) {
+    const char *As = smem + stage * STAGE;
+    const char *Bs = As + BN * 128;
     const int ch = ks * 2 + hk;
 #pragma unroll
     for (int i = 0; i < FS; ++i)
@@ -321,51 +218,81 @@ __global__ __launch_bounds__(256) void k_gemm_v3(GemmArgs a, int m_tiles_total, 
         acc[i][j] = Mfma<T>::mma(fr[ks][i], fr[ks][FS + j], acc[i][j]);
   };
 
+  // single operations, so the loop below can fix their order exactly
+  auto mma_one = [&](int ks, int idx) {  // idx = 4 i + j
+    acc[idx >> 2][idx & 3] =
+        Mfma<T>::mma(fr[ks][idx >> 2], fr[ks][FS + (idx & 3)], acc[idx >> 2][idx & 3]);
+  };
+  auto read_one = [&](int stage, int ks, int f) {  // f < 4: weight rows, else token rows
+    const char *As = smem + stage * STAGE;
+    const char *Bs = As + BN * 128;
+    const int ch = ks * 2 + hk;
+    if (f < FS)
+      fr[ks][f] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + f * 32 + r32, ch));
+    else
+      fr[ks][f] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + (f - FS) * 32 + r32, ch));
+  };
+  auto write_one = [&](int stage, int i) {  // i < 8: weight chunk, else token chunk
+    char *As = smem + stage * STAGE;
+    char *Bs = As + BN * 128;
+    if (i < LA)
+      *reinterpret_cast<u32x4 *>(As + swz(lrow + i * (NT / 8), lchunk)) = ra[i];
+    else
+      *reinterpret_cast<u32x4 *>(Bs + swz(lrow + (i - LA) * (NT / 8), lchunk)) = rb[i - LA];
+  };
+  auto gload_one = [&](int kt, int i) {
+    const int k0 = kt * BK + lchunk * 8;
+    if (i < LA)
+      ra[i] = *reinterpret_cast<const u32x4 *>(W + (size_t)(lrow + i * (NT / 8)) * K + k0);
+    else
+      rb[i - LA] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + (i - LA) * (NT / 8)) *
+                                                    a.ldx + k0);
+  };
+
   const int KT = K / BK;
   gload(0);
-  sstore();
+  sstore(0);
   gload(KT > 1 ? 1 : 0);
   lds_sync();
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) lread(ks);
-  // every k-tile but the last: all memory operations unconditional (the prefetch index is
-  // clamped; a repeated last tile is harmless) so the interleave below spans one region
+  lread(0, 0);
+  lread(0, 1);
   for (int kt = 0; kt + 1 < KT; ++kt) {
-    lds_sync();                         // every wave holds its fragments of k-tile kt
-    sstore();                           // k-tile kt+1 into LDS
-    gload(min(kt + 2, KT - 1));
+    const int cur = kt & 1;
+    const int nk = min(kt + 2, KT - 1);  // clamped: a repeated last tile is harmless
+    // before the barrier: MFMAs of k-steps 0..2; after MFMA m comes fragment read m/3 (k-steps
+    // 2 then 3 of tile kt), LDS write m/3 (tile kt+1) or global load m/3 (tile kt+2)
+#pragma unroll
+    for (int m = 0; m < 48; ++m) {
+      mma_one(m >> 4, m & 15);
+      const int q = m / 3;
+      if (m % 3 == 0) read_one(cur, 2 + (q >> 3), q & 7);
+      else if (m % 3 == 1) write_one(cur ^ 1, q);
+      else gload_one(nk, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_sync();  // tile kt+1 written by every wave; tile kt's reads done
+    // after the barrier: MFMAs of k-step 3, each after one read of tile kt+1 (k-steps 0, 1)
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      read_one(cur ^ 1, m >> 3, m & 7);
+      mma_one(3, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  {
+    const int cur = (KT - 1) & 1;
     mma_step(0);
+    lread(cur, 2);
     mma_step(1);
-    lds_sync();                         // k-tile kt+1 visible
-    lread(0);
-    lread(1);
+    lread(cur, 3);
     mma_step(2);
     mma_step(3);
-    lread(2);
-    lread(3);
-    // 16 x {LDS write, MFMA, global load, MFMA}, then 16 x {LDS read, MFMA, MFMA}, 16 reads
-#pragma unroll
-    for (int i = 0; i < LA + LB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * (FS + TS); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FS + TS), 0);
   }
-  lds_sync();
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) mma_step(ks);
   epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
 }
 
 template <typename T, int EPI>
-hipError_t launch_v3(const GemmArgs &a, hipStream_t s) {
+hipError_t launch(const GemmArgs &a, hipStream_t s) {
   constexpr int BM = 256;
   int tb[4] = {0, 0, 0, 0};
   for (int i = 0; i < 3; ++i) tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
@@ -373,47 +300,18 @@ hipError_t launch_v3(const GemmArgs &a, hipStream_t s) {
   if (m_tiles == 0) return hipSuccess;
   const int total = m_tiles * (a.n / BN);
   const int grid = (total + 7) / 8 * 8;
-  k_gemm_v3<T, EPI><<<grid, 256, 0, s>>>(a, m_tiles, tb[1], tb[2], total);
-  return hipGetLastError();
-}
-
-template <typename T, int BM, int WN, int WM, int EPI>
-hipError_t launch(const GemmArgs &a, hipStream_t s) {
-  int tb[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 3; ++i) tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
-  const int m_tiles = tb[3];
-  if (m_tiles == 0) return hipSuccess;
-  const int total = m_tiles * (a.n / BN);
-  const int grid = (total + 7) / 8 * 8;
-  k_gemm_mfma<T, BM, WN, WM, EPI><<<grid, 64 * WN * WM, 0, s>>>(a, m_tiles, tb[1], tb[2], total);
+  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, m_tiles, tb[1], tb[2], total);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_impl() {
-  static int impl = -1;
-  if (impl < 0) {
-    const char *e = getenv("DIT_GEMM_IMPL");
-    impl = e ? atoi(e) : 3;
-  }
-  return impl;
-}
-
-template <typename T, int EPI>
-hipError_t launch_sel(const GemmArgs &a, hipStream_t s) {
-  switch (gemm_impl()) {
-    case 0: return launch<T, 256, 2, 4, EPI>(a, s);
-    default: return launch_v3<T, EPI>(a, s);
-  }
-}
-
 template <typename T>
 hipError_t dispatch(const GemmArgs &a, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_QKV_SWIGLU: return launch_sel<T, EPI_QKV_SWIGLU>(a, s);
-    case EPI_RESID: return launch_sel<T, EPI_RESID>(a, s);
-    case EPI_STORE_F32: return launch_sel<T, EPI_STORE_F32>(a, s);
+    case EPI_QKV_SWIGLU: return launch<T, EPI_QKV_SWIGLU>(a, s);
+    case EPI_RESID: return launch<T, EPI_RESID>(a, s);
+    case EPI_STORE_F32: return launch<T, EPI_STORE_F32>(a, s);
   }
   return hipErrorInvalidValue;
 }
