@@ -70,7 +70,7 @@ typedef struct {
   int head_dim;         /* must be 128: four 32-dim RoPE axes (t, h, w, l)  (128)  */
   int mlp_hidden;       /* F, SwiGLU width; multiple of 128                 (9216) */
   int in_channels;      /* C, latent channels per token; multiple of 64     (128)  */
-  int time_dim;         /* sinusoidal timestep embedding width; mult. of 16 (256)  */
+  int time_dim;         /* sinusoidal timestep embedding width; mult. of 16, <= 4096 (256) */
   int n_stream_blocks;  /* double (FLUX2) or per-mode (FLUX3) blocks        (5)    */
   int n_shared_blocks;  /* single (FLUX2) or joint (FLUX3) blocks           (20/28) */
   int max_tokens;       /* largest N any call will use (sizes the workspace)       */

@@ -106,6 +106,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = fbase + i * 32 + 8 * g;
+          if (a.n_store > 0 && n >= a.n_store) continue;
           f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                      acc[i][j][4 * g + 3]};
           if (a.accumulate) {

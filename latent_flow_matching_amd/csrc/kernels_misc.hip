@@ -274,56 +274,147 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
 // in Diffusers", "Modulation pro Token-Typ ...": scale, shift and gate come from the
 // timestep embedding).  4 waves x 4 rows per workgroup; the input vectors sit in LDS.
 // ------------------------------------------------------------------------------------------
+// Eight consecutive weights as raw registers (16-bit: one 16-byte load; fp32: two) and their
+// conversion to floats.
+template <typename TW> struct Load16;
+template <> struct Load16<bf16> {
+  typedef u32x4 raw;
+  static __device__ __forceinline__ raw load(const bf16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
+  static __device__ __forceinline__ void unpack(float (&o)[8], const raw &v) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = __uint_as_float(u[e] << 16);
+      o[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Load16<f16> {
+  typedef _Float16 raw __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ raw load(const f16 *p) { return *reinterpret_cast<const raw *>(p); }
+  static __device__ __forceinline__ void unpack(float (&o)[8], const raw &v) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+  }
+};
+struct F32x8 {
+  f32x4 a, b;
+};
+template <> struct Load16<float> {
+  typedef F32x8 raw;
+  static __device__ __forceinline__ raw load(const float *p) {
+    return F32x8{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
+  }
+  static __device__ __forceinline__ void unpack(float (&o)[8], const raw &v) {
+    o[0] = v.a.x; o[1] = v.a.y; o[2] = v.a.z; o[3] = v.a.w;
+    o[4] = v.b.x; o[5] = v.b.y; o[6] = v.b.z; o[7] = v.b.w;
+  }
+};
+
+// GEMV over up to 3 vectors, bound by streaming the weights once.  The (activated) vectors are
+// copied into LDS by every workgroup of 16 rows; each wave owns 4 rows and issues all of its
+// 16-byte weight loads (4 rows x k/512 per lane) before using any, so about 4 waves per SIMD
+// keep the HBM pipe full; one wave reduction per (row, vector) at the end.
+constexpr int kGemvRows = 4, kGemvChunks = 8;  // rows per wave; k <= 512 * kGemvChunks
+
+__global__ void k_silu(float *dst, const float *src, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = silu(src[i]);
+}
+
 template <typename TW>
 __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, int k,
-                                               const float *x, int nvec, int silu_in) {
+                                               const float *x, int nvec) {
   extern __shared__ float xs[];  // [nvec][k]
-  for (int i = threadIdx.x; i < nvec * k; i += 256) {
-    float z = x[i];
-    xs[i] = silu_in ? silu(z) : z;
+  for (int i = threadIdx.x * 4; i < nvec * k; i += 256 * 4)
+    *reinterpret_cast<f32x4 *>(xs + i) = *reinterpret_cast<const f32x4 *>(x + i);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wave) * kGemvRows;
+  typedef typename Load16<TW>::raw Raw;
+  Raw raw[kGemvRows][kGemvChunks];
+#pragma unroll
+  for (int i = 0; i < kGemvChunks; ++i) {
+    const int c = (i * 64 + lane) * 8;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+      if (c < k && row0 + r < rows) raw[r][i] = Load16<TW>::load(w + (size_t)(row0 + r) * k + c);
   }
   __syncthreads();
-  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rr = 0; rr < 4; ++rr) {
-    int row = blockIdx.x * 16 + wave * 4 + rr;
-    if (row >= rows) break;
-    const TW *wr = w + (size_t)row * k;
-    float acc[3] = {0.f, 0.f, 0.f};
-    // lane takes 4 consecutive k per step: float4 LDS reads of consecutive lanes are
-    // contiguous (no bank conflicts)
-    for (int c = lane * 4; c < k; c += 256) {
-      float wv[4];
+  float acc[kGemvRows][3];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wv[e] = to_f32(wr[c + e]);
+  for (int r = 0; r < kGemvRows; ++r)
 #pragma unroll
-      for (int v = 0; v < 3; ++v) {
-        if (v < nvec) {
-          const f32x4 xv = *reinterpret_cast<const f32x4 *>(xs + v * k + c);
-          acc[v] += (wv[0] * xv.x + wv[1] * xv.y) + (wv[2] * xv.z + wv[3] * xv.w);
-        }
-      }
-    }
+    for (int v = 0; v < 3; ++v) acc[r][v] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGemvChunks; ++i) {
+    const int c = (i * 64 + lane) * 8;
+    if (c >= k) break;
 #pragma unroll
     for (int v = 0; v < 3; ++v) {
       if (v < nvec) {
-        float t = wave_sum(acc[v]);
-        if (lane == 0) y[(size_t)v * rows + row] = t;
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(xs + v * k + c);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(xs + v * k + c + 4);
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+          if (row0 + r < rows) {
+            float wv[8];
+            Load16<TW>::unpack(wv, raw[r][i]);
+            acc[r][v] += ((wv[0] * x0.x + wv[1] * x0.y) + (wv[2] * x0.z + wv[3] * x0.w)) +
+                         ((wv[4] * x1.x + wv[5] * x1.y) + (wv[6] * x1.z + wv[7] * x1.w));
+          }
+        }
       }
     }
   }
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      if (v < nvec) {
+        const float t = wave_sum(acc[r][v]);
+        if (lane == 0 && row0 + r < rows) y[(size_t)v * rows + row0 + r] = t;
+      }
+    }
 }
 
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
-                int silu_in, hipStream_t s) {
-  if (nvec < 1 || nvec > 3 || k % 4) return hipErrorInvalidValue;
-  size_t lds = sizeof(float) * nvec * k;
-  dim3 grid((rows + 15) / 16);
+                int silu_in, float *scratch, hipStream_t s) {
+  if (nvec < 1 || nvec > 3 || k % 8 || k > 512 * kGemvChunks) return hipErrorInvalidValue;
+  if (silu_in) {
+    if (!scratch) return hipErrorInvalidValue;
+    k_silu<<<(nvec * k + 255) / 256, 256, 0, s>>>(scratch, x, nvec * k);
+    x = scratch;
+  }
+  const size_t lds = sizeof(float) * nvec * k;
+  const dim3 grid((rows + 4 * kGemvRows - 1) / (4 * kGemvRows));
   switch (w_type) {
-    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec, silu_in); break;
-    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec, silu_in); break;
-    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec, silu_in); break;
+    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec); break;
+    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec); break;
+    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// fp32 -> 16-bit rounding of a contiguous array (four elements per thread).
+template <typename T>
+__global__ void k_to_half(T *dst, const float *src, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(src + i);
+    store4(dst + i, v.x, v.y, v.z, v.w);
+  } else {
+    for (int64_t j = i; j < n; ++j) dst[j] = from_f32<T>(src[j]);
+  }
+}
+
+hipError_t to_half(void *dst, int type, const float *src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (type == OP_BF16) k_to_half<bf16><<<blocks, 256, 0, s>>>((bf16 *)dst, src, n);
+  else if (type == OP_F16) k_to_half<f16><<<blocks, 256, 0, s>>>((f16 *)dst, src, n);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

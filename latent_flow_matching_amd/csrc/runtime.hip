@@ -67,6 +67,7 @@ struct dit_ctx {
   std::vector<std::vector<Set>> blk;
   void *mod[2][3] = {{nullptr}};
   void *img_in = nullptr, *temb1 = nullptr, *temb2 = nullptr, *fmod = nullptr, *fout = nullptr;
+  void *fout_pad = nullptr;  // 16-bit paths: final.out with zero rows up to a multiple of 256
 
   int rows_alloc = 0, ldv = 0;
   float *x = nullptr;        // [rows_alloc][D] residual of dit_forward / dit_denoise
@@ -81,7 +82,8 @@ struct dit_ctx {
   float *temb_e = nullptr;   // [3][time_dim]
   float *temb_h = nullptr;   // [3][D]
   float *fmodv = nullptr;    // [3][2D]
-  float *xf = nullptr;       // [max_tokens][D]
+  float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
+  float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
 
   // per-kernel timing: hipEvents recorded on the call's stream around each launch
   struct ProfRec {
@@ -182,8 +184,9 @@ int validate_config(const dit_config *c) {
     return fail(DIT_EUNSUPPORTED, "mlp_hidden must be a positive multiple of 128, got %d", c->mlp_hidden);
   if (c->in_channels < 16 || c->in_channels % 64)
     return fail(DIT_EUNSUPPORTED, "in_channels must be a positive multiple of 64, got %d", c->in_channels);
-  if (c->time_dim < 8 || c->time_dim % 16)
-    return fail(DIT_EUNSUPPORTED, "time_dim must be a positive multiple of 16, got %d", c->time_dim);
+  if (c->time_dim < 8 || c->time_dim % 16 || c->time_dim > 4096)
+    return fail(DIT_EUNSUPPORTED, "time_dim must be a positive multiple of 16, at most 4096, got %d",
+                c->time_dim);
   if (c->n_stream_blocks < 0 || c->n_shared_blocks < 0 || c->n_stream_blocks + c->n_shared_blocks < 1)
     return fail(DIT_EINVAL, "need at least one block");
   if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
@@ -399,7 +402,19 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)3 * T * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)3 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->act, (size_t)3 * D * 4);
+  if (ctx->op == OP_F32) {
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
+  } else if (!rc) {
+    // the output head runs through the MFMA GEMM, whose feature tiles are 256 wide
+    const size_t cpad = (size_t)(c.in_channels + 255) / 256 * 256;
+    rc = dalloc(ctx, &ctx->fout_pad, cpad * D * es);
+    if (!rc) {
+      hipError_t e = hipMemcpy(ctx->fout_pad, ctx->fout, (size_t)c.in_channels * D * es,
+                               hipMemcpyDeviceToDevice);
+      if (e != hipSuccess) rc = hip_fail(e, "final.out padding");
+    }
+  }
   if (rc) {
     std::string msg = g_err;
     dit_ctx_free(ctx);
@@ -418,7 +433,7 @@ Segs make_segs(int n_txt, int n_img, int n_ref) { return Segs{n_txt, n_txt + n_i
 int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) {
   const int D = ctx->D();
   for (int s = 0; s < ctx->nsets_kind(kind); ++s)
-    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, 3 * D, D, cond, 3, 1, stream),
+    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, 3 * D, D, cond, 3, 1, ctx->act, stream),
               "modulation gemv");
   return 0;
 }
@@ -550,13 +565,13 @@ int prepare_conditioning(dit_ctx *ctx, double t, hipStream_t stream) {
   double tv[3] = {t, t, t};
   if (c.arch == DIT_FLUX3) tv[0] = tv[2] = 0.0;
   DIT_CHECK(timestep_embed(ctx->temb_e, tv, 3, c.time_dim, stream), "timestep_embed");
-  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, c.time_dim, ctx->temb_e, 3, 0, stream), "temb l1");
-  DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, stream), "temb l2");
+  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, c.time_dim, ctx->temb_e, 3, 0, nullptr, stream), "temb l1");
+  DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, ctx->act, stream), "temb l2");
   if (c.n_stream_blocks > 0)
     if (int rc = compute_mods(ctx, 0, ctx->cond, stream)) return rc;
   if (c.n_shared_blocks > 0)
     if (int rc = compute_mods(ctx, 1, ctx->cond, stream)) return rc;
-  DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, stream), "final modulation");
+  DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, ctx->act, stream), "final modulation");
   return 0;
 }
 
@@ -578,34 +593,58 @@ int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
   // sequence: text embeddings as they are, latents through the input projection
   DIT_CHECK(copy_rows_f32(ctx->x, D, txt, D, n_txt, D, stream), "copy text");
   GemmArgs ae = {};
-  ae.g[0] = GemmGroup{lat, ctx->img_in, n_img, n_txt};
-  ae.ng = 1;
-  if (n_ref > 0) ae.g[ae.ng++] = GemmGroup{ref_lat, ctx->img_in, n_ref, n_txt + n_img};
   ae.n = D;
   ae.k = C;
   ae.ldx = C;
   ae.out = ctx->x;
   ae.ldo = D;
-  DIT_TIMED(P_EMBED, 2.0 * (n_img + n_ref) * (double)C * D, 0.0,
-            gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  const double fle = 2.0 * (n_img + n_ref) * (double)C * D;
+  if (ctx->op == OP_F32) {
+    ae.g[0] = GemmGroup{lat, ctx->img_in, n_img, n_txt};
+    ae.ng = 1;
+    if (n_ref > 0) ae.g[ae.ng++] = GemmGroup{ref_lat, ctx->img_in, n_ref, n_txt + n_img};
+    DIT_TIMED(P_EMBED, fle, 0.0, gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  } else {
+    // latents rounded to the operand type (into the free xm buffer, [n_img + n_ref][C]), then
+    // the MFMA GEMM
+    char *lh = reinterpret_cast<char *>(ctx->xm);
+    const size_t es = ctx->esz();
+    DIT_TIMED(P_EMBED, 0.0, 0.0, to_half(lh, ctx->op, lat, (int64_t)n_img * C, stream), "img_in cast");
+    ae.g[0] = GemmGroup{lh, ctx->img_in, n_img, n_txt};
+    ae.ng = 1;
+    if (n_ref > 0) {
+      char *rh = lh + (size_t)n_img * C * es;
+      DIT_TIMED(P_EMBED, 0.0, 0.0, to_half(rh, ctx->op, ref_lat, (int64_t)n_ref * C, stream), "img_in cast");
+      ae.g[ae.ng++] = GemmGroup{rh, ctx->img_in, n_ref, n_txt + n_img};
+    }
+    DIT_TIMED(P_EMBED, fle, 0.0, gemm_mfma(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  }
   for (int b = 0; b < ctx->nblocks(); ++b)
     if (int rc = run_block(ctx, b, ctx->x, sg, DIT_MASK_DEFAULT, stream)) return rc;
   // output head on the image rows
   const float *fm = ctx->fmodv + 2 * D;  // image segment's (shift, scale)
   const float *fms[3] = {fm, fm, fm};
-  DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
   GemmArgs af = {};
-  af.g[0] = GemmGroup{ctx->xf, ctx->fout, n_img, 0};
   af.ng = 1;
-  af.n = C;
   af.k = D;
   af.ldx = D;
   af.out = out;
   af.ldo = C;
   af.accumulate = accumulate;
   af.alpha = alpha;
-  DIT_TIMED(P_FINAL, 2.0 * n_img * (double)C * D, 0.0,
-            gemm_simple(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+  const double flf = 2.0 * n_img * (double)C * D;
+  if (ctx->op == OP_F32) {
+    DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
+    af.g[0] = GemmGroup{ctx->xf, ctx->fout, n_img, 0};
+    af.n = C;
+    DIT_TIMED(P_FINAL, flf, 0.0, gemm_simple(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+  } else {
+    DIT_CHECK(ln_modulate(ctx->xm, ctx->op, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
+    af.g[0] = GemmGroup{ctx->xm, ctx->fout_pad, n_img, 0};
+    af.n = (C + 255) / 256 * 256;  // zero weight rows past C; only the first C columns are stored
+    af.n_store = C;
+    DIT_TIMED(P_FINAL, flf, 0.0, gemm_mfma(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+  }
   return 0;
 }
 

@@ -58,6 +58,7 @@ def _table(cfg=TINY2, drop=None, extra=None, bad_numel=None):
     ("max_tokens", 0, "max_tokens"),
     ("n_stream_blocks", -1, "block"),
     ("rope_theta", 0.0, "positive"),
+    ("time_dim", 8192, "time_dim"),
 ])
 def test_bad_config_rejected(lib, field, value, msg):
     arr, n, keep = _table()
