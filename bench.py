@@ -34,8 +34,9 @@ COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per
 KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma)?I.*Li1EEEv"),
                   ("linear2", r"k_gemm(?:_v3|_mfma)?I.*Li2EEEv"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
-                  ("ln_modulate", r"k_ln_modulate"), ("final/embed", r"k_gemm_simple"),
-                  ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
+                  ("ln_modulate", r"k_ln_modulate"),
+                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma)?I.*Li0EEEv|k_to_half"),
+                  ("conditioning", r"k_gemv|k_timestep_embed|k_silu"), ("euler noise", r"k_philox")]
 
 
 def log(*a):
@@ -151,6 +152,35 @@ def summarize_rocprof(args):
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote {out}")
+    if args.mfma_dir:
+        acc = {}
+        for r in _csv_rows(args.mfma_dir, "counter_collection.csv"):
+            cls = _kernel_class(r["Kernel_Name"])
+            if cls is None:
+                continue
+            c = acc.setdefault(cls, {})
+            c.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if not acc:
+            raise SystemExit(f"no counter_collection.csv rows under {args.mfma_dir}")
+        lines = [f"# MFMA utilisation per kernel: {wl}, {args.compute}", "",
+                 "rocprofv3 derived counters: MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / "
+                 "(max(GRBM_GUI_ACTIVE) x SIMD count) x 100, the share of SIMD-cycles the matrix "
+                 "cores were busy while the kernel ran; MfmaFlopsF16 = MFMA f16 MOPS x 512, the "
+                 "executed matrix flops.", "", "Command (from /tmp, TMPDIR=/tmp):", "", "```",
+                 args.mfma_cmd, "```", "",
+                 "| kernel class | launches | MFMA busy % (mean) | executed MFMA TFLOP per launch |",
+                 "|---|---|---|---|"]
+        for cls, c in sorted(acc.items()):
+            util = c.get("MfmaUtil", [])
+            fl = c.get("MfmaFlopsF16", []) or c.get("MfmaFlopsBF16", [])
+            n = max(len(util), len(fl))
+            lines.append(f"| {cls} | {n} | {sum(util) / len(util):.1f} | "
+                         f"{(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |" if util else
+                         f"| {cls} | {n} | - | {(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |")
+        out = os.path.join(PROFILES, f"mfma_util_{wl}.md")
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote {out}")
     if args.fetch_dir and args.write_dir and args.copy_fetch_dir and args.copy_write_dir:
         def per_kernel(d, counter):
             acc = {}
@@ -226,6 +256,8 @@ def main():
     ap.add_argument("--copy-write-dir")
     ap.add_argument("--pmc-cmd", action="append", default=[])
     ap.add_argument("--traffic-kernel", default="linear1")
+    ap.add_argument("--mfma-dir")
+    ap.add_argument("--mfma-cmd", default="")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args)

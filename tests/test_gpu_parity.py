@@ -286,3 +286,50 @@ def test_flux3_block_1024px_ref_sampled_rows(b):
     n = 512 + 4096 + 4096
     err, _ = run_block(cfg, b, 512, (64, 64), (64, 64), rows=_rows(n), max_tokens=n)
     assert err <= BF16_TOL
+
+
+# ----------------------------------------------------------------- whole stack, teacher-forced per block
+
+_STACK_WL = S.WORKLOADS["flux2_stack_512txt_1024img_4step"]
+
+
+@pytest.fixture(scope="module")
+def flux2_stack_run():
+    """All 25 FLUX.2 blocks at 512 text + 1024 image tokens (512x512 px) run on the GPU in
+    order; each block's input (the previous GPU block's output) and sampled output rows."""
+    from latent_flow_matching_amd import dit
+    wl = _STACK_WL
+    cfg = wl.model
+    segs = (wl.n_txt, wl.n_img, 0)
+    n = wl.n_tokens
+    _CTX.clear()
+    ctx = dit.DiT(cfg, S.gen_weights(cfg, bits=True), max_tokens=n)
+    x0 = S.gen_tokens(n, cfg.hidden, key=(7,))
+    cond = S.gen_cond(3, cfg.hidden)
+    pos = O.positions(wl.n_txt, wl.grid)
+    rows = _rows(n, k=14, seed=3)
+    xt = dev(x0)
+    ins, outs = [], []
+    for b in range(cfg.n_blocks):
+        ins.append(xt.cpu().numpy())
+        ctx.block_forward(b, xt, *segs, dev(pos), dev(cond))
+        torch.cuda.synchronize()
+        outs.append(xt.cpu().numpy()[rows])
+    ctx.close()
+    return cfg, segs, pos, cond, rows, ins, outs
+
+
+@pytest.mark.parametrize("b", range(_STACK_WL.model.n_blocks))
+def test_flux2_stack_512txt_1024img_per_block(flux2_stack_run, b):
+    """Teacher-forced stack parity: the oracle block runs on the GPU's own input to block b,
+    sampled output rows compared (full attention over all keys for those rows)."""
+    cfg, segs, pos, cond, rows, ins, outs = flux2_stack_run
+    kind, _, _ = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
+    w = S.gen_block_weights(cfg, b)
+    w.update(S.gen_weights(cfg, names={f"mod.{kind}.s{s}" for s in range(cfg.n_mod_sets(kind))}))
+    x = ins[b]
+    ref = oracle_block(cfg, w, b, x, segs, pos, cond, rows=rows)
+    err = rel_err(outs[b], ref)
+    derr = rel_err(outs[b] - x[rows], ref - f64(x[rows]))
+    print(f"block {b}: out err {err:.3e}  delta err {derr:.3e}", flush=True)
+    assert err <= BF16_TOL
