@@ -161,21 +161,6 @@ template <> struct Pair<float> {
   static __device__ float hi(float2 v) { return v.y; }
   static __device__ float2 make(float a, float b) { return make_float2(a, b); }
 };
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-template <> struct Pair<bf16> {
-  typedef bf16x2 type;
-  static __device__ float lo(bf16x2 v) { return to_f32(v.x); }
-  static __device__ float hi(bf16x2 v) { return to_f32(v.y); }
-  static __device__ bf16x2 make(float a, float b) { return bf16x2{to_bf16(a), to_bf16(b)}; }
-};
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-template <> struct Pair<f16> {
-  typedef f16x2 type;
-  static __device__ float lo(f16x2 v) { return to_f32(v.x); }
-  static __device__ float hi(f16x2 v) { return to_f32(v.y); }
-  static __device__ f16x2 make(float a, float b) { return f16x2{to_f16(a), to_f16(b)}; }
-};
-
 template <typename T>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_model, T *vt,
                                                        int ldv, const float *cs, int n,
@@ -213,31 +198,107 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
     *reinterpret_cast<P2 *>(qp) = Pair<T>::make(q0 * c.x - q1 * c.y, q0 * c.y + q1 * c.x);
     *reinterpret_cast<P2 *>(kp) = Pair<T>::make(k0 * c.x - k1 * c.y, k0 * c.y + k1 * c.x);
   }
-  if constexpr (sizeof(T) == 2) {
-    if (vt == nullptr) return;
-    // V transpose through LDS: tile [64 tokens][128 dims]
-    __shared__ __attribute__((aligned(16))) T tile[64][128 + 8];
-    const T *vsrc = qkv;
-    for (int c = threadIdx.x; c < 64 * 16; c += 256) {
-      int r = c >> 4, ch = c & 15;
-      int tok = t0 + r;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (tok < n)
-        val = *reinterpret_cast<const u32x4 *>(vsrc + (size_t)tok * ldq + 2 * d_model + h * 128 + ch * 8);
-      // 16-byte LDS writes into a padded row (row stride 272 B keeps them 16-byte aligned)
-      *reinterpret_cast<u32x4 *>(&tile[r][ch * 8]) = val;
+}
+
+// 16-bit path: each lane owns 8 consecutive dims of one (token, head) row (16-byte loads and
+// stores; its four RoPE pairs stay in the lane), 16 lanes per row, so a wave handles 4 tokens
+// at once and reduces the sum of squares with 4 xor-shuffles inside its 16-lane group.  All
+// loads of a wave's 16 tokens are issued before any arithmetic.  The workgroup then writes V
+// of its 64 tokens transposed into vt (zeros past n): the P.V operand layout of the attention
+// kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_model, T *vt,
+                                                         int ldv, const float *cs, int n,
+                                                         const float *qn0, const float *qn1,
+                                                         const float *qn2, const float *kn0,
+                                                         const float *kn1, const float *kn2,
+                                                         int b1, int b2, float eps) {
+  typedef typename Mfma<T>::v8 V8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y, t0 = blockIdx.x * 64;
+  const int sub = lane >> 4, c8 = (lane & 15) * 8;
+  V8 qv[4], kv[4];
+  f32x4 ca[4], cb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = t0 + wave * 16 + i * 4 + sub;
+    if (tok < n) {
+      const T *qp = qkv + (size_t)tok * ldq + h * 128 + c8;
+      qv[i] = *reinterpret_cast<const V8 *>(qp);
+      kv[i] = *reinterpret_cast<const V8 *>(qp + d_model);
+      const float *cp = cs + (size_t)tok * 128 + c8;  // (cos, sin) of pairs c8/2 .. c8/2 + 3
+      ca[i] = *reinterpret_cast<const f32x4 *>(cp);
+      cb[i] = *reinterpret_cast<const f32x4 *>(cp + 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[i][e] = kv[i][e] = (T)0.f;
+      ca[i] = cb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    for (int c = threadIdx.x; c < 128 * 8; c += 256) {
-      int d = c & 127, ch = c >> 7;  // consecutive lanes take consecutive dims
-      typename Mfma<T>::v8 o;
-      // within every 16 tokens the middle two quads are swapped (column order 0-3, 8-11,
-      // 4-7, 12-15), so the eight keys one attention lane multiplies are contiguous
-      const int base = (ch >> 1) * 16 + ((ch & 1) ? 4 : 0);
-  #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = tile[base + (e < 4 ? e : e + 4)][d];
-      *reinterpret_cast<typename Mfma<T>::v8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = t0 + wave * 16 + i * 4 + sub;
+    float q[8], k[8];
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q[e] = (float)qv[i][e];
+      k[e] = (float)kv[i][e];
+      sq += q[e] * q[e];
+      sk += k[e] * k[e];
     }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {  // sum over the 16 lanes of this row
+      sq += __shfl_xor(sq, m, 16);
+      sk += __shfl_xor(sk, m, 16);
+    }
+    if (tok >= n) continue;
+    const int seg = segment_of(tok, b1, b2);
+    const float *qn = (seg == 0 ? qn0 : (seg == 1 ? qn1 : qn2)) + c8;
+    const float *kn = (seg == 0 ? kn0 : (seg == 1 ? kn1 : kn2)) + c8;
+    const float rq = 1.0f / sqrtf(sq * (1.0f / 128.f) + eps);
+    const float rk = 1.0f / sqrtf(sk * (1.0f / 128.f) + eps);
+    const f32x4 wq0 = *reinterpret_cast<const f32x4 *>(qn), wq1 = *reinterpret_cast<const f32x4 *>(qn + 4);
+    const f32x4 wk0 = *reinterpret_cast<const f32x4 *>(kn), wk1 = *reinterpret_cast<const f32x4 *>(kn + 4);
+    const float wq[8] = {wq0.x, wq0.y, wq0.z, wq0.w, wq1.x, wq1.y, wq1.z, wq1.w};
+    const float wk[8] = {wk0.x, wk0.y, wk0.z, wk0.w, wk1.x, wk1.y, wk1.z, wk1.w};
+    const float cv[8] = {ca[i].x, ca[i].y, ca[i].z, ca[i].w, cb[i].x, cb[i].y, cb[i].z, cb[i].w};
+    V8 qo, ko;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float c = cv[2 * p], sn = cv[2 * p + 1];
+      const float qa = q[2 * p] * rq * wq[2 * p], qb = q[2 * p + 1] * rq * wq[2 * p + 1];
+      const float ka = k[2 * p] * rk * wk[2 * p], kb = k[2 * p + 1] * rk * wk[2 * p + 1];
+      qo[2 * p] = from_f32<T>(qa * c - qb * sn);
+      qo[2 * p + 1] = from_f32<T>(qa * sn + qb * c);
+      ko[2 * p] = from_f32<T>(ka * c - kb * sn);
+      ko[2 * p + 1] = from_f32<T>(ka * sn + kb * c);
+    }
+    T *qp = qkv + (size_t)tok * ldq + h * 128 + c8;
+    *reinterpret_cast<V8 *>(qp) = qo;
+    *reinterpret_cast<V8 *>(qp + d_model) = ko;
+  }
+  if (vt == nullptr) return;
+  // V transpose through LDS: tile [64 tokens][128 dims]
+  __shared__ __attribute__((aligned(16))) T tile[64][128 + 8];
+  for (int c = threadIdx.x; c < 64 * 16; c += 256) {
+    const int r = c >> 4, ch = c & 15;
+    const int tok = t0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (tok < n)
+      val = *reinterpret_cast<const u32x4 *>(qkv + (size_t)tok * ldq + 2 * d_model + h * 128 + ch * 8);
+    *reinterpret_cast<u32x4 *>(&tile[r][ch * 8]) = val;  // 272-B rows keep 16-byte alignment
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < 128 * 8; c += 256) {
+    const int d = c & 127, ch = c >> 7;  // consecutive lanes take consecutive dims
+    V8 o;
+    // within every 16 tokens the middle two quads are swapped (column order 0-3, 8-11, 4-7,
+    // 12-15), so the eight keys one attention lane multiplies are contiguous
+    const int base = (ch >> 1) * 16 + ((ch & 1) ? 4 : 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = tile[base + (e < 4 ? e : e + 4)][d];
+    *reinterpret_cast<V8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
   }
 }
 
@@ -248,12 +309,12 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
   dim3 grid(n / 64 + 2, heads);  // covers [0, n + 64) for the V transpose
   switch (type) {
     case OP_BF16:
-      k_qk_norm_rope<bf16><<<grid, 256, 0, s>>>((bf16 *)qkv, ldq, d_model, (bf16 *)vt, ldv, cs, n,
+      k_qk_norm_rope16<bf16><<<grid, 256, 0, s>>>((bf16 *)qkv, ldq, d_model, (bf16 *)vt, ldv, cs, n,
                                                 qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
                                                 segs.b2, eps);
       break;
     case OP_F16:
-      k_qk_norm_rope<f16><<<grid, 256, 0, s>>>((f16 *)qkv, ldq, d_model, (f16 *)vt, ldv, cs, n,
+      k_qk_norm_rope16<f16><<<grid, 256, 0, s>>>((f16 *)qkv, ldq, d_model, (f16 *)vt, ldv, cs, n,
                                                qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
                                                segs.b2, eps);
       break;
