@@ -333,3 +333,44 @@ def test_flux2_stack_512txt_1024img_per_block(flux2_stack_run, b):
     derr = rel_err(outs[b] - x[rows], ref - f64(x[rows]))
     print(f"block {b}: out err {err:.3e}  delta err {derr:.3e}", flush=True)
     assert err <= BF16_TOL
+
+
+@pytest.fixture(scope="module")
+def flux3_stack_run():
+    """All 33 FLUX.3 blocks (5 per-mode, block-diagonal; 28 joint) at 128 text + 16x16 image +
+    16x16 reference tokens, run on the GPU in order."""
+    from latent_flow_matching_amd import dit
+    cfg = S.FLUX3_KLEIN
+    n_txt, grid, ref_grid = 128, (16, 16), (16, 16)
+    segs = (n_txt, 256, 256)
+    n = sum(segs)
+    _CTX.clear()
+    ctx = dit.DiT(cfg, S.gen_weights(cfg, bits=True), max_tokens=n)
+    x0 = S.gen_tokens(n, cfg.hidden, key=(8,))
+    cond = S.gen_cond(3, cfg.hidden)
+    pos = O.positions(n_txt, grid, (ref_grid,))
+    rows = _rows(n, k=14, seed=4)
+    xt = dev(x0)
+    ins, outs = [], []
+    for b in range(cfg.n_blocks):
+        ins.append(xt.cpu().numpy())
+        ctx.block_forward(b, xt, *segs, dev(pos), dev(cond))
+        torch.cuda.synchronize()
+        outs.append(xt.cpu().numpy()[rows])
+    ctx.close()
+    return cfg, segs, pos, cond, rows, ins, outs
+
+
+@pytest.mark.parametrize("b", range(S.FLUX3_KLEIN.n_blocks))
+def test_flux3_stack_128txt_256img_256ref_per_block(flux3_stack_run, b):
+    """Teacher-forced FLUX.3 stack parity, per block, on the GPU's own block inputs."""
+    cfg, segs, pos, cond, rows, ins, outs = flux3_stack_run
+    kind, _, _ = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
+    w = S.gen_block_weights(cfg, b)
+    w.update(S.gen_weights(cfg, names={f"mod.{kind}.s{s}" for s in range(cfg.n_mod_sets(kind))}))
+    x = ins[b]
+    ref = oracle_block(cfg, w, b, x, segs, pos, cond, rows=rows)
+    err = rel_err(outs[b], ref)
+    derr = rel_err(outs[b] - x[rows], ref - f64(x[rows]))
+    print(f"block {b}: out err {err:.3e}  delta err {derr:.3e}", flush=True)
+    assert err <= BF16_TOL
