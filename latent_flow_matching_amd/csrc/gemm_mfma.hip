@@ -134,7 +134,9 @@ __device__ __forceinline__ void lds_sync() {
 // barrier the MFMAs of k-step 3 overlap the reads of k-steps 0 and 1 of tile kt+1.  A stage is
 // rewritten only after the barrier that follows the last reads of its previous tile.  The
 // order of every MFMA and memory operation is pinned (sched_barrier), one memory operation
-// after each MFMA, so the LDS and global latencies sit under MFMAs.
+// after each MFMA, so the LDS and global latencies sit under MFMAs.  Token rows, which miss L2
+// more often than weight rows under the grouped tile order, get two staging sets and so two
+// k-tiles of latency cover.
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int t_before1,
                                                   int t_before2, int total_tiles) {
@@ -171,17 +173,33 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
   const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
   const int lchunk = tid & 7, lrow = tid >> 3;
 
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK + lchunk * 8;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      ra[i] = *reinterpret_cast<const u32x4 *>(W + (size_t)(lrow + i * (NT / 8)) * K + k0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      rb[i] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + i * (NT / 8)) * a.ldx + k0);
+  // Global loads are buffer loads: one descriptor per operand (the weight tile's 256 rows; the
+  // token rows from m0 to the group's end, so rows past it read as zero), one per-lane byte
+  // offset, and the row / k-tile offsets in scalar registers.
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)W, (short)0, (int)min((long long)BN * K * 2, 0x7FFFFFFFll), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)X, (short)0, (int)min((long long)(grp.rows - m0) * a.ldx * 2, 0x7FFFFFFFll),
+      0x00020000);
+  const int vo_w = (lrow * K + lchunk * 8) * 2, vo_x = (lrow * a.ldx + lchunk * 8) * 2;
+  auto load_w = [&](int kt, int i) -> u32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs_w, vo_w, (i * (NT / 8) * K + kt * BK) * 2, 0);
   };
-  auto sstore = [&](int stage) {
+  auto load_x = [&](int kt, int i) -> u32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs_x, vo_x, (i * (NT / 8) * a.ldx + kt * BK) * 2, 0);
+  };
+  // staging registers: weight rows one set (tile kt+2 loads while tile kt+1 is written to
+  // LDS), token rows two sets (tile j in set j % 2, loaded three k-tiles ahead)
+  u32x4 ra[LA], rb0[LB], rb1[LB];
+  auto gload_a = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[i] = load_w(kt, i);
+  };
+  auto gload_b = [&](int kt, u32x4 (&rb)[LB]) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = load_x(kt, i);
+  };
+  auto sstore = [&](int stage, const u32x4 (&rb)[LB]) {
     char *As = smem + stage * STAGE;
     char *Bs = As + BN * 128;
 #pragma unroll
@@ -233,7 +251,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
     else
       fr[ks][f] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + (f - FS) * 32 + r32, ch));
   };
-  auto write_one = [&](int stage, int i) {  // i < 8: weight chunk, else token chunk
+  auto write_one = [&](int stage, int i, const u32x4 (&rb)[LB]) {  // i < 8: weights
     char *As = smem + stage * STAGE;
     char *Bs = As + BN * 128;
     if (i < LA)
@@ -241,34 +259,34 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
     else
       *reinterpret_cast<u32x4 *>(Bs + swz(lrow + (i - LA) * (NT / 8), lchunk)) = rb[i - LA];
   };
-  auto gload_one = [&](int kt, int i) {
-    const int k0 = kt * BK + lchunk * 8;
-    if (i < LA)
-      ra[i] = *reinterpret_cast<const u32x4 *>(W + (size_t)(lrow + i * (NT / 8)) * K + k0);
-    else
-      rb[i - LA] = *reinterpret_cast<const u32x4 *>(X + (size_t)(lrow + (i - LA) * (NT / 8)) *
-                                                    a.ldx + k0);
+  auto gload_one = [&](int kta, int ktb, int i, u32x4 (&rb)[LB]) {  // weights kta, tokens ktb
+    if (i < LA) ra[i] = load_w(kta, i);
+    else rb[i - LA] = load_x(ktb, i - LA);
   };
 
   const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  gload(KT > 1 ? 1 : 0);
+  gload_a(0);
+  gload_b(0, rb0);
+  sstore(0, rb0);
+  gload_a(min(1, KT - 1));
+  gload_b(min(1, KT - 1), rb1);
+  gload_b(min(2, KT - 1), rb0);
   lds_sync();
   lread(0, 0);
   lread(0, 1);
-  for (int kt = 0; kt + 1 < KT; ++kt) {
+  // one k-tile; rb holds the token rows of tile kt+1 and receives those of tile kt+3
+  auto ktile = [&](int kt, u32x4 (&rb)[LB]) {
     const int cur = kt & 1;
-    const int nk = min(kt + 2, KT - 1);  // clamped: a repeated last tile is harmless
+    const int na = min(kt + 2, KT - 1), nb = min(kt + 3, KT - 1);  // clamped: repeats harmless
     // before the barrier: MFMAs of k-steps 0..2; after MFMA m comes fragment read m/3 (k-steps
-    // 2 then 3 of tile kt), LDS write m/3 (tile kt+1) or global load m/3 (tile kt+2)
+    // 2 then 3 of tile kt), LDS write m/3 (tile kt+1) or global load m/3
 #pragma unroll
     for (int m = 0; m < 48; ++m) {
       mma_one(m >> 4, m & 15);
       const int q = m / 3;
       if (m % 3 == 0) read_one(cur, 2 + (q >> 3), q & 7);
-      else if (m % 3 == 1) write_one(cur ^ 1, q);
-      else gload_one(nk, q);
+      else if (m % 3 == 1) write_one(cur ^ 1, q, rb);
+      else gload_one(na, nb, q, rb);
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_sync();  // tile kt+1 written by every wave; tile kt's reads done
@@ -279,7 +297,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
       mma_one(3, m);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    ktile(kt, rb1);
+    ktile(kt + 1, rb0);
   }
+  if (kt + 1 < KT) ktile(kt, rb1);
   {
     const int cur = (KT - 1) & 1;
     mma_step(0);
