@@ -167,6 +167,10 @@ const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t
  * Kernel classes: "ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2",
  * "conditioning", "embed", "final". */
 int dit_profile_start(dit_ctx *ctx, int max_launches);
+/* Restrict the timed launches to a comma-separated list of kernel classes (for example
+ * "linear1"), so that a benchmark can time one class with few events in the stream; NULL or ""
+ * selects every class.  Unknown names: DIT_EINVAL, selection unchanged. */
+int dit_profile_select(dit_ctx *ctx, const char *kernels);
 int dit_profile_stop(dit_ctx *ctx);
 int dit_profile_get(dit_ctx *ctx, const char *kernel, double *ms, int64_t *launches,
                     double *flops, double *bytes);

@@ -92,6 +92,7 @@ struct dit_ctx {
     int e0, e1;
   };
   bool prof_on = false;
+  unsigned prof_mask = ~0u;  // kernel classes that record events (bit per class)
   std::vector<hipEvent_t> prof_ev;
   std::vector<ProfRec> prof_rec;
   int prof_next = 0;
@@ -137,8 +138,10 @@ const char *const kProfNames[P_NCLASS] = {"ln_modulate", "linear1", "qk_norm_rop
                                           "linear2", "conditioning", "embed", "final"};
 
 // Start / end markers around one launch when timing is on (no-op otherwise).
-int prof_begin(dit_ctx *ctx, hipStream_t stream) {
-  if (!ctx->prof_on || ctx->prof_next + 2 > (int)ctx->prof_ev.size()) return -1;
+int prof_begin(dit_ctx *ctx, int cls, hipStream_t stream) {
+  if (!ctx->prof_on || !((ctx->prof_mask >> cls) & 1u) ||
+      ctx->prof_next + 2 > (int)ctx->prof_ev.size())
+    return -1;
   const int e = ctx->prof_next;
   ctx->prof_next += 2;
   (void)hipEventRecord(ctx->prof_ev[e], stream);
@@ -152,7 +155,7 @@ void prof_end(dit_ctx *ctx, int e, int cls, double flops, double bytes, hipStrea
 
 #define DIT_TIMED(cls, flops, bytes, call, what)               \
   do {                                                          \
-    const int pe_ = prof_begin(ctx, stream);                    \
+    const int pe_ = prof_begin(ctx, cls, stream);               \
     DIT_CHECK(call, what);                                      \
     prof_end(ctx, pe_, cls, flops, bytes, stream);              \
   } while (0)
@@ -584,7 +587,7 @@ int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
   const int n_img = gh * gw, n_ref = rgh * rgw;
   const Segs sg = make_segs(n_txt, n_img, n_ref);
   {
-    const int pe = prof_begin(ctx, stream);
+    const int pe = prof_begin(ctx, P_COND, stream);
     if (int rc = prepare_conditioning(ctx, t, stream)) return rc;
     prof_end(ctx, pe, P_COND, 0.0, 0.0, stream);
   }
@@ -745,6 +748,30 @@ extern "C" int dit_profile_start(dit_ctx *ctx, int max_launches) {
   ctx->prof_rec.clear();
   ctx->prof_next = 0;
   ctx->prof_on = true;
+  return 0;
+}
+
+extern "C" int dit_profile_select(dit_ctx *ctx, const char *kernels) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (!kernels || !kernels[0]) {
+    ctx->prof_mask = ~0u;
+    return 0;
+  }
+  unsigned mask = 0;
+  std::string list(kernels);
+  size_t pos = 0;
+  while (pos <= list.size()) {
+    const size_t end = std::min(list.find(',', pos), list.size());
+    const std::string name = list.substr(pos, end - pos);
+    int cls = -1;
+    for (int i = 0; i < P_NCLASS; ++i)
+      if (name == kProfNames[i]) cls = i;
+    if (cls < 0) return fail(DIT_EINVAL, "unknown kernel class '%s'", name.c_str());
+    mask |= 1u << cls;
+    pos = end + 1;
+  }
+  ctx->prof_mask = mask;
   return 0;
 }
 

@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.dit_debug_buffer.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(I), ctypes.POINTER(I64)]
     lib.dit_profile_start.restype = I
     lib.dit_profile_start.argtypes = [P, I]
+    lib.dit_profile_select.restype = I
+    lib.dit_profile_select.argtypes = [P, ctypes.c_char_p]
     lib.dit_profile_stop.restype = I
     lib.dit_profile_stop.argtypes = [P]
     D = ctypes.POINTER(ctypes.c_double)
@@ -185,8 +187,11 @@ class DiT:
     KERNELS = ("ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2", "conditioning",
                "embed", "final")
 
-    def profile_start(self, max_launches: int = 100000):
-        _check(load_library().dit_profile_start(self._h, max_launches))
+    def profile_start(self, max_launches: int = 100000, kernels: str | None = None):
+        """Time the following launches; kernels = comma-separated classes (None: all)."""
+        lib = load_library()
+        _check(lib.dit_profile_select(self._h, None if kernels is None else kernels.encode()))
+        _check(lib.dit_profile_start(self._h, max_launches))
 
     def profile_stop(self) -> dict:
         """Stop timing; {kernel: (ms, launches, flops, bytes)} over the recorded launches."""

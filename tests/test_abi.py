@@ -94,6 +94,9 @@ def test_null_context_calls_fail(lib):
     assert lib.dit_denoise(None, None, None, 1, 1, 1, None, 0, 0, 4, -1, None) == dit.DIT_EINVAL
     assert lib.dit_fill_noise(None, 4, 1, None) == dit.DIT_EINVAL
     assert lib.dit_debug_buffer(None, b"xm", None, None) is None
+    assert lib.dit_profile_start(None, 10) == dit.DIT_EINVAL
+    assert lib.dit_profile_select(None, b"linear1") == dit.DIT_EINVAL
+    assert lib.dit_profile_stop(None) == dit.DIT_EINVAL
     lib.dit_ctx_free(None)   # no-op
 
 
