@@ -79,7 +79,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU with the hardware reciprocal (1 ulp) instead of an IEEE division: z * 1 / (1 + e^-z),
+// which still gives -0 for z -> -inf (e^-z = inf) and z for large z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Segment (0 text, 1 image, 2 reference) of token row m given the two boundaries.
 __device__ __forceinline__ int segment_of(int m, int b1, int b2) {
