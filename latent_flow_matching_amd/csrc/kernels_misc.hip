@@ -69,72 +69,80 @@ hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream
 // LayerNorm without affine parameters, then y * (1 + scale_s) + shift_s with the segment's
 // modulation ("FLUX.3 Image Klein in Diffusers", "Modulation pro Token-Typ ...": each block
 // starts with a parameter-free LayerNorm whose scale and shift come from the timestep
-// embedding).  One wave per row; the row stays in registers (D <= 4096, D % 256 == 0).
+// embedding).  One 256-thread workgroup per row (D <= 4096, D % 256 == 0): thread t holds
+// the float4 columns t, t + 256, ... and that row's shift/scale, all loaded up front, and the
+// two-pass mean/variance reduce through LDS.  Many small workgroups with few registers keep
+// HBM busier than one wave per row with the whole row in one wave's registers.
 // ------------------------------------------------------------------------------------------
-constexpr int kLnMaxVec = 16;  // float4 per lane -> D <= 64 * 4 * 16 = 4096
+constexpr int kLnMaxVec = 4;  // float4 per thread -> D <= 256 * 4 * 4 = 4096
 
 template <typename TO>
 __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const float *x, int ldx,
-                                                      int rows, int row0, int d, float eps,
+                                                      int row0, int d, float eps,
                                                       const float *m0, const float *m1,
                                                       const float *m2, int b1, int b2) {
-  int lane = threadIdx.x & 63;
-  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  int tok = row0 + r;
+  __shared__ float red[2][4];
+  const int t = threadIdx.x, w = t >> 6;
+  const int r = blockIdx.x, tok = row0 + r;
+  const int nv4 = d >> 2;  // float4 columns; a multiple of 64, so each wave is all in or all out
   const float *xr = x + (size_t)tok * ldx;
-  int nv = d >> 8;
-  f32x4 v[kLnMaxVec];
+  const int seg = segment_of(tok, b1, b2);
+  const float *shift = seg == 0 ? m0 : (seg == 1 ? m1 : m2), *scale = shift + d;
+  f32x4 v[kLnMaxVec], sh[kLnMaxVec], sc[kLnMaxVec];
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i)
+    if (i * 256 + t < nv4) v[i] = *reinterpret_cast<const f32x4 *>(xr + (i * 256 + t) * 4);
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i)
+    if (i * 256 + t < nv4) {
+      sh[i] = *reinterpret_cast<const f32x4 *>(shift + (i * 256 + t) * 4);
+      sc[i] = *reinterpret_cast<const f32x4 *>(scale + (i * 256 + t) * 4);
+    }
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
-      v[i] = *reinterpret_cast<const f32x4 *>(xr + (i * 64 + lane) * 4);
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
-  }
-  float mean = wave_sum(sum) / (float)d;
+  for (int i = 0; i < kLnMaxVec; ++i)
+    if (i * 256 + t < nv4) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  sum = wave_sum(sum);
+  if ((t & 63) == 0) red[0][w] = sum;
+  __syncthreads();
+  const float mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)d;
   float sq = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
-      float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+  for (int i = 0; i < kLnMaxVec; ++i)
+    if (i * 256 + t < nv4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
       sq += (a * a + b * b) + (c * c + e * e);
     }
-  }
-  float var = wave_sum(sq) / (float)d;
-  float rstd = 1.0f / sqrtf(var + eps);
-  int seg = segment_of(tok, b1, b2);
-  const float *mod = seg == 0 ? m0 : (seg == 1 ? m1 : m2);
-  const float *shift = mod, *scale = mod + d;
+  sq = wave_sum(sq);
+  if ((t & 63) == 0) red[1][w] = sq;
+  __syncthreads();
+  const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)d;
+  const float rstd = 1.0f / sqrtf(var + eps);
   TO *orow = out + (size_t)r * ldo;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
-      int c = (i * 64 + lane) * 4;
-      f32x4 sh = *reinterpret_cast<const f32x4 *>(shift + c);
-      f32x4 sc = *reinterpret_cast<const f32x4 *>(scale + c);
-      float y0 = (v[i].x - mean) * rstd * (1.f + sc.x) + sh.x;
-      float y1 = (v[i].y - mean) * rstd * (1.f + sc.y) + sh.y;
-      float y2 = (v[i].z - mean) * rstd * (1.f + sc.z) + sh.z;
-      float y3 = (v[i].w - mean) * rstd * (1.f + sc.w) + sh.w;
+  for (int i = 0; i < kLnMaxVec; ++i)
+    if (i * 256 + t < nv4) {
+      const int c = (i * 256 + t) * 4;
+      const float y0 = (v[i].x - mean) * rstd * (1.f + sc[i].x) + sh[i].x;
+      const float y1 = (v[i].y - mean) * rstd * (1.f + sc[i].y) + sh[i].y;
+      const float y2 = (v[i].z - mean) * rstd * (1.f + sc[i].z) + sh[i].z;
+      const float y3 = (v[i].w - mean) * rstd * (1.f + sc[i].w) + sh[i].w;
       store4(orow + c, y0, y1, y2, y3);
     }
-  }
 }
 
 template <typename TO>
 void launch_ln(void *out, int ldo, const float *x, int ldx, int rows, int row0, int d, float eps,
                const float *const m[3], Segs sg, hipStream_t s) {
-  k_ln_modulate<TO><<<(rows + 3) / 4, 256, 0, s>>>((TO *)out, ldo, x, ldx, rows, row0, d, eps,
-                                                   m[0], m[1], m[2], sg.b1, sg.b2);
+  k_ln_modulate<TO><<<rows, 256, 0, s>>>((TO *)out, ldo, x, ldx, row0, d, eps, m[0], m[1], m[2],
+                                          sg.b1, sg.b2);
 }
 
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
                        int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d % 256 || d > 64 * 4 * kLnMaxVec) return hipErrorInvalidValue;
+  if (d % 256 || d > 256 * 4 * kLnMaxVec) return hipErrorInvalidValue;
   switch (out_type) {
     case OP_F32: launch_ln<float>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
     case OP_BF16: launch_ln<bf16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
@@ -279,25 +287,32 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
     *reinterpret_cast<V8 *>(qp + d_model) = ko;
   }
   if (vt == nullptr) return;
-  // V transpose through LDS: tile [64 tokens][128 dims]
-  __shared__ __attribute__((aligned(16))) T tile[64][128 + 8];
+  // V transpose through LDS: tile [64 tokens][128 dims] with a 130-element (65-dword) pitch,
+  // so the eight rows one read instruction touches fall in distinct banks
+  constexpr int kPitch = 130;
+  __shared__ __attribute__((aligned(16))) T tile[64 * kPitch];
   for (int c = threadIdx.x; c < 64 * 16; c += 256) {
     const int r = c >> 4, ch = c & 15;
     const int tok = t0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (tok < n)
       val = *reinterpret_cast<const u32x4 *>(qkv + (size_t)tok * ldq + 2 * d_model + h * 128 + ch * 8);
-    *reinterpret_cast<u32x4 *>(&tile[r][ch * 8]) = val;  // 272-B rows keep 16-byte alignment
+    uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[r * kPitch + ch * 8]);  // 4-byte aligned
+    dst[0] = val.x;
+    dst[1] = val.y;
+    dst[2] = val.z;
+    dst[3] = val.w;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < 128 * 8; c += 256) {
-    const int d = c & 127, ch = c >> 7;  // consecutive lanes take consecutive dims
+    // eight consecutive lanes write the 128 contiguous bytes (64 keys) of one dim's row
+    const int d = c >> 3, ch = c & 7;
     V8 o;
     // within every 16 tokens the middle two quads are swapped (column order 0-3, 8-11, 4-7,
     // 12-15), so the eight keys one attention lane multiplies are contiguous
     const int base = (ch >> 1) * 16 + ((ch & 1) ? 4 : 0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = tile[base + (e < 4 ? e : e + 4)][d];
+    for (int e = 0; e < 8; ++e) o[e] = tile[(base + (e < 4 ? e : e + 4)) * kPitch + d];
     *reinterpret_cast<V8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
   }
 }
