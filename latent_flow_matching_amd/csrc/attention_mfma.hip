@@ -21,6 +21,14 @@
 // (scale * log2(e) folded into one FMA before exp2).
 // Groups: each (q0, q1, k0, k1) range gets its own query tiles; key tiles start at k0
 // rounded down to 64 and keys outside [k0, k1) are masked to -inf.
+//
+// Load balance: a unit is (head, 256-query tile) and needs one pass over its key tiles.  When
+// there are more units than compute units, the grid is one workgroup per compute unit and
+// each takes an equal share of all (unit, key tile) iterations, so the last round does not
+// leave part of the chip idle.  A unit cut by a share boundary is computed in pieces; each
+// piece stores its unnormalised O with its row max and row sum, and the piece that finishes
+// last (a per-unit counter) merges the pieces in piece order, so the result does not depend
+// on which workgroup finished first.  Nothing ever waits on another workgroup.
 #include <math.h>
 
 #include <type_traits>
@@ -60,38 +68,78 @@ __device__ __forceinline__ int v_off(int row, int chunk) {
 // while a wave may still read it.
 constexpr int BQ = 256;
 
+// Work plan: units are numbered head-major, query tiles within a head in group order; the
+// iterations of a unit are its key tiles.
+struct AttnPlan {
+  int tb1, tb2, q_tiles;  // first query tile of groups 1 and 2; query tiles per head
+  int nk[3];              // key tiles per unit of each group
+  int cum1, cum2;         // iterations of a head before groups 1 and 2
+  int iters_head, iters;  // iterations per head, in total
+  int total;              // units
+  int lean;               // 1: equal iteration shares over the grid; 0: one unit per workgroup
+};
+
+struct Unit {
+  int head, qt, g, t;  // head, query tile, group, key tile within the unit
+};
+__device__ __forceinline__ Unit decode(const AttnPlan &p, int it) {
+  Unit u;
+  u.head = it / p.iters_head;
+  const int r = it - u.head * p.iters_head;
+  u.g = (r >= p.cum1) + (r >= p.cum2);
+  const int rr = r - (u.g == 0 ? 0 : (u.g == 1 ? p.cum1 : p.cum2));
+  const int ql = rr / p.nk[u.g];
+  u.t = rr - ql * p.nk[u.g];
+  u.qt = (u.g == 0 ? 0 : (u.g == 1 ? p.tb1 : p.tb2)) + ql;
+  return u;
+}
+// first iteration of the share of workgroup w, and the workgroup whose share holds it
+__device__ __forceinline__ int share_begin(const AttnPlan &p, int w, int grid) {
+  return (int)((long long)p.iters * w / grid);
+}
+__device__ __forceinline__ int share_owner(const AttnPlan &p, int it, int grid) {
+  return (int)(((long long)(it + 1) * grid + p.iters - 1) / p.iters) - 1;
+}
+
+// Partial results of a piece: O as 16 float4 per lane and wave, then (max, sum) per lane.
+constexpr int kPartO = 8 * 16 * 64 * 4;
+constexpr int kPartFloats = kPartO + 8 * 64 * 2;
+static_assert(kPartFloats == attn_part_floats, "partial slot size");
+constexpr int kSc1 = 16;  // buffer access cache policy: device-coherent (sc1)
+
 template <typename T>
-__global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, int qt_before1, int qt_before2,
-                                                     int q_tiles, int total) {
+__global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   typedef typename Mfma<T>::v8 V8;
   __shared__ __attribute__((aligned(16))) char smem[2 * KT_BYTES + 2 * VT_BYTES];
+  __shared__ int merge_flag;
 
-  const int per = gridDim.x >> 3;
+  const int G = gridDim.x;
+  const int per = G >> 3;
   const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lid >= total) return;
-  const int head = lid / q_tiles;
-  const int qt = lid - head * q_tiles;
-  const int gi = (qt >= qt_before1) + (qt >= qt_before2);
-  const AttnGroup grp = a.g[gi];
-  const int q_tile0 =
-      grp.q0 + (qt - (gi == 0 ? 0 : (gi == 1 ? qt_before1 : qt_before2))) * BQ;
+  int it0, it1;
+  if (p.lean) {
+    it0 = share_begin(p, lid, G);
+    it1 = share_begin(p, lid + 1, G);
+  } else {
+    if (lid >= p.total) return;
+    const int hd = lid / p.q_tiles, qt = lid - hd * p.q_tiles;
+    const int g = (qt >= p.tb1) + (qt >= p.tb2);
+    it0 = hd * p.iters_head + (g == 0 ? 0 : (g == 1 ? p.cum1 : p.cum2)) +
+          (qt - (g == 0 ? 0 : (g == 1 ? p.tb1 : p.tb2))) * p.nk[g];
+    it1 = it0 + p.nk[g];
+  }
+  if (it0 >= it1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, hk = lane >> 5;
   const int half = wave >> 2;  // waves w and w+4 of a workgroup share a SIMD
   const T *qkv = reinterpret_cast<const T *>(a.qkv);
-  const T *vt = reinterpret_cast<const T *>(a.vt) + (size_t)head * HD * a.ldv;
 
-  const int q = q_tile0 + wave * 32 + r32;
+  // state of the piece being computed (set at the top of the piece loop)
+  int head = 0, q = 0, kv_begin = 0, n = 0;
+  AttnGroup grp = a.g[0];
+  const T *vt = nullptr;
   V8 qf[8];
-  {
-    const T *qp = qkv + (size_t)q * a.ldqkv + head * HD + hk * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const V8 *>(qp + kk * 16);
-  }
-
-  const int kv_begin = (grp.k0 / BKV) * BKV;
-  const int n = (grp.k1 - kv_begin + BKV - 1) / BKV;
 
   u32x4 rk[2], rv[2];
   const int k_row = tid >> 4, k_ch = tid & 15;   // K: rows k_row + 32 i
@@ -226,41 +274,173 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, int qt_before1, 
   using I0 = std::integral_constant<int, 0>;
   using I16 = std::integral_constant<int, 16>;
   using I32 = std::integral_constant<int, 32>;
-  // Local phase 2t is M(t), 2t+1 is V(t); half B runs one global phase behind half A (one
-  // extra barrier up front, one fewer at the end).  io(t) belongs to global phase 2t+1: the
-  // V phase of half A, the M phase of half B.
-  gload_k(0);
-  store_k(0);
-  if (n > 1) gload_k(1);
-  gload_v(0);
-  sync();
-  if (half) sync();
-  if (half) io(0);
-  mphase(I0{}, I16{}, 0);
-  sync();
-  if (!half) io(0);
-  vphase(0);
-  sync();
-  for (int t = 1; t < n; ++t) {
-    if (half) io(t);
-    mphase(I0{}, I32{}, t);
-    sync();
-    if (!half) io(t);
-    vphase(t);
-    sync();
-  }
-  mphase(I16{}, I32{}, n);
-  if (!half) sync();
 
-  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
-  if (q < grp.q1) {
+  // Pieces of this workgroup's share: a partial piece at the end of the share first (the
+  // head of a unit the next workgroup finishes), then the first piece, then whole units.
+  const Unit uf = decode(p, it0);
+  const int len_first = min(it1 - it0, p.nk[uf.g] - uf.t);
+  const Unit ul = decode(p, it1 - 1);
+  const bool last_partial = (it0 + len_first < it1) && (ul.t + 1 < p.nk[ul.g]);
+  const int len_last = last_partial ? ul.t + 1 : 0;
+  const int mid_end = it1 - len_last;
+  int mid = it0 + len_first;
+  int step = last_partial ? 0 : 1;
+  for (;;) {
+    int pit, plen, slot;
+    if (step == 0) {
+      pit = it1 - len_last;
+      plen = len_last;
+      slot = 2 * lid + 1;
+      step = 1;
+    } else if (step == 1) {
+      pit = it0;
+      plen = len_first;
+      slot = 2 * lid;
+      step = 2;
+    } else {
+      if (mid >= mid_end) break;
+      pit = mid;
+      plen = p.nk[decode(p, mid).g];
+      slot = -1;
+      mid += plen;
+    }
+    const Unit u = decode(p, pit);
+    const int nku = p.nk[u.g];
+    head = u.head;
+    grp = a.g[u.g];
+    q = grp.q0 + (u.qt - (u.g == 0 ? 0 : (u.g == 1 ? p.tb1 : p.tb2))) * BQ + wave * 32 + r32;
+    kv_begin = (grp.k0 / BKV) * BKV + u.t * BKV;
+    n = plen;
+    vt = reinterpret_cast<const T *>(a.vt) + (size_t)head * HD * a.ldv;
+    {
+      const T *qp = qkv + (size_t)q * a.ldqkv + head * HD + hk * 8;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const V8 *>(qp + kk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    // Local phase 2t is M(t), 2t+1 is V(t); half B runs one global phase behind half A (one
+    // extra barrier up front, one fewer at the end).  io(t) belongs to global phase 2t+1: the
+    // V phase of half A, the M phase of half B.
+    gload_k(0);
+    store_k(0);
+    if (n > 1) gload_k(1);
+    gload_v(0);
+    sync();
+    if (half) sync();
+    if (half) io(0);
+    mphase(I0{}, I16{}, 0);
+    sync();
+    if (!half) io(0);
+    vphase(0);
+    sync();
+    for (int t = 1; t < n; ++t) {
+      if (half) io(t);
+      mphase(I0{}, I32{}, t);
+      sync();
+      if (!half) io(t);
+      vphase(t);
+      sync();
+    }
+    mphase(I16{}, I32{}, n);
+    if (!half) sync();
+
     T *op = reinterpret_cast<T *>(a.out) + (size_t)q * a.ldo + head * HD + 4 * hk;
+    if (u.t == 0 && plen == nku) {  // the whole unit: normalise and store
+      const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
+      if (q < grp.q1) {
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
+        for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4(op + ds * 32 + 8 * g, o[ds][4 * g] * inv, o[ds][4 * g + 1] * inv,
-               o[ds][4 * g + 2] * inv, o[ds][4 * g + 3] * inv);
+          for (int g = 0; g < 4; ++g)
+            store4(op + ds * 32 + 8 * g, o[ds][4 * g] * inv, o[ds][4 * g + 1] * inv,
+                   o[ds][4 * g + 2] * inv, o[ds][4 * g + 3] * inv);
+      }
+      continue;
+    }
+
+    // A piece: publish (O, max, sum); the last piece of the unit to finish merges them.  The
+    // partials are written and read with device-coherent (sc1) buffer accesses: the stores
+    // write through the XCD's L2 and have completed before the piece counter is raised, and
+    // the merging loads do not hit lines another XCD's L2 may hold, so no cache-wide
+    // writeback or invalidate is needed.
+    const __amdgpu_buffer_rsrc_t rs_part = __builtin_amdgcn_make_buffer_rsrc(
+        a.part, (short)0, (int)((size_t)2 * G * kPartFloats * 4), 0x00020000);
+    const int o_off = (wave * 16 * 64 + lane) * 16, ml_off = kPartO * 4 + (wave * 64 + lane) * 8;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(o[c >> 2][4 * (c & 3)]), __float_as_uint(o[c >> 2][4 * (c & 3) + 1]),
+                __float_as_uint(o[c >> 2][4 * (c & 3) + 2]),
+                __float_as_uint(o[c >> 2][4 * (c & 3) + 3])},
+          rs_part, o_off + c * 64 * 16, slot * kPartFloats * 4, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_run), __float_as_uint(l_run)},
+                                          rs_part, ml_off, slot * kPartFloats * 4, kSc1);
+    const int unit = u.head * p.q_tiles + u.qt;
+    const int u0 = pit - u.t;  // first iteration of the unit
+    const int w0 = share_owner(p, u0, G), w1 = share_owner(p, u0 + nku - 1, G);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
+    __syncthreads();
+    if (tid == 0)
+      merge_flag = __hip_atomic_fetch_add(a.cnt + unit, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
+    __syncthreads();
+    if (merge_flag) {
+      float mp[8], mx = -INFINITY;
+      int sl[8];
+      const int np = w1 - w0 + 1;  // at most 8 pieces (checked by the launcher)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < np) {
+          const int w = w0 + i;
+          sl[i] = share_begin(p, w, G) >= u0 ? 2 * w : 2 * w + 1;
+          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_part, ml_off,
+                                                                sl[i] * kPartFloats * 4, kSc1);
+          mp[i] = __uint_as_float(ml.x);
+          mx = fmaxf(mx, mp[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < np) {
+          const float wgt = __builtin_amdgcn_exp2f(mp[i] - mx);
+          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_part, ml_off,
+                                                                sl[i] * kPartFloats * 4, kSc1);
+          l += wgt * __uint_as_float(ml.y);
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                rs_part, o_off + c * 64 * 16, sl[i] * kPartFloats * 4, kSc1);
+            o[c >> 2][4 * (c & 3)] += wgt * __uint_as_float(v.x);
+            o[c >> 2][4 * (c & 3) + 1] += wgt * __uint_as_float(v.y);
+            o[c >> 2][4 * (c & 3) + 2] += wgt * __uint_as_float(v.z);
+            o[c >> 2][4 * (c & 3) + 3] += wgt * __uint_as_float(v.w);
+          }
+        }
+      }
+      const float inv = 1.0f / (l + __shfl_xor(l, 32, 64));
+      if (q < grp.q1) {
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4(op + ds * 32 + 8 * g, o[ds][4 * g] * inv, o[ds][4 * g + 1] * inv,
+                   o[ds][4 * g + 2] * inv, o[ds][4 * g + 3] * inv);
+      }
+      if (tid == 0)  // ready for the next launch
+        __hip_atomic_store(a.cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
   }
 }
 
@@ -269,17 +449,45 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, int qt_before1, 
 hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
   if (a.ng < 1 || a.ng > 3) return hipErrorInvalidValue;
   if (op != OP_BF16 && op != OP_F16) return hipErrorInvalidValue;
-  int tb[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 3; ++i)
-    tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].q1 - a.g[i].q0 + BQ - 1) / BQ : 0);
-  const int q_tiles = tb[3];
-  if (q_tiles == 0) return hipSuccess;
-  const int total = q_tiles * a.heads;
-  const int grid = (total + 7) / 8 * 8;
+  AttnPlan p = {};
+  int tb[4] = {0, 0, 0, 0}, cum[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 3; ++i) {
+    const bool on = i < a.ng && a.g[i].q1 > a.g[i].q0;
+    if (on && a.g[i].k1 <= a.g[i].k0) return hipErrorInvalidValue;  // a query needs a key
+    const int qt = on ? (a.g[i].q1 - a.g[i].q0 + BQ - 1) / BQ : 0;
+    p.nk[i] = on ? (a.g[i].k1 - a.g[i].k0 / BKV * BKV + BKV - 1) / BKV : 1;
+    tb[i + 1] = tb[i] + qt;
+    cum[i + 1] = cum[i] + qt * p.nk[i];
+  }
+  p.tb1 = tb[1];
+  p.tb2 = tb[2];
+  p.q_tiles = tb[3];
+  p.cum1 = cum[1];
+  p.cum2 = cum[2];
+  p.iters_head = cum[3];
+  if (p.q_tiles == 0) return hipSuccess;
+  p.total = p.q_tiles * a.heads;
+  if ((long long)p.iters_head * a.heads > 0x7fffffffLL) return hipErrorInvalidValue;
+  p.iters = p.iters_head * a.heads;
+  int grid = (p.total + 7) / 8 * 8;
+  const int lg = a.lean_grid / 8 * 8;
+  // Equal shares when one unit per workgroup would leave over a tenth of the last round
+  // idle.  A share of iters / lg iterations cuts a unit into at most ceil(nk / share) + 1
+  // pieces, which the merge supports up to 8; shares under 8 key tiles are not worth a merge.
+  const long long rounds = (p.total + lg - 1) / (lg > 0 ? lg : 1);
+  if (a.part != nullptr && a.cnt != nullptr && lg > 0 && 10LL * p.total < 9LL * rounds * lg) {
+    int nk_max = 1;
+    for (int i = 0; i < 3; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
+    const int share = p.iters / lg;
+    if (share >= 8 && (nk_max + share - 1) / share + 1 <= 8) {
+      p.lean = 1;
+      grid = lg;
+    }
+  }
   if (op == OP_BF16)
-    k_attn_pp<bf16><<<grid, 512, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
+    k_attn_pp<bf16><<<grid, 512, 0, s>>>(a, p);
   else
-    k_attn_pp<f16><<<grid, 512, 0, s>>>(a, tb[1], tb[2], q_tiles, total);
+    k_attn_pp<f16><<<grid, 512, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

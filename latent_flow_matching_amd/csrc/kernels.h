@@ -58,7 +58,15 @@ struct AttnArgs {
   AttnGroup g[3]; int ng;
   int heads;
   float scale;                              // 1/sqrt(head_dim)
+  // MFMA path load balance: when one workgroup per (head, 256-query) unit would leave part
+  // of the last round of lean_grid workgroups idle, lean_grid workgroups take equal shares of
+  // the key-tile iterations, and units cut between shares merge through part (2 * lean_grid
+  // slots of attn_part_floats) and cnt (one zeroed int per unit, left zeroed).  lean_grid = 0
+  // or part = nullptr: one workgroup per unit.
+  float *part; int *cnt; int lean_grid;
 };
+// floats per partial slot of the MFMA attention
+constexpr int attn_part_floats = 8 * 16 * 64 * 4 + 8 * 64 * 2;
 hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s);
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s);  // V read from qkv at 2*d_model
 

@@ -84,6 +84,9 @@ struct dit_ctx {
   float *fmodv = nullptr;    // [3][2D]
   float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
   float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
+  int lean_grid = 0;         // attention: one workgroup per compute unit (multiple of 8)
+  float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
+  int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 3)] per-unit piece counters
 
   // per-kernel timing: hipEvents recorded on the call's stream around each launch
   struct ProfRec {
@@ -346,6 +349,16 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   ctx->cfg = c;
   ctx->device = dev;
   ctx->op = c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
+  ctx->lean_grid = prop.multiProcessorCount / 8 * 8;
+  if (const char *ag = getenv("DIT_ATTN_GRID")) {  // attention share count (0: off)
+    const int v = atoi(ag);
+    if (v < 0 || v > 4096 || v % 8) {
+      delete ctx;
+      fail(DIT_EINVAL, "DIT_ATTN_GRID must be 0 or a multiple of 8 up to 4096, got '%s'", ag);
+      return nullptr;
+    }
+    ctx->lean_grid = v;
+  }
   const char *ds = getenv("DIT_DEBUG_SYNC");
   ctx->debug_sync = ds && ds[0] == '1';
 
@@ -406,6 +419,12 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)3 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->act, (size_t)3 * D * 4);
+  if (ctx->op != OP_F32 && ctx->lean_grid > 0) {
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_part,
+                          (size_t)2 * ctx->lean_grid * attn_part_floats * 4);
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_cnt,
+                          (size_t)c.heads * (c.max_tokens / 256 + 3) * 4);
+  }
   if (ctx->op == OP_F32) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
   } else if (!rc) {
@@ -514,6 +533,9 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   at.ldo = D + F;
   at.heads = c.heads;
   at.scale = 1.0f / sqrtf(128.0f);
+  at.part = ctx->attn_part;
+  at.cnt = ctx->attn_cnt;
+  at.lean_grid = ctx->lean_grid;
   if (mask == DIT_MASK_SEGMENT) {
     for (int s = 0; s < 3; ++s)
       if (bounds[s + 1] > bounds[s])

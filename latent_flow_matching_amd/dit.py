@@ -44,11 +44,13 @@ class DitError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libdit.so and declare its signatures.  Raises if it is not built."""
+def load_library(path: str = None):
+    """Load libdit.so (LIB_PATH unless given) and declare its signatures.  Raises if it is
+    not built."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built (run __graft_entry__.build() or "
                            "python -m latent_flow_matching_amd.build)")

@@ -263,6 +263,61 @@ def test_block_is_deterministic():
     assert np.array_equal(outs[0], outs[1])
 
 
+# ----------------------------------------------------------------- attention split into equal shares
+
+def _split_plan(groups, heads, lean_grid):
+    """Whether the MFMA attention launch takes equal key-tile shares, and the most pieces a
+    unit is cut into: the launcher's rule restated, so each case below provably exercises it."""
+    q_tiles = [(q1 - q0 + 255) // 256 for q0, q1, _, _ in groups]
+    nk = [(k1 - k0 // 64 * 64 + 63) // 64 for _, _, k0, k1 in groups]
+    total = sum(q_tiles) * heads
+    iters = sum(q * k for q, k in zip(q_tiles, nk)) * heads
+    rounds = -(-total // lean_grid)
+    share = iters // lean_grid
+    lean = 10 * total < 9 * rounds * lean_grid and share >= 8 and -(-max(nk) // share) + 1 <= 8
+    return lean, -(-max(nk) // max(share, 1)) + 1
+
+
+@pytest.mark.parametrize("case", [
+    ("flux2_single_full_mask", TINY2, 1, 300, (40, 40), None, 56),
+    ("flux2_single_full_mask_bf16", C16[0], 1, 300, (40, 40), None, 56),
+    ("flux3_per_mode_block_diagonal", TINY3, 0, 300, (40, 40), (30, 30), 16),
+    ("flux3_joint_full_mask", TINY3, 1, 300, (40, 40), (30, 30), 40),
+], ids=lambda c: c[0])
+def test_attention_equal_shares_match_oracle(case, monkeypatch):
+    """Attention with a forced share count (DIT_ATTN_GRID), so that units are cut into several
+    pieces that merge through the partial buffer; every output row against the oracle, and two
+    runs bitwise equal (the merge order does not depend on which piece finished last)."""
+    _, cfg, b, n_txt, grid, ref_grid, lean_grid = case
+    segs = (n_txt, grid[0] * grid[1], 0 if ref_grid is None else ref_grid[0] * ref_grid[1])
+    n = sum(segs)
+    if cfg.arch == S.ARCH_FLUX3 and b < cfg.n_stream_blocks:
+        bounds = np.cumsum((0,) + segs)
+        groups = [(bounds[i], bounds[i + 1], bounds[i], bounds[i + 1]) for i in range(3) if segs[i]]
+    else:
+        groups = [(0, n, 0, n)]
+    lean, pieces = _split_plan(groups, cfg.heads, lean_grid)
+    assert lean and pieces >= 2, (lean, pieces)
+    monkeypatch.setenv("DIT_ATTN_GRID", str(lean_grid))
+    _CTX.clear()
+    try:
+        err, _ = run_block(cfg, b, n_txt, grid, ref_grid, max_tokens=n + 1)
+        assert err <= tol(cfg, full_width=False)
+        ctx, _ = context(cfg, n + 1)
+        x = S.gen_tokens(n, cfg.hidden, key=(5,))
+        cond = S.gen_cond(3, cfg.hidden)
+        pos = O.positions(n_txt, grid, (ref_grid,) if ref_grid else ())
+        outs = []
+        for _ in range(2):
+            xt = dev(x)
+            ctx.block_forward(b, xt, segs[0], segs[1], segs[2], dev(pos), dev(cond))
+            torch.cuda.synchronize()
+            outs.append(xt.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1])
+    finally:
+        _CTX.clear()
+
+
 # ----------------------------------------------------------------- full benchmark shapes, sampled rows
 
 def _rows(n, k=24, seed=0):
