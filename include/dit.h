@@ -19,6 +19,10 @@
  *     environment, which synchronises and checks after every kernel.
  *   - One context serves one stream at a time: calls that overlap on one context race on
  *     its workspace.
+ *   - DIT_ATTN_GRID=<n> in the environment at dit_ctx_create (0, or a multiple of 8 up to
+ *     4096) sets how many equal shares the attention's key-tile iterations may be split into
+ *     (default: the device's compute units; 0 = one workgroup per 256-query tile and head).
+ *     Other values make dit_ctx_create fail with DIT_EINVAL.
  *   - Row-major everywhere.  "D" = hidden, "C" = in_channels, N = n_txt + n_img + n_ref.
  *   - Return values: 0 on success, or DIT_EINVAL / DIT_ENOMEM / DIT_EHIP / DIT_EUNSUPPORTED;
  *     dit_ctx_create returns NULL on failure.  dit_get_error() then describes the failure.

@@ -351,13 +351,14 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   ctx->op = c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
   ctx->lean_grid = prop.multiProcessorCount / 8 * 8;
   if (const char *ag = getenv("DIT_ATTN_GRID")) {  // attention share count (0: off)
-    const int v = atoi(ag);
-    if (v < 0 || v > 4096 || v % 8) {
+    char *end = nullptr;
+    const long v = strtol(ag, &end, 10);
+    if (end == ag || *end != '\0' || v < 0 || v > 4096 || v % 8) {
       delete ctx;
       fail(DIT_EINVAL, "DIT_ATTN_GRID must be 0 or a multiple of 8 up to 4096, got '%s'", ag);
       return nullptr;
     }
-    ctx->lean_grid = v;
+    ctx->lean_grid = (int)v;
   }
   const char *ds = getenv("DIT_DEBUG_SYNC");
   ctx->debug_sync = ds && ds[0] == '1';

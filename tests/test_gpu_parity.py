@@ -318,6 +318,15 @@ def test_attention_equal_shares_match_oracle(case, monkeypatch):
         _CTX.clear()
 
 
+@pytest.mark.parametrize("bad", ["7", "-8", "8192", "x"])
+def test_attention_grid_override_rejects_bad_values(bad, monkeypatch):
+    from latent_flow_matching_amd import dit
+    monkeypatch.setenv("DIT_ATTN_GRID", bad)
+    w = gpu_weights(TINY2, S.gen_weights(TINY2))
+    with pytest.raises(dit.DitError, match="DIT_ATTN_GRID"):
+        dit.DiT(TINY2, w, 64)
+
+
 # ----------------------------------------------------------------- full benchmark shapes, sampled rows
 
 def _rows(n, k=24, seed=0):
