@@ -466,6 +466,41 @@ def denoise(model: Model, noise: np.ndarray, txt: np.ndarray, grid, n_steps: int
 
 
 # ----------------------------------------------------------------------------------------
+# Classifier-free guidance.  The C tool's generation parameters carry a CFG scale ([HK]
+# CライブラリAPI, guidance_scale); the non-distilled base checkpoint samples with guidance
+# 3.5 over 50 steps and the distilled one without guidance ([WE] checkpoint table; [KS]
+# "Was sich geändert hat").  reading: the pages print no formula; the standard combination of
+# J. Ho and T. Salimans, "Classifier-Free Diffusion Guidance" (2022), in velocity form, with
+# the unconditional branch being the same call on the unconditional text embeddings.
+# ----------------------------------------------------------------------------------------
+
+def guided_velocity(v_cond: np.ndarray, v_uncond: np.ndarray, guidance: float) -> np.ndarray:
+    """v = v_u + g (v_c - v_u): g = 1 is the conditional prediction, g = 0 the unconditional
+    one, g > 1 extrapolates away from the unconditional prediction."""
+    return v_uncond + guidance * (v_cond - v_uncond)
+
+
+def forward_cfg(model: Model, lat: np.ndarray, txt: np.ndarray, txt_uncond: np.ndarray, grid,
+                t: float, guidance: float, ref_lat: np.ndarray | None = None, ref_grid=None):
+    """Guided velocity of one Euler step: the transformer on the conditional and on the
+    unconditional text, same latents, references and time, combined by guided_velocity."""
+    v_c = forward(model, lat, txt, grid, t, ref_lat, ref_grid)
+    v_u = forward(model, lat, txt_uncond, grid, t, ref_lat, ref_grid)
+    return guided_velocity(v_c, v_u, guidance)
+
+
+def denoise_cfg(model: Model, noise: np.ndarray, txt: np.ndarray, txt_uncond: np.ndarray, grid,
+                n_steps: int, guidance: float, ref_lat=None, ref_grid=None) -> np.ndarray:
+    """The Euler loop of denoise with the guided velocity at every step."""
+    ts = euler_schedule(n_steps)
+    lat = noise.astype(np.float64).copy()
+    for i in range(n_steps):
+        v = forward_cfg(model, lat, txt, txt_uncond, grid, ts[i], guidance, ref_lat, ref_grid)
+        lat = euler_step(lat, v, ts[i], ts[i + 1])
+    return lat
+
+
+# ----------------------------------------------------------------------------------------
 # Seeded starting noise.  The C tool makes generation reproducible from a seed ([HK]
 # 再現性・シード管理); the noise here is a counter-based generator written from its
 # published definition: Philox-4x32 with 10 rounds (J. K. Salmon, M. A. Moraes, R. O. Dror,

@@ -420,6 +420,43 @@ def test_forward_stack_is_block_composition():
             assert not np.allclose(seen2[1][7:], seen[1][7:])
 
 
+# ------------------------------------------------------------------ classifier-free guidance
+
+def test_guided_velocity_closed_forms():
+    """g = 1 gives the conditional velocity, g = 0 the unconditional one; the result is affine
+    in g (g = 2 gives 2 v_c - v_u); equal branches give that velocity at any g."""
+    r = rng(30)
+    vc, vu = r.normal(size=(5, 4)), r.normal(size=(5, 4))
+    np.testing.assert_allclose(O.guided_velocity(vc, vu, 1.0), vc, atol=1e-15)
+    np.testing.assert_array_equal(O.guided_velocity(vc, vu, 0.0), vu)
+    np.testing.assert_allclose(O.guided_velocity(vc, vu, 2.0), 2 * vc - vu, atol=1e-14)
+    np.testing.assert_allclose(O.guided_velocity(vc, vc, 3.5), vc, atol=1e-14)
+
+
+def test_forward_cfg_branches():
+    """The guided call is the conditional call at g = 1 and the unconditional one at g = 0;
+    with the same text for both branches it does not depend on g; the guided denoise at g = 1
+    is the plain denoise."""
+    r = rng(31)
+    for arch in (O.ARCH_FLUX2, O.ARCH_FLUX3):
+        m = tiny_model(arch, r)
+        lat = r.normal(size=(4, TINY.in_channels))
+        ref_lat = r.normal(size=(4, TINY.in_channels))
+        tc, tu = r.normal(size=(3, TINY.hidden)), r.normal(size=(3, TINY.hidden))
+        vc = O.forward(m, lat, tc, (2, 2), 0.7, ref_lat, (2, 2))
+        vu = O.forward(m, lat, tu, (2, 2), 0.7, ref_lat, (2, 2))
+        assert not np.allclose(vc, vu)
+        np.testing.assert_allclose(O.forward_cfg(m, lat, tc, tu, (2, 2), 0.7, 1.0, ref_lat, (2, 2)), vc, atol=1e-13)
+        np.testing.assert_allclose(O.forward_cfg(m, lat, tc, tu, (2, 2), 0.7, 0.0, ref_lat, (2, 2)), vu, atol=1e-13)
+        np.testing.assert_allclose(O.forward_cfg(m, lat, tc, tc, (2, 2), 0.7, 3.5, ref_lat, (2, 2)), vc, atol=1e-13)
+        g = 3.5
+        np.testing.assert_allclose(O.forward_cfg(m, lat, tc, tu, (2, 2), 0.7, g, ref_lat, (2, 2)),
+                                   vu + g * (vc - vu), atol=1e-12)
+        noise = r.normal(size=(4, TINY.in_channels))
+        np.testing.assert_allclose(O.denoise_cfg(m, noise, tc, tu, (2, 2), 2, 1.0),
+                                   O.denoise(m, noise, tc, (2, 2), 2), atol=1e-12)
+
+
 # ------------------------------------------------------------------ the pins catch planted slips
 
 def _wrong_rope(x, angles):
@@ -495,6 +532,11 @@ def test_pins_catch_planted_slips(monkeypatch):
     monkeypatch.setattr(O, "PHILOX_MUL", (O.PHILOX_MUL[1], O.PHILOX_MUL[0]))
     with pytest.raises(AssertionError):
         test_philox_known_answers()
+    monkeypatch.undo()
+    # guidance with the branches swapped
+    monkeypatch.setattr(O, "guided_velocity", lambda vc, vu, g: vc + g * (vu - vc))
+    with pytest.raises(AssertionError):
+        test_guided_velocity_closed_forms()
     monkeypatch.undo()
     # a slightly wrong activation
     orig = O.silu
