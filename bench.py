@@ -81,7 +81,9 @@ def cpu_baseline(wl, cfg):
             "kind": "oracle",
             "sample": f"blocks {', '.join(map(str, blocks))} of the stack in sequence at "
                       f"{'+'.join(str(s) for s in segs if s)} tokens, all rows, float64 "
-                      f"NumPy/OpenBLAS, {dt:.1f} s of oracle time"}
+                      f"NumPy/OpenBLAS, {dt:.1f} s of oracle time"
+                      + ("; with guidance the oracle runs each branch as such a sequence"
+                         if wl.guidance is not None else "")}
 
 
 def source_sha256(path=GEMM_SOURCE):
@@ -292,29 +294,35 @@ def main():
         raise SystemExit(f"{args.workload} is a parity configuration, not a bench workload")
     cfg = replace(wl.model, compute=args.compute)
     n = wl.n_tokens
+    nseq = 1 if wl.guidance is None else 2  # guidance: both branches as one batch of 2
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     weights = S.gen_weights(cfg, bits=True)
     log(f"weights generated in {time.perf_counter() - t0:.1f} s")
     t0 = time.perf_counter()
-    ctx = dit.DiT(cfg, weights, max_tokens=n)
+    ctx = dit.DiT(cfg, weights, max_tokens=n * nseq)
     del weights
     log(f"context created in {time.perf_counter() - t0:.1f} s")
     txt = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden), device="cuda")
+    txt_u = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden, seed=S.SEED_T + 7), device="cuda")
     ref = (torch.tensor(S.gen_latents(wl.n_ref, cfg.in_channels, key=(1,)), device="cuda")
            if wl.n_ref else None)
     lat = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
     ref_grid = wl.ref_grid or (0, 0)
 
     def step(i):
-        ctx.denoise(lat, txt, wl.grid, wl.steps, seed=1000 + i, ref_lat=ref, ref_grid=ref_grid)
+        if nseq == 2:
+            ctx.denoise_cfg(lat, txt, txt_u, wl.grid, wl.steps, wl.guidance, seed=1000 + i,
+                            ref_lat=ref, ref_grid=ref_grid)
+        else:
+            ctx.denoise(lat, txt, wl.grid, wl.steps, seed=1000 + i, ref_lat=ref, ref_grid=ref_grid)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     # one untimed step with every kernel class timed: the per-kernel breakdown, and which class
     # dominates (the roofline kernel)
-    launches = wl.steps * (cfg.n_blocks * 5 + 8) + 64
+    launches = wl.steps * (cfg.n_blocks * 5 + 8 + 4 * nseq) + 64
     ctx.profile_start(launches)
     step(args.warmup)
     torch.cuda.synchronize()
@@ -335,7 +343,7 @@ def main():
 
     per_step_ms = ms / args.steps
     blocks = cfg.n_blocks
-    block_tokens = n * blocks * wl.steps * args.steps
+    block_tokens = n * nseq * blocks * wl.steps * args.steps
     # headline: GEMM + attention flops of the timed steps over their whole wall time (norms,
     # RoPE, conditioning, output head and Euler update included in the time)
     total_flops = sum(prof[k][2] for k in ("linear1", "linear2", "attention")) * args.steps
@@ -372,7 +380,8 @@ def main():
         "ms_per_step": round(per_step_ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": args.compute, "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": n, "n_txt": wl.n_txt, "n_img": wl.n_img,
+        "config": {"workload": wl.name, "tokens": n * nseq, "sequences": nseq,
+                   "guidance": wl.guidance, "n_txt": wl.n_txt, "n_img": wl.n_img,
                    "n_ref": wl.n_ref, "blocks": blocks, "euler_steps": wl.steps,
                    "weights": "bf16", "accumulate": "f32", "parallelism": "none"},
         "tflops": round(tflops, 1),

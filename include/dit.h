@@ -150,6 +150,28 @@ int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, i
                 const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed,
                 void *stream);
 
+/* Classifier-free guidance: one call of the transformer on two sequences at once, the
+ * conditional text txt and the unconditional text txt_uncond (both dev fp32 [n_txt, D]), each
+ * with the same latents, references and time, and
+ *   v = v_u + guidance * (v_c - v_u),
+ * computed as guidance * v_c + (1 - guidance) * v_u, conditional branch first.
+ * (Guidance scale: the C tool's generation parameters, hakusoku FLUX.2-klein-4B article,
+ * "CライブラリAPI"; the non-distilled base checkpoint samples with guidance 3.5, we0.ai
+ * "FLUX 3 Image Klein" article, checkpoint table.  The combination is the standard one of
+ * classifier-free guidance; the pages print no formula.)
+ * The two sequences are stacked as one batch of 2 (n_txt + gh*gw + rgh*rgw rows each), so
+ * max_tokens must cover twice the sequence.  Each sequence attends only to itself.
+ * guidance must be finite; other arguments as in dit_forward. */
+int dit_forward_cfg(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt,
+                    const float *txt_uncond, int n_txt, int gh, int gw, int rgh, int rgw,
+                    float t, float guidance, float *v, void *stream);
+
+/* dit_denoise with the guided velocity of dit_forward_cfg at every step:
+ * lat <- lat + (t_i - t_{i+1}) * (guidance * v_c + (1 - guidance) * v_u). */
+int dit_denoise_cfg(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond,
+                    int n_txt, int gh, int gw, const float *ref_lat, int rgh, int rgw,
+                    int n_steps, float guidance, int64_t seed, void *stream);
+
 /* Fill dst (dev fp32, n elements) with the N(0,1) noise dit_denoise draws for seed. */
 int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
 

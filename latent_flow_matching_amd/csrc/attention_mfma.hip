@@ -71,10 +71,11 @@ constexpr int BQ = 256;
 // Work plan: units are numbered head-major, query tiles within a head in group order; the
 // iterations of a unit are its key tiles.
 struct AttnPlan {
-  int tb1, tb2, q_tiles;  // first query tile of groups 1 and 2; query tiles per head
-  int nk[3];              // key tiles per unit of each group
-  int cum1, cum2;         // iterations of a head before groups 1 and 2
-  int iters_head, iters;  // iterations per head, in total
+  int tb[kMaxGroups + 1];   // first query tile of each group (the rest: query tiles per head)
+  int cum[kMaxGroups + 1];  // iterations of a head before each group (the rest: all of them)
+  int nk[kMaxGroups];       // key tiles per unit of each group
+  int q_tiles;              // query tiles per head
+  int iters_head, iters;    // iterations per head, in total
   int total;              // units
   int lean;               // 1: equal iteration shares over the grid; 0: one unit per workgroup
 };
@@ -86,11 +87,13 @@ __device__ __forceinline__ Unit decode(const AttnPlan &p, int it) {
   Unit u;
   u.head = it / p.iters_head;
   const int r = it - u.head * p.iters_head;
-  u.g = (r >= p.cum1) + (r >= p.cum2);
-  const int rr = r - (u.g == 0 ? 0 : (u.g == 1 ? p.cum1 : p.cum2));
+  u.g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) u.g += r >= p.cum[i];
+  const int rr = r - p.cum[u.g];
   const int ql = rr / p.nk[u.g];
   u.t = rr - ql * p.nk[u.g];
-  u.qt = (u.g == 0 ? 0 : (u.g == 1 ? p.tb1 : p.tb2)) + ql;
+  u.qt = p.tb[u.g] + ql;
   return u;
 }
 // first iteration of the share of workgroup w, and the workgroup whose share holds it
@@ -123,9 +126,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   } else {
     if (lid >= p.total) return;
     const int hd = lid / p.q_tiles, qt = lid - hd * p.q_tiles;
-    const int g = (qt >= p.tb1) + (qt >= p.tb2);
-    it0 = hd * p.iters_head + (g == 0 ? 0 : (g == 1 ? p.cum1 : p.cum2)) +
-          (qt - (g == 0 ? 0 : (g == 1 ? p.tb1 : p.tb2))) * p.nk[g];
+    int g = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i) g += qt >= p.tb[i];
+    it0 = hd * p.iters_head + p.cum[g] + (qt - p.tb[g]) * p.nk[g];
     it1 = it0 + p.nk[g];
   }
   if (it0 >= it1) return;
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     const int nku = p.nk[u.g];
     head = u.head;
     grp = a.g[u.g];
-    q = grp.q0 + (u.qt - (u.g == 0 ? 0 : (u.g == 1 ? p.tb1 : p.tb2))) * BQ + wave * 32 + r32;
+    q = grp.q0 + (u.qt - p.tb[u.g]) * BQ + wave * 32 + r32;
     kv_begin = (grp.k0 / BKV) * BKV + u.t * BKV;
     n = plen;
     vt = reinterpret_cast<const T *>(a.vt) + (size_t)head * HD * a.ldv;
@@ -447,24 +451,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
 }  // namespace
 
 hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
-  if (a.ng < 1 || a.ng > 3) return hipErrorInvalidValue;
+  if (a.ng < 1 || a.ng > kMaxGroups) return hipErrorInvalidValue;
   if (op != OP_BF16 && op != OP_F16) return hipErrorInvalidValue;
   AttnPlan p = {};
-  int tb[4] = {0, 0, 0, 0}, cum[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < kMaxGroups; ++i) {
     const bool on = i < a.ng && a.g[i].q1 > a.g[i].q0;
     if (on && a.g[i].k1 <= a.g[i].k0) return hipErrorInvalidValue;  // a query needs a key
     const int qt = on ? (a.g[i].q1 - a.g[i].q0 + BQ - 1) / BQ : 0;
     p.nk[i] = on ? (a.g[i].k1 - a.g[i].k0 / BKV * BKV + BKV - 1) / BKV : 1;
-    tb[i + 1] = tb[i] + qt;
-    cum[i + 1] = cum[i] + qt * p.nk[i];
+    p.tb[i + 1] = p.tb[i] + qt;
+    p.cum[i + 1] = p.cum[i] + qt * p.nk[i];
   }
-  p.tb1 = tb[1];
-  p.tb2 = tb[2];
-  p.q_tiles = tb[3];
-  p.cum1 = cum[1];
-  p.cum2 = cum[2];
-  p.iters_head = cum[3];
+  p.q_tiles = p.tb[kMaxGroups];
+  p.iters_head = p.cum[kMaxGroups];
   if (p.q_tiles == 0) return hipSuccess;
   p.total = p.q_tiles * a.heads;
   if ((long long)p.iters_head * a.heads > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -477,7 +476,7 @@ hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
   const long long rounds = (p.total + lg - 1) / (lg > 0 ? lg : 1);
   if (a.part != nullptr && a.cnt != nullptr && lg > 0 && 10LL * p.total < 9LL * rounds * lg) {
     int nk_max = 1;
-    for (int i = 0; i < 3; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
+    for (int i = 0; i < kMaxGroups; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
     const int share = p.iters / lg;
     if (share >= 8 && (nk_max + share - 1) / share + 1 <= 8) {
       p.lean = 1;

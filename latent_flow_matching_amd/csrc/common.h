@@ -89,5 +89,9 @@ __device__ __forceinline__ float silu(float z) {
 __device__ __forceinline__ int segment_of(int m, int b1, int b2) {
   return (m >= b1) + (m >= b2);
 }
+// The same for row m of one of two sequences of per rows each (m < 2 * per).
+__device__ __forceinline__ int segment_of(int m, int b1, int b2, int per) {
+  return segment_of(m >= per ? m - per : m, b1, b2);
+}
 
 }  // namespace dit

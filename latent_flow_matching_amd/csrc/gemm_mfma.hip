@@ -59,7 +59,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
     if (m >= grp.rows) continue;
     const int tok = grp.out_row0 + m;
     if constexpr (EPI == EPI_RESID) {
-      const int seg = segment_of(tok, a.b1, a.b2);
+      const int seg = segment_of(tok, a.b1, a.b2, a.per);
       const float *gate = a.gate[seg];
       float *xr = a.x + (size_t)tok * a.ldres;
 #pragma unroll
@@ -109,9 +109,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
           if (a.n_store > 0 && n >= a.n_store) continue;
           f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                      acc[i][j][4 * g + 3]};
-          if (a.accumulate) {
+          if (a.accumulate == 1) {
             f32x4 o = *reinterpret_cast<const f32x4 *>(orow + n);
             v = o + a.alpha * v;
+          } else if (a.accumulate == 2) {
+            v = a.alpha * v;
           }
           *reinterpret_cast<f32x4 *>(orow + n) = v;
         }
@@ -137,9 +139,14 @@ __device__ __forceinline__ void lds_sync() {
 // after each MFMA, so the LDS and global latencies sit under MFMAs.  Token rows, which miss L2
 // more often than weight rows under the grouped tile order, get two staging sets and so two
 // k-tiles of latency cover.
+// First token tile of each row group (entries past the last group hold the total).
+struct TileBounds {
+  int t[kMaxGroups + 1];
+};
+
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int t_before1,
-                                                  int t_before2, int total_tiles) {
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_tiles_total,
+                                                  int total_tiles) {
   constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
   constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
   constexpr int FS = WTN / 32, TS = WTM / 32;  // 4 x 4
@@ -160,8 +167,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
   const int rem = lid - group * in_group;
   const int tile_n = first_n + rem % gsize;
   const int mt = rem / gsize;
-  const int gi = (mt >= t_before1) + (mt >= t_before2);
-  const int lmt = mt - (gi == 0 ? 0 : (gi == 1 ? t_before1 : t_before2));
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
+  const int lmt = mt - tb.t[gi];
   const GemmGroup grp = a.g[gi];
   const int n0 = tile_n * BN;
   const int m0 = lmt * BM;
@@ -319,13 +328,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, int m_tiles_total, int
 template <typename T, int EPI>
 hipError_t launch(const GemmArgs &a, hipStream_t s) {
   constexpr int BM = 256;
-  int tb[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 3; ++i) tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
-  const int m_tiles = tb[3];
+  TileBounds tb = {};
+  for (int i = 0; i < kMaxGroups; ++i)
+    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
+  const int m_tiles = tb.t[kMaxGroups];
   if (m_tiles == 0) return hipSuccess;
   const int total = m_tiles * (a.n / BN);
   const int grid = (total + 7) / 8 * 8;
-  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, m_tiles, tb[1], tb[2], total);
+  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total);
   return hipGetLastError();
 }
 
@@ -342,7 +352,7 @@ hipError_t dispatch(const GemmArgs &a, int epi, hipStream_t s) {
 }
 
 hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s) {
-  if (a.n % BN || a.k % BK || a.ng < 1 || a.ng > 3) return hipErrorInvalidValue;
+  if (a.n % BN || a.k % BK || a.ng < 1 || a.ng > kMaxGroups) return hipErrorInvalidValue;
   if (op == OP_BF16) return dispatch<bf16>(a, epi, s);
   if (op == OP_F16) return dispatch<f16>(a, epi, s);
   return hipErrorInvalidValue;

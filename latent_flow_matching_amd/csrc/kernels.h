@@ -8,10 +8,15 @@ namespace dit {
 // Element types of activations / weights (same codes as the C ABI's compute types).
 enum ElemType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
 
-// Token rows are ordered text [0, b1) | image [b1, b2) | reference [b2, n).
+// Token rows: one or two sequences of per rows each (the conditional and unconditional
+// branches of classifier-free guidance), each ordered text [0, b1) | image [b1, b2) |
+// reference [b2, per); n = rows in total.  A row's segment is that of its offset in its
+// sequence.
 struct Segs {
-  int b1, b2, n;
+  int b1, b2, n, per;
 };
+// Most row groups of one GEMM or attention launch: three segments of two sequences.
+constexpr int kMaxGroups = 6;
 
 // --- GEMM row groups: up to three row ranges, each with its own input rows and weights.
 struct GemmGroup {
@@ -28,16 +33,17 @@ enum Epilogue {
 };
 
 struct GemmArgs {
-  GemmGroup g[3];
+  GemmGroup g[kMaxGroups];
   int ng;
   int n, k;            // output columns, reduction length
   int ldx;             // input row stride (elements)
-  // EPI_STORE_F32 (columns >= n_store are computed but not stored when n_store > 0)
+  // EPI_STORE_F32: accumulate 0: out = acc, 1: out += alpha * acc, 2: out = alpha * acc
+  // (columns >= n_store are computed but not stored when n_store > 0)
   float *out; int ldo; int accumulate; float alpha; int n_store;
   // EPI_QKV_SWIGLU
   void *qkv; int ldq; int split; void *cat; int ldc; int cat_off;
   // EPI_RESID
-  float *x; int ldres; const float *gate[3]; int b1, b2;
+  float *x; int ldres; const float *gate[3]; int b1, b2, per;
 };
 
 // MFMA GEMM: input and weights of 16-bit type op (OP_BF16 / OP_F16), fp32 accumulation.
@@ -55,7 +61,7 @@ struct AttnArgs {
   const void *qkv; int ldqkv; int d_model;  // q at column h*128, k at d_model + h*128
   const void *vt; int ldv;                  // MFMA path: V transposed [heads][128][ldv]
   void *out; int ldo;                       // out[q][h*128 + d]
-  AttnGroup g[3]; int ng;
+  AttnGroup g[kMaxGroups]; int ng;
   int heads;
   float scale;                              // 1/sqrt(head_dim)
   // MFMA path load balance: when one workgroup per (head, 256-query) unit would leave part

@@ -80,13 +80,13 @@ template <typename TO>
 __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const float *x, int ldx,
                                                       int row0, int d, float eps,
                                                       const float *m0, const float *m1,
-                                                      const float *m2, int b1, int b2) {
+                                                      const float *m2, int b1, int b2, int per) {
   __shared__ float red[2][4];
   const int t = threadIdx.x, w = t >> 6;
   const int r = blockIdx.x, tok = row0 + r;
   const int nv4 = d >> 2;  // float4 columns; a multiple of 64, so each wave is all in or all out
   const float *xr = x + (size_t)tok * ldx;
-  const int seg = segment_of(tok, b1, b2);
+  const int seg = segment_of(tok, b1, b2, per);
   const float *shift = seg == 0 ? m0 : (seg == 1 ? m1 : m2), *scale = shift + d;
   f32x4 v[kLnMaxVec], sh[kLnMaxVec], sc[kLnMaxVec];
 #pragma unroll
@@ -135,7 +135,7 @@ template <typename TO>
 void launch_ln(void *out, int ldo, const float *x, int ldx, int rows, int row0, int d, float eps,
                const float *const m[3], Segs sg, hipStream_t s) {
   k_ln_modulate<TO><<<rows, 256, 0, s>>>((TO *)out, ldo, x, ldx, row0, d, eps, m[0], m[1], m[2],
-                                          sg.b1, sg.b2);
+                                          sg.b1, sg.b2, sg.per);
 }
 
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
                                                        const float *qn0, const float *qn1,
                                                        const float *qn2, const float *kn0,
                                                        const float *kn1, const float *kn2,
-                                                       int b1, int b2, float eps) {
+                                                       int b1, int b2, int per, float eps) {
   typedef typename Pair<T>::type P2;
   int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int h = blockIdx.y;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
   for (int i = 0; i < 16; ++i) {
     int tok = t0 + wave * 16 + i;
     if (tok >= n) break;
-    int seg = segment_of(tok, b1, b2);
+    int seg = segment_of(tok, b1, b2, per);
     const float *qn = seg == 0 ? qn0 : (seg == 1 ? qn1 : qn2);
     const float *kn = seg == 0 ? kn0 : (seg == 1 ? kn1 : kn2);
     T *qp = qkv + (size_t)tok * ldq + h * 128 + 2 * lane;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
                                                          const float *qn0, const float *qn1,
                                                          const float *qn2, const float *kn0,
                                                          const float *kn1, const float *kn2,
-                                                         int b1, int b2, float eps) {
+                                                         int b1, int b2, int per, float eps) {
   typedef typename Mfma<T>::v8 V8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y, t0 = blockIdx.x * 64;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
       sk += __shfl_xor(sk, m, 16);
     }
     if (tok >= n) continue;
-    const int seg = segment_of(tok, b1, b2);
+    const int seg = segment_of(tok, b1, b2, per);
     const float *qn = (seg == 0 ? qn0 : (seg == 1 ? qn1 : qn2)) + c8;
     const float *kn = (seg == 0 ? kn0 : (seg == 1 ? kn1 : kn2)) + c8;
     const float rq = 1.0f / sqrtf(sq * (1.0f / 128.f) + eps);
@@ -326,17 +326,17 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
     case OP_BF16:
       k_qk_norm_rope16<bf16><<<grid, 256, 0, s>>>((bf16 *)qkv, ldq, d_model, (bf16 *)vt, ldv, cs, n,
                                                 qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
-                                                segs.b2, eps);
+                                                segs.b2, segs.per, eps);
       break;
     case OP_F16:
       k_qk_norm_rope16<f16><<<grid, 256, 0, s>>>((f16 *)qkv, ldq, d_model, (f16 *)vt, ldv, cs, n,
                                                qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
-                                               segs.b2, eps);
+                                               segs.b2, segs.per, eps);
       break;
     case OP_F32:
       k_qk_norm_rope<float><<<dim3((n + 63) / 64, heads), 256, 0, s>>>(
           (float *)qkv, ldq, d_model, nullptr, 0, cs, n, qn[0], qn[1], qn[2], kn[0], kn[1], kn[2],
-          segs.b1, segs.b2, eps);
+          segs.b1, segs.b2, segs.per, eps);
       break;
     default:
       return hipErrorInvalidValue;

@@ -9,6 +9,7 @@
 //   linear2          cat . W2^T -> x += gate * .    gated residual
 // Stream blocks (double / per-mode) run the two projections as row groups with one weight
 // set per stream; shared blocks (single / joint) use one set for all rows.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -86,7 +87,7 @@ struct dit_ctx {
   float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
   int lean_grid = 0;         // attention: one workgroup per compute unit (multiple of 8)
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
-  int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 3)] per-unit piece counters
+  int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 6)] per-unit piece counters
 
   // per-kernel timing: hipEvents recorded on the call's stream around each launch
   struct ProfRec {
@@ -424,7 +425,7 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_part,
                           (size_t)2 * ctx->lean_grid * attn_part_floats * 4);
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_cnt,
-                          (size_t)c.heads * (c.max_tokens / 256 + 3) * 4);
+                          (size_t)c.heads * (c.max_tokens / 256 + kMaxGroups) * 4);
   }
   if (ctx->op == OP_F32) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
@@ -450,7 +451,11 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
 // ------------------------------------------------------------------------------------------
 namespace {
 
-Segs make_segs(int n_txt, int n_img, int n_ref) { return Segs{n_txt, n_txt + n_img, n_txt + n_img + n_ref}; }
+// nseq sequences (1, or 2 for the two branches of guidance) of [text | image | reference].
+Segs make_segs(int n_txt, int n_img, int n_ref, int nseq = 1) {
+  const int per = n_txt + n_img + n_ref;
+  return Segs{n_txt, n_txt + n_img, per * nseq, per};
+}
 
 // mod[kind][set][seg] = W_mod[kind][set] . SiLU(cond[seg]) for every set of the kind
 int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) {
@@ -482,24 +487,27 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
             ln_modulate(ctx->xm, ctx->op, D, x, D, N, 0, D, c.ln_eps, mseg, sg, stream), "ln_modulate");
 
-  // row groups: one per distinct weight set over contiguous rows
-  const int bounds[4] = {0, sg.b1, sg.b2, sg.n};
-  GemmGroup g1[3], g2[3];
+  // row groups: one per distinct weight set over contiguous rows, sequence by sequence
+  const int nseq = sg.n / sg.per;
+  const int lb[4] = {0, sg.b1, sg.b2, sg.per};
+  GemmGroup g1[kMaxGroups], g2[kMaxGroups];
   int ng = 0;
-  for (int s = 0; s < 3; ++s) {
-    if (bounds[s + 1] == bounds[s]) continue;
-    const int set = sos[s];
-    if (ng > 0 && (const void *)g1[ng - 1].w == ctx->blk[b][set].w1) {  // extend
-      g1[ng - 1].rows += bounds[s + 1] - bounds[s];
-      g2[ng - 1].rows += bounds[s + 1] - bounds[s];
-      continue;
+  for (int qs = 0; qs < nseq; ++qs)
+    for (int s = 0; s < 3; ++s) {
+      const int r0 = qs * sg.per + lb[s], r1 = qs * sg.per + lb[s + 1];
+      if (r1 == r0) continue;
+      const int set = sos[s];
+      if (ng > 0 && (const void *)g1[ng - 1].w == ctx->blk[b][set].w1 &&
+          g1[ng - 1].out_row0 + g1[ng - 1].rows == r0) {  // extend
+        g1[ng - 1].rows += r1 - r0;
+        g2[ng - 1].rows += r1 - r0;
+        continue;
+      }
+      g1[ng] = GemmGroup{(const char *)ctx->xm + (size_t)r0 * D * es, ctx->blk[b][set].w1, r1 - r0, r0};
+      g2[ng] = GemmGroup{(const char *)ctx->cat + (size_t)r0 * (D + F) * es, ctx->blk[b][set].w2,
+                         r1 - r0, r0};
+      ++ng;
     }
-    g1[ng] = GemmGroup{(const char *)ctx->xm + (size_t)bounds[s] * D * es, ctx->blk[b][set].w1,
-                       bounds[s + 1] - bounds[s], bounds[s]};
-    g2[ng] = GemmGroup{(const char *)ctx->cat + (size_t)bounds[s] * (D + F) * es, ctx->blk[b][set].w2,
-                       bounds[s + 1] - bounds[s], bounds[s]};
-    ++ng;
-  }
   GemmArgs a1 = {};
   for (int i = 0; i < ng; ++i) a1.g[i] = g1[i];
   a1.ng = ng;
@@ -537,13 +545,16 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   at.part = ctx->attn_part;
   at.cnt = ctx->attn_cnt;
   at.lean_grid = ctx->lean_grid;
-  if (mask == DIT_MASK_SEGMENT) {
-    for (int s = 0; s < 3; ++s)
-      if (bounds[s + 1] > bounds[s])
-        at.g[at.ng++] = AttnGroup{bounds[s], bounds[s + 1], bounds[s], bounds[s + 1]};
-  } else {
-    at.g[0] = AttnGroup{0, N, 0, N};
-    at.ng = 1;
+  // each sequence attends only to itself; per-mode blocks only within each segment
+  for (int qs = 0; qs < nseq; ++qs) {
+    if (mask == DIT_MASK_SEGMENT) {
+      for (int s = 0; s < 3; ++s) {
+        const int r0 = qs * sg.per + lb[s], r1 = qs * sg.per + lb[s + 1];
+        if (r1 > r0) at.g[at.ng++] = AttnGroup{r0, r1, r0, r1};
+      }
+    } else {
+      at.g[at.ng++] = AttnGroup{qs * sg.per, (qs + 1) * sg.per, qs * sg.per, (qs + 1) * sg.per};
+    }
   }
   double pairs = 0.0;
   for (int i = 0; i < at.ng; ++i)
@@ -565,6 +576,7 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   for (int s = 0; s < 3; ++s) a2.gate[s] = gate[s];
   a2.b1 = sg.b1;
   a2.b2 = sg.b2;
+  a2.per = sg.per;
   const double fl2 = 2.0 * N * (double)(D + F) * D;
   if (ctx->op != OP_F32)
     DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
@@ -573,12 +585,13 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   return 0;
 }
 
-int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref) {
+int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref, int nseq = 1) {
   if (n_txt < 0 || n_img < 0 || n_ref < 0) return fail(DIT_EINVAL, "negative token count");
   const long long n = (long long)n_txt + n_img + n_ref;
   if (n < 1) return fail(DIT_EINVAL, "empty sequence");
-  if (n > ctx->cfg.max_tokens)
-    return fail(DIT_EINVAL, "%lld tokens exceed max_tokens %d", n, ctx->cfg.max_tokens);
+  if (n * nseq > ctx->cfg.max_tokens)
+    return fail(DIT_EINVAL, "%lld tokens (%d sequence%s of %lld) exceed max_tokens %d", n * nseq, nseq,
+                nseq > 1 ? "s" : "", n, ctx->cfg.max_tokens);
   return 0;
 }
 
@@ -601,87 +614,109 @@ int prepare_conditioning(dit_ctx *ctx, double t, hipStream_t stream) {
   return 0;
 }
 
-// Embed, run every block, output head.  out = v (accumulate 0) or out += alpha * v.
-int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt, int n_txt,
-                int gh, int gw, int rgh, int rgw, double t, float *out, int accumulate, float alpha,
-                hipStream_t stream) {
+// How the output head's velocity of one sequence lands in `out`: the GEMM's store modes
+// (0: out = v, 1: out += alpha * v, 2: out = alpha * v).
+struct HeadStore {
+  int mode;
+  float alpha;
+};
+
+// Embed, run every block, output head.  nseq = 1: the sequence of txt[0]; nseq = 2: the
+// conditional (txt[0]) and unconditional (txt[1]) branches of guidance stacked as two
+// sequences that share latents, references and time.  The head stores sequence 0 first,
+// then sequence 1, each with its own HeadStore.
+int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *const txt[2],
+                int nseq, int n_txt, int gh, int gw, int rgh, int rgw, double t, float *out,
+                const HeadStore hs[2], hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = c.hidden, C = c.in_channels;
   const int n_img = gh * gw, n_ref = rgh * rgw;
-  const Segs sg = make_segs(n_txt, n_img, n_ref);
+  const Segs sg = make_segs(n_txt, n_img, n_ref, nseq);
+  const int per = sg.per;
   {
     const int pe = prof_begin(ctx, P_COND, stream);
     if (int rc = prepare_conditioning(ctx, t, stream)) return rc;
     prof_end(ctx, pe, P_COND, 0.0, 0.0, stream);
   }
-  DIT_CHECK(fill_positions(ctx->pos, n_txt, gh, gw, rgh, rgw, stream), "positions");
+  for (int qs = 0; qs < nseq; ++qs)
+    DIT_CHECK(fill_positions(ctx->pos + (size_t)qs * per * 4, n_txt, gh, gw, rgh, rgw, stream),
+              "positions");
   DIT_CHECK(rope_table(ctx->cs, ctx->pos, sg.n, c.rope_theta, stream), "rope_table");
   // sequence: text embeddings as they are, latents through the input projection
-  DIT_CHECK(copy_rows_f32(ctx->x, D, txt, D, n_txt, D, stream), "copy text");
+  for (int qs = 0; qs < nseq; ++qs)
+    DIT_CHECK(copy_rows_f32(ctx->x + (size_t)qs * per * D, D, txt[qs], D, n_txt, D, stream),
+              "copy text");
   GemmArgs ae = {};
   ae.n = D;
   ae.k = C;
   ae.ldx = C;
   ae.out = ctx->x;
   ae.ldo = D;
-  const double fle = 2.0 * (n_img + n_ref) * (double)C * D;
-  if (ctx->op == OP_F32) {
-    ae.g[0] = GemmGroup{lat, ctx->img_in, n_img, n_txt};
-    ae.ng = 1;
-    if (n_ref > 0) ae.g[ae.ng++] = GemmGroup{ref_lat, ctx->img_in, n_ref, n_txt + n_img};
-    DIT_TIMED(P_EMBED, fle, 0.0, gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
-  } else {
+  const double fle = 2.0 * nseq * (n_img + n_ref) * (double)C * D;
+  const void *lsrc = lat, *rsrc = ref_lat;
+  if (ctx->op != OP_F32) {
     // latents rounded to the operand type (into the free xm buffer, [n_img + n_ref][C]), then
     // the MFMA GEMM
     char *lh = reinterpret_cast<char *>(ctx->xm);
     const size_t es = ctx->esz();
     DIT_TIMED(P_EMBED, 0.0, 0.0, to_half(lh, ctx->op, lat, (int64_t)n_img * C, stream), "img_in cast");
-    ae.g[0] = GemmGroup{lh, ctx->img_in, n_img, n_txt};
-    ae.ng = 1;
+    lsrc = lh;
     if (n_ref > 0) {
       char *rh = lh + (size_t)n_img * C * es;
       DIT_TIMED(P_EMBED, 0.0, 0.0, to_half(rh, ctx->op, ref_lat, (int64_t)n_ref * C, stream), "img_in cast");
-      ae.g[ae.ng++] = GemmGroup{rh, ctx->img_in, n_ref, n_txt + n_img};
+      rsrc = rh;
     }
-    DIT_TIMED(P_EMBED, fle, 0.0, gemm_mfma(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
   }
+  for (int qs = 0; qs < nseq; ++qs) {
+    ae.g[ae.ng++] = GemmGroup{lsrc, ctx->img_in, n_img, qs * per + n_txt};
+    if (n_ref > 0) ae.g[ae.ng++] = GemmGroup{rsrc, ctx->img_in, n_ref, qs * per + n_txt + n_img};
+  }
+  if (ctx->op == OP_F32)
+    DIT_TIMED(P_EMBED, fle, 0.0, gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  else
+    DIT_TIMED(P_EMBED, fle, 0.0, gemm_mfma(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
   for (int b = 0; b < ctx->nblocks(); ++b)
     if (int rc = run_block(ctx, b, ctx->x, sg, DIT_MASK_DEFAULT, stream)) return rc;
-  // output head on the image rows
+  // output head on the image rows of each sequence
   const float *fm = ctx->fmodv + 2 * D;  // image segment's (shift, scale)
   const float *fms[3] = {fm, fm, fm};
-  GemmArgs af = {};
-  af.ng = 1;
-  af.k = D;
-  af.ldx = D;
-  af.out = out;
-  af.ldo = C;
-  af.accumulate = accumulate;
-  af.alpha = alpha;
   const double flf = 2.0 * n_img * (double)C * D;
-  if (ctx->op == OP_F32) {
-    DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
-    af.g[0] = GemmGroup{ctx->xf, ctx->fout, n_img, 0};
-    af.n = C;
-    DIT_TIMED(P_FINAL, flf, 0.0, gemm_simple(af, EPI_STORE_F32, ctx->op, stream), "final projection");
-  } else {
-    DIT_CHECK(ln_modulate(ctx->xm, ctx->op, D, ctx->x, D, n_img, n_txt, D, c.ln_eps, fms, sg, stream), "final norm");
-    af.g[0] = GemmGroup{ctx->xm, ctx->fout_pad, n_img, 0};
-    af.n = (C + 255) / 256 * 256;  // zero weight rows past C; only the first C columns are stored
-    af.n_store = C;
-    DIT_TIMED(P_FINAL, flf, 0.0, gemm_mfma(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+  for (int qs = 0; qs < nseq; ++qs) {
+    GemmArgs af = {};
+    af.ng = 1;
+    af.k = D;
+    af.ldx = D;
+    af.out = out;
+    af.ldo = C;
+    af.accumulate = hs[qs].mode;
+    af.alpha = hs[qs].alpha;
+    const int row0 = qs * per + n_txt;
+    if (ctx->op == OP_F32) {
+      DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, row0, D, c.ln_eps, fms, sg, stream),
+                "final norm");
+      af.g[0] = GemmGroup{ctx->xf, ctx->fout, n_img, 0};
+      af.n = C;
+      DIT_TIMED(P_FINAL, flf, 0.0, gemm_simple(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+    } else {
+      DIT_CHECK(ln_modulate(ctx->xm, ctx->op, D, ctx->x, D, n_img, row0, D, c.ln_eps, fms, sg, stream),
+                "final norm");
+      af.g[0] = GemmGroup{ctx->xm, ctx->fout_pad, n_img, 0};
+      af.n = (C + 255) / 256 * 256;  // zero weight rows past C; only the first C columns are stored
+      af.n_store = C;
+      DIT_TIMED(P_FINAL, flf, 0.0, gemm_mfma(af, EPI_STORE_F32, ctx->op, stream), "final projection");
+    }
   }
   return 0;
 }
 
 int check_grid(dit_ctx *ctx, const float *lat, const float *txt, int n_txt, int gh, int gw,
-               const float *ref_lat, int rgh, int rgw) {
+               const float *ref_lat, int rgh, int rgw, int nseq = 1) {
   if (gh < 1 || gw < 1) return fail(DIT_EINVAL, "image grid must be at least 1x1");
   if (rgh < 0 || rgw < 0 || (rgh == 0) != (rgw == 0)) return fail(DIT_EINVAL, "bad reference grid");
   if (!lat) return fail(DIT_EINVAL, "lat is NULL");
   if (n_txt > 0 && !txt) return fail(DIT_EINVAL, "txt is NULL");
   if (rgh > 0 && !ref_lat) return fail(DIT_EINVAL, "ref_lat is NULL");
-  return check_tokens(ctx, n_txt, gh * gw, rgh * rgw);
+  return check_tokens(ctx, n_txt, gh * gw, rgh * rgw, nseq);
 }
 
 }  // namespace
@@ -709,28 +744,76 @@ extern "C" int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat,
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
   if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
   if (!v) return fail(DIT_EINVAL, "v is NULL");
-  return run_forward(ctx, lat, ref_lat, txt, n_txt, gh, gw, rgh, rgw, (double)t, v, 0, 0.f,
+  const float *txts[2] = {txt, nullptr};
+  const HeadStore hs[2] = {{0, 0.f}, {0, 0.f}};
+  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t, v, hs,
                      (hipStream_t)stream);
 }
 
-extern "C" int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, int gw,
-                           const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed, void *stream_) {
+extern "C" int dit_forward_cfg(dit_ctx *ctx, const float *lat, const float *ref_lat,
+                               const float *txt, const float *txt_uncond, int n_txt, int gh, int gw,
+                               int rgh, int rgw, float t, float guidance, float *v, void *stream) {
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw, 2)) return rc;
+  if (n_txt > 0 && !txt_uncond) return fail(DIT_EINVAL, "txt_uncond is NULL");
+  if (!v) return fail(DIT_EINVAL, "v is NULL");
+  if (!isfinite(guidance)) return fail(DIT_EINVAL, "guidance must be finite");
+  // v = g v_c + (1 - g) v_u  (= v_u + g (v_c - v_u))
+  const float *txts[2] = {txt, txt_uncond};
+  const HeadStore hs[2] = {{2, guidance}, {1, 1.0f - guidance}};
+  return run_forward(ctx, lat, ref_lat, txts, 2, n_txt, gh, gw, rgh, rgw, (double)t, v, hs,
+                     (hipStream_t)stream);
+}
+
+namespace {
+
+int denoise(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond, int nseq,
+            float guidance, int n_txt, int gh, int gw, const float *ref_lat, int rgh, int rgw,
+            int n_steps, int64_t seed, hipStream_t stream) {
   if (n_steps < 1) return fail(DIT_EINVAL, "n_steps must be >= 1, got %d", n_steps);
-  hipStream_t stream = (hipStream_t)stream_;
   if (seed >= 0)
     DIT_CHECK(philox_normal(lat, (int64_t)gh * gw * ctx->cfg.in_channels, (uint64_t)seed, stream), "noise");
+  const float *txts[2] = {txt, txt_uncond};
   for (int i = 0; i < n_steps; ++i) {
     const double t_cur = 1.0 - (double)i / n_steps;
     const double t_next = 1.0 - (double)(i + 1) / n_steps;
-    // Euler: lat += (t_i - t_{i+1}) * v, fused into the output projection's epilogue
-    if (int rc = run_forward(ctx, lat, ref_lat, txt, n_txt, gh, gw, rgh, rgw, t_cur, lat, 1,
-                             (float)(t_cur - t_next), stream))
+    const float dt = (float)(t_cur - t_next);
+    // Euler: lat += (t_i - t_{i+1}) * v, fused into the output projection's epilogue; with
+    // guidance v = g v_c + (1 - g) v_u, added branch by branch
+    HeadStore hs[2] = {{1, dt}, {1, 0.f}};
+    if (nseq == 2) {
+      hs[0].alpha = dt * guidance;
+      hs[1].alpha = dt * (1.0f - guidance);
+    }
+    if (int rc = run_forward(ctx, lat, ref_lat, txts, nseq, n_txt, gh, gw, rgh, rgw, t_cur, lat,
+                             hs, stream))
       return rc;
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, int gw,
+                           const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
+  return denoise(ctx, lat, txt, nullptr, 1, 1.0f, n_txt, gh, gw, ref_lat, rgh, rgw, n_steps, seed,
+                 (hipStream_t)stream);
+}
+
+extern "C" int dit_denoise_cfg(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond,
+                               int n_txt, int gh, int gw, const float *ref_lat, int rgh, int rgw,
+                               int n_steps, float guidance, int64_t seed, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw, 2)) return rc;
+  if (n_txt > 0 && !txt_uncond) return fail(DIT_EINVAL, "txt_uncond is NULL");
+  if (!isfinite(guidance)) return fail(DIT_EINVAL, "guidance must be finite");
+  return denoise(ctx, lat, txt, txt_uncond, 2, guidance, n_txt, gh, gw, ref_lat, rgh, rgw, n_steps,
+                 seed, (hipStream_t)stream);
 }
 
 extern "C" int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream) {

@@ -16,15 +16,21 @@ namespace {
 
 constexpr int TN = 64, TM = 64, TK = 16;
 
+// First token tile of each row group (entries past the last group hold the total).
+struct TileStarts {
+  int t[kMaxGroups + 1];
+};
+
 template <typename TW, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, int m_tiles_total,
-                                                      int t_before1, int t_before2) {
+__global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, int m_tiles_total) {
   __shared__ float ws[TK][TN + 4];
   __shared__ float xs[TK][TM + 4];
   const int tile_n = blockIdx.x / m_tiles_total;
   const int mt = blockIdx.x - tile_n * m_tiles_total;
-  const int gi = (mt >= t_before1) + (mt >= t_before2);
-  const int lmt = mt - (gi == 0 ? 0 : (gi == 1 ? t_before1 : t_before2));
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
+  const int lmt = mt - tb.t[gi];
   const GemmGroup grp = a.g[gi];
   const int n0 = tile_n * TN, m0 = lmt * TM;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -64,9 +70,11 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, int m_tiles_tot
       float *o = a.out + (size_t)tok * a.ldo + n0 + tx;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[16 * i] = a.accumulate ? o[16 * i] + a.alpha * acc[i][j] : acc[i][j];
+        o[16 * i] = a.accumulate == 1   ? o[16 * i] + a.alpha * acc[i][j]
+                    : a.accumulate == 2 ? a.alpha * acc[i][j]
+                                        : acc[i][j];
     } else if constexpr (EPI == EPI_RESID) {
-      const float *gate = a.gate[segment_of(tok, a.b1, a.b2)] + n0 + tx;
+      const float *gate = a.gate[segment_of(tok, a.b1, a.b2, a.per)] + n0 + tx;
       float *xr = a.x + (size_t)tok * a.ldres + n0 + tx;
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr[16 * i] += gate[16 * i] * acc[i][j];
@@ -88,10 +96,12 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, int m_tiles_tot
 
 template <typename TW, int EPI>
 hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
-  int tb[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 3; ++i) tb[i + 1] = tb[i] + (i < a.ng ? (a.g[i].rows + TM - 1) / TM : 0);
-  if (tb[3] == 0) return hipSuccess;
-  k_gemm_simple<TW, EPI><<<tb[3] * (a.n / TN), 256, 0, s>>>(a, tb[3], tb[1], tb[2]);
+  TileStarts tb = {};
+  for (int i = 0; i < kMaxGroups; ++i)
+    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + TM - 1) / TM : 0);
+  const int m_tiles = tb.t[kMaxGroups];
+  if (m_tiles == 0) return hipSuccess;
+  k_gemm_simple<TW, EPI><<<m_tiles * (a.n / TN), 256, 0, s>>>(a, tb, m_tiles);
   return hipGetLastError();
 }
 
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_q) {
 }  // namespace
 
 hipError_t gemm_simple(const GemmArgs &a, int epi, int w_type, hipStream_t s) {
-  if (a.n % TN || a.k % TK || a.ng < 1 || a.ng > 3) return hipErrorInvalidValue;
+  if (a.n % TN || a.k % TK || a.ng < 1 || a.ng > kMaxGroups) return hipErrorInvalidValue;
   switch (w_type) {
     case OP_F32: return dispatch_simple<float>(a, epi, s);
     case OP_BF16: return dispatch_simple<bf16>(a, epi, s);

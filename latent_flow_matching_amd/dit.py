@@ -66,6 +66,10 @@ def load_library(path: str = None):
     lib.dit_forward.argtypes = [P, P, P, P, I, I, I, I, I, F, P, P]
     lib.dit_denoise.restype = I
     lib.dit_denoise.argtypes = [P, P, P, I, I, I, P, I, I, I, I64, P]
+    lib.dit_forward_cfg.restype = I
+    lib.dit_forward_cfg.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, P, P]
+    lib.dit_denoise_cfg.restype = I
+    lib.dit_denoise_cfg.argtypes = [P, P, P, P, I, I, I, P, I, I, I, F, I64, P]
     lib.dit_fill_noise.restype = I
     lib.dit_fill_noise.argtypes = [P, I64, I64, P]
     lib.dit_debug_buffer.restype = P
@@ -185,6 +189,30 @@ class DiT:
         _check(load_library().dit_denoise(self._h, _ptr(lat), _ptr(txt), txt.shape[0], grid[0],
                                           grid[1], _ptr(ref_lat), ref_grid[0], ref_grid[1],
                                           n_steps, seed, _stream(stream)))
+
+    def forward_cfg(self, lat, txt, txt_uncond, grid, t, guidance, v, ref_lat=None,
+                    ref_grid=(0, 0), stream=None):
+        """Guided velocity v_u + guidance * (v_c - v_u) from one batch-of-two call."""
+        for a, w in ((lat, "lat"), (txt, "txt"), (txt_uncond, "txt_uncond"), (v, "v"),
+                     (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        if tuple(txt_uncond.shape) != tuple(txt.shape):
+            raise ValueError("txt and txt_uncond must have the same shape")
+        _check(load_library().dit_forward_cfg(self._h, _ptr(lat), _ptr(ref_lat), _ptr(txt),
+                                              _ptr(txt_uncond), txt.shape[0], grid[0], grid[1],
+                                              ref_grid[0], ref_grid[1], float(t), float(guidance),
+                                              _ptr(v), _stream(stream)))
+
+    def denoise_cfg(self, lat, txt, txt_uncond, grid, n_steps, guidance, seed=-1, ref_lat=None,
+                    ref_grid=(0, 0), stream=None):
+        for a, w in ((lat, "lat"), (txt, "txt"), (txt_uncond, "txt_uncond"), (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        if tuple(txt_uncond.shape) != tuple(txt.shape):
+            raise ValueError("txt and txt_uncond must have the same shape")
+        _check(load_library().dit_denoise_cfg(self._h, _ptr(lat), _ptr(txt), _ptr(txt_uncond),
+                                              txt.shape[0], grid[0], grid[1], _ptr(ref_lat),
+                                              ref_grid[0], ref_grid[1], n_steps, float(guidance),
+                                              seed, _stream(stream)))
 
     KERNELS = ("ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2", "conditioning",
                "embed", "final")

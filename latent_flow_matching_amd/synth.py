@@ -75,6 +75,7 @@ class Workload:
     steps: int
     blocks: str          # "one" = a single block through dit_block_forward, "stack" = full denoise
     description: str
+    guidance: float | None = None  # classifier-free guidance scale: both branches as a batch of 2
 
     @property
     def n_img(self) -> int:
@@ -110,6 +111,11 @@ WORKLOADS = {
         "flux3_stack_512txt_4096img_4096ref_1step", FLUX3_KLEIN, 512, (64, 64), (64, 64), 1,
         "stack",
         "5 per-mode + 28 joint blocks, 512 text + 4096 image + 4096 reference tokens, 1 step"),
+    "flux3_cfg_512txt_4096img_50step": Workload(
+        "flux3_cfg_512txt_4096img_50step", FLUX3_KLEIN, 512, (64, 64), None, 50, "stack",
+        "5 per-mode + 28 joint blocks, 512 text + 4096 image tokens, 50 Euler steps with "
+        "classifier-free guidance 3.5 (the base checkpoint's published setting): conditional and "
+        "unconditional branch as one batch of 2 sequences", guidance=3.5),
 }
 
 

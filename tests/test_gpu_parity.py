@@ -213,6 +213,97 @@ def test_denoise_tiny(cfg):
     assert err <= BF16_TOL
 
 
+# ----------------------------------------------------------------- classifier-free guidance (batch of 2)
+
+def _cfg_inputs(cfg, n_txt, grid, ref_grid):
+    lat = S.gen_latents(grid[0] * grid[1], cfg.in_channels)
+    ref = S.gen_latents(ref_grid[0] * ref_grid[1], cfg.in_channels, key=(1,)) if ref_grid else None
+    txt = S.gen_text(n_txt, cfg.hidden)
+    txt_u = S.gen_text(n_txt, cfg.hidden, seed=S.SEED_T + 7)
+    return lat, ref, txt, txt_u
+
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3, C16[0], C16[1], F32[1]],
+                         ids=["flux2", "flux3", "flux2_bf16", "flux3_bf16", "flux3_f32"])
+@pytest.mark.parametrize("guidance", [1.0, 0.0, 3.5], ids=["g1", "g0", "g3.5"])
+def test_forward_cfg_matches_oracle(cfg, guidance):
+    """Both branches of guidance as one batch of two sequences (FLUX.3: six row groups in the
+    per-mode block) against the oracle's two separate calls combined.  g = 1 and g = 0 return
+    one branch through the batched path and meet the bar of a transformer output.  Other g
+    combine the branches linearly, so the branch errors add with weights |g| and |1 - g|:
+    the bound is tol * (|g| RMS(v_c) + |1 - g| RMS(v_u))."""
+    ctx, w = context(cfg, 600)
+    grid = (9, 7)
+    ref_grid = (6, 5) if cfg.arch == S.ARCH_FLUX3 else None
+    lat, ref, txt, txt_u = _cfg_inputs(cfg, 50, grid, ref_grid)
+    v = torch.empty((grid[0] * grid[1], cfg.in_channels), device="cuda")
+    print(f"[forward_cfg] arch={cfg.arch} compute={cfg.compute} g={guidance}", flush=True)
+    ctx.forward_cfg(dev(lat), dev(txt), dev(txt_u), grid, 0.75, guidance, v,
+                    None if ref is None else dev(ref), ref_grid or (0, 0))
+    torch.cuda.synchronize()
+    m = oracle_model(cfg, w)
+    t = float(np.float32(0.75))
+    rl = None if ref is None else f64(ref)
+    vc = O.forward(m, f64(lat), f64(txt), grid, t, rl, ref_grid)
+    vu = O.forward(m, f64(lat), f64(txt_u), grid, t, rl, ref_grid)
+    want = O.guided_velocity(vc, vu, guidance)
+    got = v.cpu().numpy().astype(np.float64)
+    rms = lambda a: float(np.sqrt(np.mean(a * a)))
+    err = float(np.max(np.abs(got - want)))
+    bound = tol(cfg, full_width=False) * (abs(guidance) * rms(vc) + abs(1 - guidance) * rms(vu))
+    print(f"    forward_cfg max err {err:.3e}, bound {bound:.3e} (rel to RMS(v) {err / rms(want):.3e})",
+          flush=True)
+    assert err <= bound
+
+
+def test_forward_cfg_without_text_ignores_guidance():
+    """With no text tokens both branches are the same sequence, so every guidance scale gives
+    the plain velocity."""
+    cfg = TINY2
+    ctx, w = context(cfg, 600)
+    grid = (5, 6)
+    lat = S.gen_latents(30, cfg.in_channels)
+    empty = torch.empty((0, cfg.hidden), device="cuda")
+    v = torch.empty((30, cfg.in_channels), device="cuda")
+    ctx.forward_cfg(dev(lat), empty, empty, grid, 0.5, 4.0, v)
+    torch.cuda.synchronize()
+    want = O.forward(oracle_model(cfg, w), f64(lat), np.zeros((0, cfg.hidden)), grid, 0.5)
+    assert rel_err(v.cpu().numpy(), want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3], ids=["flux2", "flux3"])
+def test_denoise_cfg_matches_oracle(cfg):
+    ctx, w = context(cfg, 600)
+    grid = (8, 6)
+    ref_grid = (4, 4) if cfg.arch == S.ARCH_FLUX3 else None
+    noise = S.gen_latents(48, cfg.in_channels, key=(2,))
+    _, ref, txt, txt_u = _cfg_inputs(cfg, 20, grid, ref_grid)
+    lat = dev(noise)
+    ctx.denoise_cfg(lat, dev(txt), dev(txt_u), grid, 3, 2.5, -1, None if ref is None else dev(ref),
+                    ref_grid or (0, 0))
+    torch.cuda.synchronize()
+    want = O.denoise_cfg(oracle_model(cfg, w), f64(noise), f64(txt), f64(txt_u), grid, 3, 2.5,
+                         None if ref is None else f64(ref), ref_grid)
+    err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
+    print(f"denoise_cfg update err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_cfg_rejects_two_sequences_over_max_tokens():
+    from latent_flow_matching_amd import dit
+    cfg = TINY2
+    ctx, _ = context(cfg, 600)
+    grid = (16, 16)  # 50 + 256 tokens fit once, not twice
+    lat = torch.zeros((256, cfg.in_channels), device="cuda")
+    txt = torch.zeros((50, cfg.hidden), device="cuda")
+    v = torch.empty_like(lat)
+    ctx.forward(lat, txt, grid, 0.5, v)
+    with pytest.raises(dit.DitError, match="max_tokens"):
+        ctx.forward_cfg(lat, txt, txt, grid, 0.5, 2.0, v)
+    with pytest.raises(dit.DitError, match="guidance"):
+        ctx.forward_cfg(lat[:4], txt, txt, (2, 2), 0.5, float("nan"), v[:4])
+
+
 @pytest.mark.parametrize("n,seed", [(1001, 7), (4, (1 << 40) + 5), ((1 << 20) + 3, 2 ** 63 - 1), (1, 0)],
                          ids=["ragged", "high_seed", "1M", "one"])
 def test_fill_noise_matches_oracle(n, seed):
