@@ -376,6 +376,17 @@ def cond_rows(arch: int, t: float, w_l1, w_l2):
     return [c0, ct, c0]
 
 
+def flow_map_cond_rows(arch: int, t: float, t_target: float, w_l1, w_l2, w_tl1, w_tl2):
+    """Conditioning rows of a flow-map (timestep-distilled) model: besides its current time,
+    the model is told the time its step jumps to, through an embedding of its own that is
+    added to the modulation of every token ([MV] Modulation/RoPE, flow-map distillation).
+    reading: the target time goes through the same sinusoid and a separate two-layer MLP
+    (w_tl1, w_tl2), and the result is added to every segment's conditioning vector, the
+    input of all modulation projections."""
+    tgt = cond_vector(t_target, w_tl1, w_tl2)
+    return [c + tgt for c in cond_rows(arch, t, w_l1, w_l2)]
+
+
 def segment_mods(w_mod_sets: list[np.ndarray], set_of_segment, conds):
     """Per-segment [3D] modulation vectors for one block kind."""
     return [modulation(w_mod_sets[set_of_segment[s]], conds[s]) for s in range(3)]
@@ -408,10 +419,38 @@ class Model:
     final_out: np.ndarray         # [C, D]
     mods: list = field(default_factory=list)
     blocks: list = field(default_factory=list)
+    temb_tgt_l1: np.ndarray | None = None   # [D, time_dim]  flow-map models only
+    temb_tgt_l2: np.ndarray | None = None   # [D, D]
+    txt_in: np.ndarray | None = None        # [D, 8 * 2560]  text-feature projection
+
+
+# ----------------------------------------------------------------------------------------
+# Text features ([MV] Tokens): the text encoder's hidden states of layers 4, 8, ..., 32 (of
+# 36) are stacked per token to 8 x 2560 = 20480 values and projected by one linear layer to
+# the transformer width 3072.
+# ----------------------------------------------------------------------------------------
+
+TEXT_ENCODER_DEPTH = 36
+TEXT_FEATURE_LAYERS = (4, 8, 12, 16, 20, 24, 28, 32)
+TEXT_HIDDEN = 2560
+
+
+def stack_text_features(hidden_by_layer: dict) -> np.ndarray:
+    """hidden_by_layer[l] = [n_txt, hidden] state after encoder layer l; the result is
+    [n_txt, 8 * hidden] with the layers in the order listed.  reading: stacking is
+    concatenation along the feature axis, shallowest layer first."""
+    return np.concatenate([np.asarray(hidden_by_layer[l], np.float64)
+                           for l in TEXT_FEATURE_LAYERS], axis=1)
+
+
+def project_text(feat: np.ndarray, w_txt_in: np.ndarray) -> np.ndarray:
+    """[n_txt, D] text rows of the transformer sequence.  reading: no bias (Q10)."""
+    return feat @ w_txt_in.T
 
 
 def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
-            ref_lat: np.ndarray | None = None, ref_grid=None, block_hook=None):
+            ref_lat: np.ndarray | None = None, ref_grid=None, block_hook=None,
+            t_target: float | None = None):
     """One transformer call: velocity [n_img, C] for latents lat [n_img, C] at time t.
 
     Sequence = text || image || reference ([MV] Blocks).  Image and reference latents go
@@ -429,7 +468,13 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
         ref_grids = (ref_grid,)
     x = np.concatenate(parts, axis=0)
     pos = positions(n_txt, grid, ref_grids)
-    conds = cond_rows(model.arch, t, model.temb_l1, model.temb_l2)
+    if model.temb_tgt_l1 is not None:
+        if t_target is None:
+            raise ValueError("a flow-map model needs the target time of the step")
+        conds = flow_map_cond_rows(model.arch, t, t_target, model.temb_l1, model.temb_l2,
+                                   model.temb_tgt_l1, model.temb_tgt_l2)
+    else:
+        conds = cond_rows(model.arch, t, model.temb_l1, model.temb_l2)
     for b in range(model.n_stream + model.n_shared):
         kind, sos, mask = block_plan(model.arch, b, model.n_stream)
         mods = segment_mods(model.mods[kind], sos, conds)
@@ -460,7 +505,7 @@ def denoise(model: Model, noise: np.ndarray, txt: np.ndarray, grid, n_steps: int
     ts = euler_schedule(n_steps)
     lat = noise.astype(np.float64).copy()
     for i in range(n_steps):
-        v = forward(model, lat, txt, grid, ts[i], ref_lat, ref_grid)
+        v = forward(model, lat, txt, grid, ts[i], ref_lat, ref_grid, t_target=ts[i + 1])
         lat = euler_step(lat, v, ts[i], ts[i + 1])
     return lat
 
@@ -481,11 +526,12 @@ def guided_velocity(v_cond: np.ndarray, v_uncond: np.ndarray, guidance: float) -
 
 
 def forward_cfg(model: Model, lat: np.ndarray, txt: np.ndarray, txt_uncond: np.ndarray, grid,
-                t: float, guidance: float, ref_lat: np.ndarray | None = None, ref_grid=None):
+                t: float, guidance: float, ref_lat: np.ndarray | None = None, ref_grid=None,
+                t_target: float | None = None):
     """Guided velocity of one Euler step: the transformer on the conditional and on the
     unconditional text, same latents, references and time, combined by guided_velocity."""
-    v_c = forward(model, lat, txt, grid, t, ref_lat, ref_grid)
-    v_u = forward(model, lat, txt_uncond, grid, t, ref_lat, ref_grid)
+    v_c = forward(model, lat, txt, grid, t, ref_lat, ref_grid, t_target=t_target)
+    v_u = forward(model, lat, txt_uncond, grid, t, ref_lat, ref_grid, t_target=t_target)
     return guided_velocity(v_c, v_u, guidance)
 
 
@@ -495,7 +541,8 @@ def denoise_cfg(model: Model, noise: np.ndarray, txt: np.ndarray, txt_uncond: np
     ts = euler_schedule(n_steps)
     lat = noise.astype(np.float64).copy()
     for i in range(n_steps):
-        v = forward_cfg(model, lat, txt, txt_uncond, grid, ts[i], guidance, ref_lat, ref_grid)
+        v = forward_cfg(model, lat, txt, txt_uncond, grid, ts[i], guidance, ref_lat, ref_grid,
+                        t_target=ts[i + 1])
         lat = euler_step(lat, v, ts[i], ts[i + 1])
     return lat
 

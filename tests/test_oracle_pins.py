@@ -457,6 +457,80 @@ def test_forward_cfg_branches():
                                    O.denoise(m, noise, tc, (2, 2), 2), atol=1e-12)
 
 
+# ------------------------------------------------------------------ FLUX.3 conditioning preamble
+
+def test_text_feature_layout_matches_printed_values():
+    with open(os.path.join(os.path.dirname(GOLDEN), "text_features.json")) as f:
+        g = json.load(f)
+    assert O.TEXT_ENCODER_DEPTH == g["encoder_layers_total"]
+    assert list(O.TEXT_FEATURE_LAYERS) == g["layers"]
+    assert O.TEXT_HIDDEN == g["hidden"]
+    assert len(O.TEXT_FEATURE_LAYERS) * O.TEXT_HIDDEN == g["stacked_width"]
+    # every 4th layer of 36, none past the last
+    assert all(l % 4 == 0 and 0 < l <= g["encoder_layers_total"] for l in g["layers"])
+    # stacking keeps the listed layer order: layer l's state fills its own column block
+    n = 3
+    hid = {l: np.full((n, 5), float(l)) for l in O.TEXT_FEATURE_LAYERS}
+    st = O.stack_text_features(hid)
+    assert st.shape == (n, 8 * 5)
+    np.testing.assert_array_equal(st[0], np.repeat(np.array(g["layers"], float), 5))
+
+
+def test_text_projection_identities():
+    """A one-hot feature picks that column of txt_in (catches a transposed weight); the
+    projection is additive."""
+    r = rng(40)
+    w = r.normal(size=(6, 32))
+    e = np.zeros((1, 32))
+    e[0, 7] = 1.0
+    np.testing.assert_array_equal(O.project_text(e, w)[0], w[:, 7])
+    a, b = r.normal(size=(4, 32)), r.normal(size=(4, 32))
+    np.testing.assert_allclose(O.project_text(a + b, w), O.project_text(a, w) + O.project_text(b, w),
+                               atol=1e-13)
+
+
+def test_flow_map_cond_rows():
+    """A zero target-time MLP leaves the plain conditioning; otherwise every segment's row
+    moves by the same vector, the target time's own embedding, whatever the segment's time."""
+    r = rng(41)
+    d, td = 8, 16
+    l1, l2 = r.normal(size=(d, td)), r.normal(size=(d, d))
+    tl1, tl2 = r.normal(size=(d, td)), r.normal(size=(d, d))
+    for arch in (O.ARCH_FLUX2, O.ARCH_FLUX3):
+        plain = O.cond_rows(arch, 0.6, l1, l2)
+        zero = O.flow_map_cond_rows(arch, 0.6, 0.3, l1, l2, np.zeros_like(tl1), np.zeros_like(tl2))
+        for a, b in zip(zero, plain):
+            np.testing.assert_array_equal(a, b)
+        fm = O.flow_map_cond_rows(arch, 0.6, 0.3, l1, l2, tl1, tl2)
+        want = l2 @ O.silu(l1 @ O.timestep_embedding(0.6, td))
+        tgt = tl2 @ O.silu(tl1 @ O.timestep_embedding(0.3, td))
+        for s in range(3):
+            np.testing.assert_allclose(fm[s] - plain[s], tgt, atol=1e-12)
+        np.testing.assert_allclose(fm[1], want + tgt, atol=1e-12)
+        other = O.flow_map_cond_rows(arch, 0.6, 0.1, l1, l2, tl1, tl2)
+        assert not np.allclose(other[1], fm[1])
+
+
+def test_flow_map_forward():
+    """A flow-map model with a zero target MLP is the plain model; it needs the target time;
+    with a real target MLP the velocity depends on the target time."""
+    r = rng(42)
+    for arch in (O.ARCH_FLUX2, O.ARCH_FLUX3):
+        m = tiny_model(arch, r)
+        lat = r.normal(size=(4, TINY.in_channels))
+        txt = r.normal(size=(3, TINY.hidden))
+        v_plain = O.forward(m, lat, txt, (2, 2), 0.6)
+        m.temb_tgt_l1 = np.zeros((TINY.hidden, TINY.time_dim))
+        m.temb_tgt_l2 = np.zeros((TINY.hidden, TINY.hidden))
+        np.testing.assert_array_equal(O.forward(m, lat, txt, (2, 2), 0.6, t_target=0.2), v_plain)
+        with pytest.raises(ValueError):
+            O.forward(m, lat, txt, (2, 2), 0.6)
+        m.temb_tgt_l1 = r.normal(0, 0.1, (TINY.hidden, TINY.time_dim))
+        m.temb_tgt_l2 = r.normal(0, 0.1, (TINY.hidden, TINY.hidden))
+        assert not np.allclose(O.forward(m, lat, txt, (2, 2), 0.6, t_target=0.2),
+                               O.forward(m, lat, txt, (2, 2), 0.6, t_target=0.4))
+
+
 # ------------------------------------------------------------------ the pins catch planted slips
 
 def _wrong_rope(x, angles):
@@ -533,6 +607,17 @@ def test_pins_catch_planted_slips(monkeypatch):
     with pytest.raises(AssertionError):
         test_philox_known_answers()
     monkeypatch.undo()
+    # the target time added to the image row only
+    orig_fm = O.flow_map_cond_rows
+
+    def image_only(arch, t, tt, l1, l2, tl1, tl2):
+        rows = O.cond_rows(arch, t, l1, l2)
+        rows[1] = rows[1] + O.cond_vector(tt, tl1, tl2)
+        return rows
+    monkeypatch.setattr(O, "flow_map_cond_rows", image_only)
+    with pytest.raises(AssertionError):
+        test_flow_map_cond_rows()
+    monkeypatch.setattr(O, "flow_map_cond_rows", orig_fm)
     # guidance with the branches swapped
     monkeypatch.setattr(O, "guided_velocity", lambda vc, vu, g: vc + g * (vu - vc))
     with pytest.raises(AssertionError):
