@@ -82,6 +82,11 @@ typedef struct {
   float rope_theta;     /* RoPE base (10000)      */
   float ln_eps;         /* LayerNorm epsilon (1e-6) */
   float rms_eps;        /* QK RMSNorm epsilon (1e-6) */
+  int txt_feat_dim;     /* 0, or the width of stacked text-encoder features that
+                         * dit_text_features projects to D with txt_in (FLUX.3: 8 hidden
+                         * states of 2560 = 20480); multiple of 64, <= 65536 */
+  int flow_map;         /* 1: flow-map (timestep-distilled) model: every conditioning row
+                         * also gets the embedding of the step's target time (temb_tgt) */
 } dit_config;
 
 /* One named weight tensor in host memory, row-major [out, in].  dtype DIT_F32: float
@@ -90,6 +95,8 @@ typedef struct {
  * Names and shapes (b = block index, s = weight set):
  *   img_in      [D, C]       input projection of image and reference latents
  *   temb.l1     [D, time_dim], temb.l2 [D, D]   timestep MLP
+ *   temb_tgt.l1 [D, time_dim], temb_tgt.l2 [D, D]   target-time MLP (flow_map = 1 only)
+ *   txt_in      [D, txt_feat_dim]   text-feature projection (txt_feat_dim > 0 only)
  *   final.mod   [2D, D]      output-head modulation (shift || scale)
  *   final.out   [C, D]       output projection to the velocity
  *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) of stream blocks, per set
@@ -149,6 +156,26 @@ int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
 int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt, int gh, int gw,
                 const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed,
                 void *stream);
+
+/* FLUX.3 text features to transformer width: txt = feat . txt_in^T.
+ *   feat  dev fp32 [n_txt, txt_feat_dim]: per text token the hidden states of text-encoder
+ *         layers 4, 8, ..., 32 (of 36) stacked in that order, 8 x 2560 values
+ *   txt   dev fp32 [n_txt, D] output, the txt argument of the calls below
+ * ("FLUX.3 Image Klein in Diffusers", "Zweistufiger Transformer und Tokenisierung im
+ * Detail": eight hidden states of Qwen3-VL per token, stacked to 20480 values, one linear
+ * layer to 3072.)  Runs once per prompt, outside the sampling loop.  Requires
+ * txt_feat_dim > 0 and 1 <= n_txt <= max_tokens. */
+int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, float *txt, void *stream);
+
+/* dit_forward for a flow-map model (flow_map = 1): the call also receives the time t_target
+ * its step jumps to, whose embedding (temb_tgt) is added to every conditioning row
+ * ("FLUX.3 Image Klein in Diffusers", "Modulation pro Token-Typ, Flow-Map-Destillation und
+ * 4D-RoPE": the distilled checkpoint gets the target timestep through its own embedding,
+ * added to every token's modulation).  dit_forward and dit_forward_cfg fail on a flow-map
+ * context; dit_denoise and dit_denoise_cfg pass t_{i+1} as the target of step i. */
+int dit_forward_flow(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt,
+                     int n_txt, int gh, int gw, int rgh, int rgw, float t, float t_target,
+                     float *v, void *stream);
 
 /* Classifier-free guidance: one call of the transformer on two sequences at once, the
  * conditional text txt and the unconditional text txt_uncond (both dev fp32 [n_txt, D]), each

@@ -94,10 +94,12 @@ hipError_t to_half(void *dst, int type, const float *src, int64_t n, hipStream_t
 // (silu_in: the vectors go through SiLU first, into scratch [nvec][k] fp32)
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
                 int silu_in, float *scratch, hipStream_t s);
-// e[v] = [cos(1000 t_v f_j), sin(1000 t_v f_j)], f_j = 10000^(-j/(dim/2))
+// e[v] = [cos(1000 t_v f_j), sin(1000 t_v f_j)], f_j = 10000^(-j/(dim/2)), 1 <= nvec <= 4
 hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s);
 hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,
                          hipStream_t s);
 hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s);
+// y[r][:] += v for rows r < nrows of d floats
+hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s);
 
 }  // namespace dit

@@ -497,7 +497,7 @@ hipError_t to_half(void *dst, int type, const float *src, int64_t n, hipStream_t
 // Sinusoidal timestep embedding (reading: the Transformer / DiT sinusoid with time factor
 // 1000 and max period 10000), in fp64: e = [cos(1000 t f_j) | sin(1000 t f_j)].
 struct TVals {
-  double t[3];
+  double t[4];
 };
 __global__ void k_timestep_embed(float *e, TVals tv, int nvec, int dim) {
   int j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -511,8 +511,9 @@ __global__ void k_timestep_embed(float *e, TVals tv, int nvec, int dim) {
 }
 
 hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s) {
-  TVals tv = {{0.0, 0.0, 0.0}};
-  for (int i = 0; i < nvec && i < 3; ++i) tv.t[i] = t_host[i];
+  if (nvec < 1 || nvec > 4) return hipErrorInvalidValue;
+  TVals tv = {{0.0, 0.0, 0.0, 0.0}};
+  for (int i = 0; i < nvec; ++i) tv.t[i] = t_host[i];
   int tot = nvec * dim;
   k_timestep_embed<<<(tot + 255) / 256, 256, 0, s>>>(e, tv, nvec, dim);
   return hipGetLastError();
@@ -571,6 +572,19 @@ __global__ void k_philox_normal(float *dst, int64_t n, uint64_t seed) {
   }
   for (int e = 0; e < 4; ++e)
     if (g * 4 + e < n) dst[g * 4 + e] = (float)out[e];
+}
+
+__global__ void k_add_row(float *y, int nrows, int d, const float *v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d) return;
+  const float a = v[i];
+  for (int r = 0; r < nrows; ++r) y[(size_t)r * d + i] += a;
+}
+
+hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s) {
+  if (nrows <= 0 || d <= 0) return hipSuccess;
+  k_add_row<<<(d + 255) / 256, 256, 0, s>>>(y, nrows, d, v);
+  return hipGetLastError();
 }
 
 hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s) {

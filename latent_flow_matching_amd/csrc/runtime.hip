@@ -69,6 +69,8 @@ struct dit_ctx {
   void *mod[2][3] = {{nullptr}};
   void *img_in = nullptr, *temb1 = nullptr, *temb2 = nullptr, *fmod = nullptr, *fout = nullptr;
   void *fout_pad = nullptr;  // 16-bit paths: final.out with zero rows up to a multiple of 256
+  void *ttgt1 = nullptr, *ttgt2 = nullptr;  // flow-map target-time MLP
+  void *txt_in = nullptr;                   // [D][txt_feat_dim] text-feature projection
 
   int rows_alloc = 0, ldv = 0;
   float *x = nullptr;        // [rows_alloc][D] residual of dit_forward / dit_denoise
@@ -80,8 +82,9 @@ struct dit_ctx {
   float *cs = nullptr;       // [rows_alloc][128]
   float *modbuf = nullptr;   // [2][3][3][3D]
   float *cond = nullptr;     // [3][D]
-  float *temb_e = nullptr;   // [3][time_dim]
-  float *temb_h = nullptr;   // [3][D]
+  float *temb_e = nullptr;   // [4][time_dim]: the three segment times, then the target time
+  float *temb_h = nullptr;   // [4][D]
+  float *tgt = nullptr;      // [D] target-time embedding (flow-map models)
   float *fmodv = nullptr;    // [3][2D]
   float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
   float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
@@ -202,6 +205,10 @@ int validate_config(const dit_config *c) {
     return fail(DIT_EINVAL, "unknown compute type %d", c->compute);
   if (!(c->rope_theta > 0.f) || !(c->ln_eps > 0.f) || !(c->rms_eps > 0.f))
     return fail(DIT_EINVAL, "rope_theta, ln_eps and rms_eps must be positive");
+  if (c->txt_feat_dim < 0 || c->txt_feat_dim % 64 || c->txt_feat_dim > 65536)
+    return fail(DIT_EUNSUPPORTED, "txt_feat_dim must be 0 or a multiple of 64 up to 65536, got %d",
+                c->txt_feat_dim);
+  if (c->flow_map != 0 && c->flow_map != 1) return fail(DIT_EINVAL, "flow_map must be 0 or 1");
   return 0;
 }
 
@@ -277,6 +284,11 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   want["temb.l2"] = (int64_t)D * D;
   want["final.mod"] = (int64_t)2 * D * D;
   want["final.out"] = (int64_t)C * D;
+  if (c.flow_map) {
+    want["temb_tgt.l1"] = (int64_t)D * T;
+    want["temb_tgt.l2"] = (int64_t)D * D;
+  }
+  if (c.txt_feat_dim > 0) want["txt_in"] = (int64_t)D * c.txt_feat_dim;
   const int nsets0 = c.arch == DIT_FLUX2 ? 2 : 3;
   if (c.n_stream_blocks > 0)
     for (int s = 0; s < nsets0; ++s) want["mod.0.s" + std::to_string(s)] = (int64_t)3 * D * D;
@@ -381,6 +393,11 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : up(&ctx->img_in, "img_in", false);
   rc = rc ? rc : up(&ctx->temb1, "temb.l1", false);
   rc = rc ? rc : up(&ctx->temb2, "temb.l2", false);
+  if (c.flow_map) {
+    rc = rc ? rc : up(&ctx->ttgt1, "temb_tgt.l1", false);
+    rc = rc ? rc : up(&ctx->ttgt2, "temb_tgt.l2", false);
+  }
+  if (c.txt_feat_dim > 0) rc = rc ? rc : up(&ctx->txt_in, "txt_in", false);
   rc = rc ? rc : up(&ctx->fmod, "final.mod", false);
   rc = rc ? rc : up(&ctx->fout, "final.out", false);
   for (int k = 0; k < 2 && !rc; ++k) {
@@ -417,8 +434,9 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs, R * 128 * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (size_t)2 * 3 * 3 * 3 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cond, (size_t)3 * D * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)3 * T * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)3 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)4 * T * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)4 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->tgt, (size_t)D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->act, (size_t)3 * D * 4);
   if (ctx->op != OP_F32 && ctx->lean_grid > 0) {
@@ -597,15 +615,24 @@ int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref, int nseq = 1) {
 
 // Conditioning for one transformer call at time t: cond rows per segment, modulation of
 // every block kind, output-head modulation.  FLUX.2: one timestep for all tokens; FLUX.3:
-// image tokens at t, text and reference tokens at t = 0.
-int prepare_conditioning(dit_ctx *ctx, double t, hipStream_t stream) {
+// image tokens at t, text and reference tokens at t = 0.  Flow-map models add the embedding
+// of the target time t_target (its own MLP) to every cond row.
+int prepare_conditioning(dit_ctx *ctx, double t, double t_target, hipStream_t stream) {
   const dit_config &c = ctx->cfg;
-  const int D = c.hidden;
-  double tv[3] = {t, t, t};
+  const int D = c.hidden, T = c.time_dim;
+  double tv[4] = {t, t, t, t_target};
   if (c.arch == DIT_FLUX3) tv[0] = tv[2] = 0.0;
-  DIT_CHECK(timestep_embed(ctx->temb_e, tv, 3, c.time_dim, stream), "timestep_embed");
-  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, c.time_dim, ctx->temb_e, 3, 0, nullptr, stream), "temb l1");
+  const int ne = c.flow_map ? 4 : 3;
+  DIT_CHECK(timestep_embed(ctx->temb_e, tv, ne, T, stream), "timestep_embed");
+  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, T, ctx->temb_e, 3, 0, nullptr, stream), "temb l1");
   DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, ctx->act, stream), "temb l2");
+  if (c.flow_map) {
+    DIT_CHECK(gemv(ctx->temb_h + 3 * D, ctx->ttgt1, ctx->op, D, T, ctx->temb_e + 3 * T, 1, 0, nullptr,
+                   stream), "target temb l1");
+    DIT_CHECK(gemv(ctx->tgt, ctx->ttgt2, ctx->op, D, D, ctx->temb_h + 3 * D, 1, 1, ctx->act, stream),
+              "target temb l2");
+    DIT_CHECK(add_row(ctx->cond, 3, D, ctx->tgt, stream), "target time");
+  }
   if (c.n_stream_blocks > 0)
     if (int rc = compute_mods(ctx, 0, ctx->cond, stream)) return rc;
   if (c.n_shared_blocks > 0)
@@ -626,8 +653,8 @@ struct HeadStore {
 // sequences that share latents, references and time.  The head stores sequence 0 first,
 // then sequence 1, each with its own HeadStore.
 int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *const txt[2],
-                int nseq, int n_txt, int gh, int gw, int rgh, int rgw, double t, float *out,
-                const HeadStore hs[2], hipStream_t stream) {
+                int nseq, int n_txt, int gh, int gw, int rgh, int rgw, double t, double t_target,
+                float *out, const HeadStore hs[2], hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = c.hidden, C = c.in_channels;
   const int n_img = gh * gw, n_ref = rgh * rgw;
@@ -635,7 +662,7 @@ int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
   const int per = sg.per;
   {
     const int pe = prof_begin(ctx, P_COND, stream);
-    if (int rc = prepare_conditioning(ctx, t, stream)) return rc;
+    if (int rc = prepare_conditioning(ctx, t, t_target, stream)) return rc;
     prof_end(ctx, pe, P_COND, 0.0, 0.0, stream);
   }
   for (int qs = 0; qs < nseq; ++qs)
@@ -744,10 +771,64 @@ extern "C" int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat,
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
   if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
   if (!v) return fail(DIT_EINVAL, "v is NULL");
+  if (ctx->cfg.flow_map) return fail(DIT_EINVAL, "flow-map model: call dit_forward_flow with the target time");
   const float *txts[2] = {txt, nullptr};
   const HeadStore hs[2] = {{0, 0.f}, {0, 0.f}};
-  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t, v, hs,
-                     (hipStream_t)stream);
+  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t, (double)t, v,
+                     hs, (hipStream_t)stream);
+}
+
+extern "C" int dit_forward_flow(dit_ctx *ctx, const float *lat, const float *ref_lat,
+                                const float *txt, int n_txt, int gh, int gw, int rgh, int rgw,
+                                float t, float t_target, float *v, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  if (!ctx->cfg.flow_map) return fail(DIT_EINVAL, "dit_forward_flow needs a flow-map model (flow_map = 1)");
+  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
+  if (!v) return fail(DIT_EINVAL, "v is NULL");
+  if (!isfinite(t) || !isfinite(t_target)) return fail(DIT_EINVAL, "t and t_target must be finite");
+  const float *txts[2] = {txt, nullptr};
+  const HeadStore hs[2] = {{0, 0.f}, {0, 0.f}};
+  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t,
+                     (double)t_target, v, hs, (hipStream_t)stream);
+}
+
+extern "C" int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, float *txt,
+                                 void *stream_) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  const int K = ctx->cfg.txt_feat_dim, D = ctx->cfg.hidden;
+  if (K <= 0) return fail(DIT_EINVAL, "the model has no text-feature projection (txt_feat_dim = 0)");
+  if (n_txt < 1 || n_txt > ctx->cfg.max_tokens)
+    return fail(DIT_EINVAL, "n_txt %d out of range [1, max_tokens %d]", n_txt, ctx->cfg.max_tokens);
+  if (!feat || !txt) return fail(DIT_EINVAL, "feat and txt must be device pointers");
+  hipStream_t stream = (hipStream_t)stream_;
+  GemmArgs a = {};
+  a.ng = 1;
+  a.n = D;
+  a.k = K;
+  a.ldx = K;
+  a.ldo = D;
+  if (ctx->op == OP_F32) {
+    a.g[0] = GemmGroup{feat, ctx->txt_in, n_txt, 0};
+    a.out = txt;
+    DIT_CHECK(gemm_simple(a, EPI_STORE_F32, ctx->op, stream), "text projection");
+    return 0;
+  }
+  // 16-bit operands: features rounded in chunks of rows through the cat workspace
+  const size_t cap = (size_t)ctx->rows_alloc * (D + ctx->F());  // 16-bit elements of cat
+  size_t fit = cap / K;  // feature rows the workspace holds (whole 256-row tiles when it can)
+  if (fit >= 256) fit = fit / 256 * 256;
+  const int chunk = (int)std::min<size_t>((size_t)n_txt, fit);
+  if (chunk < 1) return fail(DIT_EUNSUPPORTED, "txt_feat_dim %d too wide for the workspace", K);
+  for (int r0 = 0; r0 < n_txt; r0 += chunk) {
+    const int rows = std::min(chunk, n_txt - r0);
+    DIT_CHECK(to_half(ctx->cat, ctx->op, feat + (size_t)r0 * K, (int64_t)rows * K, stream), "feature cast");
+    a.g[0] = GemmGroup{ctx->cat, ctx->txt_in, rows, 0};
+    a.out = txt + (size_t)r0 * D;
+    DIT_CHECK(gemm_mfma(a, EPI_STORE_F32, ctx->op, stream), "text projection");
+  }
+  return 0;
 }
 
 extern "C" int dit_forward_cfg(dit_ctx *ctx, const float *lat, const float *ref_lat,
@@ -759,11 +840,13 @@ extern "C" int dit_forward_cfg(dit_ctx *ctx, const float *lat, const float *ref_
   if (n_txt > 0 && !txt_uncond) return fail(DIT_EINVAL, "txt_uncond is NULL");
   if (!v) return fail(DIT_EINVAL, "v is NULL");
   if (!isfinite(guidance)) return fail(DIT_EINVAL, "guidance must be finite");
+  if (ctx->cfg.flow_map)
+    return fail(DIT_EINVAL, "flow-map model: dit_forward_cfg takes no target time; use dit_denoise_cfg");
   // v = g v_c + (1 - g) v_u  (= v_u + g (v_c - v_u))
   const float *txts[2] = {txt, txt_uncond};
   const HeadStore hs[2] = {{2, guidance}, {1, 1.0f - guidance}};
-  return run_forward(ctx, lat, ref_lat, txts, 2, n_txt, gh, gw, rgh, rgw, (double)t, v, hs,
-                     (hipStream_t)stream);
+  return run_forward(ctx, lat, ref_lat, txts, 2, n_txt, gh, gw, rgh, rgw, (double)t, (double)t, v,
+                     hs, (hipStream_t)stream);
 }
 
 namespace {
@@ -786,8 +869,9 @@ int denoise(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond,
       hs[0].alpha = dt * guidance;
       hs[1].alpha = dt * (1.0f - guidance);
     }
-    if (int rc = run_forward(ctx, lat, ref_lat, txts, nseq, n_txt, gh, gw, rgh, rgw, t_cur, lat,
-                             hs, stream))
+    // flow-map models also see the time the step jumps to
+    if (int rc = run_forward(ctx, lat, ref_lat, txts, nseq, n_txt, gh, gw, rgh, rgw, t_cur, t_next,
+                             lat, hs, stream))
       return rc;
   }
   return 0;

@@ -27,7 +27,8 @@ class DitConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "arch", "hidden", "heads", "head_dim", "mlp_hidden", "in_channels", "time_dim",
         "n_stream_blocks", "n_shared_blocks", "max_tokens", "compute")] + \
-        [(n, ctypes.c_float) for n in ("rope_theta", "ln_eps", "rms_eps")]
+        [(n, ctypes.c_float) for n in ("rope_theta", "ln_eps", "rms_eps")] + \
+        [(n, ctypes.c_int) for n in ("txt_feat_dim", "flow_map")]
 
 
 class DitTensor(ctypes.Structure):
@@ -66,6 +67,10 @@ def load_library(path: str = None):
     lib.dit_forward.argtypes = [P, P, P, P, I, I, I, I, I, F, P, P]
     lib.dit_denoise.restype = I
     lib.dit_denoise.argtypes = [P, P, P, I, I, I, P, I, I, I, I64, P]
+    lib.dit_forward_flow.restype = I
+    lib.dit_forward_flow.argtypes = [P, P, P, P, I, I, I, I, I, F, F, P, P]
+    lib.dit_text_features.restype = I
+    lib.dit_text_features.argtypes = [P, P, I, P, P]
     lib.dit_forward_cfg.restype = I
     lib.dit_forward_cfg.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, P, P]
     lib.dit_denoise_cfg.restype = I
@@ -109,7 +114,7 @@ def make_config(cfg: ModelConfig, max_tokens: int) -> DitConfig:
     return DitConfig(cfg.arch, cfg.hidden, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
                      cfg.in_channels, cfg.time_dim, cfg.n_stream_blocks, cfg.n_shared_blocks,
                      max_tokens, COMPUTE[cfg.compute], cfg.rope_theta, cfg.ln_eps,
-                     cfg.rms_eps)
+                     cfg.rms_eps, cfg.txt_feat_dim, int(cfg.flow_map))
 
 
 def _ptr(t):
@@ -189,6 +194,25 @@ class DiT:
         _check(load_library().dit_denoise(self._h, _ptr(lat), _ptr(txt), txt.shape[0], grid[0],
                                           grid[1], _ptr(ref_lat), ref_grid[0], ref_grid[1],
                                           n_steps, seed, _stream(stream)))
+
+    def forward_flow(self, lat, txt, grid, t, t_target, v, ref_lat=None, ref_grid=(0, 0),
+                     stream=None):
+        """Velocity of a flow-map model for the step from t to t_target."""
+        for a, w in ((lat, "lat"), (txt, "txt"), (v, "v"), (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        _check(load_library().dit_forward_flow(self._h, _ptr(lat), _ptr(ref_lat), _ptr(txt),
+                                               txt.shape[0], grid[0], grid[1], ref_grid[0],
+                                               ref_grid[1], float(t), float(t_target), _ptr(v),
+                                               _stream(stream)))
+
+    def text_features(self, feat, txt, stream=None):
+        """txt [n, D] = feat [n, txt_feat_dim] . txt_in^T."""
+        _need(feat, "float32", "feat")
+        _need(txt, "float32", "txt")
+        if feat.shape[0] != txt.shape[0] or feat.dim() != 2 or txt.dim() != 2:
+            raise ValueError("feat [n, txt_feat_dim] and txt [n, D] need the same row count")
+        _check(load_library().dit_text_features(self._h, _ptr(feat), feat.shape[0], _ptr(txt),
+                                                _stream(stream)))
 
     def forward_cfg(self, lat, txt, txt_uncond, grid, t, guidance, v, ref_lat=None,
                     ref_grid=(0, 0), stream=None):

@@ -45,6 +45,8 @@ class ModelConfig:
     rope_theta: float = 10000.0
     ln_eps: float = 1e-6
     rms_eps: float = 1e-6
+    txt_feat_dim: int = 0        # > 0: text features of this width are projected by txt_in
+    flow_map: bool = False       # timestep-distilled model with a target-time embedding
 
     @property
     def n_blocks(self) -> int:
@@ -152,6 +154,11 @@ def weight_specs(cfg: ModelConfig):
         ("final.mod", (2 * d, d), "linear", (_G_GLOBAL, 3)),
         ("final.out", (c, d), "linear", (_G_GLOBAL, 4)),
     ]
+    if cfg.flow_map:
+        specs.append(("temb_tgt.l1", (d, td), "linear", (_G_GLOBAL, 5)))
+        specs.append(("temb_tgt.l2", (d, d), "linear", (_G_GLOBAL, 6)))
+    if cfg.txt_feat_dim:
+        specs.append(("txt_in", (d, cfg.txt_feat_dim), "linear", (_G_GLOBAL, 7)))
     for kind in (0, 1):
         if (kind == 0 and cfg.n_stream_blocks == 0) or (kind == 1 and cfg.n_shared_blocks == 0):
             continue

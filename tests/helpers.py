@@ -54,6 +54,10 @@ def oracle_model(cfg, w) -> O.Model:
     m.mods = [oracle_mod_sets(cfg, w, 0) if cfg.n_stream_blocks else [],
               oracle_mod_sets(cfg, w, 1) if cfg.n_shared_blocks else []]
     m.blocks = [oracle_sets(cfg, w, b) for b in range(cfg.n_blocks)]
+    if cfg.flow_map:
+        m.temb_tgt_l1, m.temb_tgt_l2 = f64(w["temb_tgt.l1"]), f64(w["temb_tgt.l2"])
+    if cfg.txt_feat_dim:
+        m.txt_in = f64(w["txt_in"])
     return m
 
 
