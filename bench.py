@@ -310,7 +310,12 @@ def main():
     lat = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
     ref_grid = wl.ref_grid or (0, 0)
 
+    feat = (torch.tensor(S.gen_normal((wl.n_txt, cfg.txt_feat_dim), S.SEED_T, (5,)), device="cuda")
+            if cfg.txt_feat_dim else None)
+
     def step(i):
+        if feat is not None:  # the text projection runs once per image, inside the step
+            ctx.text_features(feat, txt)
         if nseq == 2:
             ctx.denoise_cfg(lat, txt, txt_u, wl.grid, wl.steps, wl.guidance, seed=1000 + i,
                             ref_lat=ref, ref_grid=ref_grid)

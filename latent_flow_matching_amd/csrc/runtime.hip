@@ -812,7 +812,8 @@ extern "C" int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, flo
   if (ctx->op == OP_F32) {
     a.g[0] = GemmGroup{feat, ctx->txt_in, n_txt, 0};
     a.out = txt;
-    DIT_CHECK(gemm_simple(a, EPI_STORE_F32, ctx->op, stream), "text projection");
+    DIT_TIMED(P_EMBED, 2.0 * n_txt * (double)K * D, 0.0, gemm_simple(a, EPI_STORE_F32, ctx->op, stream),
+              "text projection");
     return 0;
   }
   // 16-bit operands: features rounded in chunks of rows through the cat workspace
@@ -823,10 +824,12 @@ extern "C" int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, flo
   if (chunk < 1) return fail(DIT_EUNSUPPORTED, "txt_feat_dim %d too wide for the workspace", K);
   for (int r0 = 0; r0 < n_txt; r0 += chunk) {
     const int rows = std::min(chunk, n_txt - r0);
-    DIT_CHECK(to_half(ctx->cat, ctx->op, feat + (size_t)r0 * K, (int64_t)rows * K, stream), "feature cast");
+    DIT_TIMED(P_EMBED, 0.0, 0.0, to_half(ctx->cat, ctx->op, feat + (size_t)r0 * K, (int64_t)rows * K, stream),
+              "feature cast");
     a.g[0] = GemmGroup{ctx->cat, ctx->txt_in, rows, 0};
     a.out = txt + (size_t)r0 * D;
-    DIT_CHECK(gemm_mfma(a, EPI_STORE_F32, ctx->op, stream), "text projection");
+    DIT_TIMED(P_EMBED, 2.0 * rows * (double)K * D, 0.0, gemm_mfma(a, EPI_STORE_F32, ctx->op, stream),
+              "text projection");
   }
   return 0;
 }

@@ -113,6 +113,12 @@ WORKLOADS = {
         "flux3_stack_512txt_4096img_4096ref_1step", FLUX3_KLEIN, 512, (64, 64), (64, 64), 1,
         "stack",
         "5 per-mode + 28 joint blocks, 512 text + 4096 image + 4096 reference tokens, 1 step"),
+    "flux3_distilled_512txt_4096img_16step": Workload(
+        "flux3_distilled_512txt_4096img_16step",
+        replace(FLUX3_KLEIN, flow_map=True, txt_feat_dim=20480), 512, (64, 64), None, 16, "stack",
+        "timestep-distilled FLUX.3 (flow map, the distilled checkpoint's 16 steps, no guidance): "
+        "text-encoder features [512, 20480] projected once per image, then 5 per-mode + 28 joint "
+        "blocks on 512 text + 4096 image tokens per step"),
     "flux3_cfg_512txt_4096img_50step": Workload(
         "flux3_cfg_512txt_4096img_50step", FLUX3_KLEIN, 512, (64, 64), None, 50, "stack",
         "5 per-mode + 28 joint blocks, 512 text + 4096 image tokens, 50 Euler steps with "
