@@ -456,7 +456,9 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
     Sequence = text || image || reference ([MV] Blocks).  Image and reference latents go
     through the same input projection (same VAE and packing, [MV] Tokens); text embeddings
     enter at width D (reading: precomputed embeddings, cf. the C tool's embeddings option,
-    [HK] コマンドラインオプション)."""
+    [HK] コマンドラインオプション).  ref_grid is one (rows, cols) grid, or a list of grids for
+    several reference images whose latents follow one another in ref_lat (up to ten, [WE];
+    each keeps its own size, [MV] Tokens)."""
     dims = model.dims
     n_txt = txt.shape[0]
     n_img = lat.shape[0]
@@ -465,7 +467,8 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
     ref_grids = ()
     if n_ref:
         parts.append(ref_lat @ model.img_in.T)
-        ref_grids = (ref_grid,)
+        ref_grids = tuple(ref_grid) if isinstance(ref_grid, list) else (ref_grid,)
+        assert sum(h * w for h, w in ref_grids) == n_ref
     x = np.concatenate(parts, axis=0)
     pos = positions(n_txt, grid, ref_grids)
     if model.temb_tgt_l1 is not None:
@@ -506,6 +509,44 @@ def denoise(model: Model, noise: np.ndarray, txt: np.ndarray, grid, n_steps: int
     lat = noise.astype(np.float64).copy()
     for i in range(n_steps):
         v = forward(model, lat, txt, grid, ts[i], ref_lat, ref_grid, t_target=ts[i + 1])
+        lat = euler_step(lat, v, ts[i], ts[i + 1])
+    return lat
+
+
+# ----------------------------------------------------------------------------------------
+# Image-to-image.  The C tool transforms an input image with a strength in [0, 1], default
+# 0.75 ([HK] コマンドラインオプション, -t/--strength; CライブラリAPI, strength).  reading: as
+# in rectified-flow image-to-image, the clean latents are moved to the time t_s = strength
+# along the straight path to the noise, x_t = t noise + (1 - t) x, and the Euler loop runs
+# only the last floor(n strength) of its n steps (the schedule is cut, not re-spaced).
+# ----------------------------------------------------------------------------------------
+
+def img2img_first_step(n_steps: int, strength: float) -> int:
+    """Index of the first Euler step that runs: n - floor(n strength)."""
+    return n_steps - int(math.floor(n_steps * strength))
+
+
+def noise_mix(x_clean: np.ndarray, noise: np.ndarray, t: float) -> np.ndarray:
+    """The point at time t on the straight path from the clean latents (t = 0) to the noise
+    (t = 1)."""
+    return t * noise + (1.0 - t) * x_clean
+
+
+def img2img(model: Model, x_clean: np.ndarray, noise: np.ndarray, txt: np.ndarray, grid,
+            n_steps: int, strength: float, ref_lat=None, ref_grid=None, txt_uncond=None,
+            guidance: float = 1.0) -> np.ndarray:
+    """Image-to-image sampling; strength 1 starts from pure noise and is denoise()."""
+    ts = euler_schedule(n_steps)
+    i0 = img2img_first_step(n_steps, strength)
+    if i0 >= n_steps:
+        raise ValueError("strength too small for any step")
+    lat = noise_mix(np.asarray(x_clean, np.float64), np.asarray(noise, np.float64), ts[i0])
+    for i in range(i0, n_steps):
+        if txt_uncond is None:
+            v = forward(model, lat, txt, grid, ts[i], ref_lat, ref_grid, t_target=ts[i + 1])
+        else:
+            v = forward_cfg(model, lat, txt, txt_uncond, grid, ts[i], guidance, ref_lat,
+                            ref_grid, t_target=ts[i + 1])
         lat = euler_step(lat, v, ts[i], ts[i + 1])
     return lat
 

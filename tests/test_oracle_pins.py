@@ -457,6 +457,46 @@ def test_forward_cfg_branches():
                                    O.denoise(m, noise, tc, (2, 2), 2), atol=1e-12)
 
 
+# ------------------------------------------------------------------ image-to-image, several references
+
+def test_img2img_schedule_and_mix():
+    """The straight path from the clean latents (t = 0) to the noise (t = 1); the loop runs
+    the last floor(n s) steps; strength 1 is the plain sampler from the noise."""
+    r = rng(50)
+    x, e = r.normal(size=(5, 4)), r.normal(size=(5, 4))
+    np.testing.assert_array_equal(O.noise_mix(x, e, 0.0), x)
+    np.testing.assert_array_equal(O.noise_mix(x, e, 1.0), e)
+    np.testing.assert_allclose(O.noise_mix(x, e, 0.25), x + 0.25 * (e - x), atol=1e-15)
+    assert [O.img2img_first_step(4, s) for s in (1.0, 0.75, 0.5, 0.25, 0.2)] == [0, 1, 2, 3, 4]
+    assert O.img2img_first_step(50, 0.75) == 13          # 37 of 50 steps
+    m = tiny_model(O.ARCH_FLUX2, r)
+    txt = r.normal(size=(3, TINY.hidden))
+    x = r.normal(size=(4, TINY.in_channels))
+    e = r.normal(size=(4, TINY.in_channels))
+    np.testing.assert_array_equal(O.img2img(m, x, e, txt, (2, 2), 3, 1.0), O.denoise(m, e, txt, (2, 2), 3))
+    with pytest.raises(ValueError):
+        O.img2img(m, x, e, txt, (2, 2), 4, 0.2)
+    # a zero output head: the result is the starting point on the path, t = 3/4
+    mz = tiny_model(O.ARCH_FLUX2, r, zero_out=True)
+    np.testing.assert_array_equal(O.img2img(mz, x, e, txt, (2, 2), 4, 0.75), O.noise_mix(x, e, 0.75))
+
+
+def test_several_references_use_their_own_sequence_axis():
+    """Two references are two images at l = -1 and l = -2: the same latents laid out as one
+    taller reference (all at l = -1) give a different velocity, and a list of one grid is the
+    single-reference call."""
+    r = rng(51)
+    m = tiny_model(O.ARCH_FLUX3, r)
+    lat = r.normal(size=(4, TINY.in_channels))
+    refs = r.normal(size=(8, TINY.in_channels))
+    txt = r.normal(size=(3, TINY.hidden))
+    two = O.forward(m, lat, txt, (2, 2), 0.6, refs, [(2, 2), (2, 2)])
+    tall = O.forward(m, lat, txt, (2, 2), 0.6, refs, (4, 2))
+    assert not np.allclose(two, tall)
+    np.testing.assert_array_equal(O.forward(m, lat, txt, (2, 2), 0.6, refs[:4], [(2, 2)]),
+                                  O.forward(m, lat, txt, (2, 2), 0.6, refs[:4], (2, 2)))
+
+
 # ------------------------------------------------------------------ FLUX.3 conditioning preamble
 
 def test_text_feature_layout_matches_printed_values():
