@@ -199,6 +199,47 @@ int dit_denoise_cfg(dit_ctx *ctx, float *lat, const float *txt, const float *txt
                     int n_txt, int gh, int gw, const float *ref_lat, int rgh, int rgw,
                     int n_steps, float guidance, int64_t seed, void *stream);
 
+/* One generation request for dit_forward_ex / dit_denoise_ex: the inputs besides the
+ * latents, in one place, so that guidance, several reference images and image-to-image
+ * combine freely.  D, C as above. */
+typedef struct {
+  const float *txt;         /* dev fp32 [n_txt, D] text embeddings (conditional branch) */
+  const float *txt_uncond;  /* dev fp32 [n_txt, D] unconditional text, or NULL: no guidance */
+  int n_txt;
+  float guidance;           /* guidance scale g when txt_uncond != NULL (as dit_forward_cfg) */
+  int gh, gw;               /* image token grid (16x16 px per token) */
+  const float *ref_lat;     /* dev fp32 [sum_k rows_k * cols_k, C]: the latents of the reference
+                             * images one after another, or NULL with n_refs = 0 */
+  int n_refs;               /* 0..10 reference images; reference k (from 0) sits at sequence
+                             * coordinate l = -(k+1) on the image's (h, w) grid */
+  const int *ref_grids;     /* host int [n_refs][2]: (rows, cols) of each reference */
+} dit_request;
+/* ("Up to ten reference images": we0.ai "FLUX 3 Image Klein" article, model summary; each
+ * keeps its own size and gets l = -(k+1): "FLUX.3 Image Klein in Diffusers", sections
+ * "Zweistufiger Transformer und Tokenisierung im Detail" and "Modulation pro Token-Typ,
+ * Flow-Map-Destillation und 4D-RoPE".) */
+
+/* One transformer call for a request at time t; t_target is read by flow-map models only
+ * (the step's target time, as dit_forward_flow).  With guidance v = g v_c + (1 - g) v_u.
+ * max_tokens must cover n_txt + gh*gw + all reference tokens, twice with guidance. */
+int dit_forward_ex(dit_ctx *ctx, const dit_request *request, const float *lat, float t,
+                   float t_target, float *v, void *stream);
+
+/* Sampling for a request: n_steps Euler steps on t_i = 1 - i/n_steps, of which the last
+ * floor(n_steps * strength) run.
+ *   strength = 1: text-to-image.  lat is the starting noise: drawn from seed when seed >= 0,
+ *     else copied from noise when noise != NULL, else used as it is.
+ *   0 < strength < 1: image-to-image ("-t, --strength", 0.0-1.0, default 0.75, hakusoku
+ *     FLUX.2-klein-4B article, "コマンドラインオプション"; strength in the C API's generation
+ *     parameters).  lat holds the clean latents of the input image.  They are moved to
+ *     t_s = floor(n_steps * strength) / n_steps on the straight path to the noise:
+ *       lat = t_s * noise + (1 - t_s) * lat,
+ *     with noise from the noise argument (dev fp32 [gh*gw, C]) or, when it is NULL, drawn
+ *     from seed (then seed >= 0 is required).  n_steps * strength >= 1 is required.
+ * lat dev fp32 [gh*gw, C] in/out. */
+int dit_denoise_ex(dit_ctx *ctx, const dit_request *request, float *lat, int n_steps,
+                   float strength, const float *noise, int64_t seed, void *stream);
+
 /* Fill dst (dev fp32, n elements) with the N(0,1) noise dit_denoise draws for seed. */
 int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
 

@@ -77,7 +77,12 @@ hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s);
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s);  // V read from qkv at 2*d_model
 
 // --- norms, RoPE, small ops
-hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, int rgh, int rgw, hipStream_t s);
+// Reference images per call: the model takes up to ten (we0.ai "FLUX 3 Image Klein" article,
+// model summary).
+constexpr int kMaxRefs = 10;
+// pos [n_txt + gh*gw + sum of reference tokens][4]; ref_grids host [n_refs][2] (rows, cols)
+hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, const int *ref_grids,
+                          int n_refs, hipStream_t s);
 hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream_t s);
 // out[r] = LN(x[r]) * (1 + scale_seg) + shift_seg, mod_seg[s] = [shift | scale | ...]
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
@@ -99,6 +104,8 @@ hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hip
 hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,
                          hipStream_t s);
 hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s);
+// x = t * noise + (1 - t) * x  (the straight path from clean latents to noise)
+hipError_t noise_mix(float *x, const float *noise, int64_t n, float t, hipStream_t s);
 // y[r][:] += v for rows r < nrows of d floats
 hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s);
 

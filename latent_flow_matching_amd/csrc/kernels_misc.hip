@@ -9,14 +9,20 @@
 namespace dit {
 
 // ------------------------------------------------------------------------------------------
-// 4D RoPE coordinates: text i -> (0,0,0,i), image (r,c) -> (0,r,c,0), reference (r,c) ->
-// (0,r,c,-1), tokens ordered text | image | reference, row-major inside an image
+// 4D RoPE coordinates: text i -> (0,0,0,i), image (r,c) -> (0,r,c,0), token (r,c) of reference
+// k -> (0,r,c,-(k+1)), tokens ordered text | image | references, row-major inside an image
 // ("FLUX.3 Image Klein in Diffusers", section "Modulation pro Token-Typ, Flow-Map-Destillation
 // und 4D-RoPE").  The page's row/2, col/2 counts VAE-latent cells, two per token side.
 // ------------------------------------------------------------------------------------------
-__global__ void k_positions(float *pos, int n_txt, int gw, int n_img, int rgw, int n_ref) {
+struct RefGrids {
+  int start[kMaxRefs + 1];  // first token of each reference after the image (then the end)
+  int cols[kMaxRefs];
+  int n;
+};
+
+__global__ void k_positions(float *pos, int n_txt, int gw, int n_img, RefGrids rg) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  int n = n_txt + n_img + n_ref;
+  int n = n_txt + n_img + rg.start[rg.n];
   if (i >= n) return;
   float h = 0.f, w = 0.f, l = 0.f;
   if (i < n_txt) {
@@ -27,20 +33,30 @@ __global__ void k_positions(float *pos, int n_txt, int gw, int n_img, int rgw, i
     w = (float)(j % gw);
   } else {
     int j = i - n_txt - n_img;
-    h = (float)(j / rgw);
-    w = (float)(j % rgw);
-    l = -1.f;
+    int k = 0;
+    while (k + 1 < rg.n && j >= rg.start[k + 1]) ++k;
+    j -= rg.start[k];
+    h = (float)(j / rg.cols[k]);
+    w = (float)(j % rg.cols[k]);
+    l = -(float)(k + 1);
   }
   f32x4 v = {0.f, h, w, l};
   *reinterpret_cast<f32x4 *>(pos + 4 * (size_t)i) = v;
 }
 
-hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, int rgh, int rgw,
-                          hipStream_t s) {
-  int n = n_txt + gh * gw + rgh * rgw;
+hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, const int *ref_grids,
+                          int n_refs, hipStream_t s) {
+  if (n_refs < 0 || n_refs > kMaxRefs) return hipErrorInvalidValue;
+  RefGrids rg = {};
+  rg.n = n_refs;
+  for (int k = 0; k < n_refs; ++k) {
+    if (ref_grids[2 * k] < 1 || ref_grids[2 * k + 1] < 1) return hipErrorInvalidValue;
+    rg.start[k + 1] = rg.start[k] + ref_grids[2 * k] * ref_grids[2 * k + 1];
+    rg.cols[k] = ref_grids[2 * k + 1];
+  }
+  int n = n_txt + gh * gw + rg.start[n_refs];
   if (n <= 0) return hipSuccess;
-  k_positions<<<(n + 255) / 256, 256, 0, s>>>(pos, n_txt, gw > 0 ? gw : 1, gh * gw,
-                                               rgw > 0 ? rgw : 1, rgh * rgw);
+  k_positions<<<(n + 255) / 256, 256, 0, s>>>(pos, n_txt, gw > 0 ? gw : 1, gh * gw, rg);
   return hipGetLastError();
 }
 
@@ -572,6 +588,17 @@ __global__ void k_philox_normal(float *dst, int64_t n, uint64_t seed) {
   }
   for (int e = 0; e < 4; ++e)
     if (g * 4 + e < n) dst[g * 4 + e] = (float)out[e];
+}
+
+__global__ void k_noise_mix(float *x, const float *noise, int64_t n, float t) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = t * noise[i] + (1.0f - t) * x[i];
+}
+
+hipError_t noise_mix(float *x, const float *noise, int64_t n, float t, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_noise_mix<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, noise, n, t);
+  return hipGetLastError();
 }
 
 __global__ void k_add_row(float *y, int nrows, int d, const float *v) {

@@ -85,6 +85,7 @@ struct dit_ctx {
   float *temb_e = nullptr;   // [4][time_dim]: the three segment times, then the target time
   float *temb_h = nullptr;   // [4][D]
   float *tgt = nullptr;      // [D] target-time embedding (flow-map models)
+  float *noise = nullptr;    // [max_tokens][C] image-to-image noise drawn from a seed
   float *fmodv = nullptr;    // [3][2D]
   float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
   float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
@@ -437,6 +438,7 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)4 * T * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)4 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->tgt, (size_t)D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->noise, (size_t)c.max_tokens * C * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->act, (size_t)3 * D * 4);
   if (ctx->op != OP_F32 && ctx->lean_grid > 0) {
@@ -648,16 +650,34 @@ struct HeadStore {
   float alpha;
 };
 
+// What one transformer call sees besides the latents: text (one sequence, or the two
+// branches of guidance), the image grid and the reference images.
+struct Req {
+  const float *txt[2] = {nullptr, nullptr};
+  int nseq = 1, n_txt = 0, gh = 0, gw = 0;
+  float guidance = 1.f;
+  const float *ref_lat = nullptr;
+  int n_refs = 0;
+  int grids[2 * kMaxRefs] = {0};
+  int n_ref() const {
+    int n = 0;
+    for (int k = 0; k < n_refs; ++k) n += grids[2 * k] * grids[2 * k + 1];
+    return n;
+  }
+};
+
 // Embed, run every block, output head.  nseq = 1: the sequence of txt[0]; nseq = 2: the
 // conditional (txt[0]) and unconditional (txt[1]) branches of guidance stacked as two
 // sequences that share latents, references and time.  The head stores sequence 0 first,
 // then sequence 1, each with its own HeadStore.
-int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *const txt[2],
-                int nseq, int n_txt, int gh, int gw, int rgh, int rgw, double t, double t_target,
+int run_forward(dit_ctx *ctx, const float *lat, const Req &rq, double t, double t_target,
                 float *out, const HeadStore hs[2], hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = c.hidden, C = c.in_channels;
-  const int n_img = gh * gw, n_ref = rgh * rgw;
+  const int nseq = rq.nseq, n_txt = rq.n_txt, gh = rq.gh, gw = rq.gw;
+  const float *const *txt = rq.txt;
+  const float *ref_lat = rq.ref_lat;
+  const int n_img = gh * gw, n_ref = rq.n_ref();
   const Segs sg = make_segs(n_txt, n_img, n_ref, nseq);
   const int per = sg.per;
   {
@@ -666,7 +686,8 @@ int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
     prof_end(ctx, pe, P_COND, 0.0, 0.0, stream);
   }
   for (int qs = 0; qs < nseq; ++qs)
-    DIT_CHECK(fill_positions(ctx->pos + (size_t)qs * per * 4, n_txt, gh, gw, rgh, rgw, stream),
+    DIT_CHECK(fill_positions(ctx->pos + (size_t)qs * per * 4, n_txt, gh, gw, rq.grids, rq.n_refs,
+                             stream),
               "positions");
   DIT_CHECK(rope_table(ctx->cs, ctx->pos, sg.n, c.rope_theta, stream), "rope_table");
   // sequence: text embeddings as they are, latents through the input projection
@@ -736,14 +757,77 @@ int run_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const floa
   return 0;
 }
 
-int check_grid(dit_ctx *ctx, const float *lat, const float *txt, int n_txt, int gh, int gw,
-               const float *ref_lat, int rgh, int rgw, int nseq = 1) {
-  if (gh < 1 || gw < 1) return fail(DIT_EINVAL, "image grid must be at least 1x1");
-  if (rgh < 0 || rgw < 0 || (rgh == 0) != (rgw == 0)) return fail(DIT_EINVAL, "bad reference grid");
+int check_request(dit_ctx *ctx, const float *lat, const Req &rq) {
+  if (rq.gh < 1 || rq.gw < 1) return fail(DIT_EINVAL, "image grid must be at least 1x1");
   if (!lat) return fail(DIT_EINVAL, "lat is NULL");
-  if (n_txt > 0 && !txt) return fail(DIT_EINVAL, "txt is NULL");
-  if (rgh > 0 && !ref_lat) return fail(DIT_EINVAL, "ref_lat is NULL");
-  return check_tokens(ctx, n_txt, gh * gw, rgh * rgw, nseq);
+  if (rq.n_txt > 0 && !rq.txt[0]) return fail(DIT_EINVAL, "txt is NULL");
+  if (rq.nseq == 2 && rq.n_txt > 0 && !rq.txt[1]) return fail(DIT_EINVAL, "txt_uncond is NULL");
+  if (rq.nseq == 2 && !isfinite(rq.guidance)) return fail(DIT_EINVAL, "guidance must be finite");
+  if (rq.n_refs < 0 || rq.n_refs > kMaxRefs)
+    return fail(DIT_EINVAL, "n_refs %d out of range [0, %d]", rq.n_refs, kMaxRefs);
+  for (int k = 0; k < rq.n_refs; ++k)
+    if (rq.grids[2 * k] < 1 || rq.grids[2 * k + 1] < 1)
+      return fail(DIT_EINVAL, "reference %d grid must be at least 1x1", k);
+  if (rq.n_refs > 0 && !rq.ref_lat) return fail(DIT_EINVAL, "ref_lat is NULL");
+  return check_tokens(ctx, rq.n_txt, rq.gh * rq.gw, rq.n_ref(), rq.nseq);
+}
+
+// The request of the single-reference entry points (rgh = rgw = 0: no reference).
+int legacy_req(Req *rq, const float *txt, const float *txt_uncond, int nseq, int n_txt, int gh,
+               int gw, const float *ref_lat, int rgh, int rgw, float guidance) {
+  if (rgh < 0 || rgw < 0 || (rgh == 0) != (rgw == 0)) return fail(DIT_EINVAL, "bad reference grid");
+  rq->txt[0] = txt;
+  rq->txt[1] = txt_uncond;
+  rq->nseq = nseq;
+  rq->n_txt = n_txt;
+  rq->gh = gh;
+  rq->gw = gw;
+  rq->guidance = guidance;
+  rq->ref_lat = ref_lat;
+  rq->n_refs = rgh > 0 ? 1 : 0;
+  rq->grids[0] = rgh;
+  rq->grids[1] = rgw;
+  return 0;
+}
+
+// The request of dit_forward_ex / dit_denoise_ex.
+int public_req(Req *rq, const dit_request *r) {
+  if (!r) return fail(DIT_EINVAL, "request is NULL");
+  if (r->n_refs < 0 || r->n_refs > kMaxRefs)
+    return fail(DIT_EINVAL, "n_refs %d out of range [0, %d]", r->n_refs, kMaxRefs);
+  if (r->n_refs > 0 && !r->ref_grids) return fail(DIT_EINVAL, "ref_grids is NULL");
+  rq->txt[0] = r->txt;
+  rq->txt[1] = r->txt_uncond;
+  rq->nseq = r->txt_uncond ? 2 : 1;
+  rq->n_txt = r->n_txt;
+  rq->gh = r->gh;
+  rq->gw = r->gw;
+  rq->guidance = r->txt_uncond ? r->guidance : 1.f;
+  rq->ref_lat = r->ref_lat;
+  rq->n_refs = r->n_refs;
+  for (int k = 0; k < 2 * r->n_refs; ++k) rq->grids[k] = r->ref_grids[k];
+  return 0;
+}
+
+// Store modes of the output head for one call: plain velocity, or the guided combination.
+void head_stores(const Req &rq, HeadStore hs[2]) {
+  if (rq.nseq == 2) {  // v = g v_c + (1 - g) v_u  (= v_u + g (v_c - v_u))
+    hs[0] = HeadStore{2, rq.guidance};
+    hs[1] = HeadStore{1, 1.0f - rq.guidance};
+  } else {
+    hs[0] = HeadStore{0, 0.f};
+    hs[1] = HeadStore{0, 0.f};
+  }
+}
+
+int forward_call(dit_ctx *ctx, const float *lat, const Req &rq, double t, double t_target,
+                 float *v, hipStream_t stream) {
+  if (int rc = check_request(ctx, lat, rq)) return rc;
+  if (!v) return fail(DIT_EINVAL, "v is NULL");
+  if (!isfinite(t) || !isfinite(t_target)) return fail(DIT_EINVAL, "t and t_target must be finite");
+  HeadStore hs[2];
+  head_stores(rq, hs);
+  return run_forward(ctx, lat, rq, t, t_target, v, hs, stream);
 }
 
 }  // namespace
@@ -769,13 +853,10 @@ extern "C" int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat,
                            int n_txt, int gh, int gw, int rgh, int rgw, float t, float *v, void *stream) {
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
-  if (!v) return fail(DIT_EINVAL, "v is NULL");
   if (ctx->cfg.flow_map) return fail(DIT_EINVAL, "flow-map model: call dit_forward_flow with the target time");
-  const float *txts[2] = {txt, nullptr};
-  const HeadStore hs[2] = {{0, 0.f}, {0, 0.f}};
-  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t, (double)t, v,
-                     hs, (hipStream_t)stream);
+  Req rq;
+  if (int rc = legacy_req(&rq, txt, nullptr, 1, n_txt, gh, gw, ref_lat, rgh, rgw, 1.f)) return rc;
+  return forward_call(ctx, lat, rq, t, t, v, (hipStream_t)stream);
 }
 
 extern "C" int dit_forward_flow(dit_ctx *ctx, const float *lat, const float *ref_lat,
@@ -784,13 +865,9 @@ extern "C" int dit_forward_flow(dit_ctx *ctx, const float *lat, const float *ref
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
   if (!ctx->cfg.flow_map) return fail(DIT_EINVAL, "dit_forward_flow needs a flow-map model (flow_map = 1)");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
-  if (!v) return fail(DIT_EINVAL, "v is NULL");
-  if (!isfinite(t) || !isfinite(t_target)) return fail(DIT_EINVAL, "t and t_target must be finite");
-  const float *txts[2] = {txt, nullptr};
-  const HeadStore hs[2] = {{0, 0.f}, {0, 0.f}};
-  return run_forward(ctx, lat, ref_lat, txts, 1, n_txt, gh, gw, rgh, rgw, (double)t,
-                     (double)t_target, v, hs, (hipStream_t)stream);
+  Req rq;
+  if (int rc = legacy_req(&rq, txt, nullptr, 1, n_txt, gh, gw, ref_lat, rgh, rgw, 1.f)) return rc;
+  return forward_call(ctx, lat, rq, t, t_target, v, (hipStream_t)stream);
 }
 
 extern "C" int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, float *txt,
@@ -839,43 +916,67 @@ extern "C" int dit_forward_cfg(dit_ctx *ctx, const float *lat, const float *ref_
                                int rgh, int rgw, float t, float guidance, float *v, void *stream) {
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw, 2)) return rc;
-  if (n_txt > 0 && !txt_uncond) return fail(DIT_EINVAL, "txt_uncond is NULL");
-  if (!v) return fail(DIT_EINVAL, "v is NULL");
-  if (!isfinite(guidance)) return fail(DIT_EINVAL, "guidance must be finite");
   if (ctx->cfg.flow_map)
-    return fail(DIT_EINVAL, "flow-map model: dit_forward_cfg takes no target time; use dit_denoise_cfg");
-  // v = g v_c + (1 - g) v_u  (= v_u + g (v_c - v_u))
-  const float *txts[2] = {txt, txt_uncond};
-  const HeadStore hs[2] = {{2, guidance}, {1, 1.0f - guidance}};
-  return run_forward(ctx, lat, ref_lat, txts, 2, n_txt, gh, gw, rgh, rgw, (double)t, (double)t, v,
-                     hs, (hipStream_t)stream);
+    return fail(DIT_EINVAL, "flow-map model: dit_forward_cfg takes no target time; use dit_forward_ex");
+  Req rq;
+  if (int rc = legacy_req(&rq, txt, txt_uncond, 2, n_txt, gh, gw, ref_lat, rgh, rgw, guidance)) return rc;
+  return forward_call(ctx, lat, rq, t, t, v, (hipStream_t)stream);
+}
+
+extern "C" int dit_forward_ex(dit_ctx *ctx, const dit_request *request, const float *lat,
+                              float t, float t_target, float *v, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  Req rq;
+  if (int rc = public_req(&rq, request)) return rc;
+  // only flow-map models read the target time
+  return forward_call(ctx, lat, rq, t, ctx->cfg.flow_map ? t_target : t, v, (hipStream_t)stream);
 }
 
 namespace {
 
-int denoise(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond, int nseq,
-            float guidance, int n_txt, int gh, int gw, const float *ref_lat, int rgh, int rgw,
-            int n_steps, int64_t seed, hipStream_t stream) {
+// The sampling loop.  strength 1: lat is the starting noise (drawn from seed when seed >= 0,
+// copied from noise when given, else used as it is).  strength < 1 (image-to-image): lat holds
+// clean latents; they are moved to t = floor(n s) / n on the straight path to the noise
+// (noise, or drawn from seed) and the last floor(n s) Euler steps run.
+int denoise(dit_ctx *ctx, const Req &rq, float *lat, int n_steps, float strength,
+            const float *noise, int64_t seed, hipStream_t stream) {
+  if (int rc = check_request(ctx, lat, rq)) return rc;
   if (n_steps < 1) return fail(DIT_EINVAL, "n_steps must be >= 1, got %d", n_steps);
-  if (seed >= 0)
-    DIT_CHECK(philox_normal(lat, (int64_t)gh * gw * ctx->cfg.in_channels, (uint64_t)seed, stream), "noise");
-  const float *txts[2] = {txt, txt_uncond};
-  for (int i = 0; i < n_steps; ++i) {
+  if (!(strength > 0.f && strength <= 1.f)) return fail(DIT_EINVAL, "strength must be in (0, 1], got %g", strength);
+  const int steps_run = (int)floor((double)n_steps * strength);
+  if (steps_run < 1)
+    return fail(DIT_EINVAL, "strength %g runs no step of %d (needs n_steps * strength >= 1)", strength, n_steps);
+  const int i0 = n_steps - steps_run;
+  const int64_t nl = (int64_t)rq.gh * rq.gw * ctx->cfg.in_channels;
+  if (i0 == 0) {
+    if (noise) {
+      DIT_CHECK(hipMemcpyAsync(lat, noise, (size_t)nl * 4, hipMemcpyDeviceToDevice, stream), "noise copy");
+    } else if (seed >= 0) {
+      DIT_CHECK(philox_normal(lat, nl, (uint64_t)seed, stream), "noise");
+    }
+  } else {
+    const float *eps = noise;
+    if (!eps) {
+      if (seed < 0) return fail(DIT_EINVAL, "image-to-image needs noise or a seed >= 0");
+      DIT_CHECK(philox_normal(ctx->noise, nl, (uint64_t)seed, stream), "noise");
+      eps = ctx->noise;
+    }
+    DIT_CHECK(noise_mix(lat, eps, nl, (float)(1.0 - (double)i0 / n_steps), stream), "noise mix");
+  }
+  for (int i = i0; i < n_steps; ++i) {
     const double t_cur = 1.0 - (double)i / n_steps;
     const double t_next = 1.0 - (double)(i + 1) / n_steps;
     const float dt = (float)(t_cur - t_next);
     // Euler: lat += (t_i - t_{i+1}) * v, fused into the output projection's epilogue; with
     // guidance v = g v_c + (1 - g) v_u, added branch by branch
     HeadStore hs[2] = {{1, dt}, {1, 0.f}};
-    if (nseq == 2) {
-      hs[0].alpha = dt * guidance;
-      hs[1].alpha = dt * (1.0f - guidance);
+    if (rq.nseq == 2) {
+      hs[0].alpha = dt * rq.guidance;
+      hs[1].alpha = dt * (1.0f - rq.guidance);
     }
     // flow-map models also see the time the step jumps to
-    if (int rc = run_forward(ctx, lat, ref_lat, txts, nseq, n_txt, gh, gw, rgh, rgw, t_cur, t_next,
-                             lat, hs, stream))
-      return rc;
+    if (int rc = run_forward(ctx, lat, rq, t_cur, t_next, lat, hs, stream)) return rc;
   }
   return 0;
 }
@@ -886,9 +987,9 @@ extern "C" int dit_denoise(dit_ctx *ctx, float *lat, const float *txt, int n_txt
                            const float *ref_lat, int rgh, int rgw, int n_steps, int64_t seed, void *stream) {
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw)) return rc;
-  return denoise(ctx, lat, txt, nullptr, 1, 1.0f, n_txt, gh, gw, ref_lat, rgh, rgw, n_steps, seed,
-                 (hipStream_t)stream);
+  Req rq;
+  if (int rc = legacy_req(&rq, txt, nullptr, 1, n_txt, gh, gw, ref_lat, rgh, rgw, 1.f)) return rc;
+  return denoise(ctx, rq, lat, n_steps, 1.f, nullptr, seed, (hipStream_t)stream);
 }
 
 extern "C" int dit_denoise_cfg(dit_ctx *ctx, float *lat, const float *txt, const float *txt_uncond,
@@ -896,11 +997,18 @@ extern "C" int dit_denoise_cfg(dit_ctx *ctx, float *lat, const float *txt, const
                                int n_steps, float guidance, int64_t seed, void *stream) {
   g_err.clear();
   if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
-  if (int rc = check_grid(ctx, lat, txt, n_txt, gh, gw, ref_lat, rgh, rgw, 2)) return rc;
-  if (n_txt > 0 && !txt_uncond) return fail(DIT_EINVAL, "txt_uncond is NULL");
-  if (!isfinite(guidance)) return fail(DIT_EINVAL, "guidance must be finite");
-  return denoise(ctx, lat, txt, txt_uncond, 2, guidance, n_txt, gh, gw, ref_lat, rgh, rgw, n_steps,
-                 seed, (hipStream_t)stream);
+  Req rq;
+  if (int rc = legacy_req(&rq, txt, txt_uncond, 2, n_txt, gh, gw, ref_lat, rgh, rgw, guidance)) return rc;
+  return denoise(ctx, rq, lat, n_steps, 1.f, nullptr, seed, (hipStream_t)stream);
+}
+
+extern "C" int dit_denoise_ex(dit_ctx *ctx, const dit_request *request, float *lat, int n_steps,
+                              float strength, const float *noise, int64_t seed, void *stream) {
+  g_err.clear();
+  if (!ctx) return fail(DIT_EINVAL, "ctx is NULL");
+  Req rq;
+  if (int rc = public_req(&rq, request)) return rc;
+  return denoise(ctx, rq, lat, n_steps, strength, noise, seed, (hipStream_t)stream);
 }
 
 extern "C" int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream) {

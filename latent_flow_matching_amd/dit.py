@@ -36,6 +36,13 @@ class DitTensor(ctypes.Structure):
                 ("dtype", ctypes.c_int)]
 
 
+class DitRequest(ctypes.Structure):
+    _fields_ = [("txt", ctypes.c_void_p), ("txt_uncond", ctypes.c_void_p), ("n_txt", ctypes.c_int),
+                ("guidance", ctypes.c_float), ("gh", ctypes.c_int), ("gw", ctypes.c_int),
+                ("ref_lat", ctypes.c_void_p), ("n_refs", ctypes.c_int),
+                ("ref_grids", ctypes.POINTER(ctypes.c_int))]
+
+
 class DitError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"dit error {code}: {msg}")
@@ -67,6 +74,10 @@ def load_library(path: str = None):
     lib.dit_forward.argtypes = [P, P, P, P, I, I, I, I, I, F, P, P]
     lib.dit_denoise.restype = I
     lib.dit_denoise.argtypes = [P, P, P, I, I, I, P, I, I, I, I64, P]
+    lib.dit_forward_ex.restype = I
+    lib.dit_forward_ex.argtypes = [P, ctypes.POINTER(DitRequest), P, F, F, P, P]
+    lib.dit_denoise_ex.restype = I
+    lib.dit_denoise_ex.argtypes = [P, ctypes.POINTER(DitRequest), P, I, F, P, I64, P]
     lib.dit_forward_flow.restype = I
     lib.dit_forward_flow.argtypes = [P, P, P, P, I, I, I, I, I, F, F, P, P]
     lib.dit_text_features.restype = I
@@ -194,6 +205,40 @@ class DiT:
         _check(load_library().dit_denoise(self._h, _ptr(lat), _ptr(txt), txt.shape[0], grid[0],
                                           grid[1], _ptr(ref_lat), ref_grid[0], ref_grid[1],
                                           n_steps, seed, _stream(stream)))
+
+    @staticmethod
+    def _request(txt, grid, txt_uncond, guidance, ref_lat, ref_grids):
+        for a, w in ((txt, "txt"), (txt_uncond, "txt_uncond"), (ref_lat, "ref_lat")):
+            _need(a, "float32", w)
+        if txt_uncond is not None and tuple(txt_uncond.shape) != tuple(txt.shape):
+            raise ValueError("txt and txt_uncond must have the same shape")
+        grids = [int(v) for g in ref_grids for v in g]
+        arr = (ctypes.c_int * max(1, len(grids)))(*grids)
+        req = DitRequest(txt.data_ptr() if txt.numel() else None,
+                         None if txt_uncond is None else (txt_uncond.data_ptr() or None),
+                         txt.shape[0], float(guidance), grid[0], grid[1],
+                         None if ref_lat is None else ref_lat.data_ptr(), len(ref_grids), arr)
+        return req, arr
+
+    def forward_ex(self, lat, txt, grid, t, v, t_target=None, txt_uncond=None, guidance=1.0,
+                   ref_lat=None, ref_grids=(), stream=None):
+        """One call for a request: optional guidance (txt_uncond), any number of reference
+        images (ref_lat = their latents one after another, ref_grids = [(rows, cols), ...])."""
+        _need(lat, "float32", "lat")
+        _need(v, "float32", "v")
+        req, keep = self._request(txt, grid, txt_uncond, guidance, ref_lat, ref_grids)
+        _check(load_library().dit_forward_ex(self._h, ctypes.byref(req), _ptr(lat), float(t),
+                                             float(t if t_target is None else t_target), _ptr(v),
+                                             _stream(stream)))
+
+    def denoise_ex(self, lat, txt, grid, n_steps, strength=1.0, noise=None, seed=-1,
+                   txt_uncond=None, guidance=1.0, ref_lat=None, ref_grids=(), stream=None):
+        """Sampling for a request; strength < 1 is image-to-image from the clean latents in lat."""
+        _need(lat, "float32", "lat")
+        _need(noise, "float32", "noise")
+        req, keep = self._request(txt, grid, txt_uncond, guidance, ref_lat, ref_grids)
+        _check(load_library().dit_denoise_ex(self._h, ctypes.byref(req), _ptr(lat), n_steps,
+                                             float(strength), _ptr(noise), seed, _stream(stream)))
 
     def forward_flow(self, lat, txt, grid, t, t_target, v, ref_lat=None, ref_grid=(0, 0),
                      stream=None):

@@ -213,6 +213,98 @@ def test_denoise_tiny(cfg):
     assert err <= BF16_TOL
 
 
+# ----------------------------------------------------------------- several references, image-to-image
+
+REF_GRIDS = [(6, 5), (4, 7), (3, 3)]
+
+
+@pytest.mark.parametrize("cfg", [TINY3, C16[1], F32[1], TINY2],
+                         ids=["flux3_f16", "flux3_bf16", "flux3_f32", "flux2_f16"])
+def test_forward_several_references_matches_oracle(cfg):
+    """Three reference images of different sizes at l = -1, -2, -3 (FLUX.3 per-mode blocks keep
+    them in the reference stream; FLUX.2 double blocks give them the image weights)."""
+    ctx, w = context(cfg, 600)
+    grid = (9, 7)
+    n_ref = sum(h * w_ for h, w_ in REF_GRIDS)
+    lat = S.gen_latents(63, cfg.in_channels)
+    ref = S.gen_latents(n_ref, cfg.in_channels, key=(1,))
+    txt = S.gen_text(50, cfg.hidden)
+    v = torch.empty((63, cfg.in_channels), device="cuda")
+    ctx.forward_ex(dev(lat), dev(txt), grid, 0.75, v, ref_lat=dev(ref), ref_grids=REF_GRIDS)
+    torch.cuda.synchronize()
+    want = O.forward(oracle_model(cfg, w), f64(lat), f64(txt), grid, float(np.float32(0.75)),
+                     f64(ref), list(REF_GRIDS))
+    err = rel_err(v.cpu().numpy(), want)
+    print(f"several references err {err:.3e}")
+    assert err <= tol(cfg, full_width=False)
+
+
+@pytest.mark.parametrize("seeded", [True, False], ids=["seeded_noise", "given_noise"])
+def test_img2img_matches_oracle(seeded):
+    """Image-to-image at strength 0.6 of 5 steps: the clean latents moved to t = 3/5 on the
+    path to the noise, then the last 3 Euler steps."""
+    cfg = TINY2
+    ctx, w = context(cfg, 600)
+    grid, n_steps, strength, seed = (8, 6), 5, 0.6, 77
+    x = S.gen_latents(48, cfg.in_channels, key=(6,))
+    txt = S.gen_text(20, cfg.hidden)
+    eps = O.noise(48 * cfg.in_channels, seed).reshape(48, cfg.in_channels)
+    lat = dev(x)
+    if seeded:
+        ctx.denoise_ex(lat, dev(txt), grid, n_steps, strength=strength, seed=seed)
+    else:
+        ctx.denoise_ex(lat, dev(txt), grid, n_steps, strength=strength, noise=dev(eps))
+    torch.cuda.synchronize()
+    m = oracle_model(cfg, w)
+    want = O.img2img(m, f64(x), eps, f64(txt), grid, n_steps, strength)
+    start = O.noise_mix(f64(x), eps, 1.0 - O.img2img_first_step(n_steps, strength) / n_steps)
+    err = rel_err(lat.cpu().numpy() - start, want - start)
+    print(f"img2img update err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_request_with_guidance_references_and_img2img():
+    """Everything at once on FLUX.3: guidance 2.5, two references, strength 0.75 of 4 steps."""
+    cfg = TINY3
+    ctx, w = context(cfg, 600)
+    grid, grids = (8, 6), [(4, 4), (3, 5)]
+    x = S.gen_latents(48, cfg.in_channels, key=(6,))
+    ref = S.gen_latents(31, cfg.in_channels, key=(1,))
+    txt = S.gen_text(20, cfg.hidden)
+    txt_u = S.gen_text(20, cfg.hidden, seed=S.SEED_T + 7)
+    eps = O.noise(48 * cfg.in_channels, 5).reshape(48, cfg.in_channels)
+    lat = dev(x)
+    ctx.denoise_ex(lat, dev(txt), grid, 4, strength=0.75, noise=dev(eps), txt_uncond=dev(txt_u),
+                   guidance=2.5, ref_lat=dev(ref), ref_grids=grids)
+    torch.cuda.synchronize()
+    want = O.img2img(oracle_model(cfg, w), f64(x), eps, f64(txt), grid, 4, 0.75, f64(ref), grids,
+                     txt_uncond=f64(txt_u), guidance=2.5)
+    start = O.noise_mix(f64(x), eps, 0.75)
+    err = rel_err(lat.cpu().numpy() - start, want - start)
+    print(f"guided img2img with two references err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_request_checks():
+    from latent_flow_matching_amd import dit
+    cfg = TINY3
+    ctx, _ = context(cfg, 600)
+    lat = torch.zeros((4, cfg.in_channels), device="cuda")
+    txt = torch.zeros((3, cfg.hidden), device="cuda")
+    v = torch.empty_like(lat)
+    refs = torch.zeros((11, cfg.in_channels), device="cuda")
+    with pytest.raises(dit.DitError, match="n_refs"):
+        ctx.forward_ex(lat, txt, (2, 2), 0.5, v, ref_lat=refs, ref_grids=[(1, 1)] * 11)
+    with pytest.raises(dit.DitError, match="grid"):
+        ctx.forward_ex(lat, txt, (2, 2), 0.5, v, ref_lat=refs, ref_grids=[(0, 3)])
+    with pytest.raises(dit.DitError, match="strength"):
+        ctx.denoise_ex(lat, txt, (2, 2), 4, strength=0.0, seed=1)
+    with pytest.raises(dit.DitError, match="runs no step"):
+        ctx.denoise_ex(lat, txt, (2, 2), 4, strength=0.2, seed=1)
+    with pytest.raises(dit.DitError, match="noise or a seed"):
+        ctx.denoise_ex(lat, txt, (2, 2), 4, strength=0.5)
+
+
 # ----------------------------------------------------------------- FLUX.3 conditioning preamble
 
 TINY3_FM = replace(TINY3, flow_map=True, txt_feat_dim=20480)
