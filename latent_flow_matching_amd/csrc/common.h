@@ -39,18 +39,25 @@ template <typename T> __device__ __forceinline__ T from_f32_inrange(float f) {
   return static_cast<T>(f);
 }
 
-// MFMA operand traits: 16-bit operand type -> 8-element vector and the 32x32x16 MFMA.
+// MFMA operand traits: 16-bit operand type -> 8-element vector, the 32x32x16 and the 16x16x32
+// MFMAs.
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {
   typedef bf16x8 v8;
   static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 template <> struct Mfma<f16> {
   typedef f16x8 v8;
   static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 

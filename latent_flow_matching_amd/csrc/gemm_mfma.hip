@@ -3,13 +3,15 @@
 //
 //   out[token][n] = sum_k X[token][k] * W[n][k]       (X = activations, W = [N, K] weights)
 //
-// Both operands are K-contiguous, which is the per-lane layout of v_mfma_f32_32x32x16_{bf16,f16}
-// (lane l holds 8 consecutive k of row l%32, k-half l/32).  The weight tile is the MFMA A
+// Both operands are K-contiguous, which is the per-lane layout of v_mfma_f32_16x16x32_{bf16,f16}
+// (lane l holds 8 consecutive k of row l%16, k-quarter l/16).  The weight tile is the MFMA A
 // operand and the token tile the B operand, so each lane's accumulator holds one token and
 // four consecutive output features: stores are 8-byte (bf16) or 16-byte (fp32) vectors.
+// The 16x16x32 form moves a quarter of the accumulator registers per flop of the 32x32x16
+// one; under the chip's power limit it holds a clock about 15% higher on the same work.
 //
-// Workgroup tile 256 features x 256 tokens, 4 waves (2 x 2) each owning 128 x 128 (16
-// accumulators of 32x32 in AGPRs, one wave per SIMD).  k advances in tiles of 64 through two
+// Workgroup tile 256 features x 256 tokens, 4 waves (2 x 2) each owning 128 x 128 (64
+// accumulators of 16x16 in AGPRs, one wave per SIMD).  k advances in tiles of 64 through two
 // LDS stages (128 KB) with one barrier per k-tile; global loads are staged through registers
 // one k-tile ahead.  LDS rows are 128 B (64 values) with the 16-byte chunk index XOR-swizzled
 // by ((row >> 1) & 7): gfx950's LDS serves 256 B (64 banks) per cycle, i.e. two consecutive
@@ -43,19 +45,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // byte offset inside 
 
 constexpr int kGroupN = 4;  // feature tiles per ordering group (4 x 8 tiles per XCD round)
 
-// Epilogue: lane owns token (lane & 31) and features
-// 8 g + 4 (lane >> 5) + {0..3} of every 32x32 sub-tile.
+// Epilogue: lane owns token (lane & 15) and features 4 (lane >> 4) + {0..3} of every 16x16
+// sub-tile.
 template <typename T, int BM, int WN, int WM, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp, int n0, int m0,
                                          int wn, int wm, int lane,
-                                         f32x16 (&acc)[BN / WN / 32][BM / WM / 32]) {
+                                         f32x4 (&acc)[BN / WN / 16][BM / WM / 16]) {
   constexpr int WTN = BN / WN, WTM = BM / WM;
-  constexpr int FS = WTN / 32, TS = WTM / 32;
-  const int r32 = lane & 31, hk = lane >> 5;
-  const int fbase = n0 + wn * WTN + 4 * hk;
+  constexpr int FS = WTN / 16, TS = WTM / 16;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int fbase = n0 + wn * WTN + 4 * q4;
 #pragma unroll
   for (int j = 0; j < TS; ++j) {
-    const int m = m0 + wm * WTM + j * 32 + r32;  // row inside the group
+    const int m = m0 + wm * WTM + j * 16 + r16;  // row inside the group
     if (m >= grp.rows) continue;
     const int tok = grp.out_row0 + m;
     if constexpr (EPI == EPI_RESID) {
@@ -63,52 +65,45 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
       const float *gate = a.gate[seg];
       float *xr = a.x + (size_t)tok * a.ldres;
 #pragma unroll
-      for (int i = 0; i < FS; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = fbase + i * 32 + 8 * g;
-          f32x4 gv = *reinterpret_cast<const f32x4 *>(gate + n);
-          f32x4 xv = *reinterpret_cast<const f32x4 *>(xr + n);
-          xv.x += gv.x * acc[i][j][4 * g + 0];
-          xv.y += gv.y * acc[i][j][4 * g + 1];
-          xv.z += gv.z * acc[i][j][4 * g + 2];
-          xv.w += gv.w * acc[i][j][4 * g + 3];
-          *reinterpret_cast<f32x4 *>(xr + n) = xv;
-        }
+      for (int i = 0; i < FS; ++i) {
+        const int n = fbase + i * 16;
+        f32x4 gv = *reinterpret_cast<const f32x4 *>(gate + n);
+        f32x4 xv = *reinterpret_cast<const f32x4 *>(xr + n);
+        xv.x += gv.x * acc[i][j][0];
+        xv.y += gv.y * acc[i][j][1];
+        xv.z += gv.z * acc[i][j][2];
+        xv.w += gv.w * acc[i][j][3];
+        *reinterpret_cast<f32x4 *>(xr + n) = xv;
+      }
     } else if constexpr (EPI == EPI_QKV_SWIGLU) {
       if (n0 < a.split) {
         T *qr = reinterpret_cast<T *>(a.qkv) + (size_t)tok * a.ldq;
 #pragma unroll
         for (int i = 0; i < FS; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4(qr + fbase + i * 32 + 8 * g, acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          store4(qr + fbase + i * 16, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       } else {
-        // sub-tiles (2p, 2p+1) = gate / up rows of SwiGLU features [32c, 32c + 32)
+        // rows of a 64-row chunk: gate of SwiGLU features [32c, 32c + 32), then their up rows;
+        // sub-tiles 4p + h (gate) and 4p + 2 + h (up) hold features 32p + 16h + [0, 16)
         T *cr = reinterpret_cast<T *>(a.cat) + (size_t)tok * a.ldc + a.cat_off;
         const int jb = (n0 - a.split + wn * WTN) / 2;  // first SwiGLU feature of the wave
 #pragma unroll
-        for (int p = 0; p < FS / 2; ++p)
+        for (int p = 0; p < FS / 4; ++p)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
+          for (int h = 0; h < 2; ++h) {
             float o[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              o[r] = silu(acc[2 * p][j][4 * g + r]) * acc[2 * p + 1][j][4 * g + r];
-            store4(cr + jb + p * 32 + 8 * g + 4 * hk, o[0], o[1], o[2], o[3]);
+              o[r] = silu(acc[4 * p + h][j][r]) * acc[4 * p + 2 + h][j][r];
+            store4(cr + jb + p * 32 + h * 16 + 4 * q4, o[0], o[1], o[2], o[3]);
           }
       }
     } else {
       float *orow = a.out + (size_t)tok * a.ldo;
 #pragma unroll
-      for (int i = 0; i < FS; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = fbase + i * 32 + 8 * g;
+      for (int i = 0; i < FS; ++i) {
+          const int n = fbase + i * 16;
           if (a.n_store > 0 && n >= a.n_store) continue;
-          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                     acc[i][j][4 * g + 3]};
+          f32x4 v = acc[i][j];
           if (a.accumulate == 1) {
             f32x4 o = *reinterpret_cast<const f32x4 *>(orow + n);
             v = o + a.alpha * v;
@@ -149,9 +144,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
                                                   int total_tiles) {
   constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
   constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
-  constexpr int FS = WTN / 32, TS = WTM / 32;  // 4 x 4
+  constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 sub-tiles of 16 x 16
   constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 16-byte loads per thread
-  constexpr int KS = BK / 16;                  // 4 k-steps per k-tile
+  constexpr int KS = BK / 32;                  // 2 k-steps of 32 per k-tile
   constexpr int STAGE = (BN + BM) * BK * 2;    // 64 KB
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   typedef typename Mfma<T>::v8 V8;
@@ -218,47 +213,47 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
     for (int i = 0; i < LB; ++i)
       *reinterpret_cast<u32x4 *>(Bs + swz(lrow + i * (NT / 8), lchunk)) = rb[i];
   };
-  const int r32 = lane & 31, hk = lane >> 5;
-  V8 fr[KS][FS + TS];
+  const int r16 = lane & 15, q4 = lane >> 4;
+  V8 fr[KS][FS + TS];  // fragments of a whole k-tile: [k-step][weight sub-tiles | token sub-tiles]
   auto lread = [&](int stage, int ks) {
     const char *As = smem + stage * STAGE;
     const char *Bs = As + BN * 128;
-    const int ch = ks * 2 + hk;
+    const int ch = ks * 4 + q4;
 #pragma unroll
     for (int i = 0; i < FS; ++i)
-      fr[ks][i] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + i * 32 + r32, ch));
+      fr[ks][i] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + i * 16 + r16, ch));
 #pragma unroll
     for (int j = 0; j < TS; ++j)
-      fr[ks][FS + j] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + j * 32 + r32, ch));
+      fr[ks][FS + j] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + j * 16 + r16, ch));
   };
-  f32x16 acc[FS][TS];
+  f32x4 acc[FS][TS];
 #pragma unroll
   for (int i = 0; i < FS; ++i)
 #pragma unroll
     for (int j = 0; j < TS; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
   auto mma_step = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < FS; ++i)
 #pragma unroll
       for (int j = 0; j < TS; ++j)
-        acc[i][j] = Mfma<T>::mma(fr[ks][i], fr[ks][FS + j], acc[i][j]);
+        acc[i][j] = Mfma<T>::mma16(fr[ks][i], fr[ks][FS + j], acc[i][j]);
   };
 
   // single operations, so the loop below can fix their order exactly
-  auto mma_one = [&](int ks, int idx) {  // idx = 4 i + j
-    acc[idx >> 2][idx & 3] =
-        Mfma<T>::mma(fr[ks][idx >> 2], fr[ks][FS + (idx & 3)], acc[idx >> 2][idx & 3]);
+  auto mma_one = [&](int ks, int idx) {  // idx = 8 i + j
+    acc[idx >> 3][idx & 7] =
+        Mfma<T>::mma16(fr[ks][idx >> 3], fr[ks][FS + (idx & 7)], acc[idx >> 3][idx & 7]);
   };
-  auto read_one = [&](int stage, int ks, int f) {  // f < 4: weight rows, else token rows
+  auto read_one = [&](int stage, int ks, int f) {  // f < 8: weight rows, else token rows
     const char *As = smem + stage * STAGE;
     const char *Bs = As + BN * 128;
-    const int ch = ks * 2 + hk;
+    const int ch = ks * 4 + q4;
     if (f < FS)
-      fr[ks][f] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + f * 32 + r32, ch));
+      fr[ks][f] = *reinterpret_cast<const V8 *>(As + swz(wn * WTN + f * 16 + r16, ch));
     else
-      fr[ks][f] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + (f - FS) * 32 + r32, ch));
+      fr[ks][f] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + (f - FS) * 16 + r16, ch));
   };
   auto write_one = [&](int stage, int i, const u32x4 (&rb)[LB]) {  // i < 8: weights
     char *As = smem + stage * STAGE;
@@ -282,28 +277,35 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   gload_b(min(2, KT - 1), rb0);
   lds_sync();
   lread(0, 0);
-  lread(0, 1);
+  // Order of the fragment reads: k-step 1 of the tile reads its token sub-tiles first (every
+  // MFMA row needs all of them), the next tile's k-step 0 reads weight sub-tile 0, the token
+  // sub-tiles, then the other weight sub-tiles (the order its first MFMAs use them).
+  auto frag_k1 = [](int r) { return r < 8 ? 8 + r : r - 8; };
+  auto frag_k0 = [](int r) { return r == 0 ? 0 : (r <= 8 ? 7 + r : r - 8); };
   // one k-tile; rb holds the token rows of tile kt+1 and receives those of tile kt+3
   auto ktile = [&](int kt, u32x4 (&rb)[LB]) {
     const int cur = kt & 1;
     const int na = min(kt + 2, KT - 1), nb = min(kt + 3, KT - 1);  // clamped: repeats harmless
-    // before the barrier: MFMAs of k-steps 0..2; after MFMA m comes fragment read m/3 (k-steps
-    // 2 then 3 of tile kt), LDS write m/3 (tile kt+1) or global load m/3
+    // before the barrier: 96 MFMAs (k-step 0, half of k-step 1); after every second one comes
+    // in turn a fragment read of k-step 1, an LDS write of tile kt+1 or a global load
 #pragma unroll
-    for (int m = 0; m < 48; ++m) {
-      mma_one(m >> 4, m & 15);
-      const int q = m / 3;
-      if (m % 3 == 0) read_one(cur, 2 + (q >> 3), q & 7);
-      else if (m % 3 == 1) write_one(cur ^ 1, q, rb);
-      else gload_one(na, nb, q, rb);
+    for (int m = 0; m < 96; ++m) {
+      mma_one(m >> 6, m & 63);
+      if ((m & 1) == 0) {
+        const int q = m >> 1, r = q / 3;
+        if (q % 3 == 0) read_one(cur, 1, frag_k1(r));
+        else if (q % 3 == 1) write_one(cur ^ 1, r, rb);
+        else gload_one(na, nb, r, rb);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_sync();  // tile kt+1 written by every wave; tile kt's reads done
-    // after the barrier: MFMAs of k-step 3, each after one read of tile kt+1 (k-steps 0, 1)
+    // after the barrier: the other 32 MFMAs of k-step 1, every second one after a read of
+    // tile kt+1's k-step 0
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      read_one(cur ^ 1, m >> 3, m & 7);
-      mma_one(3, m);
+    for (int m = 96; m < 128; ++m) {
+      if ((m & 1) == 0) read_one(cur ^ 1, 0, frag_k0((m - 96) >> 1));
+      mma_one(1, m & 63);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -316,11 +318,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   {
     const int cur = (KT - 1) & 1;
     mma_step(0);
-    lread(cur, 2);
+    lread(cur, 1);
     mma_step(1);
-    lread(cur, 3);
-    mma_step(2);
-    mma_step(3);
   }
   epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
 }
