@@ -141,7 +141,7 @@ struct TileBounds {
 
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_tiles_total,
-                                                  int total_tiles) {
+                                                  int total_tiles, int splits) {
   constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
   constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
   constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 sub-tiles of 16 x 16
@@ -152,8 +152,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   typedef typename Mfma<T>::v8 V8;
 
   const int per = gridDim.x >> 3;
-  const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lid >= total_tiles) return;
+  const int uid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (uid >= total_tiles * splits) return;
+  const int lid = uid / splits, slice = uid - lid * splits;  // tile, k-slice
   const int n_tiles = a.n / BN;
   const int in_group = kGroupN * m_tiles_total;
   const int group = lid / in_group;
@@ -177,6 +178,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
   const int lchunk = tid & 7, lrow = tid >> 3;
 
+  // k-tiles [kt0, kt0 + KT) of the tile's K / BK are this unit's slice
+  const int kt_all = K / BK;
+  const int kt0 = (int)((long long)kt_all * slice / splits);
+  const int KT = (int)((long long)kt_all * (slice + 1) / splits) - kt0;
+  W += (size_t)kt0 * BK;
+  X += (size_t)kt0 * BK;
   // Global loads are buffer loads: one descriptor per operand (the weight tile's 256 rows; the
   // token rows from m0 to the group's end, so rows past it read as zero), one per-lane byte
   // offset, and the row / k-tile offsets in scalar registers.
@@ -268,7 +275,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
     else rb[i - LA] = load_x(ktb, i - LA);
   };
 
-  const int KT = K / BK;
   gload_a(0);
   gload_b(0, rb0);
   sstore(0, rb0);
@@ -321,7 +327,71 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
     lread(cur, 1);
     mma_step(1);
   }
+  if (splits > 1) {  // partial tile: [wave][sub-tile][lane] float4, in slice-major order
+    f32x4 *pp = reinterpret_cast<f32x4 *>(a.part) +
+                ((size_t)(slice * total_tiles + lid) * 4 + wave) * (FS * TS * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < FS; ++i)
+#pragma unroll
+      for (int j = 0; j < TS; ++j) pp[(i * TS + j) * 64] = acc[i][j];
+    return;
+  }
   epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
+}
+
+// Sum of the k-slices of one partial tile (slice order fixed) and the tile's epilogue.  Grid:
+// (tiles, 64 sub-tiles); 256 threads = the GEMM's 4 waves x 64 lanes, same accumulator layout.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, TileBounds tb, int m_tiles_total,
+                                                     int total_tiles, int splits) {
+  constexpr int BM = 256, WTN = 128, WTM = 128, TS = 8;
+  const int lid = blockIdx.x, sub = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  // tile coordinates, as in k_gemm
+  const int n_tiles = a.n / BN;
+  const int in_group = kGroupN * m_tiles_total;
+  const int group = lid / in_group;
+  const int first_n = group * kGroupN;
+  const int gsize = min(n_tiles - first_n, kGroupN);
+  const int rem = lid - group * in_group;
+  const int tile_n = first_n + rem % gsize;
+  const int mt = rem / gsize;
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
+  const GemmGroup grp = a.g[gi];
+  const int n0 = tile_n * BN, m0 = (mt - tb.t[gi]) * BM;
+  const int i = sub / TS, j = sub - i * TS;
+  const int m = m0 + wm * WTM + j * 16 + (lane & 15);
+  if (m >= grp.rows) return;
+  const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.part) +
+                    ((size_t)lid * 4 + wave) * (64 * 64) + sub * 64 + lane;
+  const size_t slice_stride = (size_t)total_tiles * 4 * 64 * 64;
+  f32x4 v = pp[0];
+  for (int s = 1; s < splits; ++s) v += pp[s * slice_stride];
+  const int tok = grp.out_row0 + m;
+  const int n = n0 + wn * WTN + i * 16 + 4 * (lane >> 4);
+  if constexpr (EPI == EPI_RESID) {
+    const float *gate = a.gate[segment_of(tok, a.b1, a.b2, a.per)];
+    float *xr = a.x + (size_t)tok * a.ldres + n;
+    const f32x4 gv = *reinterpret_cast<const f32x4 *>(gate + n);
+    f32x4 xv = *reinterpret_cast<const f32x4 *>(xr);
+    xv.x += gv.x * v.x;
+    xv.y += gv.y * v.y;
+    xv.z += gv.z * v.z;
+    xv.w += gv.w * v.w;
+    *reinterpret_cast<f32x4 *>(xr) = xv;
+  } else {
+    if (a.n_store > 0 && n >= a.n_store) return;
+    float *orow = a.out + (size_t)tok * a.ldo + n;
+    if (a.accumulate == 1) {
+      v = *reinterpret_cast<const f32x4 *>(orow) + a.alpha * v;
+    } else if (a.accumulate == 2) {
+      v = a.alpha * v;
+    }
+    *reinterpret_cast<f32x4 *>(orow) = v;
+  }
 }
 
 template <typename T, int EPI>
@@ -333,8 +403,19 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
   const int m_tiles = tb.t[kMaxGroups];
   if (m_tiles == 0) return hipSuccess;
   const int total = m_tiles * (a.n / BN);
-  const int grid = (total + 7) / 8 * 8;
-  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total);
+  // k-slices: only for tiles that fill under half of the compute units, with at least 8
+  // k-tiles per slice
+  int splits = 1;
+  if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * total <= a.split_grid) {
+    splits = min(8, min(a.split_grid / total, (a.k / BK) / 8));
+    if (splits < 2 || (long long)splits * total > a.part_tiles) splits = 1;
+  }
+  const int grid = (total * splits + 7) / 8 * 8;
+  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
+  if (splits > 1) {
+    if constexpr (EPI != EPI_QKV_SWIGLU)
+      k_gemm_reduce<EPI><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);
+  }
   return hipGetLastError();
 }
 

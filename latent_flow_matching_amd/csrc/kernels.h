@@ -44,7 +44,14 @@ struct GemmArgs {
   void *qkv; int ldq; int split; void *cat; int ldc; int cat_off;
   // EPI_RESID
   float *x; int ldres; const float *gate[3]; int b1, b2, per;
+  // Split K (EPI_RESID and EPI_STORE_F32): when the tiles fill under half of split_grid
+  // compute units and k is long, each tile's k-tiles are cut into S slices; every slice stores
+  // its fp32 partial tile to part (room for part_tiles tiles of 256 x 256), and a second kernel
+  // adds the slices in slice order and applies the epilogue.  split_grid = 0: never.
+  float *part; int part_tiles; int split_grid;
 };
+// floats per 256 x 256 partial tile of the split-K GEMM
+constexpr int gemm_part_floats = 256 * 256;
 
 // MFMA GEMM: input and weights of 16-bit type op (OP_BF16 / OP_F16), fp32 accumulation.
 // n % 256 == 0, k % 64 == 0, input rows readable up to 256 past each group's end.

@@ -89,9 +89,11 @@ struct dit_ctx {
   float *fmodv = nullptr;    // [3][2D]
   float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
   float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
+  int cus = 0;               // compute units, rounded down to a multiple of 8
   int lean_grid = 0;         // attention: one workgroup per compute unit (multiple of 8)
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
   int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 6)] per-unit piece counters
+  float *gemm_part = nullptr;  // [lean_grid][gemm_part_floats] split-K partial tiles
 
   // per-kernel timing: hipEvents recorded on the call's stream around each launch
   struct ProfRec {
@@ -106,6 +108,12 @@ struct dit_ctx {
   int prof_next = 0;
 
   int D() const { return cfg.hidden; }
+  // lets an MFMA GEMM cut long k into slices when its tiles fill too few compute units
+  void split_k(GemmArgs *a) const {
+    a->part = gemm_part;
+    a->part_tiles = gemm_part ? cus : 0;
+    a->split_grid = gemm_part ? cus : 0;
+  }
   int F() const { return cfg.mlp_hidden; }
   size_t esz() const { return op == OP_F32 ? 4 : 2; }
   int nblocks() const { return cfg.n_stream_blocks + cfg.n_shared_blocks; }
@@ -363,7 +371,8 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   ctx->cfg = c;
   ctx->device = dev;
   ctx->op = c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
-  ctx->lean_grid = prop.multiProcessorCount / 8 * 8;
+  ctx->cus = prop.multiProcessorCount / 8 * 8;
+  ctx->lean_grid = ctx->cus;
   if (const char *ag = getenv("DIT_ATTN_GRID")) {  // attention share count (0: off)
     char *end = nullptr;
     const long v = strtol(ag, &end, 10);
@@ -447,6 +456,8 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_cnt,
                           (size_t)c.heads * (c.max_tokens / 256 + kMaxGroups) * 4);
   }
+  if (ctx->op != OP_F32 && ctx->cus > 0)
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->gemm_part, (size_t)ctx->cus * gemm_part_floats * 4);
   if (ctx->op == OP_F32) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
   } else if (!rc) {
@@ -597,6 +608,7 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   a2.b1 = sg.b1;
   a2.b2 = sg.b2;
   a2.per = sg.per;
+  ctx->split_k(&a2);
   const double fl2 = 2.0 * N * (double)(D + F) * D;
   if (ctx->op != OP_F32)
     DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
@@ -738,6 +750,7 @@ int run_forward(dit_ctx *ctx, const float *lat, const Req &rq, double t, double 
     af.ldo = C;
     af.accumulate = hs[qs].mode;
     af.alpha = hs[qs].alpha;
+    ctx->split_k(&af);
     const int row0 = qs * per + n_txt;
     if (ctx->op == OP_F32) {
       DIT_CHECK(ln_modulate(ctx->xf, OP_F32, D, ctx->x, D, n_img, row0, D, c.ln_eps, fms, sg, stream),
@@ -886,6 +899,7 @@ extern "C" int dit_text_features(dit_ctx *ctx, const float *feat, int n_txt, flo
   a.k = K;
   a.ldx = K;
   a.ldo = D;
+  ctx->split_k(&a);
   if (ctx->op == OP_F32) {
     a.g[0] = GemmGroup{feat, ctx->txt_in, n_txt, 0};
     a.out = txt;

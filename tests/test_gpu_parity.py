@@ -587,6 +587,25 @@ def test_attention_grid_override_rejects_bad_values(bad, monkeypatch):
         dit.DiT(TINY2, w, 64)
 
 
+def test_forward_full_width_split_head_matches_oracle():
+    """A full-width FLUX.2 call (one double and one single block) at 512 text + 1024 image
+    tokens: linear2's 72 tiles and the output head's 4 tiles fill few compute units, so both
+    run as k-slices summed by the reduce kernel."""
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
+    ctx, w = context(cfg, 1536)
+    grid = (32, 32)
+    lat = S.gen_latents(1024, cfg.in_channels)
+    txt = S.gen_text(512, cfg.hidden)
+    v = torch.empty((1024, cfg.in_channels), device="cuda")
+    print("[forward] FLUX.2 full width, 512+1024 tokens", flush=True)
+    ctx.forward(dev(lat), dev(txt), grid, 0.6, v)
+    torch.cuda.synchronize()
+    want = O.forward(oracle_model(cfg, w), f64(lat), f64(txt), grid, float(np.float32(0.6)))
+    err = rel_err(v.cpu().numpy(), want)
+    print(f"    full-width forward err {err:.3e}", flush=True)
+    assert err <= BF16_TOL
+
+
 # ----------------------------------------------------------------- full benchmark shapes, sampled rows
 
 def _rows(n, k=24, seed=0):
