@@ -7,17 +7,20 @@
 // Attention-Blöcke").  Padded prompt tokens are attended like any other token ("...",
 // section "Verarbeitung einzelner Prompts und Batching-Architektur in der Praxis").
 //
-// Work split: a workgroup of 8 waves takes 256 queries of one head (32 per wave) and walks
-// the allowed keys in tiles of 64, staged through LDS.  Per wave and key tile:
-//   S^T = K Q^T   (A = K fragments from LDS, B = the wave's queries held in registers): each
-//                 lane owns one query and 32 of the tile's keys, so the row max needs one
-//                 exchange with the partner lane l^32.
-//   O^T += V^T P^T (A = V^T fragments from LDS, B = P straight from the S registers).
+// Work split: a workgroup of 8 waves takes 256 queries of one head (32 per wave, two blocks of
+// 16) and walks the allowed keys in tiles of 64, staged through LDS.  Per wave and key tile, with
+// v_mfma_f32_16x16x32 (which holds a higher clock than the 32x32x16 form under the power limit):
+//   S^T = K Q^T   (A = K fragments from LDS, B = the wave's queries held in registers): a lane
+//                 owns one query of each block and 16 of the tile's keys, so a row max takes
+//                 two exchanges (lanes l^16, l^32).
+//   O^T += V^T P^T (A = V^T fragments from LDS, B = P straight from the S registers: a lane's S
+//                 values of a 32-key chunk are keys 4q..4q+3 and 16+4q..16+4q+3, q = lane/16,
+//                 the B operand's k positions 8q..8q+7 in that order).
 // The running max is raised lazily: P is formed against the stored max unless some row's
 // max grew by more than 2^8, so O is rescaled only when that happens (P <= 256 fits fp16).
 // V is read in the transposed layout written by the QK-norm kernel, vt[h][d][token'] with the
-// middle two quads of every 16 tokens swapped, so that the eight keys a lane multiplies in
-// one P.V MFMA form a single 16-byte chunk.  Scores are kept in the log2 domain
+// tokens of every 32 reordered so that 16-byte chunk q holds tokens 4q..4q+3, 16+4q..16+4q+3:
+// the eight keys a lane multiplies in one P.V MFMA form a single chunk.  Scores are kept in the log2 domain
 // (scale * log2(e) folded into one FMA before exp2).
 // Groups: each (q0, q1, k0, k1) range gets its own query tiles; key tiles start at k0
 // rounded down to 64 and keys outside [k0, k1) are masked to -inf.
@@ -104,9 +107,10 @@ __device__ __forceinline__ int share_owner(const AttnPlan &p, int it, int grid) 
   return (int)(((long long)(it + 1) * grid + p.iters - 1) / p.iters) - 1;
 }
 
-// Partial results of a piece: O as 16 float4 per lane and wave, then (max, sum) per lane.
+// Partial results of a piece: O as 16 float4 per lane and wave, then (max, max, sum, sum) of the
+// lane's two queries.
 constexpr int kPartO = 8 * 16 * 64 * 4;
-constexpr int kPartFloats = kPartO + 8 * 64 * 2;
+constexpr int kPartFloats = kPartO + 8 * 64 * 4;
 static_assert(kPartFloats == attn_part_floats, "partial slot size");
 constexpr int kSc1 = 16;  // buffer access cache policy: device-coherent (sc1)
 
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   if (it0 >= it1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r32 = lane & 31, hk = lane >> 5;
+  const int r16 = lane & 15, q4 = lane >> 4;
   const int half = wave >> 2;  // waves w and w+4 of a workgroup share a SIMD
   const T *qkv = reinterpret_cast<const T *>(a.qkv);
 
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   int head = 0, q = 0, kv_begin = 0, n = 0;
   AttnGroup grp = a.g[0];
   const T *vt = nullptr;
-  V8 qf[8];
+  V8 qf[2][4];  // [query block][32-d step]
 
   u32x4 rk[2], rv[2];
   const int k_row = tid >> 4, k_ch = tid & 15;   // K: rows k_row + 32 i
@@ -180,35 +184,36 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     asm volatile("" ::: "memory");
   };
 
-  f32x16 o[4], s[2];
-  V8 pf[4];
+  f32x4 o[2][8], s[2][4];  // O^T [query block][16-d block], S^T [query block][16-key block]
+  V8 pf[2][2];              // P^T [query block][32-key chunk]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < 8; ++i) o[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  // M phase: the 16 S MFMAs (K fragments) then the 16 P.V MFMAs (V^T fragments); fragment
-  // j + kPre is read from LDS while MFMA j runs, so the LDS latency stays off the MFMA chain.
+  // M phase: 16 K fragments, each for the S MFMAs of both query blocks, then 16 V^T fragments,
+  // each for the P.V MFMAs of both blocks; fragment j + kPre is read from LDS while fragment j's
+  // MFMAs run, so the LDS latency stays off the MFMA chain.
   constexpr int kPre = 4;
   auto frag = [&](int t, int j) __attribute__((always_inline)) -> V8 {
-    if (j < 16) {  // K tile t: kk = j >> 1, st = j & 1
+    if (j < 16) {  // K tile t: key block kb = j & 3, 32-d step ds = j >> 2
       const char *ks = smem + (t & 1) * KT_BYTES;
-      return *reinterpret_cast<const V8 *>(ks + k_off((j & 1) * 32 + r32, 2 * (j >> 1) + hk));
+      return *reinterpret_cast<const V8 *>(ks + k_off((j & 3) * 16 + r16, 4 * (j >> 2) + q4));
     }
-    const int i = j - 16;  // V tile t-1: kc = i >> 2, ds = i & 3 (accumulators alternate)
+    const int i = j - 16;  // V tile t-1: 16-d block db = i & 7, 32-key chunk kc = i >> 3
     const char *vs = smem + 2 * KT_BYTES + ((t - 1) & 1) * VT_BYTES;
-    return *reinterpret_cast<const V8 *>(vs + v_off((i & 3) * 32 + r32, 2 * (i >> 2) + hk));
+    return *reinterpret_cast<const V8 *>(vs + v_off((i & 7) * 16 + r16, 4 * (i >> 3) + q4));
   };
   auto mphase = [&](auto j0c, auto j1c, int t) __attribute__((always_inline)) {
     constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
     __builtin_amdgcn_s_setprio(1);
     if constexpr (J0 == 0) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
+        for (int kb = 0; kb < 4; ++kb) s[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     V8 fr[kPre];
 #pragma unroll
@@ -217,56 +222,71 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     for (int j = J0; j < J1; ++j) {
       const V8 f = fr[j % kPre];
       if (j + kPre < J1) fr[j % kPre] = frag(t, j + kPre);
-      if (j < 16) s[j & 1] = Mfma<T>::mma(f, qf[j >> 1], s[j & 1]);
-      else o[(j - 16) & 3] = Mfma<T>::mma(f, pf[(j - 16) >> 2], o[(j - 16) & 3]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (j < 16) s[b][j & 3] = Mfma<T>::mma16(f, qf[b][j >> 2], s[b][j & 3]);
+        else o[b][(j - 16) & 7] = Mfma<T>::mma16(f, pf[b][(j - 16) >> 3], o[b][(j - 16) & 7]);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
     for (int j = J0; j < J1 - kPre; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPre, 0);
     __builtin_amdgcn_s_setprio(0);
   };
   auto vphase = [&](int t) __attribute__((always_inline)) {
     const int kv0 = kv_begin + t * BKV;
     if ((kv0 < grp.k0) || (kv0 + BKV > grp.k1)) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + st * 32 + 8 * (e >> 2) + 4 * hk + (e & 3);
-          if (key < grp.k0 || key >= grp.k1) s[st][e] = -INFINITY;
-        }
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kv0 + kb * 16 + 4 * q4 + e;
+            if (key < grp.k0 || key >= grp.k1) s[b][kb][e] = -INFINITY;
+          }
     }
-    float mx = -INFINITY;
+    float mx[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int b = 0; b < 2; ++b) {
+      float m = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-    if (__ballot(mx > m_run + kLazy)) {  // wave-uniform: raise the stored max, rescale O
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, s[b][kb][e]);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      mx[b] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
     }
-    const float nm = -m_run;
-    float psum = 0.f;
+    // wave-uniform: raise the stored maxima, rescale O
+    if (__ballot(mx[0] > m_run[0] + kLazy || mx[1] > m_run[1] + kLazy)) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int b = 0; b < 2; ++b) {
+        const float m_new = fmaxf(m_run[b], mx[b]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
+        m_run[b] = m_new;
+        l_run[b] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[st][e], sl2, nm));
-        psum += p;
-        pf[2 * st + (e >> 3)][e & 7] = from_f32_inrange<T>(p);  // p <= 256
+        for (int i = 0; i < 8; ++i) o[b][i] *= alpha;
       }
-    l_run += psum;
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float nm = -m_run[b];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][kb][e], sl2, nm));
+          psum += p;
+          pf[b][kb >> 1][4 * (kb & 1) + e] = from_f32_inrange<T>(p);  // p <= 256
+        }
+      l_run[b] += psum;
+    }
   };
   auto io = [&](int t) __attribute__((always_inline)) {  // global phase 2t+1
     if (t + 1 < n) store_k(t + 1);
@@ -312,21 +332,20 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     const int nku = p.nk[u.g];
     head = u.head;
     grp = a.g[u.g];
-    q = grp.q0 + (u.qt - p.tb[u.g]) * BQ + wave * 32 + r32;
+    q = grp.q0 + (u.qt - p.tb[u.g]) * BQ + wave * 32 + r16;  // query of block 0; block 1: q + 16
     kv_begin = (grp.k0 / BKV) * BKV + u.t * BKV;
     n = plen;
     vt = reinterpret_cast<const T *>(a.vt) + (size_t)head * HD * a.ldv;
-    {
-      const T *qp = qkv + (size_t)q * a.ldqkv + head * HD + hk * 8;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const V8 *>(qp + kk * 16);
+    for (int b = 0; b < 2; ++b) {
+      const T *qp = qkv + (size_t)(q + 16 * b) * a.ldqkv + head * HD + q4 * 8;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) qf[b][ds] = *reinterpret_cast<const V8 *>(qp + ds * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[b] = -INFINITY;
+      l_run[b] = 0.f;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-    m_run = -INFINITY;
-    l_run = 0.f;
 
     // Local phase 2t is M(t), 2t+1 is V(t); half B runs one global phase behind half A (one
     // extra barrier up front, one fewer at the end).  io(t) belongs to global phase 2t+1: the
@@ -354,17 +373,26 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     mphase(I16{}, I32{}, n);
     if (!half) sync();
 
-    T *op = reinterpret_cast<T *>(a.out) + (size_t)q * a.ldo + head * HD + 4 * hk;
-    if (u.t == 0 && plen == nku) {  // the whole unit: normalise and store
-      const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
-      if (q < grp.q1) {
+    // lane: query q (block 0) and q + 16 (block 1), dims 16 i + 4 q4 + {0..3} of each block
+    auto store_rows = [&](const float inv[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds)
+      for (int b = 0; b < 2; ++b) {
+        if (q + 16 * b >= grp.q1) continue;
+        T *op = reinterpret_cast<T *>(a.out) + (size_t)(q + 16 * b) * a.ldo + head * HD + 4 * q4;
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4(op + ds * 32 + 8 * g, o[ds][4 * g] * inv, o[ds][4 * g + 1] * inv,
-                   o[ds][4 * g + 2] * inv, o[ds][4 * g + 3] * inv);
+        for (int i = 0; i < 8; ++i)
+          store4(op + i * 16, o[b][i][0] * inv[b], o[b][i][1] * inv[b], o[b][i][2] * inv[b],
+                 o[b][i][3] * inv[b]);
       }
+    };
+    // row sum: the four lanes l, l^16, l^32, l^48 hold a query's 64 keys between them
+    auto full_sum = [](float l) __attribute__((always_inline)) {
+      l += __shfl_xor(l, 16, 64);
+      return l + __shfl_xor(l, 32, 64);
+    };
+    if (u.t == 0 && plen == nku) {  // the whole unit: normalise and store
+      const float inv[2] = {1.0f / full_sum(l_run[0]), 1.0f / full_sum(l_run[1])};
+      store_rows(inv);
       continue;
     }
 
@@ -375,16 +403,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     // writeback or invalidate is needed.
     const __amdgpu_buffer_rsrc_t rs_part = __builtin_amdgcn_make_buffer_rsrc(
         a.part, (short)0, (int)((size_t)2 * G * kPartFloats * 4), 0x00020000);
-    const int o_off = (wave * 16 * 64 + lane) * 16, ml_off = kPartO * 4 + (wave * 64 + lane) * 8;
+    const int o_off = (wave * 16 * 64 + lane) * 16, ml_off = kPartO * 4 + (wave * 64 + lane) * 16;
 #pragma unroll
     for (int c = 0; c < 16; ++c)
       __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{__float_as_uint(o[c >> 2][4 * (c & 3)]), __float_as_uint(o[c >> 2][4 * (c & 3) + 1]),
-                __float_as_uint(o[c >> 2][4 * (c & 3) + 2]),
-                __float_as_uint(o[c >> 2][4 * (c & 3) + 3])},
+          u32x4{__float_as_uint(o[c >> 3][c & 7][0]), __float_as_uint(o[c >> 3][c & 7][1]),
+                __float_as_uint(o[c >> 3][c & 7][2]), __float_as_uint(o[c >> 3][c & 7][3])},
           rs_part, o_off + c * 64 * 16, slot * kPartFloats * 4, kSc1);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m_run), __float_as_uint(l_run)},
-                                          rs_part, ml_off, slot * kPartFloats * 4, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(m_run[0]), __float_as_uint(m_run[1]), __float_as_uint(l_run[0]),
+              __float_as_uint(l_run[1])},
+        rs_part, ml_off, slot * kPartFloats * 4, kSc1);
     const int unit = u.head * p.q_tiles + u.qt;
     const int u0 = pit - u.t;  // first iteration of the unit
     const int w0 = share_owner(p, u0, G), w1 = share_owner(p, u0 + nku - 1, G);
@@ -395,52 +424,44 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
                                           __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
     __syncthreads();
     if (merge_flag) {
-      float mp[8], mx = -INFINITY;
-      int sl[8];
-      const int np = w1 - w0 + 1;  // at most 8 pieces (checked by the launcher)
+      // two passes over the pieces (at most 8, checked by the launcher): the maxima, then the
+      // weighted sums; each pass recomputes the piece's slot rather than holding a table
+      const int np = w1 - w0 + 1;
+      auto slot_of = [&](int i) __attribute__((always_inline)) {
+        const int w = w0 + i;
+        return share_begin(p, w, G) >= u0 ? 2 * w : 2 * w + 1;
+      };
+      float mx[2] = {-INFINITY, -INFINITY};
+      for (int i = 0; i < np; ++i) {
+        const u32x4 ml = __builtin_amdgcn_raw_buffer_load_b128(rs_part, ml_off,
+                                                               slot_of(i) * kPartFloats * 4, kSc1);
+        mx[0] = fmaxf(mx[0], __uint_as_float(ml.x));
+        mx[1] = fmaxf(mx[1], __uint_as_float(ml.y));
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < np) {
-          const int w = w0 + i;
-          sl[i] = share_begin(p, w, G) >= u0 ? 2 * w : 2 * w + 1;
-          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_part, ml_off,
-                                                                sl[i] * kPartFloats * 4, kSc1);
-          mp[i] = __uint_as_float(ml.x);
-          mx = fmaxf(mx, mp[i]);
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float l[2] = {0.f, 0.f};
+      for (int i = 0; i < np; ++i) {
+        const int so = slot_of(i) * kPartFloats * 4;
+        const u32x4 ml = __builtin_amdgcn_raw_buffer_load_b128(rs_part, ml_off, so, kSc1);
+        const float wgt[2] = {__builtin_amdgcn_exp2f(__uint_as_float(ml.x) - mx[0]),
+                              __builtin_amdgcn_exp2f(__uint_as_float(ml.y) - mx[1])};
+        l[0] += wgt[0] * __uint_as_float(ml.z);
+        l[1] += wgt[1] * __uint_as_float(ml.w);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs_part, o_off + c * 64 * 16, so, kSc1);
+          const float w = wgt[c >> 3];
+          o[c >> 3][c & 7][0] += w * __uint_as_float(v.x);
+          o[c >> 3][c & 7][1] += w * __uint_as_float(v.y);
+          o[c >> 3][c & 7][2] += w * __uint_as_float(v.z);
+          o[c >> 3][c & 7][3] += w * __uint_as_float(v.w);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-      float l = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < np) {
-          const float wgt = __builtin_amdgcn_exp2f(mp[i] - mx);
-          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_part, ml_off,
-                                                                sl[i] * kPartFloats * 4, kSc1);
-          l += wgt * __uint_as_float(ml.y);
-#pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                rs_part, o_off + c * 64 * 16, sl[i] * kPartFloats * 4, kSc1);
-            o[c >> 2][4 * (c & 3)] += wgt * __uint_as_float(v.x);
-            o[c >> 2][4 * (c & 3) + 1] += wgt * __uint_as_float(v.y);
-            o[c >> 2][4 * (c & 3) + 2] += wgt * __uint_as_float(v.z);
-            o[c >> 2][4 * (c & 3) + 3] += wgt * __uint_as_float(v.w);
-          }
-        }
-      }
-      const float inv = 1.0f / (l + __shfl_xor(l, 32, 64));
-      if (q < grp.q1) {
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4(op + ds * 32 + 8 * g, o[ds][4 * g] * inv, o[ds][4 * g + 1] * inv,
-                   o[ds][4 * g + 2] * inv, o[ds][4 * g + 3] * inv);
-      }
+      const float inv[2] = {1.0f / full_sum(l[0]), 1.0f / full_sum(l[1])};
+      store_rows(inv);
       if (tid == 0)  // ready for the next launch
         __hip_atomic_store(a.cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

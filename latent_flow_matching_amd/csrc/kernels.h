@@ -79,7 +79,7 @@ struct AttnArgs {
   float *part; int *cnt; int lean_grid;
 };
 // floats per partial slot of the MFMA attention
-constexpr int attn_part_floats = 8 * 16 * 64 * 4 + 8 * 64 * 2;
+constexpr int attn_part_floats = 8 * 16 * 64 * 4 + 8 * 64 * 4;
 hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s);
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s);  // V read from qkv at 2*d_model
 

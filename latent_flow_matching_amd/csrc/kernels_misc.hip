@@ -174,8 +174,8 @@ hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx
 // keys are RMS-normalised before attention), then the 4D rotary embedding: lane p rotates
 // the adjacent pair (2p, 2p+1) by the angle of axis p/16, frequency index p%16.
 // The 16-bit paths also write V transposed, vt[h][d][token'], the layout the attention
-// kernel's P.V product reads (keys contiguous; token' swaps the middle two quads of every
-// 16 tokens), with zeros for the 64 columns past n.
+// kernel's P.V product reads (keys contiguous; token' reorders every 32 tokens so that
+// 16-byte chunk q holds tokens 4q..4q+3, 16+4q..16+4q+3), with zeros for the 64 columns past n.
 // Grid: (ceil(n/64) + 1 token tiles, heads); 4 waves, each 16 tokens of the tile.
 // ------------------------------------------------------------------------------------------
 template <typename T> struct Pair;
@@ -324,11 +324,11 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
     // eight consecutive lanes write the 128 contiguous bytes (64 keys) of one dim's row
     const int d = c >> 3, ch = c & 7;
     V8 o;
-    // within every 16 tokens the middle two quads are swapped (column order 0-3, 8-11, 4-7,
-    // 12-15), so the eight keys one attention lane multiplies are contiguous
-    const int base = (ch >> 1) * 16 + ((ch & 1) ? 4 : 0);
+    // within every 32 tokens, chunk q (8 columns) holds tokens 4q..4q+3 and 16+4q..16+4q+3:
+    // the eight keys one attention lane multiplies in a P.V MFMA, contiguous
+    const int base = (ch >> 2) * 32 + (ch & 3) * 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = tile[(base + (e < 4 ? e : e + 4)) * kPitch + d];
+    for (int e = 0; e < 8; ++e) o[e] = tile[(base + (e < 4 ? e : e + 12)) * kPitch + d];
     *reinterpret_cast<V8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
   }
 }
