@@ -341,6 +341,35 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     return out
 
 
+def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSet],
+                             set_of_segment: tuple[int, int, int], mods6: list[np.ndarray],
+                             pos: np.ndarray, mask: int, dims: Dims):
+    """A double-stream block wired in sequence (the FLUX.1-style reading of the pages' double
+    blocks, the alternative to the parallel wiring of block_forward): attention first, then
+    the MLP on the updated residual, each after its own modulated LayerNorm and with its own
+    gate; mods6[s] = [shift1 || scale1 || gate1 || shift2 || scale2 || gate2] ([6D]).
+
+    reading: the same weight tensors as block_forward, used in two halves: W1's Q|K|V rows and
+    W2's first D columns for attention, W1's gate/up rows and W2's last F columns for the
+    SwiGLU MLP."""
+    n, d = x.shape
+    f = dims.mlp_hidden
+    seg = segment_ids(*segs)
+    half1 = [np.asarray(m[:3 * d]) for m in mods6]
+    half2 = [np.asarray(m[3 * d:]) for m in mods6]
+    attn_sets = [WeightSet(np.concatenate([ws.w1[:3 * d], np.zeros((2 * f, d))], axis=0),
+                           np.concatenate([ws.w2[:, :d], np.zeros((d, f))], axis=1), ws.qn, ws.kn)
+                 for ws in sets]
+    mlp_sets = [WeightSet(np.concatenate([np.zeros((3 * d, d)), ws.w1[3 * d:]], axis=0),
+                          np.concatenate([np.zeros((d, d)), ws.w2[:, d:]], axis=1), ws.qn, ws.kn)
+                for ws in sets]
+    # attention half: zero gate/up rows give SiLU(0) * 0 = 0 for the MLP columns
+    x1 = block_forward(x, segs, attn_sets, set_of_segment, half1, pos, mask, dims)
+    # MLP half: zero Q|K|V rows give uniform attention over V = 0, which W2's zeroed attention
+    # columns drop anyway
+    return block_forward(x1, segs, mlp_sets, set_of_segment, half2, pos, mask, dims)
+
+
 # ----------------------------------------------------------------------------------------
 # Block schedule, output head, Euler loop ([GN] Architektur; [MV] Blocks/Modulation; [WE])
 # ----------------------------------------------------------------------------------------
@@ -422,6 +451,7 @@ class Model:
     temb_tgt_l1: np.ndarray | None = None   # [D, time_dim]  flow-map models only
     temb_tgt_l2: np.ndarray | None = None   # [D, D]
     txt_in: np.ndarray | None = None        # [D, 8 * 2560]  text-feature projection
+    double_wiring: int = 0                  # FLUX.2 double blocks: 0 parallel, 1 sequential
 
 
 # ----------------------------------------------------------------------------------------
@@ -483,7 +513,11 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
         mods = segment_mods(model.mods[kind], sos, conds)
         if block_hook is not None:
             block_hook(b, x)
-        x = block_forward(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos, mask, dims)
+        if model.arch == ARCH_FLUX2 and kind == 0 and model.double_wiring:
+            x = block_forward_sequential(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos,
+                                         mask, dims)
+        else:
+            x = block_forward(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos, mask, dims)
     return final_layer(x[n_txt:n_txt + n_img], conds[1], model.final_mod, model.final_out,
                        dims.ln_eps)
 

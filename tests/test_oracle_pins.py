@@ -264,6 +264,57 @@ def test_block_matches_library_composition(mask, sos, segs):
                                got[rows], rtol=0, atol=1e-12)
 
 
+def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims):
+    """Independent torch float64 composition of a sequentially wired double block: attention
+    with (shift1, scale1, gate1), then the SwiGLU MLP on the updated residual with (shift2,
+    scale2, gate2)."""
+    d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
+    seg = torch.tensor(O.segment_ids(*segs))
+    n = x.shape[0]
+    X = torch.tensor(x)
+    M = torch.stack([torch.tensor(mods6[int(s)]) for s in seg])          # [n, 6D]
+    sh1, sc1, g1, sh2, sc2, g2 = (M[:, i * d:(i + 1) * d] for i in range(6))
+    W1 = torch.stack([torch.tensor(sets[sos[int(s)]].w1) for s in seg])  # [n, 3D+2F, D]
+    W2 = torch.stack([torch.tensor(sets[sos[int(s)]].w2) for s in seg])  # [n, D, D+F]
+    xm = F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + sc1) + sh1
+    h = torch.einsum("nk,nok->no", xm, W1[:, :3 * d])
+    q, k, v = h[:, :d].reshape(n, nh, hd), h[:, d:2 * d].reshape(n, nh, hd), h[:, 2 * d:].reshape(n, nh, hd)
+    qw = torch.stack([torch.tensor(sets[sos[int(s)]].qn) for s in seg])[:, None, :]
+    kw = torch.stack([torch.tensor(sets[sos[int(s)]].kn) for s in seg])[:, None, :]
+    q = torch.tensor(rope_complex((F.rms_norm(q, (hd,), eps=dims.rms_eps) * qw).numpy(), pos, dims.rope_theta))
+    k = torch.tensor(rope_complex((F.rms_norm(k, (hd,), eps=dims.rms_eps) * kw).numpy(), pos, dims.rope_theta))
+    am = None if mask == O.MASK_FULL else (seg[:, None] == seg[None, :])
+    o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                       attn_mask=am).transpose(0, 1).reshape(n, d)
+    X1 = X + g1 * torch.einsum("nk,nok->no", o, W2[:, :, :d])
+    xm2 = F.layer_norm(X1, (d,), eps=dims.ln_eps) * (1 + sc2) + sh2
+    gu = torch.einsum("nk,nok->no", xm2, W1[:, 3 * d:])
+    m = F.silu(gu[:, :f]) * gu[:, f:]
+    return (X1 + g2 * torch.einsum("nk,nok->no", m, W2[:, :, d:])).numpy()
+
+
+@pytest.mark.parametrize("sos,segs", [((0, 1, 1), (5, 4, 3)), ((0, 1, 1), (4, 6, 0))])
+def test_sequential_block_matches_library_composition(sos, segs):
+    r = rng(60)
+    dims = TINY
+    n = sum(segs)
+    sets = [rand_set(r, dims) for _ in range(2)]
+    mods6 = [np.concatenate([a, b]) for a, b in zip(rand_mods(r, dims), rand_mods(r, dims))]
+    x = r.normal(size=(n, dims.hidden))
+    pos = O.positions(segs[0], (2, segs[1] // 2), ((segs[2], 1),) if segs[2] else ())
+    got = O.block_forward_sequential(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims)
+    ref = torch_sequential_block(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    # differs from the parallel wiring of the same weights
+    par = O.block_forward(x, segs, sets, sos, [m[:3 * dims.hidden] for m in mods6], pos,
+                          O.MASK_FULL, dims)
+    assert not np.allclose(got, par)
+    # both gates zero: identity
+    z = [np.concatenate([m[:2 * dims.hidden], np.zeros(dims.hidden), m[3 * dims.hidden:5 * dims.hidden],
+                         np.zeros(dims.hidden)]) for m in mods6]
+    np.testing.assert_array_equal(O.block_forward_sequential(x, segs, sets, sos, z, pos, O.MASK_FULL, dims), x)
+
+
 def test_block_gate_zero_is_identity():
     r = rng(9)
     x = r.normal(size=(10, TINY.hidden))
@@ -658,6 +709,19 @@ def test_pins_catch_planted_slips(monkeypatch):
     with pytest.raises(AssertionError):
         test_flow_map_cond_rows()
     monkeypatch.setattr(O, "flow_map_cond_rows", orig_fm)
+    # the sequential block's MLP half normalising the block input instead of the updated residual
+    def parallel_halves(x, segs, sets, sos, mods6, pos, mask, dims):
+        d = dims.hidden
+        a = O.block_forward(x, segs, sets, sos, [m[:3 * d] for m in mods6], pos, mask, dims)
+        mlp_only = [O.WeightSet(np.concatenate([np.zeros((3 * d, d)), ws.w1[3 * d:]]),
+                                np.concatenate([np.zeros((d, d)), ws.w2[:, d:]], axis=1), ws.qn, ws.kn)
+                    for ws in sets]
+        b = O.block_forward(x, segs, mlp_only, sos, [m[3 * d:] for m in mods6], pos, mask, dims)
+        return a + b - x
+    monkeypatch.setattr(O, "block_forward_sequential", parallel_halves)
+    with pytest.raises(AssertionError):
+        test_sequential_block_matches_library_composition((0, 1, 1), (5, 4, 3))
+    monkeypatch.undo()
     # guidance with the branches swapped
     monkeypatch.setattr(O, "guided_velocity", lambda vc, vu, g: vc + g * (vu - vc))
     with pytest.raises(AssertionError):
