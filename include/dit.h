@@ -87,6 +87,14 @@ typedef struct {
                          * states of 2560 = 20480); multiple of 64, <= 65536 */
   int flow_map;         /* 1: flow-map (timestep-distilled) model: every conditioning row
                          * also gets the embedding of the step's target time (temb_tgt) */
+  int double_wiring;    /* DIT_FLUX2 double blocks: 0 parallel (attention and SwiGLU MLP on one
+                         * normalised input, the form of the single blocks), 1 sequential
+                         * (attention, then the MLP on the updated residual, each with its own
+                         * LayerNorm, shift, scale and gate; mod.0.s{s} are then [6D, D]).
+                         * "Flux 2 Klein: Reine C-basierte Inferenz" (GeekNews), model
+                         * architecture: double-stream blocks with separate text
+                         * and image weights; the pages leave their inner wiring open.  Must
+                         * be 0 for DIT_FLUX3. */
 } dit_config;
 
 /* One named weight tensor in host memory, row-major [out, in].  dtype DIT_F32: float
@@ -99,7 +107,9 @@ typedef struct {
  *   txt_in      [D, txt_feat_dim]   text-feature projection (txt_feat_dim > 0 only)
  *   final.mod   [2D, D]      output-head modulation (shift || scale)
  *   final.out   [C, D]       output projection to the velocity
- *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) of stream blocks, per set
+ *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) of stream blocks, per set;
+ *               [6D, D] with double_wiring = 1: (shift || scale || gate) of the attention
+ *               half, then of the MLP half
  *   mod.1.s0    [3D, D]      modulation of shared (single / joint) blocks
  *   blk{b}.s{s}.w1 [3D+2F, D]  rows Q | K | V | gate | up (head-major Q, K, V)
  *   blk{b}.s{s}.w2 [D, D+F]    output projection of [attention || SwiGLU]
@@ -131,7 +141,11 @@ void dit_ctx_free(dit_ctx *ctx);
  * Computes x <- x + gate_s * ([attention || SwiGLU](LN(x) * (1 + scale_s) + shift_s) W2^T)
  * with (shift, scale, gate)_s = mod.{kind}.s{set(s)} . SiLU(cond[s])
  * ("FLUX.3 Image Klein in Diffusers": parallel attention and SwiGLU MLP on one normalised
- * input, QK RMSNorm, adaLN from the timestep embedding, 4D RoPE).
+ * input, QK RMSNorm, adaLN from the timestep embedding, 4D RoPE).  Double blocks of a
+ * double_wiring = 1 model run the two halves in sequence instead:
+ *   x <- x + gate1_s * (attention(LN(x) * (1 + scale1_s) + shift1_s) W2[:, :D]^T)
+ *   x <- x + gate2_s * (SwiGLU(LN(x) * (1 + scale2_s) + shift2_s) W2[:, D:]^T)
+ * with the Q|K|V rows of W1 in the first and its gate/up rows in the second.
  * Requires 0 <= block < n_stream_blocks + n_shared_blocks, 1 <= N <= max_tokens. */
 int dit_block_forward(dit_ctx *ctx, int block, float *x, int n_txt, int n_img, int n_ref,
                       const float *pos, const float *cond, int mask, void *stream);
@@ -246,7 +260,8 @@ int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
 /* Workspace buffer of the last call, for inspection after the stream has finished:
  * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
  * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32
- * [2][3][3][3D]: kind, set, segment, shift || scale || gate), "x" (fp32 [N, D], the
+ * [2][3][3][R]: kind, set, segment, shift || scale || gate, R = 3D, or 6D with
+ * double_wiring = 1, whose stream-block rows hold both halves), "x" (fp32 [N, D], the
  * residual stream of dit_forward / dit_denoise after the last block).  *dtype receives
  * the element type (compute type for xm, qkv, cat; DIT_F32 for mod and x); *row_stride the
  * elements per row.  NULL for an unknown name. */

@@ -173,8 +173,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
-  const int K = a.k;
-  const T *W = reinterpret_cast<const T *>(grp.w) + (size_t)n0 * K;
+  const int K = a.k, LW = a.ldw > 0 ? a.ldw : a.k;  // reduction length, weight row stride
+  const T *W = reinterpret_cast<const T *>(grp.w) + (size_t)n0 * LW;
   const T *X = reinterpret_cast<const T *>(grp.x) + (size_t)m0 * a.ldx;
   const int lchunk = tid & 7, lrow = tid >> 3;
 
@@ -188,13 +188,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   // token rows from m0 to the group's end, so rows past it read as zero), one per-lane byte
   // offset, and the row / k-tile offsets in scalar registers.
   const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)W, (short)0, (int)min((long long)BN * K * 2, 0x7FFFFFFFll), 0x00020000);
+      (void *)W, (short)0, (int)min((long long)BN * LW * 2, 0x7FFFFFFFll), 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
       (void *)X, (short)0, (int)min((long long)(grp.rows - m0) * a.ldx * 2, 0x7FFFFFFFll),
       0x00020000);
-  const int vo_w = (lrow * K + lchunk * 8) * 2, vo_x = (lrow * a.ldx + lchunk * 8) * 2;
+  const int vo_w = (lrow * LW + lchunk * 8) * 2, vo_x = (lrow * a.ldx + lchunk * 8) * 2;
   auto load_w = [&](int kt, int i) -> u32x4 {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs_w, vo_w, (i * (NT / 8) * K + kt * BK) * 2, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs_w, vo_w, (i * (NT / 8) * LW + kt * BK) * 2, 0);
   };
   auto load_x = [&](int kt, int i) -> u32x4 {
     return __builtin_amdgcn_raw_buffer_load_b128(rs_x, vo_x, (i * (NT / 8) * a.ldx + kt * BK) * 2, 0);

@@ -37,6 +37,7 @@ struct GemmArgs {
   int ng;
   int n, k;            // output columns, reduction length
   int ldx;             // input row stride (elements)
+  int ldw;             // weight row stride (elements); 0: k
   // EPI_STORE_F32: accumulate 0: out = acc, 1: out += alpha * acc, 2: out = alpha * acc
   // (columns >= n_store are computed but not stored when n_store > 0)
   float *out; int ldo; int accumulate; float alpha; int n_store;
@@ -102,10 +103,10 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
                         const float *const kn[3], Segs segs, float eps, hipStream_t s);
 // dst[i] = src[i] rounded to the 16-bit type (OP_BF16 / OP_F16), i < n
 hipError_t to_half(void *dst, int type, const float *src, int64_t n, hipStream_t s);
-// y[v][i] = sum_k W[i][k] * act(x[v][k]) for v < nvec (x, y contiguous [nvec][k|rows])
-// (silu_in: the vectors go through SiLU first, into scratch [nvec][k] fp32)
+// y[v * ldy + i] = sum_k W[i][k] * act(x[v][k]) for v < nvec (x contiguous [nvec][k];
+// ldy 0: rows).  silu_in: the vectors go through SiLU first, into scratch [nvec][k] fp32
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
-                int silu_in, float *scratch, hipStream_t s);
+                int silu_in, float *scratch, hipStream_t s, int ldy = 0);
 // e[v] = [cos(1000 t_v f_j), sin(1000 t_v f_j)], f_j = 10000^(-j/(dim/2)), 1 <= nvec <= 4
 hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s);
 hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,

@@ -416,7 +416,7 @@ __global__ void k_silu(float *dst, const float *src, int n) {
 
 template <typename TW>
 __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, int k,
-                                               const float *x, int nvec) {
+                                               const float *x, int nvec, int ldy) {
   extern __shared__ float xs[];  // [nvec][k]
   for (int i = threadIdx.x * 4; i < nvec * k; i += 256 * 4)
     *reinterpret_cast<f32x4 *>(xs + i) = *reinterpret_cast<const f32x4 *>(x + i);
@@ -464,14 +464,16 @@ __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, i
     for (int v = 0; v < 3; ++v) {
       if (v < nvec) {
         const float t = wave_sum(acc[r][v]);
-        if (lane == 0 && row0 + r < rows) y[(size_t)v * rows + row0 + r] = t;
+        if (lane == 0 && row0 + r < rows) y[(size_t)v * ldy + row0 + r] = t;
       }
     }
 }
 
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
-                int silu_in, float *scratch, hipStream_t s) {
+                int silu_in, float *scratch, hipStream_t s, int ldy) {
   if (nvec < 1 || nvec > 3 || k % 8 || k > 512 * kGemvChunks) return hipErrorInvalidValue;
+  if (ldy == 0) ldy = rows;
+  if (ldy < rows) return hipErrorInvalidValue;
   if (silu_in) {
     if (!scratch) return hipErrorInvalidValue;
     k_silu<<<(nvec * k + 255) / 256, 256, 0, s>>>(scratch, x, nvec * k);
@@ -480,9 +482,9 @@ hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const floa
   const size_t lds = sizeof(float) * nvec * k;
   const dim3 grid((rows + 4 * kGemvRows - 1) / (4 * kGemvRows));
   switch (w_type) {
-    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec); break;
-    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec); break;
-    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec); break;
+    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec, ldy); break;
+    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec, ldy); break;
+    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec, ldy); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

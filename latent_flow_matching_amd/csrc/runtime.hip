@@ -80,7 +80,7 @@ struct dit_ctx {
   void *vt = nullptr;        // [H][128][ldv] (16-bit paths)
   float *pos = nullptr;      // [rows_alloc][4]
   float *cs = nullptr;       // [rows_alloc][128]
-  float *modbuf = nullptr;   // [2][3][3][3D]
+  float *modbuf = nullptr;   // [2][3][3][mod_ld()]
   float *cond = nullptr;     // [3][D]
   float *temb_e = nullptr;   // [4][time_dim]: the three segment times, then the target time
   float *temb_h = nullptr;   // [4][D]
@@ -128,8 +128,12 @@ struct dit_ctx {
       out[0] = 0; out[1] = 1; out[2] = 2;
     }
   }
+  // sequentially wired double blocks carry two (shift, scale, gate) triples per vector
+  bool seq_block(int k) const { return k == 0 && cfg.double_wiring; }
+  int mod_rows(int k) const { return (seq_block(k) ? 6 : 3) * D(); }
+  int mod_ld() const { return (cfg.double_wiring ? 6 : 3) * D(); }
   float *mod_vec(int k, int set, int seg) const {
-    return modbuf + ((size_t)(k * 3 + set) * 3 + seg) * 3 * D();
+    return modbuf + ((size_t)(k * 3 + set) * 3 + seg) * mod_ld();
   }
 };
 
@@ -218,6 +222,9 @@ int validate_config(const dit_config *c) {
     return fail(DIT_EUNSUPPORTED, "txt_feat_dim must be 0 or a multiple of 64 up to 65536, got %d",
                 c->txt_feat_dim);
   if (c->flow_map != 0 && c->flow_map != 1) return fail(DIT_EINVAL, "flow_map must be 0 or 1");
+  if (c->double_wiring != 0 && c->double_wiring != 1) return fail(DIT_EINVAL, "double_wiring must be 0 or 1");
+  if (c->double_wiring && c->arch != DIT_FLUX2)
+    return fail(DIT_EUNSUPPORTED, "double_wiring applies to DIT_FLUX2 double blocks only");
   return 0;
 }
 
@@ -300,7 +307,8 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   if (c.txt_feat_dim > 0) want["txt_in"] = (int64_t)D * c.txt_feat_dim;
   const int nsets0 = c.arch == DIT_FLUX2 ? 2 : 3;
   if (c.n_stream_blocks > 0)
-    for (int s = 0; s < nsets0; ++s) want["mod.0.s" + std::to_string(s)] = (int64_t)3 * D * D;
+    for (int s = 0; s < nsets0; ++s)
+      want["mod.0.s" + std::to_string(s)] = (int64_t)(c.double_wiring ? 6 : 3) * D * D;
   if (c.n_shared_blocks > 0) want["mod.1.s0"] = (int64_t)3 * D * D;
   const int nb = c.n_stream_blocks + c.n_shared_blocks;
   for (int b = 0; b < nb; ++b) {
@@ -442,7 +450,7 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   if (ctx->op != OP_F32) rc = rc ? rc : dalloc(ctx, &ctx->vt, (size_t)c.heads * 128 * ctx->ldv * es);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->pos, R * 4 * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs, R * 128 * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (size_t)2 * 3 * 3 * 3 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (size_t)2 * 3 * 3 * ctx->mod_ld() * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cond, (size_t)3 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)4 * T * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)4 * D * 4);
@@ -492,27 +500,38 @@ Segs make_segs(int n_txt, int n_img, int n_ref, int nseq = 1) {
 int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) {
   const int D = ctx->D();
   for (int s = 0; s < ctx->nsets_kind(kind); ++s)
-    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, 3 * D, D, cond, 3, 1, ctx->act, stream),
+    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, ctx->mod_rows(kind), D, cond, 3, 1,
+                   ctx->act, stream, ctx->mod_ld()),
               "modulation gemv");
   return 0;
 }
 
+// One block on the residual x.  Parallel wiring: LayerNorm + modulation, linear1 (Q|K|V
+// and the SwiGLU MLP), QK RMSNorm + RoPE, attention, linear2 over [attention || SwiGLU]
+// with the gated residual.  Sequentially wired double blocks run the attention half
+// (linear1 over the Q|K|V rows, linear2 over W2's first D columns, gate 1), then a second
+// LayerNorm with the second (shift, scale) and the MLP half (linear1 over the gate/up
+// rows, linear2 over W2's last F columns, gate 2).
 int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = ctx->D(), F = ctx->F();
   const int kind = ctx->kind(b);
+  const bool seq = ctx->seq_block(kind);
   int sos[3];
   ctx->set_of_seg(kind, sos);
-  const float *mseg[3], *gate[3], *qn[3], *kn[3];
+  const float *mseg[3], *gate[3], *qn[3], *kn[3], *mseg2[3], *gate2[3];
   for (int s = 0; s < 3; ++s) {
     mseg[s] = ctx->mod_vec(kind, sos[s], s);
     gate[s] = mseg[s] + 2 * D;
+    mseg2[s] = mseg[s] + 3 * D;   // second triple: sequential blocks only
+    gate2[s] = mseg2[s] + 2 * D;
     qn[s] = ctx->blk[b][sos[s]].qn;
     kn[s] = ctx->blk[b][sos[s]].kn;
   }
   if (mask == DIT_MASK_DEFAULT) mask = (kind == 0 && c.arch == DIT_FLUX3) ? DIT_MASK_SEGMENT : DIT_MASK_FULL;
   const int N = sg.n;
   const size_t es = ctx->esz();
+  const bool mfma = ctx->op != OP_F32;
 
   const double es_d = (double)es;
   DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
@@ -542,7 +561,7 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   GemmArgs a1 = {};
   for (int i = 0; i < ng; ++i) a1.g[i] = g1[i];
   a1.ng = ng;
-  a1.n = 3 * D + 2 * F;
+  a1.n = seq ? 3 * D : 3 * D + 2 * F;
   a1.k = D;
   a1.ldx = D;
   a1.qkv = ctx->qkv;
@@ -551,8 +570,8 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   a1.cat = ctx->cat;
   a1.ldc = D + F;
   a1.cat_off = D;
-  const double fl1 = 2.0 * N * D * (3.0 * D + 2.0 * F);
-  if (ctx->op != OP_F32)
+  const double fl1 = 2.0 * N * D * (double)a1.n;
+  if (mfma)
     DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_mfma(a1, EPI_QKV_SWIGLU, ctx->op, stream), "linear1");
   else
     DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_simple(a1, EPI_QKV_SWIGLU, OP_F32, stream), "linear1");
@@ -591,30 +610,55 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   for (int i = 0; i < at.ng; ++i)
     pairs += (double)(at.g[i].q1 - at.g[i].q0) * (at.g[i].k1 - at.g[i].k0);
   const double fla = 4.0 * D * pairs;
-  if (ctx->op != OP_F32)
+  if (mfma)
     DIT_TIMED(P_ATTN, fla, 0.0, attention_mfma(at, ctx->op, stream), "attention");
   else
     DIT_TIMED(P_ATTN, fla, 0.0, attention_f32(at, stream), "attention");
 
-  GemmArgs a2 = {};
-  for (int i = 0; i < ng; ++i) a2.g[i] = g2[i];
-  a2.ng = ng;
-  a2.n = D;
-  a2.k = D + F;
-  a2.ldx = D + F;
-  a2.x = x;
-  a2.ldres = D;
-  for (int s = 0; s < 3; ++s) a2.gate[s] = gate[s];
-  a2.b1 = sg.b1;
-  a2.b2 = sg.b2;
-  a2.per = sg.per;
-  ctx->split_k(&a2);
-  const double fl2 = 2.0 * N * (double)(D + F) * D;
-  if (ctx->op != OP_F32)
-    DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
+  // linear2 with the gated residual over k columns of cat starting at column k0 (W2 columns
+  // k0 .. k0 + k of its D + F)
+  auto linear2 = [&](int k0, int k, const float *const gt[3]) -> int {
+    GemmArgs a2 = {};
+    for (int i = 0; i < ng; ++i) {
+      a2.g[i] = g2[i];
+      a2.g[i].x = (const char *)g2[i].x + (size_t)k0 * es;
+      a2.g[i].w = (const char *)g2[i].w + (size_t)k0 * es;
+    }
+    a2.ng = ng;
+    a2.n = D;
+    a2.k = k;
+    a2.ldx = D + F;
+    a2.ldw = D + F;
+    a2.x = x;
+    a2.ldres = D;
+    for (int s = 0; s < 3; ++s) a2.gate[s] = gt[s];
+    a2.b1 = sg.b1;
+    a2.b2 = sg.b2;
+    a2.per = sg.per;
+    ctx->split_k(&a2);
+    const double fl2 = 2.0 * N * (double)k * D;
+    if (mfma)
+      DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
+    else
+      DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_simple(a2, EPI_RESID, OP_F32, stream), "linear2");
+    return 0;
+  };
+  if (!seq) return linear2(0, D + F, gate);
+
+  // sequential double block: attention half, then the MLP half on the updated residual
+  if (int rc = linear2(0, D, gate)) return rc;
+  DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
+            ln_modulate(ctx->xm, ctx->op, D, x, D, N, 0, D, c.ln_eps, mseg2, sg, stream), "ln_modulate");
+  GemmArgs am = a1;
+  for (int i = 0; i < ng; ++i) am.g[i].w = (const char *)g1[i].w + (size_t)3 * D * D * es;  // gate/up rows
+  am.n = 2 * F;
+  am.split = 0;
+  const double flm = 2.0 * N * D * (2.0 * F);
+  if (mfma)
+    DIT_TIMED(P_LINEAR1, flm, 0.0, gemm_mfma(am, EPI_QKV_SWIGLU, ctx->op, stream), "linear1");
   else
-    DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_simple(a2, EPI_RESID, OP_F32, stream), "linear2");
-  return 0;
+    DIT_TIMED(P_LINEAR1, flm, 0.0, gemm_simple(am, EPI_QKV_SWIGLU, OP_F32, stream), "linear1");
+  return linear2(D, F, gate2);
 }
 
 int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref, int nseq = 1) {
@@ -1045,7 +1089,7 @@ extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dty
   if (!strcmp(name, "xm")) return ret(ctx->xm, dt, D);
   if (!strcmp(name, "qkv")) return ret(ctx->qkv, dt, 3 * D);
   if (!strcmp(name, "cat")) return ret(ctx->cat, dt, D + F);
-  if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, 3 * D);
+  if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, ctx->mod_ld());
   if (!strcmp(name, "x")) return ret(ctx->x, DIT_F32, D);
   return nullptr;
 }

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, 
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < a.k; k0 += TK) {
-    const TW *wp = W + (size_t)(n0 + lr) * a.k + k0 + lk;
+    const TW *wp = W + (size_t)(n0 + lr) * (a.ldw > 0 ? a.ldw : a.k) + k0 + lk;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ws[lk + e][lr] = to_f32(wp[e]);
     const int xr = m0 + lr;

@@ -28,7 +28,7 @@ class DitConfig(ctypes.Structure):
         "arch", "hidden", "heads", "head_dim", "mlp_hidden", "in_channels", "time_dim",
         "n_stream_blocks", "n_shared_blocks", "max_tokens", "compute")] + \
         [(n, ctypes.c_float) for n in ("rope_theta", "ln_eps", "rms_eps")] + \
-        [(n, ctypes.c_int) for n in ("txt_feat_dim", "flow_map")]
+        [(n, ctypes.c_int) for n in ("txt_feat_dim", "flow_map", "double_wiring")]
 
 
 class DitTensor(ctypes.Structure):
@@ -125,7 +125,7 @@ def make_config(cfg: ModelConfig, max_tokens: int) -> DitConfig:
     return DitConfig(cfg.arch, cfg.hidden, cfg.heads, cfg.head_dim, cfg.mlp_hidden,
                      cfg.in_channels, cfg.time_dim, cfg.n_stream_blocks, cfg.n_shared_blocks,
                      max_tokens, COMPUTE[cfg.compute], cfg.rope_theta, cfg.ln_eps,
-                     cfg.rms_eps, cfg.txt_feat_dim, int(cfg.flow_map))
+                     cfg.rms_eps, cfg.txt_feat_dim, int(cfg.flow_map), int(cfg.double_wiring))
 
 
 def _ptr(t):

@@ -47,6 +47,7 @@ class ModelConfig:
     rms_eps: float = 1e-6
     txt_feat_dim: int = 0        # > 0: text features of this width are projected by txt_in
     flow_map: bool = False       # timestep-distilled model with a target-time embedding
+    double_wiring: bool = False  # FLUX.2 double blocks: attention, then MLP (own LN and gate)
 
     @property
     def n_blocks(self) -> int:
@@ -169,7 +170,8 @@ def weight_specs(cfg: ModelConfig):
         if (kind == 0 and cfg.n_stream_blocks == 0) or (kind == 1 and cfg.n_shared_blocks == 0):
             continue
         for s in range(cfg.n_mod_sets(kind)):
-            specs.append((f"mod.{kind}.s{s}", (3 * d, d), "linear", (_G_MOD, kind, s)))
+            rows = 6 * d if (kind == 0 and cfg.double_wiring) else 3 * d
+            specs.append((f"mod.{kind}.s{s}", (rows, d), "linear", (_G_MOD, kind, s)))
     for b in range(cfg.n_blocks):
         for s in range(cfg.sets_of_block(b)):
             p = f"blk{b}.s{s}"

@@ -343,7 +343,8 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
 
 def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSet],
                              set_of_segment: tuple[int, int, int], mods6: list[np.ndarray],
-                             pos: np.ndarray, mask: int, dims: Dims):
+                             pos: np.ndarray, mask: int, dims: Dims,
+                             rows: np.ndarray | None = None):
     """A double-stream block wired in sequence (the FLUX.1-style reading of the pages' double
     blocks, the alternative to the parallel wiring of block_forward): attention first, then
     the MLP on the updated residual, each after its own modulated LayerNorm and with its own
@@ -351,7 +352,10 @@ def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: li
 
     reading: the same weight tensors as block_forward, used in two halves: W1's Q|K|V rows and
     W2's first D columns for attention, W1's gate/up rows and W2's last F columns for the
-    SwiGLU MLP."""
+    SwiGLU MLP.
+
+    rows: if given (sorted), only these output rows are computed ([len(rows), D]); the MLP
+    half is row-local, so it runs on those rows alone."""
     n, d = x.shape
     f = dims.mlp_hidden
     seg = segment_ids(*segs)
@@ -364,10 +368,15 @@ def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: li
                           np.concatenate([np.zeros((d, d)), ws.w2[:, d:]], axis=1), ws.qn, ws.kn)
                 for ws in sets]
     # attention half: zero gate/up rows give SiLU(0) * 0 = 0 for the MLP columns
-    x1 = block_forward(x, segs, attn_sets, set_of_segment, half1, pos, mask, dims)
+    x1 = block_forward(x, segs, attn_sets, set_of_segment, half1, pos, mask, dims, rows=rows)
     # MLP half: zero Q|K|V rows give uniform attention over V = 0, which W2's zeroed attention
     # columns drop anyway
-    return block_forward(x1, segs, mlp_sets, set_of_segment, half2, pos, mask, dims)
+    if rows is None:
+        return block_forward(x1, segs, mlp_sets, set_of_segment, half2, pos, mask, dims)
+    rows = np.asarray(rows)
+    assert np.all(np.diff(rows) > 0)
+    sub = tuple(int(np.sum(seg[rows] == s)) for s in range(3))
+    return block_forward(x1, sub, mlp_sets, set_of_segment, half2, pos[rows], mask, dims)
 
 
 # ----------------------------------------------------------------------------------------

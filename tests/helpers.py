@@ -58,6 +58,7 @@ def oracle_model(cfg, w) -> O.Model:
         m.temb_tgt_l1, m.temb_tgt_l2 = f64(w["temb_tgt.l1"]), f64(w["temb_tgt.l2"])
     if cfg.txt_feat_dim:
         m.txt_in = f64(w["txt_in"])
+    m.double_wiring = int(cfg.double_wiring)
     return m
 
 
@@ -65,8 +66,12 @@ def oracle_block(cfg, w, b, x, segs, pos, cond, mask=None, rows=None):
     """Oracle output of block b for residual x, conditioning rows cond[3], positions pos."""
     kind, sos, default_mask = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
     mods = O.segment_mods(oracle_mod_sets(cfg, w, kind), sos, [f64(c) for c in cond])
-    return O.block_forward(f64(x), segs, oracle_sets(cfg, w, b), sos, mods, f64(pos),
-                           default_mask if mask is None else mask, dims_of(cfg), rows=rows)
+    mask = default_mask if mask is None else mask
+    if cfg.double_wiring and kind == 0:
+        return O.block_forward_sequential(f64(x), segs, oracle_sets(cfg, w, b), sos, mods,
+                                          f64(pos), mask, dims_of(cfg), rows=rows)
+    return O.block_forward(f64(x), segs, oracle_sets(cfg, w, b), sos, mods, f64(pos), mask,
+                           dims_of(cfg), rows=rows)
 
 
 def rel_err(got, ref) -> float:

@@ -606,6 +606,70 @@ def test_forward_full_width_split_head_matches_oracle():
     assert err <= BF16_TOL
 
 
+# ----------------------------------------------------------------- sequentially wired double blocks
+
+SEQ = [replace(TINY2, double_wiring=True), replace(TINY2, double_wiring=True, compute="bf16"),
+       replace(TINY2, double_wiring=True, bf16=False, compute="f32")]
+
+
+@pytest.mark.parametrize("cfg", SEQ, ids=["f16", "bf16", "f32"])
+@pytest.mark.parametrize("b", [0, 1], ids=["double", "single"])
+@pytest.mark.parametrize("segs", [(37, (9, 11), (5, 6)), (0, (3, 5), None), (300, (1, 1), None)],
+                         ids=["ragged_ref", "no_text", "one_image_token"])
+def test_sequential_block_matches_oracle(cfg, b, segs):
+    """Double block wired attention-then-MLP (second LayerNorm, six modulation vectors per set,
+    W1 and W2 used in halves) against the oracle's sequential block; the single block of the
+    same model keeps the parallel form."""
+    n_txt, grid, ref_grid = segs
+    err, _ = run_block(cfg, b, n_txt, grid, ref_grid, stages=False)
+    assert err <= tol(cfg)
+
+
+@pytest.mark.parametrize("cfg", SEQ, ids=["f16", "bf16", "f32"])
+def test_sequential_forward_matches_oracle(cfg):
+    err = _forward_case(cfg, 50, (9, 7), (6, 5), 0.75)
+    print(f"sequential forward err {err:.3e}")
+    assert err <= tol(cfg, full_width=False)
+
+
+def test_sequential_denoise_cfg_matches_oracle():
+    cfg = SEQ[0]
+    ctx, w = context(cfg, 600)
+    grid = (8, 6)
+    noise = S.gen_latents(48, cfg.in_channels, key=(2,))
+    _, ref, txt, txt_u = _cfg_inputs(cfg, 20, grid, (4, 4))
+    lat = dev(noise)
+    print("[denoise_cfg] sequential double blocks", flush=True)
+    ctx.denoise_cfg(lat, dev(txt), dev(txt_u), grid, 3, 2.5, -1, dev(ref), (4, 4))
+    torch.cuda.synchronize()
+    want = O.denoise_cfg(oracle_model(cfg, w), f64(noise), f64(txt), f64(txt_u), grid, 3, 2.5,
+                         f64(ref), (4, 4))
+    err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
+    print(f"    sequential denoise_cfg update err {err:.3e}", flush=True)
+    assert err <= BF16_TOL
+
+
+def test_sequential_wiring_config_checks():
+    """double_wiring is for FLUX.2 double blocks only, and its stream modulation is [6D, D]."""
+    from latent_flow_matching_amd import dit
+    bad = replace(TINY3, double_wiring=True)
+    with pytest.raises(dit.DitError, match="double_wiring"):
+        dit.DiT(bad, gpu_weights(bad, S.gen_weights(bad)), 64)
+    w = gpu_weights(TINY2, S.gen_weights(TINY2))   # parallel-wiring modulation shapes
+    with pytest.raises(dit.DitError, match="mod.0.s0"):
+        dit.DiT(SEQ[0], w, 64)
+
+
+@pytest.mark.parametrize("n_img,grid", [(4096, (64, 64)), (1024, (32, 32))], ids=["4096img", "1024img"])
+def test_sequential_block_full_width_sampled_rows(n_img, grid):
+    """Full-width sequential double block at 512 text tokens: at 1024 image tokens both
+    linear2 halves fill few compute units and run as k-slices over their column ranges of W2."""
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1, double_wiring=True)
+    n = 512 + n_img
+    err, _ = run_block(cfg, 0, 512, grid, rows=_rows(n), max_tokens=n, stages=False)
+    assert err <= BF16_TOL
+
+
 # ----------------------------------------------------------------- full benchmark shapes, sampled rows
 
 def _rows(n, k=24, seed=0):

@@ -313,6 +313,11 @@ def test_sequential_block_matches_library_composition(sos, segs):
     z = [np.concatenate([m[:2 * dims.hidden], np.zeros(dims.hidden), m[3 * dims.hidden:5 * dims.hidden],
                          np.zeros(dims.hidden)]) for m in mods6]
     np.testing.assert_array_equal(O.block_forward_sequential(x, segs, sets, sos, z, pos, O.MASK_FULL, dims), x)
+    # sampled rows (text, image and reference rows among them) equal those rows of the full block
+    rows = np.array([0, segs[0], n - 1])
+    np.testing.assert_allclose(
+        O.block_forward_sequential(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims, rows=rows),
+        ref[rows], rtol=0, atol=1e-11)
 
 
 def test_block_gate_zero_is_identity():
