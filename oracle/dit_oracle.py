@@ -260,9 +260,92 @@ class WeightSet:
     kn: np.ndarray
 
 
+# ----------------------------------------------------------------------------------------
+# Row-wise FP8 ("fp8r") projections.  The FLUX.3 transformer ships as single-file weights in
+# row-wise FP8 ([KS] "Was sich geändert hat"); GPUs with fast FP8 kernels compute with them,
+# others dequantize the weights at every step ([WE] "Hardwareanforderungen, Quantisierung und
+# Inferenzlatenz").
+# reading: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+# value 448; no infinities).  One scale per row: per output feature for a weight, per token
+# for an activation; scale = max|row| / 448, code = value / scale rounded to the nearest E4M3
+# value, ties to even mantissa, saturating at +-448; a row of zeros has scale 0 and codes 0.
+# The scale and the quotient are formed in fp32 (the kernel's precision) so that both sides
+# take the same rounding decisions.  A projection y = x W^T then equals
+# scale_x scale_w sum_k code_x code_w.  Only the two big projections of every block (W1, W2)
+# and their inputs (the modulated LayerNorm output and [attention || SwiGLU]) use it.
+# ----------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value of each element (float64 in, float64 out), ties to even mantissa,
+    magnitudes beyond 448 saturate to 448.  Normal values have a quantum of 2^(e-3) in
+    binade [2^e, 2^(e+1)), e >= -6; below 2^-6 the subnormal quantum is 2^-9."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)                       # a = m 2^ex, m in [0.5, 1): binade e = ex - 1
+    e = np.maximum(ex.astype(np.float64) - 1.0, -6.0)
+    quantum = np.exp2(e - 3.0)
+    r = np.round(a / quantum) * quantum       # np.round: half to even; a / quantum is exact
+    r = np.minimum(r, E4M3_MAX)
+    return np.copysign(r, v)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """uint8 codes of values already on the E4M3 grid (|v| <= 448)."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    sign = (np.signbit(v)).astype(np.uint8) << 7
+    _, ex = np.frexp(a)
+    e = ex - 1
+    normal = a >= 2.0 ** -6
+    mant_n = np.where(normal, a / np.exp2(np.where(normal, e, 0)) * 8 - 8, 0)
+    code_n = ((e + 7) << 3) + mant_n.astype(np.int64)
+    code_s = (a / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, code_s).astype(np.uint8)
+    return code | sign
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """float64 values of uint8 E4M3 codes; the two NaN codes (exponent and mantissa all ones)
+    give NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def quantize_rows_fp8(x: np.ndarray):
+    """(codes uint8 [rows, cols], scales float32 [rows]) of the row-wise E4M3 quantization."""
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    q = (x32 / safe[:, None]).astype(np.float32)
+    q = np.where(scale[:, None] > 0, q, np.float32(0))
+    return e4m3_encode(e4m3_round(q.astype(np.float64))), scale
+
+
+def fp8_round_rows(x: np.ndarray) -> np.ndarray:
+    """The values a row-wise E4M3 operand stands for: code * scale, per row (float64)."""
+    codes, scale = quantize_rows_fp8(x)
+    return e4m3_decode(codes) * scale.astype(np.float64)[:, None]
+
+
+def quantize_weights_fp8(sets: list[WeightSet]) -> list[WeightSet]:
+    """W1 and W2 of every weight set replaced by their row-wise E4M3 values (rows = output
+    features); the RMSNorm scales stay as they are."""
+    return [WeightSet(fp8_round_rows(ws.w1), fp8_round_rows(ws.w2), ws.qn, ws.kn) for ws in sets]
+
+
 def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSet],
                   set_of_segment: tuple[int, int, int], mods: list[np.ndarray],
-                  pos: np.ndarray, mask: int, dims: Dims, rows: np.ndarray | None = None):
+                  pos: np.ndarray, mask: int, dims: Dims, rows: np.ndarray | None = None,
+                  act_fp8: bool = False):
     """One block: x + gate_s * ([attn || SwiGLU](adaLN(LN(x))) . W2^T).
 
     x: [N, D] residual; segs = (n_txt, n_img, n_ref), segments contiguous in the order text,
@@ -279,7 +362,11 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     F columns) * (second F columns).
 
     rows: if given, only these output rows are computed (keys/values still use all rows);
-    returns [len(rows), D].  Used to check sampled rows at full size."""
+    returns [len(rows), D].  Used to check sampled rows at full size.
+
+    act_fp8: the inputs of the two projections (the modulated LayerNorm output, and
+    [attention || SwiGLU]) go through the row-wise E4M3 quantization first (the fp8r path;
+    the weights are expected in their E4M3 values already, quantize_weights_fp8)."""
     n, d = x.shape
     nh, hd, f = dims.heads, dims.head_dim, dims.mlp_hidden
     seg = segment_ids(*segs)
@@ -293,6 +380,8 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
             continue
         shift, scale, _ = split_modulation(mods[s], d)
         xm[sel] = y[sel] * (1.0 + scale) + shift
+    if act_fp8:
+        xm = fp8_round_rows(xm)
     # fused projection per weight set
     h = np.empty((n, 3 * d + 2 * f))
     for s in range(3):
@@ -332,6 +421,8 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
         o[:, hh, :] = p @ v[:, hh, :]
     m = silu(g[rows]) * u[rows]
     cat = np.concatenate([o.reshape(rows.shape[0], d), m], axis=1)
+    if act_fp8:
+        cat = fp8_round_rows(cat)
     out = x[rows].copy()
     for s in range(3):
         sel = seg[rows] == s
@@ -344,7 +435,7 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
 def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSet],
                              set_of_segment: tuple[int, int, int], mods6: list[np.ndarray],
                              pos: np.ndarray, mask: int, dims: Dims,
-                             rows: np.ndarray | None = None):
+                             rows: np.ndarray | None = None, act_fp8: bool = False):
     """A double-stream block wired in sequence (the FLUX.1-style reading of the pages' double
     blocks, the alternative to the parallel wiring of block_forward): attention first, then
     the MLP on the updated residual, each after its own modulated LayerNorm and with its own
@@ -355,7 +446,9 @@ def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: li
     SwiGLU MLP.
 
     rows: if given (sorted), only these output rows are computed ([len(rows), D]); the MLP
-    half is row-local, so it runs on those rows alone."""
+    half is row-local, so it runs on those rows alone.  act_fp8 as in block_forward: each
+    half quantizes its own projection inputs (the zero columns of the other half change no
+    row maximum)."""
     n, d = x.shape
     f = dims.mlp_hidden
     seg = segment_ids(*segs)
@@ -368,15 +461,18 @@ def block_forward_sequential(x: np.ndarray, segs: tuple[int, int, int], sets: li
                           np.concatenate([np.zeros((d, d)), ws.w2[:, d:]], axis=1), ws.qn, ws.kn)
                 for ws in sets]
     # attention half: zero gate/up rows give SiLU(0) * 0 = 0 for the MLP columns
-    x1 = block_forward(x, segs, attn_sets, set_of_segment, half1, pos, mask, dims, rows=rows)
+    x1 = block_forward(x, segs, attn_sets, set_of_segment, half1, pos, mask, dims, rows=rows,
+                       act_fp8=act_fp8)
     # MLP half: zero Q|K|V rows give uniform attention over V = 0, which W2's zeroed attention
     # columns drop anyway
     if rows is None:
-        return block_forward(x1, segs, mlp_sets, set_of_segment, half2, pos, mask, dims)
+        return block_forward(x1, segs, mlp_sets, set_of_segment, half2, pos, mask, dims,
+                             act_fp8=act_fp8)
     rows = np.asarray(rows)
     assert np.all(np.diff(rows) > 0)
     sub = tuple(int(np.sum(seg[rows] == s)) for s in range(3))
-    return block_forward(x1, sub, mlp_sets, set_of_segment, half2, pos[rows], mask, dims)
+    return block_forward(x1, sub, mlp_sets, set_of_segment, half2, pos[rows], mask, dims,
+                         act_fp8=act_fp8)
 
 
 # ----------------------------------------------------------------------------------------
@@ -461,6 +557,7 @@ class Model:
     temb_tgt_l2: np.ndarray | None = None   # [D, D]
     txt_in: np.ndarray | None = None        # [D, 8 * 2560]  text-feature projection
     double_wiring: int = 0                  # FLUX.2 double blocks: 0 parallel, 1 sequential
+    fp8: bool = False                       # row-wise E4M3 block projections (fp8r)
 
 
 # ----------------------------------------------------------------------------------------
@@ -524,9 +621,10 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
             block_hook(b, x)
         if model.arch == ARCH_FLUX2 and kind == 0 and model.double_wiring:
             x = block_forward_sequential(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos,
-                                         mask, dims)
+                                         mask, dims, act_fp8=model.fp8)
         else:
-            x = block_forward(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos, mask, dims)
+            x = block_forward(x, (n_txt, n_img, n_ref), model.blocks[b], sos, mods, pos, mask, dims,
+                              act_fp8=model.fp8)
     return final_layer(x[n_txt:n_txt + n_img], conds[1], model.final_mod, model.final_out,
                        dims.ln_eps)
 

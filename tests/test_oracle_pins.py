@@ -215,15 +215,17 @@ def test_attention_invariants():
 
 # ------------------------------------------------------------------ one block
 
-def torch_block(x, segs, sets, sos, mods, pos, mask, dims):
-    """Independent composition of torch float64 library routines for one block."""
+def torch_block(x, segs, sets, sos, mods, pos, mask, dims, act=None):
+    """Independent composition of torch float64 library routines for one block; act (if
+    given) is applied to the inputs of both projections."""
+    act = act or (lambda t: t)
     d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
     seg = torch.tensor(O.segment_ids(*segs))
     n = x.shape[0]
     X = torch.tensor(x)
     M = torch.stack([torch.tensor(mods[int(s)]) for s in seg])          # [n, 3D]
     shift, scale, gate = M[:, :d], M[:, d:2 * d], M[:, 2 * d:]
-    xm = F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + scale) + shift
+    xm = act(F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + scale) + shift)
     W1 = torch.stack([torch.tensor(sets[sos[int(s)]].w1) for s in seg])  # [n, 3D+2F, D]
     h = torch.einsum("nk,nok->no", xm, W1)
     q, k, v = h[:, :d].reshape(n, nh, hd), h[:, d:2 * d].reshape(n, nh, hd), h[:, 2 * d:3 * d].reshape(n, nh, hd)
@@ -237,7 +239,7 @@ def torch_block(x, segs, sets, sos, mods, pos, mask, dims):
     o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
                                        attn_mask=am).transpose(0, 1).reshape(n, d)
     g, u = h[:, 3 * d:3 * d + f], h[:, 3 * d + f:]
-    cat = torch.cat([o, F.silu(g) * u], dim=1)
+    cat = act(torch.cat([o, F.silu(g) * u], dim=1))
     W2 = torch.stack([torch.tensor(sets[sos[int(s)]].w2) for s in seg])
     return (X + gate * torch.einsum("nk,nok->no", cat, W2)).numpy()
 
@@ -264,10 +266,11 @@ def test_block_matches_library_composition(mask, sos, segs):
                                got[rows], rtol=0, atol=1e-12)
 
 
-def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims):
+def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims, act=None):
     """Independent torch float64 composition of a sequentially wired double block: attention
     with (shift1, scale1, gate1), then the SwiGLU MLP on the updated residual with (shift2,
-    scale2, gate2)."""
+    scale2, gate2); act (if given) is applied to the inputs of each projection."""
+    act = act or (lambda t: t)
     d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
     seg = torch.tensor(O.segment_ids(*segs))
     n = x.shape[0]
@@ -276,7 +279,7 @@ def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims):
     sh1, sc1, g1, sh2, sc2, g2 = (M[:, i * d:(i + 1) * d] for i in range(6))
     W1 = torch.stack([torch.tensor(sets[sos[int(s)]].w1) for s in seg])  # [n, 3D+2F, D]
     W2 = torch.stack([torch.tensor(sets[sos[int(s)]].w2) for s in seg])  # [n, D, D+F]
-    xm = F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + sc1) + sh1
+    xm = act(F.layer_norm(X, (d,), eps=dims.ln_eps) * (1 + sc1) + sh1)
     h = torch.einsum("nk,nok->no", xm, W1[:, :3 * d])
     q, k, v = h[:, :d].reshape(n, nh, hd), h[:, d:2 * d].reshape(n, nh, hd), h[:, 2 * d:].reshape(n, nh, hd)
     qw = torch.stack([torch.tensor(sets[sos[int(s)]].qn) for s in seg])[:, None, :]
@@ -286,10 +289,10 @@ def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims):
     am = None if mask == O.MASK_FULL else (seg[:, None] == seg[None, :])
     o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
                                        attn_mask=am).transpose(0, 1).reshape(n, d)
-    X1 = X + g1 * torch.einsum("nk,nok->no", o, W2[:, :, :d])
-    xm2 = F.layer_norm(X1, (d,), eps=dims.ln_eps) * (1 + sc2) + sh2
+    X1 = X + g1 * torch.einsum("nk,nok->no", act(o), W2[:, :, :d])
+    xm2 = act(F.layer_norm(X1, (d,), eps=dims.ln_eps) * (1 + sc2) + sh2)
     gu = torch.einsum("nk,nok->no", xm2, W1[:, 3 * d:])
-    m = F.silu(gu[:, :f]) * gu[:, f:]
+    m = act(F.silu(gu[:, :f]) * gu[:, f:])
     return (X1 + g2 * torch.einsum("nk,nok->no", m, W2[:, :, d:])).numpy()
 
 
@@ -683,6 +686,122 @@ def test_noise_distribution_and_prefix():
     assert not np.array_equal(O.noise(64, 42), O.noise(64, 42 + (1 << 32)))
 
 
+# ------------------------------------------------------------------ row-wise FP8 (fp8r)
+
+def torch_fp8_rows(X):
+    """Row-wise E4M3 values through torch's float8_e4m3fn conversion (round to nearest even),
+    independent of the oracle's rounding code."""
+    X32 = X.to(torch.float32)
+    s = X32.abs().amax(dim=1, keepdim=True) / 448.0
+    q = torch.where(s > 0, X32 / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(X32))
+    return q.to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
+
+
+def _e4m3_torch(v):
+    return torch.tensor(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_library():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.tensor(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert np.nanmax(got) == 448.0 and np.sum(np.isnan(got)) == 2
+    # encoding the finite values gives their codes back (-0 included)
+    np.testing.assert_array_equal(O.e4m3_encode(got[ok]), codes[ok])
+
+
+def test_e4m3_round_matches_library():
+    r = rng(70)
+    mag = np.exp2(r.uniform(-12, np.log2(448), 20000))
+    v = (mag * r.choice([-1, 1], mag.size)).astype(np.float32).astype(np.float64)
+    # every code value and every midpoint of neighbouring positive codes, both signs
+    grid = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    v = np.concatenate([v, grid, -grid, mids, -mids])
+    np.testing.assert_array_equal(O.e4m3_round(v), _e4m3_torch(v))
+
+
+def test_e4m3_round_closed_forms():
+    v = np.array([464.0, 465.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6 - 2.0 ** -10,
+                  17.0, 18.0, 19.0, 0.0])
+    want = np.array([448.0, 448.0, 448.0, -448.0, 0.0, 2.0 ** -8, 2.0 ** -6,
+                     16.0, 18.0, 20.0, 0.0])
+    np.testing.assert_array_equal(O.e4m3_round(v), want)
+
+
+def test_quantize_rows_fp8_properties():
+    r = rng(71)
+    x = r.normal(size=(6, 300)) * np.array([1e-3, 1, 50, 3e4, 1, 1])[:, None]
+    x[4] = 0.0
+    codes, scale = O.quantize_rows_fp8(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    # the largest magnitude of each row lands on +-448; a zero row has scale 0 and codes 0
+    for i in (0, 1, 2, 3, 5):
+        j = np.argmax(np.abs(x[i]))
+        assert codes[i, j] & 0x7F == 0x7E
+    assert scale[4] == 0 and not codes[4].any()
+    # a power-of-two factor changes the scale only
+    c2, s2 = O.quantize_rows_fp8(x * 2.0 ** 7)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, scale * np.float32(2.0 ** 7))
+    # each value is within half an E4M3 step (relative 2^-4, or 2^-10 of the scale) of x
+    xr = O.fp8_round_rows(x)
+    sc = scale.astype(np.float64)[:, None]
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(xr - x) <= bound)
+    np.testing.assert_array_equal(xr, torch_fp8_rows(torch.tensor(x)).numpy())
+
+
+def test_fp8_projection_error_bound():
+    """x W^T through row-wise E4M3 stays within the first-order bound of the two roundings."""
+    r = rng(72)
+    x, w = r.normal(size=(9, 256)), r.normal(0, 0.05, size=(40, 256))
+    xr, wr = O.fp8_round_rows(x), O.fp8_round_rows(w)
+    err = np.abs(xr @ wr.T - x @ w.T)
+    bound = np.abs(xr - x) @ np.abs(w).T + np.abs(xr) @ np.abs(wr - w).T
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-12)
+    assert err.max() > 0
+
+
+@pytest.mark.parametrize("sequential", [False, True], ids=["parallel", "sequential"])
+def test_fp8_block_matches_library_composition(sequential):
+    r = rng(73)
+    dims = TINY
+    segs = (5, 4, 3)
+    sos = (0, 1, 1)
+    n = sum(segs)
+    sets = [rand_set(r, dims) for _ in range(2)]
+    x = r.normal(size=(n, dims.hidden))
+    pos = O.positions(segs[0], (2, 2), ((3, 1),))
+    q_or = O.quantize_weights_fp8(sets)
+    q_t = [O.WeightSet(torch_fp8_rows(torch.tensor(ws.w1)).numpy(),
+                       torch_fp8_rows(torch.tensor(ws.w2)).numpy(), ws.qn, ws.kn) for ws in sets]
+    if sequential:
+        mods6 = [np.concatenate([a, b]) for a, b in zip(rand_mods(r, dims), rand_mods(r, dims))]
+        got = O.block_forward_sequential(x, segs, q_or, sos, mods6, pos, O.MASK_FULL, dims, act_fp8=True)
+        ref = torch_sequential_block(x, segs, q_t, sos, mods6, pos, O.MASK_FULL, dims, act=torch_fp8_rows)
+        plain = O.block_forward_sequential(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims)
+    else:
+        mods = rand_mods(r, dims)
+        got = O.block_forward(x, segs, q_or, sos, mods, pos, O.MASK_FULL, dims, act_fp8=True)
+        ref = torch_block(x, segs, q_t, sos, mods, pos, O.MASK_FULL, dims, act=torch_fp8_rows)
+        plain = O.block_forward(x, segs, sets, sos, mods, pos, O.MASK_FULL, dims)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    # the E4M3 rounding is visible but small against the unquantized block
+    d = np.abs(got - plain).max() / np.abs(plain - x).max()
+    assert 1e-3 < d < 0.2
+
+
+def _per_tensor_quantize(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    s = np.float32(np.max(np.abs(x32)) / np.float32(448.0))
+    q = (x32 / s).astype(np.float32)
+    return O.e4m3_encode(O.e4m3_round(q.astype(np.float64))), np.full(x32.shape[0], s, np.float32)
+
+
 def _wrong_layer_norm(x, eps):
     return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + eps + 1e-3)
 
@@ -726,6 +845,11 @@ def test_pins_catch_planted_slips(monkeypatch):
     monkeypatch.setattr(O, "block_forward_sequential", parallel_halves)
     with pytest.raises(AssertionError):
         test_sequential_block_matches_library_composition((0, 1, 1), (5, 4, 3))
+    monkeypatch.undo()
+    # one scale per tensor instead of one per row
+    monkeypatch.setattr(O, "quantize_rows_fp8", _per_tensor_quantize)
+    with pytest.raises(AssertionError):
+        test_fp8_block_matches_library_composition(False)
     monkeypatch.undo()
     # guidance with the branches swapped
     monkeypatch.setattr(O, "guided_velocity", lambda vc, vu, g: vc + g * (vu - vc))
