@@ -45,8 +45,17 @@ typedef struct dit_ctx dit_ctx;
  *   DIT_F16   fp16 MFMA operands and activations (bf16 weights are held exactly, up to the
  *             fp16 subnormal grid below 2^-14), fp32 accumulation, fp32 residual; same MFMA
  *             rate as bf16 on gfx950 with 8x finer operand rounding; activations saturate at
- *             +-65504 */
-enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2 };
+ *             +-65504
+ *   DIT_FP8   row-wise FP8 ("fp8r": "FLUX.3 Image Klein: offene Gewichte ...", "Was sich
+ *             geändert hat"; we0.ai "FLUX 3 Image Klein" article, "Hardwareanforderungen,
+ *             Quantisierung und Inferenzlatenz") for the two big projections of every block:
+ *             W1 and W2 are held as OCP E4M3 codes with one fp32 scale per row (quantized at
+ *             dit_ctx_create from the given values), their inputs (the modulated LayerNorm
+ *             output, [attention || SwiGLU]) are quantized per token on the fly, and the
+ *             products run on the E4M3 MFMA at twice the 16-bit rate.  Scale = max |row| / 448,
+ *             code = value / scale rounded to nearest even E4M3.  Everything else computes as
+ *             DIT_F16. */
+enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2, DIT_FP8 = 3 };
 
 /* model families.
  * DIT_FLUX2: n_stream_blocks double-stream blocks (separate text / image weights, joint
@@ -78,7 +87,7 @@ typedef struct {
   int n_stream_blocks;  /* double (FLUX2) or per-mode (FLUX3) blocks        (5)    */
   int n_shared_blocks;  /* single (FLUX2) or joint (FLUX3) blocks           (20/28) */
   int max_tokens;       /* largest N any call will use (sizes the workspace)       */
-  int compute;          /* DIT_F16, DIT_BF16 or DIT_F32 (see above)                 */
+  int compute;          /* DIT_F16, DIT_BF16, DIT_F32 or DIT_FP8 (see above)        */
   float rope_theta;     /* RoPE base (10000)      */
   float ln_eps;         /* LayerNorm epsilon (1e-6) */
   float rms_eps;        /* QK RMSNorm epsilon (1e-6) */
@@ -257,13 +266,30 @@ int dit_denoise_ex(dit_ctx *ctx, const dit_request *request, float *lat, int n_s
 /* Fill dst (dev fp32, n elements) with the N(0,1) noise dit_denoise draws for seed. */
 int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
 
+/* Row-wise FP8 building blocks of DIT_FP8, on caller-owned device buffers (no context):
+ * dit_quantize_rows_fp8: scale[r] = max_c |x[r][c]| / 448 (fp32), q[r][c] = E4M3 code of
+ *   x[r][c] / scale[r], rounded to nearest even, saturating at 448; a zero row gets scale 0
+ *   and codes 0.  x dev fp32 [rows][ldx], q dev uint8 [rows][ldq], scale dev fp32 [rows];
+ *   cols, ldx, ldq multiples of 8.
+ * dit_gemm_fp8: y[i][j] = sx[i] * sw[j] * sum_k qx[i][k] * qw[j][k] (fp32), the E4M3 MFMA
+ *   product: qx dev uint8 [m][ldx] (rows readable up to m rounded up to 256), sx [m],
+ *   qw dev uint8 [n][ldw], sw [n], y dev fp32 [m][ldy]; n % 256 == 0, k % 128 == 0, ldx and
+ *   ldw multiples of 16, ldy of 4.  The MFMA truncates products more than about 12 bits
+ *   below the largest one of its group of k, so results differ from the exact sum by a few
+ *   units of 2^-12 of the largest products. */
+int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx, uint8_t *q, int ldq,
+                          float *scale, void *stream);
+int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
+                 const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream);
+
 /* Workspace buffer of the last call, for inspection after the stream has finished:
  * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
  * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32
  * [2][3][3][R]: kind, set, segment, shift || scale || gate, R = 3D, or 6D with
  * double_wiring = 1, whose stream-block rows hold both halves), "x" (fp32 [N, D], the
  * residual stream of dit_forward / dit_denoise after the last block).  *dtype receives
- * the element type (compute type for xm, qkv, cat; DIT_F32 for mod and x); *row_stride the
+ * the element type (compute type for xm, qkv, cat; DIT_F32 for mod and x; with DIT_FP8, xm
+ * holds E4M3 codes (DIT_FP8) and qkv, cat are DIT_F16); *row_stride the
  * elements per row.  NULL for an unknown name. */
 const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t *row_stride);
 

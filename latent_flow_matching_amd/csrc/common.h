@@ -92,6 +92,24 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// OCP E4M3 code of q (round to nearest, ties to even mantissa; magnitudes beyond 448
+// saturate to 448).  Normal binade [2^e, 2^(e+1)), e >= -6, has 8 steps of 2^(e-3); below
+// 2^-6 the step is 2^-9.  Scaling by powers of two is exact, so rintf does the rounding.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is 2^-6 = code 0x08
+  } else {
+    const int e = (int)(__float_as_uint(a) >> 23) - 127;
+    const float m = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));  // 8..16
+    code = (uint32_t)((e + 7) << 3) + (uint32_t)m - 8u;  // m = 16 carries into the exponent
+    code = min(code, 0x7Eu);
+  }
+  return code | sign;
+}
+
 // Segment (0 text, 1 image, 2 reference) of token row m given the two boundaries.
 __device__ __forceinline__ int segment_of(int m, int b1, int b2) {
   return (m >= b1) + (m >= b2);

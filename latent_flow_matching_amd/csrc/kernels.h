@@ -7,6 +7,8 @@ namespace dit {
 
 // Element types of activations / weights (same codes as the C ABI's compute types).
 enum ElemType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
+// Row-wise OCP E4M3 codes (one byte per value) with one fp32 scale per row.
+constexpr int OP_FP8 = 3;
 
 // Token rows: one or two sequences of per rows each (the conditional and unconditional
 // branches of classifier-free guidance), each ordered text [0, b1) | image [b1, b2) |
@@ -24,6 +26,7 @@ struct GemmGroup {
   const void *w;   // weights [N, K] row-major
   int rows;        // rows in the group
   int out_row0;    // token index of the first row (output row; segment lookup)
+  const float *ws = nullptr;  // FP8 GEMM: scale of each weight row (output feature)
 };
 
 enum Epilogue {
@@ -50,6 +53,8 @@ struct GemmArgs {
   // its fp32 partial tile to part (room for part_tiles tiles of 256 x 256), and a second kernel
   // adds the slices in slice order and applies the epilogue.  split_grid = 0: never.
   float *part; int part_tiles; int split_grid;
+  // FP8 GEMM: scale of each input row, indexed by token (out_row0 + row)
+  const float *xs;
 };
 // floats per 256 x 256 partial tile of the split-K GEMM
 constexpr int gemm_part_floats = 256 * 256;
@@ -57,6 +62,14 @@ constexpr int gemm_part_floats = 256 * 256;
 // MFMA GEMM: input and weights of 16-bit type op (OP_BF16 / OP_F16), fp32 accumulation.
 // n % 256 == 0, k % 64 == 0, input rows readable up to 256 past each group's end.
 hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s);
+// Row-wise FP8 GEMM: E4M3 inputs and weights (ldx, ldw, k in bytes), out = xs[token] *
+// ws[feature] * acc, then the epilogue (16-bit stores are fp16).  n % 256 == 0, k % 128 == 0,
+// ldx and the weight row stride multiples of 16.
+hipError_t gemm_fp8(const GemmArgs &a, int epi, hipStream_t s);
+// q[r][c] = E4M3 code of src[r][c] / scale[r], scale[r] = max_c |src[r][c]| / 448 (fp32),
+// for r < rows, c < cols; src of type src_type (OP_F32 / OP_BF16 / OP_F16); cols % 8 == 0.
+hipError_t quant_rows_fp8(uint8_t *q, int ldq, float *scale, const void *src, int src_type, int lds,
+                          int rows, int cols, hipStream_t s);
 // fp32-accumulating general GEMM with fp32 inputs and weights of type w_type.
 // n % 64 == 0, k % 16 == 0; any rows; input rows are not read past a group's end.
 hipError_t gemm_simple(const GemmArgs &a, int epi, int w_type, hipStream_t s);
@@ -93,9 +106,11 @@ hipError_t fill_positions(float *pos, int n_txt, int gh, int gw, const int *ref_
                           int n_refs, hipStream_t s);
 hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream_t s);
 // out[r] = LN(x[r]) * (1 + scale_seg) + shift_seg, mod_seg[s] = [shift | scale | ...]
+// out_type OP_FP8: E4M3 codes with the row scales in out_scale[r] (row-wise quantization of
+// the modulated row).
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
                        int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
-                       hipStream_t s);
+                       hipStream_t s, float *out_scale = nullptr);
 // q, k of every (token, head): RMSNorm with the segment's scale, then RoPE, in place;
 // 16-bit paths also write V transposed into vt (and zeros for columns [n, n+64)).
 hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, void *vt, int ldv,

@@ -96,8 +96,9 @@ template <typename TO>
 __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const float *x, int ldx,
                                                       int row0, int d, float eps,
                                                       const float *m0, const float *m1,
-                                                      const float *m2, int b1, int b2, int per) {
-  __shared__ float red[2][4];
+                                                      const float *m2, int b1, int b2, int per,
+                                                      float *out_scale) {
+  __shared__ float red[3][4];
   const int t = threadIdx.x, w = t >> 6;
   const int r = blockIdx.x, tok = row0 + r;
   const int nv4 = d >> 2;  // float4 columns; a multiple of 64, so each wave is all in or all out
@@ -135,34 +136,67 @@ __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const flo
   const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)d;
   const float rstd = 1.0f / sqrtf(var + eps);
   TO *orow = out + (size_t)r * ldo;
+  if constexpr (sizeof(TO) == 1) {
+    // E4M3 codes of the modulated row with one scale: max |y| / 448
+    float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i)
-    if (i * 256 + t < nv4) {
-      const int c = (i * 256 + t) * 4;
-      const float y0 = (v[i].x - mean) * rstd * (1.f + sc[i].x) + sh[i].x;
-      const float y1 = (v[i].y - mean) * rstd * (1.f + sc[i].y) + sh[i].y;
-      const float y2 = (v[i].z - mean) * rstd * (1.f + sc[i].z) + sh[i].z;
-      const float y3 = (v[i].w - mean) * rstd * (1.f + sc[i].w) + sh[i].w;
-      store4(orow + c, y0, y1, y2, y3);
-    }
+    for (int i = 0; i < kLnMaxVec; ++i)
+      if (i * 256 + t < nv4) {
+        v[i].x = (v[i].x - mean) * rstd * (1.f + sc[i].x) + sh[i].x;
+        v[i].y = (v[i].y - mean) * rstd * (1.f + sc[i].y) + sh[i].y;
+        v[i].z = (v[i].z - mean) * rstd * (1.f + sc[i].z) + sh[i].z;
+        v[i].w = (v[i].w - mean) * rstd * (1.f + sc[i].w) + sh[i].w;
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+      }
+    amax = wave_max(amax);
+    if ((t & 63) == 0) red[2][w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    const float scale = amax / 448.0f;
+    if (t == 0) out_scale[r] = scale;
+#pragma unroll
+    for (int i = 0; i < kLnMaxVec; ++i)
+      if (i * 256 + t < nv4) {
+        uint32_t packed = 0;
+        if (scale > 0.f)
+          packed = e4m3_code(v[i].x / scale) | e4m3_code(v[i].y / scale) << 8 |
+                   e4m3_code(v[i].z / scale) << 16 | e4m3_code(v[i].w / scale) << 24;
+        *reinterpret_cast<uint32_t *>(orow + (i * 256 + t) * 4) = packed;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kLnMaxVec; ++i)
+      if (i * 256 + t < nv4) {
+        const int c = (i * 256 + t) * 4;
+        const float y0 = (v[i].x - mean) * rstd * (1.f + sc[i].x) + sh[i].x;
+        const float y1 = (v[i].y - mean) * rstd * (1.f + sc[i].y) + sh[i].y;
+        const float y2 = (v[i].z - mean) * rstd * (1.f + sc[i].z) + sh[i].z;
+        const float y3 = (v[i].w - mean) * rstd * (1.f + sc[i].w) + sh[i].w;
+        store4(orow + c, y0, y1, y2, y3);
+      }
+  }
 }
 
 template <typename TO>
 void launch_ln(void *out, int ldo, const float *x, int ldx, int rows, int row0, int d, float eps,
-               const float *const m[3], Segs sg, hipStream_t s) {
+               const float *const m[3], Segs sg, hipStream_t s, float *out_scale) {
   k_ln_modulate<TO><<<rows, 256, 0, s>>>((TO *)out, ldo, x, ldx, row0, d, eps, m[0], m[1], m[2],
-                                          sg.b1, sg.b2, sg.per);
+                                          sg.b1, sg.b2, sg.per, out_scale);
 }
 
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
                        int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
-                       hipStream_t s) {
+                       hipStream_t s, float *out_scale) {
   if (rows <= 0) return hipSuccess;
   if (d % 256 || d > 256 * 4 * kLnMaxVec) return hipErrorInvalidValue;
   switch (out_type) {
-    case OP_F32: launch_ln<float>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
-    case OP_BF16: launch_ln<bf16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
-    case OP_F16: launch_ln<f16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s); break;
+    case OP_F32: launch_ln<float>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s, nullptr); break;
+    case OP_BF16: launch_ln<bf16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s, nullptr); break;
+    case OP_F16: launch_ln<f16>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s, nullptr); break;
+    case OP_FP8:
+      if (!out_scale || ldo % 4) return hipErrorInvalidValue;
+      launch_ln<uint8_t>(out, ldo, x, ldx, rows, row0, d, eps, mod_seg, segs, s, out_scale);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -485,6 +519,64 @@ hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const floa
     case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec, ldy); break;
     case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec, ldy); break;
     case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec, ldy); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Row-wise E4M3 quantization: one 256-thread workgroup per row.  Pass 1 finds max |v|, the
+// row's scale is max / 448 (fp32 division), pass 2 (the row again, from L2) writes the codes
+// of v / scale, 8 values per thread and step.  A row of zeros gets scale 0 and codes 0.
+// ------------------------------------------------------------------------------------------
+template <typename TS>
+__device__ __forceinline__ void load8(const TS *p, float (&v)[8]) {
+  typename Load16<TS>::raw r = Load16<TS>::load(p);
+  Load16<TS>::unpack(v, r);
+}
+
+template <typename TS>
+__global__ __launch_bounds__(256) void k_quant_rows(uint8_t *q, int ldq, float *scale,
+                                                    const TS *src, int lds, int cols) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const TS *row = src + (size_t)r * lds;
+  float amax = 0.f;
+  for (int c = t * 8; c < cols; c += 256 * 8) {
+    float v[8];
+    load8<TS>(row + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax / 448.0f;
+  if (t == 0) scale[r] = s;
+  uint8_t *qr = q + (size_t)r * ldq;
+  for (int c = t * 8; c < cols; c += 256 * 8) {
+    float v[8];
+    load8<TS>(row + c, v);
+    uint32_t lo = 0, hi = 0;
+    if (s > 0.f) {
+      lo = e4m3_code(v[0] / s) | e4m3_code(v[1] / s) << 8 | e4m3_code(v[2] / s) << 16 |
+           e4m3_code(v[3] / s) << 24;
+      hi = e4m3_code(v[4] / s) | e4m3_code(v[5] / s) << 8 | e4m3_code(v[6] / s) << 16 |
+           e4m3_code(v[7] / s) << 24;
+    }
+    *reinterpret_cast<uint2 *>(qr + c) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t quant_rows_fp8(uint8_t *q, int ldq, float *scale, const void *src, int src_type, int lds,
+                          int rows, int cols, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols % 8 || ldq % 8 || lds % 8) return hipErrorInvalidValue;
+  switch (src_type) {
+    case OP_F32: k_quant_rows<float><<<rows, 256, 0, s>>>(q, ldq, scale, (const float *)src, lds, cols); break;
+    case OP_BF16: k_quant_rows<bf16><<<rows, 256, 0, s>>>(q, ldq, scale, (const bf16 *)src, lds, cols); break;
+    case OP_F16: k_quant_rows<f16><<<rows, 256, 0, s>>>(q, ldq, scale, (const f16 *)src, lds, cols); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -58,12 +58,14 @@ struct dit_ctx {
   dit_config cfg;
   int device = 0;
   int op = OP_BF16;          // element type of MFMA operands, activations and weights
+  bool fp8 = false;          // DIT_FP8: block projections on E4M3 (op is OP_F16 for the rest)
   bool debug_sync = false;
   std::vector<void *> allocs;
 
   struct Set {
-    void *w1 = nullptr, *w2 = nullptr;
+    void *w1 = nullptr, *w2 = nullptr;   // compute type, or E4M3 codes with DIT_FP8
     float *qn = nullptr, *kn = nullptr;
+    float *s1 = nullptr, *s2 = nullptr;  // DIT_FP8: one scale per row of w1, w2
   };
   std::vector<std::vector<Set>> blk;
   void *mod[2][3] = {{nullptr}};
@@ -94,6 +96,9 @@ struct dit_ctx {
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
   int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 6)] per-unit piece counters
   float *gemm_part = nullptr;  // [lean_grid][gemm_part_floats] split-K partial tiles
+  // DIT_FP8 workspace: E4M3 copy of cat, row scales of xm (codes in xm) and of cat's halves
+  uint8_t *cat8 = nullptr;     // [rows_alloc][D+F]
+  float *xs = nullptr, *cs_a = nullptr, *cs_b = nullptr;  // [rows_alloc] each
 
   // per-kernel timing: hipEvents recorded on the call's stream around each launch
   struct ProfRec {
@@ -153,9 +158,10 @@ int hip_fail(hipError_t e, const char *what) {
     }                                                           \
   } while (0)
 
-enum ProfClass { P_LN, P_LINEAR1, P_QKNORM, P_ATTN, P_LINEAR2, P_COND, P_EMBED, P_FINAL, P_NCLASS };
+enum ProfClass { P_LN, P_LINEAR1, P_QKNORM, P_ATTN, P_LINEAR2, P_COND, P_EMBED, P_FINAL, P_QUANT,
+                 P_NCLASS };
 const char *const kProfNames[P_NCLASS] = {"ln_modulate", "linear1", "qk_norm_rope", "attention",
-                                          "linear2", "conditioning", "embed", "final"};
+                                          "linear2", "conditioning", "embed", "final", "fp8_quant"};
 
 // Start / end markers around one launch when timing is on (no-op otherwise).
 int prof_begin(dit_ctx *ctx, int cls, hipStream_t stream) {
@@ -214,7 +220,7 @@ int validate_config(const dit_config *c) {
     return fail(DIT_EINVAL, "need at least one block");
   if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
     return fail(DIT_EINVAL, "max_tokens out of range: %d", c->max_tokens);
-  if (c->compute != DIT_F32 && c->compute != DIT_BF16 && c->compute != DIT_F16)
+  if (c->compute != DIT_F32 && c->compute != DIT_BF16 && c->compute != DIT_F16 && c->compute != DIT_FP8)
     return fail(DIT_EINVAL, "unknown compute type %d", c->compute);
   if (!(c->rope_theta > 0.f) || !(c->ln_eps > 0.f) || !(c->rms_eps > 0.f))
     return fail(DIT_EINVAL, "rope_theta, ln_eps and rms_eps must be positive");
@@ -267,6 +273,38 @@ int upload(dit_ctx *ctx, void **dst, const dit_tensor &t, bool as_f32,
   }
   hipError_t e = hipMemcpy(*dst, stage.data(), stage.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "upload");
+  return 0;
+}
+
+// Row-wise E4M3 copy of a weight [rows][cols] (rows optionally permuted: destination row r
+// takes source row perm[r]): the fp32 values go to a temporary device buffer and the
+// quantization kernel writes the codes and one scale per row.
+int upload_fp8(dit_ctx *ctx, void **codes, float **scales, const dit_tensor &t, int cols,
+               const std::vector<int> *perm = nullptr) {
+  const int64_t n = t.numel, rows = n / cols;
+  std::vector<float> stage((size_t)n);
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t sr = perm ? (*perm)[r] : r;
+    for (int64_t c = 0; c < cols; ++c) {
+      const int64_t si = sr * cols + c;
+      stage[(size_t)(r * cols + c)] = t.dtype == DIT_BF16 ? bf16_to_f32(((const uint16_t *)t.data)[si])
+                                                          : ((const float *)t.data)[si];
+    }
+  }
+  if (int rc = dalloc(ctx, codes, (size_t)n)) return rc;
+  if (int rc = dalloc(ctx, (void **)scales, (size_t)rows * 4)) return rc;
+  float *tmp = nullptr;
+  hipError_t e = hipMalloc(&tmp, (size_t)n * 4);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DIT_ENOMEM, "hipMalloc(%zu bytes) failed for weight quantization", (size_t)n * 4);
+  }
+  e = hipMemcpy(tmp, stage.data(), (size_t)n * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = quant_rows_fp8((uint8_t *)*codes, cols, *scales, tmp, OP_F32, cols, (int)rows, cols, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipFree(tmp);
+  if (e != hipSuccess) return hip_fail(e, "weight quantization");
   return 0;
 }
 
@@ -378,7 +416,8 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   dit_ctx *ctx = new dit_ctx();
   ctx->cfg = c;
   ctx->device = dev;
-  ctx->op = c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
+  ctx->fp8 = c.compute == DIT_FP8;
+  ctx->op = ctx->fp8 ? OP_F16 : c.compute;  // DIT_F32 / DIT_BF16 / DIT_F16 share the OP_ codes
   ctx->cus = prop.multiProcessorCount / 8 * 8;
   ctx->lean_grid = ctx->cus;
   if (const char *ag = getenv("DIT_ATTN_GRID")) {  // attention share count (0: off)
@@ -432,8 +471,13 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
     for (int s = 0; s < ns && !rc; ++s) {
       std::string p = "blk" + std::to_string(b) + ".s" + std::to_string(s);
       dit_ctx::Set &st = ctx->blk[b][s];
-      rc = rc ? rc : up(&st.w1, (p + ".w1").c_str(), false, &perm1, D);
-      rc = rc ? rc : up(&st.w2, (p + ".w2").c_str(), false);
+      if (ctx->fp8) {
+        rc = rc ? rc : upload_fp8(ctx, &st.w1, &st.s1, *have[p + ".w1"], D, &perm1);
+        rc = rc ? rc : upload_fp8(ctx, &st.w2, &st.s2, *have[p + ".w2"], D + F);
+      } else {
+        rc = rc ? rc : up(&st.w1, (p + ".w1").c_str(), false, &perm1, D);
+        rc = rc ? rc : up(&st.w2, (p + ".w2").c_str(), false);
+      }
       rc = rc ? rc : up((void **)&st.qn, (p + ".qn").c_str(), true);
       rc = rc ? rc : up((void **)&st.kn, (p + ".kn").c_str(), true);
     }
@@ -466,6 +510,12 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   }
   if (ctx->op != OP_F32 && ctx->cus > 0)
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->gemm_part, (size_t)ctx->cus * gemm_part_floats * 4);
+  if (ctx->fp8) {
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->cat8, R * (D + F));
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->xs, R * 4);
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs_a, R * 4);
+    rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs_b, R * 4);
+  }
   if (ctx->op == OP_F32) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->xf, (size_t)c.max_tokens * D * 4);
   } else if (!rc) {
@@ -511,12 +561,14 @@ int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) 
 // with the gated residual.  Sequentially wired double blocks run the attention half
 // (linear1 over the Q|K|V rows, linear2 over W2's first D columns, gate 1), then a second
 // LayerNorm with the second (shift, scale) and the MLP half (linear1 over the gate/up
-// rows, linear2 over W2's last F columns, gate 2).
+// rows, linear2 over W2's last F columns, gate 2).  With DIT_FP8 the LayerNorm writes E4M3
+// codes with row scales, and linear2's input is quantized per token before its GEMM.
 int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = ctx->D(), F = ctx->F();
   const int kind = ctx->kind(b);
   const bool seq = ctx->seq_block(kind);
+  const bool f8 = ctx->fp8;
   int sos[3];
   ctx->set_of_seg(kind, sos);
   const float *mseg[3], *gate[3], *qn[3], *kn[3], *mseg2[3], *gate2[3];
@@ -531,31 +583,42 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   if (mask == DIT_MASK_DEFAULT) mask = (kind == 0 && c.arch == DIT_FLUX3) ? DIT_MASK_SEGMENT : DIT_MASK_FULL;
   const int N = sg.n;
   const size_t es = ctx->esz();
+  const size_t ex = f8 ? 1 : es;  // bytes per value of the projections' inputs and weights
   const bool mfma = ctx->op != OP_F32;
-
   const double es_d = (double)es;
-  DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
-            ln_modulate(ctx->xm, ctx->op, D, x, D, N, 0, D, c.ln_eps, mseg, sg, stream), "ln_modulate");
+
+  auto ln = [&](const float *const ms[3]) -> int {
+    DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + (double)ex),
+              ln_modulate(ctx->xm, f8 ? OP_FP8 : ctx->op, D, x, D, N, 0, D, c.ln_eps, ms, sg, stream,
+                          ctx->xs),
+              "ln_modulate");
+    return 0;
+  };
+  auto gemm = [&](const GemmArgs &ga, int epi) -> hipError_t {
+    if (f8) return gemm_fp8(ga, epi, stream);
+    if (mfma) return gemm_mfma(ga, epi, ctx->op, stream);
+    return gemm_simple(ga, epi, OP_F32, stream);
+  };
+  if (int rc = ln(mseg)) return rc;
 
   // row groups: one per distinct weight set over contiguous rows, sequence by sequence
   const int nseq = sg.n / sg.per;
   const int lb[4] = {0, sg.b1, sg.b2, sg.per};
+  const void *cat_in = f8 ? (const void *)ctx->cat8 : (const void *)ctx->cat;  // linear2 input
   GemmGroup g1[kMaxGroups], g2[kMaxGroups];
   int ng = 0;
   for (int qs = 0; qs < nseq; ++qs)
     for (int s = 0; s < 3; ++s) {
       const int r0 = qs * sg.per + lb[s], r1 = qs * sg.per + lb[s + 1];
       if (r1 == r0) continue;
-      const int set = sos[s];
-      if (ng > 0 && (const void *)g1[ng - 1].w == ctx->blk[b][set].w1 &&
-          g1[ng - 1].out_row0 + g1[ng - 1].rows == r0) {  // extend
-        g1[ng - 1].rows += r1 - r0;
+      const dit_ctx::Set &ws = ctx->blk[b][sos[s]];
+      if (ng > 0 && (const void *)g1[ng - 1].w == ws.w1 && g1[ng - 1].out_row0 + g1[ng - 1].rows == r0) {
+        g1[ng - 1].rows += r1 - r0;  // extend
         g2[ng - 1].rows += r1 - r0;
         continue;
       }
-      g1[ng] = GemmGroup{(const char *)ctx->xm + (size_t)r0 * D * es, ctx->blk[b][set].w1, r1 - r0, r0};
-      g2[ng] = GemmGroup{(const char *)ctx->cat + (size_t)r0 * (D + F) * es, ctx->blk[b][set].w2,
-                         r1 - r0, r0};
+      g1[ng] = GemmGroup{(const char *)ctx->xm + (size_t)r0 * D * ex, ws.w1, r1 - r0, r0, ws.s1};
+      g2[ng] = GemmGroup{(const char *)cat_in + (size_t)r0 * (D + F) * ex, ws.w2, r1 - r0, r0, ws.s2};
       ++ng;
     }
   GemmArgs a1 = {};
@@ -570,11 +633,8 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   a1.cat = ctx->cat;
   a1.ldc = D + F;
   a1.cat_off = D;
-  const double fl1 = 2.0 * N * D * (double)a1.n;
-  if (mfma)
-    DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_mfma(a1, EPI_QKV_SWIGLU, ctx->op, stream), "linear1");
-  else
-    DIT_TIMED(P_LINEAR1, fl1, 0.0, gemm_simple(a1, EPI_QKV_SWIGLU, OP_F32, stream), "linear1");
+  a1.xs = ctx->xs;
+  DIT_TIMED(P_LINEAR1, 2.0 * N * D * (double)a1.n, 0.0, gemm(a1, EPI_QKV_SWIGLU), "linear1");
 
   // bytes: q, k read + written, V read + V^T written, one cos/sin row per token
   DIT_TIMED(P_QKNORM, 0.0, (double)N * (6.0 * D * es_d + 512.0),
@@ -616,13 +676,18 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
     DIT_TIMED(P_ATTN, fla, 0.0, attention_f32(at, stream), "attention");
 
   // linear2 with the gated residual over k columns of cat starting at column k0 (W2 columns
-  // k0 .. k0 + k of its D + F)
-  auto linear2 = [&](int k0, int k, const float *const gt[3]) -> int {
+  // k0 .. k0 + k of its D + F); with DIT_FP8 those columns are quantized first, scales in xsc
+  auto linear2 = [&](int k0, int k, const float *const gt[3], float *xsc) -> int {
+    if (f8)
+      DIT_TIMED(P_QUANT, 0.0, (double)N * k * 3.0,
+                quant_rows_fp8(ctx->cat8 + k0, D + F, xsc, (const uint16_t *)ctx->cat + k0, OP_F16, D + F, N, k,
+                               stream),
+                "fp8 quantization");
     GemmArgs a2 = {};
     for (int i = 0; i < ng; ++i) {
       a2.g[i] = g2[i];
-      a2.g[i].x = (const char *)g2[i].x + (size_t)k0 * es;
-      a2.g[i].w = (const char *)g2[i].w + (size_t)k0 * es;
+      a2.g[i].x = (const char *)g2[i].x + (size_t)k0 * ex;
+      a2.g[i].w = (const char *)g2[i].w + (size_t)k0 * ex;
     }
     a2.ng = ng;
     a2.n = D;
@@ -635,30 +700,25 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
     a2.b1 = sg.b1;
     a2.b2 = sg.b2;
     a2.per = sg.per;
+    a2.xs = xsc;
     ctx->split_k(&a2);
-    const double fl2 = 2.0 * N * (double)k * D;
-    if (mfma)
-      DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_mfma(a2, EPI_RESID, ctx->op, stream), "linear2");
-    else
-      DIT_TIMED(P_LINEAR2, fl2, 0.0, gemm_simple(a2, EPI_RESID, OP_F32, stream), "linear2");
+    DIT_TIMED(P_LINEAR2, 2.0 * N * (double)k * D, 0.0, gemm(a2, EPI_RESID), "linear2");
     return 0;
   };
-  if (!seq) return linear2(0, D + F, gate);
+  if (!seq) return linear2(0, D + F, gate, ctx->cs_a);
 
   // sequential double block: attention half, then the MLP half on the updated residual
-  if (int rc = linear2(0, D, gate)) return rc;
-  DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + es_d),
-            ln_modulate(ctx->xm, ctx->op, D, x, D, N, 0, D, c.ln_eps, mseg2, sg, stream), "ln_modulate");
+  if (int rc = linear2(0, D, gate, ctx->cs_a)) return rc;
+  if (int rc = ln(mseg2)) return rc;
   GemmArgs am = a1;
-  for (int i = 0; i < ng; ++i) am.g[i].w = (const char *)g1[i].w + (size_t)3 * D * D * es;  // gate/up rows
+  for (int i = 0; i < ng; ++i) {  // gate/up rows of W1 (and their scales)
+    am.g[i].w = (const char *)g1[i].w + (size_t)3 * D * D * ex;
+    if (g1[i].ws) am.g[i].ws = g1[i].ws + 3 * D;
+  }
   am.n = 2 * F;
   am.split = 0;
-  const double flm = 2.0 * N * D * (2.0 * F);
-  if (mfma)
-    DIT_TIMED(P_LINEAR1, flm, 0.0, gemm_mfma(am, EPI_QKV_SWIGLU, ctx->op, stream), "linear1");
-  else
-    DIT_TIMED(P_LINEAR1, flm, 0.0, gemm_simple(am, EPI_QKV_SWIGLU, OP_F32, stream), "linear1");
-  return linear2(D, F, gate2);
+  DIT_TIMED(P_LINEAR1, 2.0 * N * D * (2.0 * F), 0.0, gemm(am, EPI_QKV_SWIGLU), "linear1");
+  return linear2(D, F, gate2, ctx->cs_b);
 }
 
 int check_tokens(dit_ctx *ctx, int n_txt, int n_img, int n_ref, int nseq = 1) {
@@ -1077,6 +1137,40 @@ extern "C" int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream)
   return 0;
 }
 
+extern "C" int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx, uint8_t *q, int ldq,
+                                     float *scale, void *stream) {
+  g_err.clear();
+  if (!x || !q || !scale || rows < 0 || cols < 8 || cols % 8 || ldx < cols || ldx % 8 || ldq < cols ||
+      ldq % 8)
+    return fail(DIT_EINVAL, "bad arguments (cols, ldx, ldq: multiples of 8, ldx, ldq >= cols)");
+  hipError_t e = quant_rows_fp8(q, ldq, scale, x, OP_F32, ldx, rows, cols, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantization");
+  return 0;
+}
+
+extern "C" int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
+                            const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream) {
+  g_err.clear();
+  if (!qx || !sx || !qw || !sw || !y || m < 0 || n < 256 || n % 256 || k < 128 || k % 128)
+    return fail(DIT_EUNSUPPORTED, "dit_gemm_fp8 needs n %% 256 == 0 and k %% 128 == 0 (n %d, k %d)", n, k);
+  if (ldx < k || ldx % 16 || ldw < k || ldw % 16 || ldy < n || ldy % 4)
+    return fail(DIT_EINVAL, "bad strides (ldx, ldw >= k, multiples of 16; ldy >= n, multiple of 4)");
+  if (m == 0) return 0;
+  GemmArgs a = {};
+  a.g[0] = GemmGroup{qx, qw, m, 0, sw};
+  a.ng = 1;
+  a.n = n;
+  a.k = k;
+  a.ldx = ldx;
+  a.ldw = ldw;
+  a.out = y;
+  a.ldo = ldy;
+  a.xs = sx;
+  hipError_t e = gemm_fp8(a, EPI_STORE_F32, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 gemm");
+  return 0;
+}
+
 extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t *row_stride) {
   if (!ctx || !name) return nullptr;
   const int D = ctx->D(), F = ctx->F();
@@ -1086,7 +1180,7 @@ extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dty
     if (row_stride) *row_stride = rs;
     return p;
   };
-  if (!strcmp(name, "xm")) return ret(ctx->xm, dt, D);
+  if (!strcmp(name, "xm")) return ret(ctx->xm, ctx->fp8 ? DIT_FP8 : dt, D);
   if (!strcmp(name, "qkv")) return ret(ctx->qkv, dt, 3 * D);
   if (!strcmp(name, "cat")) return ret(ctx->cat, dt, D + F);
   if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, ctx->mod_ld());

@@ -16,8 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdit.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dit.h")
 
-DIT_F32, DIT_BF16, DIT_F16 = 0, 1, 2
-COMPUTE = {"f32": DIT_F32, "bf16": DIT_BF16, "f16": DIT_F16}
+DIT_F32, DIT_BF16, DIT_F16, DIT_FP8 = 0, 1, 2, 3
+COMPUTE = {"f32": DIT_F32, "bf16": DIT_BF16, "f16": DIT_F16, "fp8": DIT_FP8}
 DIT_FLUX2, DIT_FLUX3 = 0, 1
 DIT_MASK_DEFAULT, DIT_MASK_FULL, DIT_MASK_SEGMENT = -1, 0, 1
 DIT_OK, DIT_EINVAL, DIT_ENOMEM, DIT_EHIP, DIT_EUNSUPPORTED = 0, -1, -2, -3, -4
@@ -88,6 +88,10 @@ def load_library(path: str = None):
     lib.dit_denoise_cfg.argtypes = [P, P, P, P, I, I, I, P, I, I, I, F, I64, P]
     lib.dit_fill_noise.restype = I
     lib.dit_fill_noise.argtypes = [P, I64, I64, P]
+    lib.dit_quantize_rows_fp8.restype = I
+    lib.dit_quantize_rows_fp8.argtypes = [P, I, I, I, P, I, P, P]
+    lib.dit_gemm_fp8.restype = I
+    lib.dit_gemm_fp8.argtypes = [P, P, I, I, P, P, I, I, I, P, I, P]
     lib.dit_debug_buffer.restype = P
     lib.dit_debug_buffer.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(I), ctypes.POINTER(I64)]
     lib.dit_profile_start.restype = I
@@ -284,7 +288,7 @@ class DiT:
                                               seed, _stream(stream)))
 
     KERNELS = ("ln_modulate", "linear1", "qk_norm_rope", "attention", "linear2", "conditioning",
-               "embed", "final")
+               "embed", "final", "fp8_quant")
 
     def profile_start(self, max_launches: int = 100000, kernels: str | None = None):
         """Time the following launches; kernels = comma-separated classes (None: all)."""
@@ -313,11 +317,38 @@ class DiT:
         if not p:
             raise KeyError(name)
         cols = rs.value if cols is None else cols
+        if dt.value == DIT_FP8:
+            raise ValueError(f"{name} holds E4M3 codes")
         tdt = {DIT_BF16: torch.bfloat16, DIT_F16: torch.float16}.get(dt.value, torch.float32)
         out = torch.empty((rows, rs.value), dtype=tdt, device="cuda")
         torch.cuda.synchronize()
         _hip_memcpy_dtod(out.data_ptr(), p, out.numel() * out.element_size())
         return out[:, :cols].float()
+
+
+def quantize_rows_fp8(x, stream=None):
+    """(codes uint8 [rows, cols], scales float32 [rows]) of the row-wise E4M3 quantization of
+    a float32 CUDA matrix x (dit_quantize_rows_fp8)."""
+    import torch
+    _need(x, "float32", "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(load_library().dit_quantize_rows_fp8(_ptr(x), rows, cols, x.stride(0), _ptr(q), cols,
+                                                _ptr(sc), _stream(stream)))
+    return q, sc
+
+
+def gemm_fp8(qx, sx, qw, sw, stream=None):
+    """y = sx[:, None] * sw[None, :] * (qx . qw^T) over E4M3 codes (dit_gemm_fp8); qx must
+    have rows readable up to its row count rounded up to 256 (pass a padded tensor's view)."""
+    import torch
+    m, k = qx.shape
+    n = qw.shape[0]
+    y = torch.empty((m, n), dtype=torch.float32, device=qx.device)
+    _check(load_library().dit_gemm_fp8(_ptr(qx), _ptr(sx), m, qx.stride(0), _ptr(qw), _ptr(sw), n,
+                                       qw.stride(0), k, _ptr(y), n, _stream(stream)))
+    return y
 
 
 def fill_noise(dst, seed: int, stream=None):

@@ -41,7 +41,8 @@ class ModelConfig:
     n_stream_blocks: int = 5
     n_shared_blocks: int = 20
     bf16: bool = True            # weights are bf16 values (the checkpoint format)
-    compute: str = "f16"         # MFMA operand type of the library: "f16", "bf16" or "f32"
+    compute: str = "f16"         # MFMA operand type of the library: "f16", "bf16", "f32", or "fp8"
+                                 # (row-wise E4M3 block projections, the rest as "f16")
     rope_theta: float = 10000.0
     ln_eps: float = 1e-6
     rms_eps: float = 1e-6

@@ -270,7 +270,9 @@ class WeightSet:
 # for an activation; scale = max|row| / 448, code = value / scale rounded to the nearest E4M3
 # value, ties to even mantissa, saturating at +-448; a row of zeros has scale 0 and codes 0.
 # The scale and the quotient are formed in fp32 (the kernel's precision) so that both sides
-# take the same rounding decisions.  A projection y = x W^T then equals
+# take the same rounding decisions; for the same reason the input of the second projection,
+# which the kernel holds in fp16, is rounded to fp16 before it is quantized (the LayerNorm
+# output is quantized from fp32).  A projection y = x W^T then equals
 # scale_x scale_w sum_k code_x code_w.  Only the two big projections of every block (W1, W2)
 # and their inputs (the modulated LayerNorm output and [attention || SwiGLU]) use it.
 # ----------------------------------------------------------------------------------------
@@ -319,9 +321,10 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return s * mag
 
 
-def quantize_rows_fp8(x: np.ndarray):
-    """(codes uint8 [rows, cols], scales float32 [rows]) of the row-wise E4M3 quantization."""
-    x32 = np.asarray(x, np.float64).astype(np.float32)
+def quantize_rows_fp8(x: np.ndarray, precision=np.float32):
+    """(codes uint8 [rows, cols], scales float32 [rows]) of the row-wise E4M3 quantization of
+    x rounded to `precision` (np.float32 or np.float16; round to nearest even)."""
+    x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
     amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
@@ -330,9 +333,9 @@ def quantize_rows_fp8(x: np.ndarray):
     return e4m3_encode(e4m3_round(q.astype(np.float64))), scale
 
 
-def fp8_round_rows(x: np.ndarray) -> np.ndarray:
+def fp8_round_rows(x: np.ndarray, precision=np.float32) -> np.ndarray:
     """The values a row-wise E4M3 operand stands for: code * scale, per row (float64)."""
-    codes, scale = quantize_rows_fp8(x)
+    codes, scale = quantize_rows_fp8(x, precision)
     return e4m3_decode(codes) * scale.astype(np.float64)[:, None]
 
 
@@ -365,8 +368,9 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     returns [len(rows), D].  Used to check sampled rows at full size.
 
     act_fp8: the inputs of the two projections (the modulated LayerNorm output, and
-    [attention || SwiGLU]) go through the row-wise E4M3 quantization first (the fp8r path;
-    the weights are expected in their E4M3 values already, quantize_weights_fp8)."""
+    [attention || SwiGLU] rounded to fp16) go through the row-wise E4M3 quantization first
+    (the fp8r path; the weights are expected in their E4M3 values already,
+    quantize_weights_fp8)."""
     n, d = x.shape
     nh, hd, f = dims.heads, dims.head_dim, dims.mlp_hidden
     seg = segment_ids(*segs)
@@ -422,7 +426,7 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     m = silu(g[rows]) * u[rows]
     cat = np.concatenate([o.reshape(rows.shape[0], d), m], axis=1)
     if act_fp8:
-        cat = fp8_round_rows(cat)
+        cat = fp8_round_rows(cat, np.float16)
     out = x[rows].copy()
     for s in range(3):
         sel = seg[rows] == s

@@ -215,10 +215,11 @@ def test_attention_invariants():
 
 # ------------------------------------------------------------------ one block
 
-def torch_block(x, segs, sets, sos, mods, pos, mask, dims, act=None):
-    """Independent composition of torch float64 library routines for one block; act (if
-    given) is applied to the inputs of both projections."""
+def torch_block(x, segs, sets, sos, mods, pos, mask, dims, act=None, act2=None):
+    """Independent composition of torch float64 library routines for one block; act and act2
+    (if given) are applied to the inputs of the first and the second projection."""
     act = act or (lambda t: t)
+    act2 = act2 or act
     d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
     seg = torch.tensor(O.segment_ids(*segs))
     n = x.shape[0]
@@ -239,7 +240,7 @@ def torch_block(x, segs, sets, sos, mods, pos, mask, dims, act=None):
     o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
                                        attn_mask=am).transpose(0, 1).reshape(n, d)
     g, u = h[:, 3 * d:3 * d + f], h[:, 3 * d + f:]
-    cat = act(torch.cat([o, F.silu(g) * u], dim=1))
+    cat = act2(torch.cat([o, F.silu(g) * u], dim=1))
     W2 = torch.stack([torch.tensor(sets[sos[int(s)]].w2) for s in seg])
     return (X + gate * torch.einsum("nk,nok->no", cat, W2)).numpy()
 
@@ -266,11 +267,13 @@ def test_block_matches_library_composition(mask, sos, segs):
                                got[rows], rtol=0, atol=1e-12)
 
 
-def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims, act=None):
+def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims, act=None, act2=None):
     """Independent torch float64 composition of a sequentially wired double block: attention
     with (shift1, scale1, gate1), then the SwiGLU MLP on the updated residual with (shift2,
-    scale2, gate2); act (if given) is applied to the inputs of each projection."""
+    scale2, gate2); act and act2 (if given) are applied to the inputs of the first and the
+    second projection of each half."""
     act = act or (lambda t: t)
+    act2 = act2 or act
     d, nh, hd, f = dims.hidden, dims.heads, dims.head_dim, dims.mlp_hidden
     seg = torch.tensor(O.segment_ids(*segs))
     n = x.shape[0]
@@ -289,10 +292,10 @@ def torch_sequential_block(x, segs, sets, sos, mods6, pos, mask, dims, act=None)
     am = None if mask == O.MASK_FULL else (seg[:, None] == seg[None, :])
     o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
                                        attn_mask=am).transpose(0, 1).reshape(n, d)
-    X1 = X + g1 * torch.einsum("nk,nok->no", act(o), W2[:, :, :d])
+    X1 = X + g1 * torch.einsum("nk,nok->no", act2(o), W2[:, :, :d])
     xm2 = act(F.layer_norm(X1, (d,), eps=dims.ln_eps) * (1 + sc2) + sh2)
     gu = torch.einsum("nk,nok->no", xm2, W1[:, 3 * d:])
-    m = act(F.silu(gu[:, :f]) * gu[:, f:])
+    m = act2(F.silu(gu[:, :f]) * gu[:, f:])
     return (X1 + g2 * torch.einsum("nk,nok->no", m, W2[:, :, d:])).numpy()
 
 
@@ -688,10 +691,10 @@ def test_noise_distribution_and_prefix():
 
 # ------------------------------------------------------------------ row-wise FP8 (fp8r)
 
-def torch_fp8_rows(X):
+def torch_fp8_rows(X, precision=torch.float32):
     """Row-wise E4M3 values through torch's float8_e4m3fn conversion (round to nearest even),
-    independent of the oracle's rounding code."""
-    X32 = X.to(torch.float32)
+    independent of the oracle's rounding code; X is rounded to `precision` first."""
+    X32 = X.to(precision).to(torch.float32)
     s = X32.abs().amax(dim=1, keepdim=True) / 448.0
     q = torch.where(s > 0, X32 / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(X32))
     return q.to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
@@ -782,12 +785,14 @@ def test_fp8_block_matches_library_composition(sequential):
     if sequential:
         mods6 = [np.concatenate([a, b]) for a, b in zip(rand_mods(r, dims), rand_mods(r, dims))]
         got = O.block_forward_sequential(x, segs, q_or, sos, mods6, pos, O.MASK_FULL, dims, act_fp8=True)
-        ref = torch_sequential_block(x, segs, q_t, sos, mods6, pos, O.MASK_FULL, dims, act=torch_fp8_rows)
+        ref = torch_sequential_block(x, segs, q_t, sos, mods6, pos, O.MASK_FULL, dims, act=torch_fp8_rows,
+                                     act2=lambda t: torch_fp8_rows(t, torch.float16))
         plain = O.block_forward_sequential(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims)
     else:
         mods = rand_mods(r, dims)
         got = O.block_forward(x, segs, q_or, sos, mods, pos, O.MASK_FULL, dims, act_fp8=True)
-        ref = torch_block(x, segs, q_t, sos, mods, pos, O.MASK_FULL, dims, act=torch_fp8_rows)
+        ref = torch_block(x, segs, q_t, sos, mods, pos, O.MASK_FULL, dims, act=torch_fp8_rows,
+                          act2=lambda t: torch_fp8_rows(t, torch.float16))
         plain = O.block_forward(x, segs, sets, sos, mods, pos, O.MASK_FULL, dims)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
     # the E4M3 rounding is visible but small against the unquantized block
@@ -795,8 +800,8 @@ def test_fp8_block_matches_library_composition(sequential):
     assert 1e-3 < d < 0.2
 
 
-def _per_tensor_quantize(x):
-    x32 = np.asarray(x, np.float64).astype(np.float32)
+def _per_tensor_quantize(x, precision=np.float32):
+    x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
     s = np.float32(np.max(np.abs(x32)) / np.float32(448.0))
     q = (x32 / s).astype(np.float32)
     return O.e4m3_encode(O.e4m3_round(q.astype(np.float64))), np.full(x32.shape[0], s, np.float32)
