@@ -53,8 +53,8 @@ typedef struct dit_ctx dit_ctx;
  *             dit_ctx_create from the given values), their inputs (the modulated LayerNorm
  *             output, [attention || SwiGLU]) are quantized per token on the fly, and the
  *             products run on the E4M3 MFMA at twice the 16-bit rate.  Scale = max |row| / 448,
- *             code = value / scale rounded to nearest even E4M3.  Everything else computes as
- *             DIT_F16. */
+ *             code = value * (448 / max |row|) rounded to nearest even E4M3.  Everything else
+ *             computes as DIT_F16. */
 enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2, DIT_FP8 = 3 };
 
 /* model families.
@@ -268,9 +268,9 @@ int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream);
 
 /* Row-wise FP8 building blocks of DIT_FP8, on caller-owned device buffers (no context):
  * dit_quantize_rows_fp8: scale[r] = max_c |x[r][c]| / 448 (fp32), q[r][c] = E4M3 code of
- *   x[r][c] / scale[r], rounded to nearest even, saturating at 448; a zero row gets scale 0
- *   and codes 0.  x dev fp32 [rows][ldx], q dev uint8 [rows][ldq], scale dev fp32 [rows];
- *   cols, ldx, ldq multiples of 8.
+ *   x[r][c] * (448 / max_c |x[r][c]|) (fp32 product, clamped to +-448), rounded to nearest
+ *   even; a zero row gets scale 0 and codes 0.  x dev fp32 [rows][ldx], q dev uint8
+ *   [rows][ldq], scale dev fp32 [rows]; cols <= 16384, cols, ldx, ldq multiples of 8.
  * dit_gemm_fp8: y[i][j] = sx[i] * sw[j] * sum_k qx[i][k] * qw[j][k] (fp32), the E4M3 MFMA
  *   product: qx dev uint8 [m][ldx] (rows readable up to m rounded up to 256), sx [m],
  *   qw dev uint8 [n][ldw], sw [n], y dev fp32 [m][ldy]; n % 256 == 0, k % 128 == 0, ldx and

@@ -92,22 +92,17 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// OCP E4M3 code of q (round to nearest, ties to even mantissa; magnitudes beyond 448
-// saturate to 448).  Normal binade [2^e, 2^(e+1)), e >= -6, has 8 steps of 2^(e-3); below
-// 2^-6 the step is 2^-9.  Scaling by powers of two is exact, so rintf does the rounding.
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fabsf(q);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is 2^-6 = code 0x08
-  } else {
-    const int e = (int)(__float_as_uint(a) >> 23) - 127;
-    const float m = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));  // 8..16
-    code = (uint32_t)((e + 7) << 3) + (uint32_t)m - 8u;  // m = 16 carries into the exponent
-    code = min(code, 0x7Eu);
-  }
-  return code | sign;
+// OCP E4M3 codes of four values, packed low byte first: each is clamped to +-448 and rounded
+// to the nearest E4M3 value, ties to even mantissa (v_cvt_pk_fp8_f32 rounds that way on
+// gfx950 but does not saturate: past 464 it gives the NaN code, hence the clamp).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return (uint32_t)p;
 }
 
 // Segment (0 text, 1 image, 2 reference) of token row m given the two boundaries.

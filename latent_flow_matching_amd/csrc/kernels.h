@@ -66,8 +66,9 @@ hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s);
 // ws[feature] * acc, then the epilogue (16-bit stores are fp16).  n % 256 == 0, k % 128 == 0,
 // ldx and the weight row stride multiples of 16.
 hipError_t gemm_fp8(const GemmArgs &a, int epi, hipStream_t s);
-// q[r][c] = E4M3 code of src[r][c] / scale[r], scale[r] = max_c |src[r][c]| / 448 (fp32),
-// for r < rows, c < cols; src of type src_type (OP_F32 / OP_BF16 / OP_F16); cols % 8 == 0.
+// q[r][c] = E4M3 code of src[r][c] * (448 / max_c |src[r][c]|), scale[r] = max_c |src[r][c]| / 448
+// (fp32), for r < rows, c < cols; src of type src_type (OP_F32 / OP_BF16 / OP_F16);
+// cols % 8 == 0, cols <= 16384.
 hipError_t quant_rows_fp8(uint8_t *q, int ldq, float *scale, const void *src, int src_type, int lds,
                           int rows, int cols, hipStream_t s);
 // fp32-accumulating general GEMM with fp32 inputs and weights of type w_type.

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const flo
   const float rstd = 1.0f / sqrtf(var + eps);
   TO *orow = out + (size_t)r * ldo;
   if constexpr (sizeof(TO) == 1) {
-    // E4M3 codes of the modulated row with one scale: max |y| / 448
+    // E4M3 codes of the modulated row: y * (448 / max |y|), dequantization scale max |y| / 448
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < kLnMaxVec; ++i)
@@ -152,17 +152,13 @@ __global__ __launch_bounds__(256) void k_ln_modulate(TO *out, int ldo, const flo
     if ((t & 63) == 0) red[2][w] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
-    const float scale = amax / 448.0f;
-    if (t == 0) out_scale[r] = scale;
+    if (t == 0) out_scale[r] = amax / 448.0f;
+    const float rcp = amax > 0.f ? 448.0f / amax : 0.f;
 #pragma unroll
     for (int i = 0; i < kLnMaxVec; ++i)
-      if (i * 256 + t < nv4) {
-        uint32_t packed = 0;
-        if (scale > 0.f)
-          packed = e4m3_code(v[i].x / scale) | e4m3_code(v[i].y / scale) << 8 |
-                   e4m3_code(v[i].z / scale) << 16 | e4m3_code(v[i].w / scale) << 24;
-        *reinterpret_cast<uint32_t *>(orow + (i * 256 + t) * 4) = packed;
-      }
+      if (i * 256 + t < nv4)
+        *reinterpret_cast<uint32_t *>(orow + (i * 256 + t) * 4) =
+            e4m3_pack4(v[i].x * rcp, v[i].y * rcp, v[i].z * rcp, v[i].w * rcp);
   } else {
 #pragma unroll
     for (int i = 0; i < kLnMaxVec; ++i)
@@ -525,15 +521,12 @@ hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const floa
 }
 
 // ------------------------------------------------------------------------------------------
-// Row-wise E4M3 quantization: one 256-thread workgroup per row.  Pass 1 finds max |v|, the
-// row's scale is max / 448 (fp32 division), pass 2 (the row again, from L2) writes the codes
-// of v / scale, 8 values per thread and step.  A row of zeros gets scale 0 and codes 0.
+// Row-wise E4M3 quantization: one 256-thread workgroup per row, which it reads once into
+// registers (8 values per thread and step, up to kQuantSteps steps: 16384 columns); the codes
+// are v * (448 / max |v|) rounded to E4M3, the row's dequantization scale max |v| / 448.  A
+// row of zeros gets scale 0 and codes 0.
 // ------------------------------------------------------------------------------------------
-template <typename TS>
-__device__ __forceinline__ void load8(const TS *p, float (&v)[8]) {
-  typename Load16<TS>::raw r = Load16<TS>::load(p);
-  Load16<TS>::unpack(v, r);
-}
+constexpr int kQuantSteps = 8;
 
 template <typename TS>
 __global__ __launch_bounds__(256) void k_quant_rows(uint8_t *q, int ldq, float *scale,
@@ -541,38 +534,39 @@ __global__ __launch_bounds__(256) void k_quant_rows(uint8_t *q, int ldq, float *
   __shared__ float red[4];
   const int r = blockIdx.x, t = threadIdx.x;
   const TS *row = src + (size_t)r * lds;
+  float v[kQuantSteps][8];
   float amax = 0.f;
-  for (int c = t * 8; c < cols; c += 256 * 8) {
-    float v[8];
-    load8<TS>(row + c, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  for (int i = 0; i < kQuantSteps; ++i) {
+    const int c = (i * 256 + t) * 8;
+    if (c < cols) {
+      typename Load16<TS>::raw raw = Load16<TS>::load(row + c);
+      Load16<TS>::unpack(v[i], raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    }
   }
   amax = wave_max(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = amax / 448.0f;
-  if (t == 0) scale[r] = s;
+  if (t == 0) scale[r] = amax / 448.0f;
+  const float rcp = amax > 0.f ? 448.0f / amax : 0.f;
   uint8_t *qr = q + (size_t)r * ldq;
-  for (int c = t * 8; c < cols; c += 256 * 8) {
-    float v[8];
-    load8<TS>(row + c, v);
-    uint32_t lo = 0, hi = 0;
-    if (s > 0.f) {
-      lo = e4m3_code(v[0] / s) | e4m3_code(v[1] / s) << 8 | e4m3_code(v[2] / s) << 16 |
-           e4m3_code(v[3] / s) << 24;
-      hi = e4m3_code(v[4] / s) | e4m3_code(v[5] / s) << 8 | e4m3_code(v[6] / s) << 16 |
-           e4m3_code(v[7] / s) << 24;
-    }
-    *reinterpret_cast<uint2 *>(qr + c) = make_uint2(lo, hi);
+#pragma unroll
+  for (int i = 0; i < kQuantSteps; ++i) {
+    const int c = (i * 256 + t) * 8;
+    if (c < cols)
+      *reinterpret_cast<uint2 *>(qr + c) =
+          make_uint2(e4m3_pack4(v[i][0] * rcp, v[i][1] * rcp, v[i][2] * rcp, v[i][3] * rcp),
+                     e4m3_pack4(v[i][4] * rcp, v[i][5] * rcp, v[i][6] * rcp, v[i][7] * rcp));
   }
 }
 
 hipError_t quant_rows_fp8(uint8_t *q, int ldq, float *scale, const void *src, int src_type, int lds,
                           int rows, int cols, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (cols % 8 || ldq % 8 || lds % 8) return hipErrorInvalidValue;
+  if (cols % 8 || ldq % 8 || lds % 8 || cols > 256 * 8 * kQuantSteps) return hipErrorInvalidValue;
   switch (src_type) {
     case OP_F32: k_quant_rows<float><<<rows, 256, 0, s>>>(q, ldq, scale, (const float *)src, lds, cols); break;
     case OP_BF16: k_quant_rows<bf16><<<rows, 256, 0, s>>>(q, ldq, scale, (const bf16 *)src, lds, cols); break;

@@ -1140,9 +1140,9 @@ extern "C" int dit_fill_noise(float *dst, int64_t n, int64_t seed, void *stream)
 extern "C" int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx, uint8_t *q, int ldq,
                                      float *scale, void *stream) {
   g_err.clear();
-  if (!x || !q || !scale || rows < 0 || cols < 8 || cols % 8 || ldx < cols || ldx % 8 || ldq < cols ||
-      ldq % 8)
-    return fail(DIT_EINVAL, "bad arguments (cols, ldx, ldq: multiples of 8, ldx, ldq >= cols)");
+  if (!x || !q || !scale || rows < 0 || cols < 8 || cols % 8 || cols > 16384 || ldx < cols || ldx % 8 ||
+      ldq < cols || ldq % 8)
+    return fail(DIT_EINVAL, "bad arguments (8 <= cols <= 16384; cols, ldx, ldq multiples of 8, ldx, ldq >= cols)");
   hipError_t e = quant_rows_fp8(q, ldq, scale, x, OP_F32, ldx, rows, cols, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp8 quantization");
   return 0;

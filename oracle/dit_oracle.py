@@ -267,10 +267,12 @@ class WeightSet:
 # Inferenzlatenz").
 # reading: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
 # value 448; no infinities).  One scale per row: per output feature for a weight, per token
-# for an activation; scale = max|row| / 448, code = value / scale rounded to the nearest E4M3
-# value, ties to even mantissa, saturating at +-448; a row of zeros has scale 0 and codes 0.
-# The scale and the quotient are formed in fp32 (the kernel's precision) so that both sides
-# take the same rounding decisions; for the same reason the input of the second projection,
+# for an activation; scale = max|row| / 448 is the dequantization factor, and the codes are
+# value * (448 / max|row|) clamped to +-448 and rounded to the nearest E4M3 value, ties to
+# even mantissa (a multiply by one reciprocal per row rather than a division per value); a
+# row of zeros has scale 0 and codes 0.  Scale, reciprocal and products are formed in fp32
+# (the kernel's precision) so that both sides take the same rounding decisions; for the same
+# reason the input of the second projection,
 # which the kernel holds in fp16, is rounded to fp16 before it is quantized (the LayerNorm
 # output is quantized from fp32).  A projection y = x W^T then equals
 # scale_x scale_w sum_k code_x code_w.  Only the two big projections of every block (W1, W2)
@@ -326,10 +328,10 @@ def quantize_rows_fp8(x: np.ndarray, precision=np.float32):
     x rounded to `precision` (np.float32 or np.float16; round to nearest even)."""
     x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
     amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
-    q = (x32 / safe[:, None]).astype(np.float32)
-    q = np.where(scale[:, None] > 0, q, np.float32(0))
+    top = np.float32(E4M3_MAX)
+    scale = (amax / top).astype(np.float32)
+    recip = np.where(amax > 0, top / np.where(amax > 0, amax, np.float32(1)), np.float32(0)).astype(np.float32)
+    q = np.clip((x32 * recip[:, None]).astype(np.float32), -top, top)
     return e4m3_encode(e4m3_round(q.astype(np.float64))), scale
 
 

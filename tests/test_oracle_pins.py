@@ -695,8 +695,10 @@ def torch_fp8_rows(X, precision=torch.float32):
     """Row-wise E4M3 values through torch's float8_e4m3fn conversion (round to nearest even),
     independent of the oracle's rounding code; X is rounded to `precision` first."""
     X32 = X.to(precision).to(torch.float32)
-    s = X32.abs().amax(dim=1, keepdim=True) / 448.0
-    q = torch.where(s > 0, X32 / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(X32))
+    amax = X32.abs().amax(dim=1, keepdim=True)
+    s = amax / 448.0
+    r = torch.where(amax > 0, 448.0 / torch.where(amax > 0, amax, torch.ones_like(amax)), torch.zeros_like(amax))
+    q = torch.clamp(X32 * r, -448.0, 448.0)
     return q.to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
 
 
@@ -802,9 +804,9 @@ def test_fp8_block_matches_library_composition(sequential):
 
 def _per_tensor_quantize(x, precision=np.float32):
     x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
-    s = np.float32(np.max(np.abs(x32)) / np.float32(448.0))
-    q = (x32 / s).astype(np.float32)
-    return O.e4m3_encode(O.e4m3_round(q.astype(np.float64))), np.full(x32.shape[0], s, np.float32)
+    amax = np.float32(np.max(np.abs(x32)))
+    q = np.clip((x32 * (np.float32(448.0) / amax)).astype(np.float32), -448, 448)
+    return O.e4m3_encode(O.e4m3_round(q.astype(np.float64))), np.full(x32.shape[0], amax / np.float32(448), np.float32)
 
 
 def _wrong_layer_norm(x, eps):
