@@ -17,9 +17,11 @@
 // Workgroup tile 256 features x 256 tokens, 4 waves each 128 x 128 (8 x 8 accumulators of
 // 16 x 16), k advances 128 per LDS stage (two stages, 128 KB).  Per k-tile each wave reads its
 // 16 fragments once (32 bytes per lane each) and issues 64 MFMAs of 32 cycles, in row order
-// (weight sub-tile outer): the token fragments are read during row 0, weight fragment i + 1
-// during row i.  The LDS writes of the next tile and the global loads two tiles ahead sit
-// between the MFMAs of rows 1..4.  Scales are applied to the accumulators before the
+// (weight sub-tile outer); weight fragment i + 1 is read during row i.  The LDS writes of the
+// next tile and the global loads two tiles ahead sit between the MFMAs of rows 1..4; a second
+// barrier after them publishes the next tile, whose weight fragment 0 is read then and whose
+// token fragment j is read right after the last MFMA that uses token fragment j of this
+// tile, so the next tile starts without waiting on LDS.  Scales are applied to the accumulators before the
 // shared epilogues (gemm_common.h).
 #include "gemm_common.h"
 
@@ -142,26 +144,30 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
   gload(0);
   sstore(0);
   gload(min(1, KT - 1));
+  lds_sync();
+  read_frag(0, 0);
+#pragma unroll
+  for (int j = 0; j < TS; ++j) read_frag(0, FS + j);
 
   // one k-tile from stage kt & 1; the staging registers hold tile kt+1 and receive tile kt+2
   // (indices past the slice are clamped: the repeats are harmless)
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     const int nk = min(kt + 2, KT - 1);
-    lds_sync();  // tile kt is in stage cur; every wave is done reading the other stage
-    read_frag(cur, 0);
-    read_frag(cur, FS);
+    lds_sync();  // every wave is done reading the other stage (tile kt-1)
 #pragma unroll
     for (int m = 0; m < FS * TS; ++m) {
       const int i = m >> 3, j = m & 7;
       acc[i][j] = mma8(fr[i], fr[FS + j], acc[i][j]);
-      if (i == 0 && j < TS - 1) read_frag(cur, FS + j + 1);
       if (j == 0 && i < FS - 1) read_frag(cur, i + 1);
       if (m >= 8 && m < 40) {
         const int r = (m - 8) >> 1;
         if ((m & 1) == 0) write_one(cur ^ 1, r);
         else gload_one(nk, r);
       }
+      if (m == 39) lds_sync();  // tile kt+1 written by every wave
+      if (m == 40) read_frag(cur ^ 1, 0);            // its weight fragment 0 (free since row 0)
+      if (i == FS - 1) read_frag(cur ^ 1, FS + j);   // its token fragment j, just freed
       __builtin_amdgcn_sched_barrier(0);
     }
   }
