@@ -7,7 +7,8 @@ QKV + SwiGLU projection, QK RMSNorm + RoPE, attention, gated output projection) 
 output head.  Inputs (weights, text embeddings) are resident in HBM before timing starts.
 Prints ONE JSON line on stdout; details go to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute f16|bf16]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute f16|bf16|fp8]
+    (fp8: the block projections in row-wise E4M3 on the FP8 MFMA, everything else f16)
     python bench.py --mode copy-calibration      # elementwise copy of 1 GiB, for PMC scaling
     python bench.py --summarize-rocprof DIR ...  # rocprofv3 CSVs -> profiles/*.md (CPU only)
 """
@@ -24,18 +25,20 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (AMD spec)
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3,    # MI355X dense MFMA (AMD spec)
+               "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SOURCE = os.path.join(ROOT, "latent_flow_matching_amd", "csrc", "gemm_mfma.hip")
+GEMM_SOURCES = {"f16": "gemm_mfma.hip", "bf16": "gemm_mfma.hip", "fp8": "gemm_fp8.hip"}
 COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
 # rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
 # (patterns match the mangled names rocprofv3 prints: the epilogue is the last template argument)
-KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma)?I.*Li1EEEv"),
-                  ("linear2", r"k_gemm(?:_v3|_mfma)?I.*Li2EEEv"),
+KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8)?I.*Li1EEEv|k_gemm8<1>"),
+                  ("linear2", r"k_gemm(?:_v3|_mfma|8)?I.*Li2EEEv|k_gemm8<2>"),
+                  ("fp8_quant", r"k_quant_rows"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
                   ("ln_modulate", r"k_ln_modulate"),
-                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma)?I.*Li0EEEv|k_to_half"),
+                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8)?I.*Li0EEEv|k_to_half"),
                   ("conditioning", r"k_gemv|k_timestep_embed|k_silu"), ("euler noise", r"k_philox")]
 
 
@@ -55,6 +58,7 @@ def cpu_baseline(wl, cfg):
 
     segs = (wl.n_txt, wl.n_img, wl.n_ref)
     n = sum(segs)
+    fp8 = cfg.compute == "fp8"
     f64 = lambda a: np.asarray(a, np.float64)
     dims = O.Dims(hidden=cfg.hidden, heads=cfg.heads, mlp_hidden=cfg.mlp_hidden,
                   in_channels=cfg.in_channels, time_dim=cfg.time_dim)
@@ -71,10 +75,12 @@ def cpu_baseline(wl, cfg):
         w.update(S.gen_weights(cfg, names={f"mod.{kind}.s{s}" for s in range(cfg.n_mod_sets(kind))}))
         sets = [O.WeightSet(*(f64(w[f"blk{b}.s{s}.{t}"]) for t in ("w1", "w2", "qn", "kn")))
                 for s in range(cfg.sets_of_block(b))]
+        if fp8:  # the weights' E4M3 values (a load-time step, not timed)
+            sets = O.quantize_weights_fp8(sets)
         mods = O.segment_mods([f64(w[f"mod.{kind}.s{s}"]) for s in range(cfg.n_mod_sets(kind))],
                               sos, cond)
         t0 = time.perf_counter()
-        x = O.block_forward(x, segs, sets, sos, mods, pos, mask, dims)
+        x = O.block_forward(x, segs, sets, sos, mods, pos, mask, dims, act_fp8=fp8)
         dt += time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": len(blocks) * n / dt, "unit": "block tokens/s", "cores": threads,
@@ -82,19 +88,25 @@ def cpu_baseline(wl, cfg):
             "sample": f"blocks {', '.join(map(str, blocks))} of the stack in sequence at "
                       f"{'+'.join(str(s) for s in segs if s)} tokens, all rows, float64 "
                       f"NumPy/OpenBLAS, {dt:.1f} s of oracle time"
+                      + ("; row-wise E4M3 projections" if fp8 else "")
                       + ("; with guidance the oracle runs each branch as such a sequence"
                          if wl.guidance is not None else "")}
 
 
-def source_sha256(path=GEMM_SOURCE):
+def source_sha256(compute="f16"):
+    path = os.path.join(ROOT, "latent_flow_matching_amd", "csrc", GEMM_SOURCES[compute])
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def traffic_name(kernel, workload, compute):
+    return f"traffic_{kernel}_{workload}" + ("_fp8" if compute == "fp8" else "") + ".md"
+
+
+def load_traffic(kernel, workload, compute="f16"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary, or None when
     there is none or the kernel source has changed since the counters were taken."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+    path = os.path.join(PROFILES, traffic_name(kernel, workload, compute))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -102,7 +114,7 @@ def load_traffic(kernel, workload):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("source_sha256") != source_sha256():
+    if d.get("source_sha256") != source_sha256(compute):
         return None
     return d
 
@@ -141,6 +153,7 @@ def summarize_rocprof(args):
     """Write profiles/*.md from rocprofv3 output folders (runs on the CPU, reads CSV only)."""
     os.makedirs(PROFILES, exist_ok=True)
     wl = args.workload
+    sfx = "_fp8" if args.compute == "fp8" else ""
     if args.trace_dir:
         rows = _csv_rows(args.trace_dir, "kernel_stats.csv")
         if not rows:
@@ -158,7 +171,7 @@ def summarize_rocprof(args):
             lines.append(f"| {cls} | `{short[:70]}` | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                          f"{float(r['TotalDurationNs']) / total:.3f} |")
-        out = os.path.join(PROFILES, f"kernel_trace_{wl}.md")
+        out = os.path.join(PROFILES, f"kernel_trace_{wl}{sfx}.md")
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote {out}")
@@ -187,7 +200,7 @@ def summarize_rocprof(args):
             lines.append(f"| {cls} | {n} | {sum(util) / len(util):.1f} | "
                          f"{(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |" if util else
                          f"| {cls} | {n} | - | {(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |")
-        out = os.path.join(PROFILES, f"mfma_util_{wl}.md")
+        out = os.path.join(PROFILES, f"mfma_util_{wl}{sfx}.md")
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote {out}")
@@ -238,11 +251,11 @@ def summarize_rocprof(args):
                             "fetch_bytes_per_launch": fb / n,
                             "write_bytes_per_launch": wb / max(nw, 1),
                             "bytes_per_launch": fb / n + wb / max(nw, 1),
-                            "source_sha256": source_sha256()}
+                            "source_sha256": source_sha256(args.compute)}
         if out_json:
             lines += ["", "Used by bench.py for `roofline.traffic` while the GEMM source hash "
                       "matches:", "", "traffic_json: " + json.dumps(out_json)]
-        out = os.path.join(PROFILES, f"traffic_{args.traffic_kernel}_{wl}.md")
+        out = os.path.join(PROFILES, traffic_name(args.traffic_kernel, wl, args.compute))
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote {out}")
@@ -254,7 +267,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="flux2_stack_512txt_4096img_4step")
-    ap.add_argument("--compute", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--compute", default="f16", choices=["f16", "bf16", "fp8"])
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration"])
     ap.add_argument("--summarize-rocprof", action="store_true")
@@ -327,7 +340,7 @@ def main():
     torch.cuda.synchronize()
     # one untimed step with every kernel class timed: the per-kernel breakdown, and which class
     # dominates (the roofline kernel)
-    launches = wl.steps * (cfg.n_blocks * 5 + 8 + 4 * nseq) + 64
+    launches = wl.steps * (cfg.n_blocks * 7 + 8 + 4 * nseq) + 64  # room for fp8 and sequential blocks
     ctx.profile_start(launches)
     step(args.warmup)
     torch.cuda.synchronize()
@@ -353,7 +366,8 @@ def main():
     # RoPE, conditioning, output head and Euler update included in the time)
     total_flops = sum(prof[k][2] for k in ("linear1", "linear2", "attention")) * args.steps
     tflops = total_flops / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[args.compute]
+    # the metric is a share of the bf16 MFMA peak whatever the operand type
+    peak = PEAK_TFLOPS["bf16"]
     kernels = {}
     step_ms = sum(v[0] for v in prof.values())
     for k, (kms, cnt, fl, by) in prof.items():
@@ -369,13 +383,16 @@ def main():
         log(f"  {k:14s} {e}")
     dms, dcnt, dfl, _ = prof_timed[dom]  # live, over the timed steps
     achieved = dfl / dcnt / (dms / dcnt * 1e-3) / 1e12
-    tr = load_traffic(dom, wl.name)
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+    tr = load_traffic(dom, wl.name, args.compute)
+    # a contraction is priced at the peak of its own operand type
+    dpeak = PEAK_TFLOPS["fp8" if args.compute == "fp8" and dom in ("linear1", "linear2") else
+                        ("f32" if args.compute == "f32" else "bf16")]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": dpeak,
+                "unit": "TFLOP/s", "frac": round(achieved / dpeak, 4),
                 "traffic": round(tr["bytes_per_launch"]) if tr else None,
                 "flops_per_launch": dfl / dcnt, "avg_launch_us": round(dms / dcnt * 1e3, 2)}
     if tr:
-        roofline["traffic_source"] = f"profiles/traffic_{dom}_{wl.name}.md"
+        roofline["traffic_source"] = "profiles/" + traffic_name(dom, wl.name, args.compute)
 
     result = {
         "metric": "DiT block tokens/sec and attention+GEMM TFLOP/s (% bf16 MFMA peak)",
@@ -388,7 +405,8 @@ def main():
         "config": {"workload": wl.name, "tokens": n * nseq, "sequences": nseq,
                    "guidance": wl.guidance, "n_txt": wl.n_txt, "n_img": wl.n_img,
                    "n_ref": wl.n_ref, "blocks": blocks, "euler_steps": wl.steps,
-                   "weights": "bf16", "accumulate": "f32", "parallelism": "none"},
+                   "weights": "e4m3 row-wise (from bf16)" if args.compute == "fp8" else "bf16",
+                   "accumulate": "f32", "parallelism": "none"},
         "tflops": round(tflops, 1),
         "pct_peak": round(100 * tflops / peak, 2),
         "kernels": kernels,
