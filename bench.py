@@ -29,7 +29,8 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3,    # MI355X dense MF
                "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SOURCES = {"f16": "gemm_mfma.hip", "bf16": "gemm_mfma.hip", "fp8": "gemm_fp8.hip"}
+GEMM_SOURCES = {"f16": ("gemm_mfma.hip", "gemm_common.h"), "bf16": ("gemm_mfma.hip", "gemm_common.h"),
+                "fp8": ("gemm_fp8.hip", "gemm_common.h")}
 COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
 # rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
 # (patterns match the mangled names rocprofv3 prints: the epilogue is the last template argument)
@@ -94,9 +95,12 @@ def cpu_baseline(wl, cfg):
 
 
 def source_sha256(compute="f16"):
-    path = os.path.join(ROOT, "latent_flow_matching_amd", "csrc", GEMM_SOURCES[compute])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the GEMM's sources (kernel file and the shared epilogue header)."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES[compute]:
+        with open(os.path.join(ROOT, "latent_flow_matching_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_name(kernel, workload, compute):

@@ -13,14 +13,14 @@ import pytest
 
 from latent_flow_matching_amd import synth as S
 from oracle import dit_oracle as O
-from tests.helpers import (FP8_UPDATE_MAX_TOL, FP8_UPDATE_RMS_TOL, TINY2, TINY3, f64,
-                           oracle_block, rel_err, tol)
+from tests.helpers import (BF16_TOL, FP8_UPDATE_MAX_TOL, FP8_UPDATE_RMS_TOL, TINY2, TINY3, f64,
+                           oracle_block, oracle_model, rel_err, tol)
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from tests.test_gpu_parity import _forward_case, _rows, context, dev  # noqa: E402
+from tests.test_gpu_parity import TINY3_FM, _cfg_inputs, _forward_case, _rows, context, dev  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -148,3 +148,39 @@ def test_fp8_flux2_block_full_width_sampled_rows(b, n_img, grid):
     cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1, compute="fp8")
     n = 512 + n_img
     check_block(cfg, b, 512, grid, rows=_rows(n), max_tokens=n)
+
+
+def test_fp8_denoise_cfg_matches_oracle():
+    """Guidance (a batch of two sequences) on the E4M3 path: FLUX.3 with a reference image."""
+    cfg = replace(TINY3, compute="fp8")
+    ctx, w = context(cfg, 600)
+    grid = (8, 6)
+    noise = S.gen_latents(48, cfg.in_channels, key=(2,))
+    _, ref, txt, txt_u = _cfg_inputs(cfg, 20, grid, (4, 4))
+    lat = dev(noise)
+    print("[fp8 denoise_cfg] FLUX.3 tiny", flush=True)
+    ctx.denoise_cfg(lat, dev(txt), dev(txt_u), grid, 3, 2.5, -1, dev(ref), (4, 4))
+    torch.cuda.synchronize()
+    want = O.denoise_cfg(oracle_model(cfg, w), f64(noise), f64(txt), f64(txt_u), grid, 3, 2.5,
+                         f64(ref), (4, 4))
+    err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
+    print(f"    fp8 denoise_cfg update err {err:.3e}", flush=True)
+    assert err <= BF16_TOL
+
+
+def test_fp8_flow_map_denoise_matches_oracle():
+    """A flow-map model on the E4M3 path: each step's target time, one reference image."""
+    cfg = replace(TINY3_FM, compute="fp8")
+    ctx, w = context(cfg, 600)
+    grid, ref_grid = (8, 6), (4, 4)
+    noise = S.gen_latents(48, cfg.in_channels, key=(2,))
+    ref = S.gen_latents(16, cfg.in_channels, key=(3,))
+    txt = S.gen_text(20, cfg.hidden)
+    lat = dev(noise)
+    print("[fp8 flow-map denoise] FLUX.3 tiny", flush=True)
+    ctx.denoise(lat, dev(txt), grid, 4, -1, dev(ref), ref_grid)
+    torch.cuda.synchronize()
+    want = O.denoise(oracle_model(cfg, w), f64(noise), f64(txt), grid, 4, f64(ref), ref_grid)
+    err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
+    print(f"    fp8 flow-map denoise update err {err:.3e}", flush=True)
+    assert err <= BF16_TOL
