@@ -54,7 +54,7 @@ typedef struct dit_ctx dit_ctx;
  *             output, [attention || SwiGLU]) are quantized per token on the fly, and the
  *             products run on the E4M3 MFMA at twice the 16-bit rate.  Scale = max |row| / 448,
  *             code = value * (448 / max |row|) rounded to nearest even E4M3.  Everything else
- *             computes as DIT_F16. */
+ *             computes as DIT_F16.  Needs hidden + mlp_hidden <= 16384. */
 enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2, DIT_FP8 = 3 };
 
 /* model families.

@@ -231,6 +231,9 @@ int validate_config(const dit_config *c) {
   if (c->double_wiring != 0 && c->double_wiring != 1) return fail(DIT_EINVAL, "double_wiring must be 0 or 1");
   if (c->double_wiring && c->arch != DIT_FLUX2)
     return fail(DIT_EUNSUPPORTED, "double_wiring applies to DIT_FLUX2 double blocks only");
+  if (c->compute == DIT_FP8 && c->hidden + c->mlp_hidden > 16384)
+    return fail(DIT_EUNSUPPORTED, "DIT_FP8 quantizes rows of at most 16384 values (hidden + mlp_hidden = %d)",
+                c->hidden + c->mlp_hidden);
   return 0;
 }
 
