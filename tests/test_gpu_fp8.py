@@ -184,3 +184,12 @@ def test_fp8_flow_map_denoise_matches_oracle():
     err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
     print(f"    fp8 flow-map denoise update err {err:.3e}", flush=True)
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("b", [0, 1], ids=["per_mode", "joint"])
+def test_fp8_flux3_block_1024px_ref_sampled_rows(b):
+    """Full-width FLUX.3 per-mode (three weight sets, block-diagonal) and joint blocks at
+    512 text + 4096 image + 4096 reference tokens on the E4M3 path."""
+    cfg = replace(S.FLUX3_KLEIN, n_stream_blocks=1, n_shared_blocks=1, compute="fp8")
+    n = 512 + 4096 + 4096
+    check_block(cfg, b, 512, (64, 64), (64, 64), rows=_rows(n), max_tokens=n)
