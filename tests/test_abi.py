@@ -1,6 +1,7 @@
 """The C-ABI library builds, loads and exports every symbol include/dit.h declares; host-side
 validation and error paths work without a GPU (no compute calls here)."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -23,6 +24,32 @@ def test_exports_every_declared_symbol(lib):
             "dit_get_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_header_compiles_as_c_and_links(lib, tmp_path):
+    """include/dit.h is plain C: a C99 translation unit that takes the address of every
+    declared function compiles and links against the built library."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = dit.header_functions()
+    src = tmp_path / "abi.c"
+    src.write_text('#include "dit.h"\n#include <stdio.h>\n'
+                   "typedef void (*fn)(void);\n"
+                   "static fn table[] = {" + ", ".join(f"(fn){n}" for n in names) + "};\n"
+                   "int main(void) { printf(\"%d\\n\", (int)(sizeof table / sizeof table[0])); "
+                   "return 0; }\n")
+    libdir = os.path.dirname(dit.LIB_PATH)
+    out = tmp_path / "abi"
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-Wno-pedantic",
+                        "-I", os.path.join(os.path.dirname(libdir), "include"), str(src),
+                        "-L", libdir, "-ldit", f"-Wl,-rpath,{libdir}", "-o", str(out)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([str(out)], capture_output=True, text=True)
+    assert run.returncode == 0 and int(run.stdout) == len(names), run.stderr
 
 
 def _cfg(**kw):
