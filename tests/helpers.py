@@ -22,6 +22,12 @@ FP8_TOL = 2e-2           # row-wise E4M3 path: forward outputs against the E4M3 
 # 0.4-0.7% and max errors of 6-14% of RMS(u); the bars keep about 3x and 1.5x margin.
 FP8_UPDATE_RMS_TOL = 2e-2
 FP8_UPDATE_MAX_TOL = 2e-1
+# Sequentially wired double blocks at full width compound those flips: the attention half's
+# error reaches the second LayerNorm, whose E4M3 codes then flip as well, and so on through
+# the MLP half.  The same emulation on that block (512 + 4096 tokens) gives 3.8% RMS and 38%
+# max; the bars keep about 2x and 1.6x margin.
+FP8_SEQ_UPDATE_RMS_TOL = 8e-2
+FP8_SEQ_UPDATE_MAX_TOL = 6e-1
 BF16_OPERAND_TOL = 5e-2   # bf16 MFMA operands at full width: rounding of xm and the SwiGLU
                            # output alone exceeds 2e-2 (CPU emulation of the rounding points)
 

@@ -670,6 +670,58 @@ def test_sequential_block_full_width_sampled_rows(n_img, grid):
     assert err <= BF16_TOL
 
 
+def test_forward_cfg_full_width_matches_oracle():
+    """Guidance at full FLUX.2 width (one double and one single block): both branches of
+    512 text + 1024 image tokens as one batch of 2 (four row groups in the double block), against
+    the oracle's two calls, with the guided bound of the small-shape test."""
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
+    ctx, w = context(cfg, 2 * 1536)
+    grid = (32, 32)
+    lat, _, txt, txt_u = _cfg_inputs(cfg, 512, grid, None)
+    v = torch.empty((1024, cfg.in_channels), device="cuda")
+    print("[forward_cfg] FLUX.2 full width, 2 x (512+1024) tokens, g=3.5", flush=True)
+    ctx.forward_cfg(dev(lat), dev(txt), dev(txt_u), grid, 0.6, 3.5, v)
+    torch.cuda.synchronize()
+    m = oracle_model(cfg, w)
+    t = float(np.float32(0.6))
+    vc = O.forward(m, f64(lat), f64(txt), grid, t)
+    vu = O.forward(m, f64(lat), f64(txt_u), grid, t)
+    want = O.guided_velocity(vc, vu, 3.5)
+    rms = lambda a: float(np.sqrt(np.mean(a * a)))
+    err = float(np.max(np.abs(v.cpu().numpy().astype(np.float64) - want)))
+    bound = BF16_TOL * (3.5 * rms(vc) + 2.5 * rms(vu))
+    print(f"    forward_cfg max err {err:.3e}, bound {bound:.3e}", flush=True)
+    assert err <= bound
+
+
+def test_sequential_fp8_block_full_width_sampled_rows():
+    """The sequentially wired double block on the E4M3 path at full width, 512 + 4096 tokens:
+    each half quantizes its own inputs (bars for the compounded code flips of this wiring)."""
+    from tests.helpers import FP8_SEQ_UPDATE_MAX_TOL, FP8_SEQ_UPDATE_RMS_TOL
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1, double_wiring=True,
+                  compute="fp8")
+    n = 512 + 4096
+    rows = _rows(n)
+    ctx, w = context(cfg, n)
+    x = S.gen_tokens(n, cfg.hidden, key=(0,))
+    cond = S.gen_cond(3, cfg.hidden)
+    pos = O.positions(512, (64, 64), ())
+    xt = dev(x)
+    from latent_flow_matching_amd import dit
+    print("[block] sequential fp8 full width 512+4096", flush=True)
+    ctx.block_forward(0, xt, 512, 4096, 0, dev(pos), dev(cond), dit.DIT_MASK_DEFAULT)
+    torch.cuda.synchronize()
+    got = xt.cpu().numpy()[rows].astype(np.float64)
+    ref = oracle_block(cfg, w, 0, x, (512, 4096, 0), pos, cond, rows=rows)
+    u_got, u_ref = got - f64(x[rows]), ref - f64(x[rows])
+    rms_u = float(np.sqrt(np.mean(u_ref ** 2)))
+    e_rms = float(np.sqrt(np.mean((u_got - u_ref) ** 2))) / rms_u
+    e_max = float(np.max(np.abs(u_got - u_ref))) / rms_u
+    print(f"    update error: RMS {e_rms:.3e} (bar {FP8_SEQ_UPDATE_RMS_TOL}), max {e_max:.3e} "
+          f"(bar {FP8_SEQ_UPDATE_MAX_TOL})", flush=True)
+    assert e_rms <= FP8_SEQ_UPDATE_RMS_TOL and e_max <= FP8_SEQ_UPDATE_MAX_TOL
+
+
 # ----------------------------------------------------------------- full benchmark shapes, sampled rows
 
 def _rows(n, k=24, seed=0):
