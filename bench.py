@@ -201,9 +201,9 @@ def summarize_rocprof(args):
             util = c.get("MfmaUtil", [])
             fl = c.get("MfmaFlopsF16", []) or c.get("MfmaFlopsBF16", [])
             n = max(len(util), len(fl))
-            lines.append(f"| {cls} | {n} | {sum(util) / len(util):.1f} | "
-                         f"{(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |" if util else
-                         f"| {cls} | {n} | - | {(sum(fl) / len(fl) / 1e12) if fl else 0:.3f} |")
+            flc = f"{sum(fl) / len(fl) / 1e12:.3f}" if fl else "- (not collected)"
+            lines.append(f"| {cls} | {n} | {sum(util) / len(util):.1f} | {flc} |" if util else
+                         f"| {cls} | {n} | - | {flc} |")
         out = os.path.join(PROFILES, f"mfma_util_{wl}{sfx}.md")
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
