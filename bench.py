@@ -40,7 +40,7 @@ KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8)?I.*Li1EEEv|k_gemm8<1>"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
                   ("ln_modulate", r"k_ln_modulate"),
                   ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8)?I.*Li0EEEv|k_to_half"),
-                  ("conditioning", r"k_gemv|k_timestep_embed|k_silu"), ("euler noise", r"k_philox")]
+                  ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
 
 
 def log(*a):

@@ -120,9 +120,9 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
 // dst[i] = src[i] rounded to the 16-bit type (OP_BF16 / OP_F16), i < n
 hipError_t to_half(void *dst, int type, const float *src, int64_t n, hipStream_t s);
 // y[v * ldy + i] = sum_k W[i][k] * act(x[v][k]) for v < nvec (x contiguous [nvec][k];
-// ldy 0: rows).  silu_in: the vectors go through SiLU first, into scratch [nvec][k] fp32
+// ldy 0: rows).  silu_in: act = SiLU (applied as the vectors are loaded), else identity
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
-                int silu_in, float *scratch, hipStream_t s, int ldy = 0);
+                int silu_in, hipStream_t s, int ldy = 0);
 // e[v] = [cos(1000 t_v f_j), sin(1000 t_v f_j)], f_j = 10000^(-j/(dim/2)), 1 <= nvec <= 4
 hipError_t timestep_embed(float *e, const double *t_host, int nvec, int dim, hipStream_t s);
 hipError_t copy_rows_f32(float *dst, int ldd, const float *src, int lds, int rows, int cols,

@@ -257,9 +257,9 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
 // 16-bit path: each lane owns 8 consecutive dims of one (token, head) row (16-byte loads and
 // stores; its four RoPE pairs stay in the lane), 16 lanes per row, so a wave handles 4 tokens
 // at once and reduces the sum of squares with 4 xor-shuffles inside its 16-lane group.  All
-// loads of a wave's 16 tokens are issued before any arithmetic.  The workgroup then writes V
-// of its 64 tokens transposed into vt (zeros past n): the P.V operand layout of the attention
-// kernel.
+// loads (V of the workgroup's 64 tokens, then q, k and the RoPE table of the wave's 16 tokens)
+// are issued before any arithmetic.  The workgroup then writes V transposed into vt (zeros
+// past n): the P.V operand layout of the attention kernel.
 template <typename T>
 __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_model, T *vt,
                                                          int ldv, const float *cs, int n,
@@ -271,6 +271,17 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y, t0 = blockIdx.x * 64;
   const int sub = lane >> 4, c8 = (lane & 15) * 8;
+  // V of the workgroup's 64 tokens (16-byte chunk c of row c / 16), loaded first so that its
+  // latency overlaps the q/k work; written transposed after it (zeros past n)
+  u32x4 vv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j, tok = t0 + (c >> 4);
+    vv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (vt != nullptr && tok < n)
+      vv[j] = *reinterpret_cast<const u32x4 *>(qkv + (size_t)tok * ldq + 2 * d_model + h * 128 +
+                                               (c & 15) * 8);
+  }
   V8 qv[4], kv[4];
   f32x4 ca[4], cb[4];
 #pragma unroll
@@ -337,17 +348,14 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_m
   // so the eight rows one read instruction touches fall in distinct banks
   constexpr int kPitch = 130;
   __shared__ __attribute__((aligned(16))) T tile[64 * kPitch];
-  for (int c = threadIdx.x; c < 64 * 16; c += 256) {
-    const int r = c >> 4, ch = c & 15;
-    const int tok = t0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (tok < n)
-      val = *reinterpret_cast<const u32x4 *>(qkv + (size_t)tok * ldq + 2 * d_model + h * 128 + ch * 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + 256 * j, r = c >> 4, ch = c & 15;
     uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[r * kPitch + ch * 8]);  // 4-byte aligned
-    dst[0] = val.x;
-    dst[1] = val.y;
-    dst[2] = val.z;
-    dst[3] = val.w;
+    dst[0] = vv[j].x;
+    dst[1] = vv[j].y;
+    dst[2] = vv[j].z;
+    dst[3] = vv[j].w;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < 128 * 8; c += 256) {
@@ -394,7 +402,7 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
 // GEMV for the conditioning path: y[v][i] = sum_k W[i][k] * act(x[v][k]), act = SiLU or
 // identity.  Used for the timestep MLP and for mod = W_mod . SiLU(cond) ("FLUX.3 Image Klein
 // in Diffusers", "Modulation pro Token-Typ ...": scale, shift and gate come from the
-// timestep embedding).  4 waves x 4 rows per workgroup; the input vectors sit in LDS.
+// timestep embedding).  4 waves x 3 rows per workgroup; the input vectors sit in LDS.
 // ------------------------------------------------------------------------------------------
 // Eight consecutive weights as raw registers (16-bit: one 16-byte load; fp32: two) and their
 // conversion to floats.
@@ -433,23 +441,20 @@ template <> struct Load16<float> {
   }
 };
 
-// GEMV over up to 3 vectors, bound by streaming the weights once.  The (activated) vectors are
-// copied into LDS by every workgroup of 16 rows; each wave owns 4 rows and issues all of its
-// 16-byte weight loads (4 rows x k/512 per lane) before using any, so about 4 waves per SIMD
-// keep the HBM pipe full; one wave reduction per (row, vector) at the end.
-constexpr int kGemvRows = 4, kGemvChunks = 8;  // rows per wave; k <= 512 * kGemvChunks
+// GEMV over up to 3 vectors, bound by streaming the weights once.  Each wave owns 3 rows and
+// issues all of its 16-byte weight loads (3 rows x k/512 per lane) first; then the workgroup
+// loads the vectors in batches of kGemvXBatch 16-byte loads per thread (SiLU applied on the
+// way when asked) and stages them in LDS, so the weights are in flight before any wait; one
+// wave reduction per (row, vector) at the end.
+constexpr int kGemvRows = 3, kGemvChunks = 8;  // rows per wave; k <= 512 * kGemvChunks
+constexpr int kGemvXPasses = 3 * 512 * kGemvChunks / 1024;  // float4 vector loads per thread
+constexpr int kGemvXBatch = 4;                              // of them in flight at once
+static_assert(kGemvXPasses % kGemvXBatch == 0, "vector staging batches");
 
-__global__ void k_silu(float *dst, const float *src, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = silu(src[i]);
-}
-
-template <typename TW>
+template <typename TW, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, int k,
                                                const float *x, int nvec, int ldy) {
   extern __shared__ float xs[];  // [nvec][k]
-  for (int i = threadIdx.x * 4; i < nvec * k; i += 256 * 4)
-    *reinterpret_cast<f32x4 *>(xs + i) = *reinterpret_cast<const f32x4 *>(x + i);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * 4 + wave) * kGemvRows;
   typedef typename Load16<TW>::raw Raw;
@@ -460,6 +465,27 @@ __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, i
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r)
       if (c < k && row0 + r < rows) raw[r][i] = Load16<TW>::load(w + (size_t)(row0 + r) * k + c);
+  }
+#pragma unroll
+  for (int p0 = 0; p0 < kGemvXPasses; p0 += kGemvXBatch) {
+    f32x4 xr[kGemvXBatch];
+#pragma unroll
+    for (int p = 0; p < kGemvXBatch; ++p) {
+      const int i = ((p0 + p) * 256 + threadIdx.x) * 4;
+      if (i < nvec * k) xr[p] = *reinterpret_cast<const f32x4 *>(x + i);
+    }
+#pragma unroll
+    for (int p = 0; p < kGemvXBatch; ++p) {
+      const int i = ((p0 + p) * 256 + threadIdx.x) * 4;
+      if (i < nvec * k) {
+        f32x4 v = xr[p];
+        if constexpr (SILU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu(v[e]);
+        }
+        *reinterpret_cast<f32x4 *>(xs + i) = v;
+      }
+    }
   }
   __syncthreads();
   float acc[kGemvRows][3];
@@ -499,25 +525,29 @@ __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, i
     }
 }
 
+template <typename TW>
+hipError_t launch_gemv(float *y, const TW *w, int rows, int k, const float *x, int nvec,
+                       int silu_in, hipStream_t s, int ldy) {
+  const size_t lds = sizeof(float) * nvec * k;
+  const dim3 grid((rows + 4 * kGemvRows - 1) / (4 * kGemvRows));
+  if (silu_in)
+    k_gemv<TW, true><<<grid, 256, lds, s>>>(y, w, rows, k, x, nvec, ldy);
+  else
+    k_gemv<TW, false><<<grid, 256, lds, s>>>(y, w, rows, k, x, nvec, ldy);
+  return hipGetLastError();
+}
+
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
-                int silu_in, float *scratch, hipStream_t s, int ldy) {
+                int silu_in, hipStream_t s, int ldy) {
   if (nvec < 1 || nvec > 3 || k % 8 || k > 512 * kGemvChunks) return hipErrorInvalidValue;
   if (ldy == 0) ldy = rows;
   if (ldy < rows) return hipErrorInvalidValue;
-  if (silu_in) {
-    if (!scratch) return hipErrorInvalidValue;
-    k_silu<<<(nvec * k + 255) / 256, 256, 0, s>>>(scratch, x, nvec * k);
-    x = scratch;
-  }
-  const size_t lds = sizeof(float) * nvec * k;
-  const dim3 grid((rows + 4 * kGemvRows - 1) / (4 * kGemvRows));
   switch (w_type) {
-    case OP_BF16: k_gemv<bf16><<<grid, 256, lds, s>>>(y, (const bf16 *)w, rows, k, x, nvec, ldy); break;
-    case OP_F16: k_gemv<f16><<<grid, 256, lds, s>>>(y, (const f16 *)w, rows, k, x, nvec, ldy); break;
-    case OP_F32: k_gemv<float><<<grid, 256, lds, s>>>(y, (const float *)w, rows, k, x, nvec, ldy); break;
-    default: return hipErrorInvalidValue;
+    case OP_BF16: return launch_gemv(y, (const bf16 *)w, rows, k, x, nvec, silu_in, s, ldy);
+    case OP_F16: return launch_gemv(y, (const f16 *)w, rows, k, x, nvec, silu_in, s, ldy);
+    case OP_F32: return launch_gemv(y, (const float *)w, rows, k, x, nvec, silu_in, s, ldy);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------------------------------

@@ -90,7 +90,6 @@ struct dit_ctx {
   float *noise = nullptr;    // [max_tokens][C] image-to-image noise drawn from a seed
   float *fmodv = nullptr;    // [3][2D]
   float *xf = nullptr;       // fp32 path: [max_tokens][D] final-norm output
-  float *act = nullptr;      // [3][D] SiLU of the GEMV input vectors
   int cus = 0;               // compute units, rounded down to a multiple of 8
   int lean_grid = 0;         // attention: one workgroup per compute unit (multiple of 8)
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
@@ -504,7 +503,6 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->tgt, (size_t)D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->noise, (size_t)c.max_tokens * C * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->act, (size_t)3 * D * 4);
   if (ctx->op != OP_F32 && ctx->lean_grid > 0) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_part,
                           (size_t)2 * ctx->lean_grid * attn_part_floats * 4);
@@ -554,7 +552,7 @@ int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) 
   const int D = ctx->D();
   for (int s = 0; s < ctx->nsets_kind(kind); ++s)
     DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, ctx->mod_rows(kind), D, cond, 3, 1,
-                   ctx->act, stream, ctx->mod_ld()),
+                   stream, ctx->mod_ld()),
               "modulation gemv");
   return 0;
 }
@@ -745,12 +743,12 @@ int prepare_conditioning(dit_ctx *ctx, double t, double t_target, hipStream_t st
   if (c.arch == DIT_FLUX3) tv[0] = tv[2] = 0.0;
   const int ne = c.flow_map ? 4 : 3;
   DIT_CHECK(timestep_embed(ctx->temb_e, tv, ne, T, stream), "timestep_embed");
-  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, T, ctx->temb_e, 3, 0, nullptr, stream), "temb l1");
-  DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, ctx->act, stream), "temb l2");
+  DIT_CHECK(gemv(ctx->temb_h, ctx->temb1, ctx->op, D, T, ctx->temb_e, 3, 0, stream), "temb l1");
+  DIT_CHECK(gemv(ctx->cond, ctx->temb2, ctx->op, D, D, ctx->temb_h, 3, 1, stream), "temb l2");
   if (c.flow_map) {
-    DIT_CHECK(gemv(ctx->temb_h + 3 * D, ctx->ttgt1, ctx->op, D, T, ctx->temb_e + 3 * T, 1, 0, nullptr,
+    DIT_CHECK(gemv(ctx->temb_h + 3 * D, ctx->ttgt1, ctx->op, D, T, ctx->temb_e + 3 * T, 1, 0,
                    stream), "target temb l1");
-    DIT_CHECK(gemv(ctx->tgt, ctx->ttgt2, ctx->op, D, D, ctx->temb_h + 3 * D, 1, 1, ctx->act, stream),
+    DIT_CHECK(gemv(ctx->tgt, ctx->ttgt2, ctx->op, D, D, ctx->temb_h + 3 * D, 1, 1, stream),
               "target temb l2");
     DIT_CHECK(add_row(ctx->cond, 3, D, ctx->tgt, stream), "target time");
   }
@@ -758,7 +756,7 @@ int prepare_conditioning(dit_ctx *ctx, double t, double t_target, hipStream_t st
     if (int rc = compute_mods(ctx, 0, ctx->cond, stream)) return rc;
   if (c.n_shared_blocks > 0)
     if (int rc = compute_mods(ctx, 1, ctx->cond, stream)) return rc;
-  DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, ctx->act, stream), "final modulation");
+  DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, stream), "final modulation");
   return 0;
 }
 

@@ -239,6 +239,29 @@ def test_forward_several_references_matches_oracle(cfg):
     assert err <= tol(cfg, full_width=False)
 
 
+REF_GRIDS_MAX = [(2, 3), (3, 2), (1, 4), (4, 1), (2, 2), (1, 1), (3, 3), (2, 5), (1, 2), (2, 1)]
+
+
+@pytest.mark.parametrize("cfg", [TINY3, TINY2], ids=["flux3_f16", "flux2_f16"])
+def test_forward_ten_references_matches_oracle(cfg):
+    """The most reference images a call takes (ten, at l = -1 .. -10), of mixed small sizes."""
+    ctx, w = context(cfg, 600)
+    grid = (9, 7)
+    n_ref = sum(h * w_ for h, w_ in REF_GRIDS_MAX)
+    lat = S.gen_latents(63, cfg.in_channels)
+    ref = S.gen_latents(n_ref, cfg.in_channels, key=(4,))
+    txt = S.gen_text(50, cfg.hidden)
+    v = torch.empty((63, cfg.in_channels), device="cuda")
+    print(f"[ten references] arch={cfg.arch} ref tokens={n_ref}", flush=True)
+    ctx.forward_ex(dev(lat), dev(txt), grid, 0.5, v, ref_lat=dev(ref), ref_grids=REF_GRIDS_MAX)
+    torch.cuda.synchronize()
+    want = O.forward(oracle_model(cfg, w), f64(lat), f64(txt), grid, 0.5, f64(ref),
+                     list(REF_GRIDS_MAX))
+    err = rel_err(v.cpu().numpy(), want)
+    print(f"    ten references err {err:.3e}", flush=True)
+    assert err <= tol(cfg, full_width=False)
+
+
 @pytest.mark.parametrize("seeded", [True, False], ids=["seeded_noise", "given_noise"])
 def test_img2img_matches_oracle(seeded):
     """Image-to-image at strength 0.6 of 5 steps: the clean latents moved to t = 3/5 on the
