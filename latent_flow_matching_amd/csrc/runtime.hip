@@ -1152,7 +1152,8 @@ extern "C" int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx
 extern "C" int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
                             const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream) {
   g_err.clear();
-  if (!qx || !sx || !qw || !sw || !y || m < 0 || n < 256 || n % 256 || k < 128 || k % 128)
+  if (!qx || !sx || !qw || !sw || !y || m < 0) return fail(DIT_EINVAL, "bad arguments");
+  if (n < 256 || n % 256 || k < 128 || k % 128)
     return fail(DIT_EUNSUPPORTED, "dit_gemm_fp8 needs n %% 256 == 0 and k %% 128 == 0 (n %d, k %d)", n, k);
   if (ldx < k || ldx % 16 || ldw < k || ldw % 16 || ldy < n || ldy % 4)
     return fail(DIT_EINVAL, "bad strides (ldx, ldw >= k, multiples of 16; ldy >= n, multiple of 4)");

@@ -94,6 +94,18 @@ def test_bad_config_rejected(lib, field, value, msg):
     assert msg in dit.last_error()
 
 
+@pytest.mark.parametrize("fields,msg", [
+    ({"double_wiring": 2}, "double_wiring must be 0 or 1"),
+    ({"double_wiring": 1, "arch": dit.DIT_FLUX3}, "DIT_FLUX2 double blocks only"),
+    ({"compute": dit.DIT_FP8, "mlp_hidden": 16384}, "at most 16384 values"),
+])
+def test_bad_config_combination_rejected(lib, fields, msg):
+    arr, n, keep = _table()
+    h = lib.dit_ctx_create(ctypes.byref(_cfg(**fields)), arr, n)
+    assert not h
+    assert msg in dit.last_error()
+
+
 @pytest.mark.parametrize("kw,msg", [
     ({"drop": "blk0.s1.w2"}, "missing weight 'blk0.s1.w2'"),
     ({"extra": "blk9.s0.w1"}, "unknown weight 'blk9.s0.w1'"),
@@ -125,6 +137,23 @@ def test_null_context_calls_fail(lib):
     assert lib.dit_profile_select(None, b"linear1") == dit.DIT_EINVAL
     assert lib.dit_profile_stop(None) == dit.DIT_EINVAL
     lib.dit_ctx_free(None)   # no-op
+
+
+def test_fp8_entries_check_arguments_before_any_launch(lib):
+    """Argument errors of the row-wise FP8 entries come back as codes, with no device touched."""
+    P = ctypes.c_void_p
+    buf = P(64)  # never dereferenced: every call below fails its checks first
+    assert lib.dit_quantize_rows_fp8(None, 2, 16, 16, buf, 16, buf, None) == dit.DIT_EINVAL
+    assert lib.dit_quantize_rows_fp8(buf, 2, 12, 12, buf, 12, buf, None) == dit.DIT_EINVAL
+    assert lib.dit_quantize_rows_fp8(buf, 2, 32, 16, buf, 32, buf, None) == dit.DIT_EINVAL
+    assert lib.dit_quantize_rows_fp8(buf, 2, 16392, 16392, buf, 16392, buf, None) == dit.DIT_EINVAL
+    assert "cols" in dit.last_error()
+    assert lib.dit_gemm_fp8(None, buf, 4, 128, buf, buf, 256, 128, 128, buf, 256, None) == dit.DIT_EINVAL
+    assert lib.dit_gemm_fp8(buf, buf, -1, 128, buf, buf, 256, 128, 128, buf, 256, None) == dit.DIT_EINVAL
+    assert lib.dit_gemm_fp8(buf, buf, 4, 128, buf, buf, 128, 128, 128, buf, 128, None) == dit.DIT_EUNSUPPORTED
+    assert lib.dit_gemm_fp8(buf, buf, 4, 64, buf, buf, 256, 64, 64, buf, 256, None) == dit.DIT_EUNSUPPORTED
+    assert lib.dit_gemm_fp8(buf, buf, 4, 120, buf, buf, 256, 128, 128, buf, 256, None) == dit.DIT_EINVAL
+    assert "strides" in dit.last_error()
 
 
 def test_binding_refuses_to_run_without_library(tmp_path):
