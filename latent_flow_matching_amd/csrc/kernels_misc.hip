@@ -402,7 +402,7 @@ hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, vo
 // GEMV for the conditioning path: y[v][i] = sum_k W[i][k] * act(x[v][k]), act = SiLU or
 // identity.  Used for the timestep MLP and for mod = W_mod . SiLU(cond) ("FLUX.3 Image Klein
 // in Diffusers", "Modulation pro Token-Typ ...": scale, shift and gate come from the
-// timestep embedding).  4 waves x 3 rows per workgroup; the input vectors sit in LDS.
+// timestep embedding).  8 rows per workgroup, k sliced over its 256 threads.
 // ------------------------------------------------------------------------------------------
 // Eight consecutive weights as raw registers (16-bit: one 16-byte load; fp32: two) and their
 // conversion to floats.
@@ -441,105 +441,119 @@ template <> struct Load16<float> {
   }
 };
 
-// GEMV over up to 3 vectors, bound by streaming the weights once.  Each wave owns 3 rows and
-// issues all of its 16-byte weight loads (3 rows x k/512 per lane) first; then the workgroup
-// loads the vectors in batches of kGemvXBatch 16-byte loads per thread (SiLU applied on the
-// way when asked) and stages them in LDS, so the weights are in flight before any wait; one
-// wave reduction per (row, vector) at the end.
-constexpr int kGemvRows = 3, kGemvChunks = 8;  // rows per wave; k <= 512 * kGemvChunks
-constexpr int kGemvXPasses = 3 * 512 * kGemvChunks / 1024;  // float4 vector loads per thread
-constexpr int kGemvXBatch = 4;                              // of them in flight at once
-static_assert(kGemvXPasses % kGemvXBatch == 0, "vector staging batches");
+// GEMV over up to 3 vectors, bound by streaming the weights once.  k-sliced: thread t owns
+// the 16-byte pieces t and t + 256 of every row (k <= 4096), so it loads the (activated)
+// vector values of its pieces once, into registers, and reuses them for the workgroup's
+// kGemvRows rows, whose weight loads it issues first.  Each (row, vector) sum is then reduced
+// over the workgroup: three halving exchanges inside each wave (a lane keeps half of its sums
+// and adds its partner's), a butterfly over the remaining 8 lanes, then the 4 waves' partial
+// sums in a fixed order through LDS.
+constexpr int kGemvRows = 8;              // rows per workgroup
+constexpr int kGemvSums = 3 * kGemvRows;  // (row, vector) sums per thread
+static_assert(kGemvSums % 8 == 0, "three halving exchanges");
+
+template <int N>
+__device__ __forceinline__ void halve(const float (&in)[2 * N], float (&out)[N], int lane, int offset) {
+  const bool up = lane & offset;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = up ? in[i + N] : in[i], send = up ? in[i] : in[i + N];
+    out[i] = keep + __shfl_xor(send, offset, kWave);
+  }
+}
 
 template <typename TW, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv(float *y, const TW *w, int rows, int k,
                                                const float *x, int nvec, int ldy) {
-  extern __shared__ float xs[];  // [nvec][k]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * 4 + wave) * kGemvRows;
+  constexpr int NS = kGemvSums;
+  __shared__ float red[4][NS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row0 = blockIdx.x * kGemvRows;
+  const int np = k >> 3;  // 16-byte pieces per row
   typedef typename Load16<TW>::raw Raw;
-  Raw raw[kGemvRows][kGemvChunks];
+  Raw raw[kGemvRows][2];
 #pragma unroll
-  for (int i = 0; i < kGemvChunks; ++i) {
-    const int c = (i * 64 + lane) * 8;
+  for (int j = 0; j < 2; ++j) {
+    const int p = t + 256 * j;
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r)
-      if (c < k && row0 + r < rows) raw[r][i] = Load16<TW>::load(w + (size_t)(row0 + r) * k + c);
+      if (p < np && row0 + r < rows) raw[r][j] = Load16<TW>::load(w + (size_t)(row0 + r) * k + 8 * p);
   }
+  float xv[2][3][8];
 #pragma unroll
-  for (int p0 = 0; p0 < kGemvXPasses; p0 += kGemvXBatch) {
-    f32x4 xr[kGemvXBatch];
+  for (int j = 0; j < 2; ++j) {
+    const int p = t + 256 * j;
 #pragma unroll
-    for (int p = 0; p < kGemvXBatch; ++p) {
-      const int i = ((p0 + p) * 256 + threadIdx.x) * 4;
-      if (i < nvec * k) xr[p] = *reinterpret_cast<const f32x4 *>(x + i);
-    }
+    for (int v = 0; v < 3; ++v) {
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+      if (p < np && v < nvec) {
+        lo = *reinterpret_cast<const f32x4 *>(x + v * k + 8 * p);
+        hi = *reinterpret_cast<const f32x4 *>(x + v * k + 8 * p + 4);
+      }
 #pragma unroll
-    for (int p = 0; p < kGemvXBatch; ++p) {
-      const int i = ((p0 + p) * 256 + threadIdx.x) * 4;
-      if (i < nvec * k) {
-        f32x4 v = xr[p];
-        if constexpr (SILU) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = silu(v[e]);
-        }
-        *reinterpret_cast<f32x4 *>(xs + i) = v;
+      for (int e = 0; e < 4; ++e) {
+        xv[j][v][e] = SILU ? silu(lo[e]) : lo[e];
+        xv[j][v][4 + e] = SILU ? silu(hi[e]) : hi[e];
       }
     }
+  }
+  float acc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (t + 256 * j >= np) continue;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      if (row0 + r >= rows) continue;
+      float wv[8];
+      Load16<TW>::unpack(wv, raw[r][j]);
+#pragma unroll
+      for (int v = 0; v < 3; ++v) {
+        const float *xx = xv[j][v];
+        acc[r * 3 + v] += ((wv[0] * xx[0] + wv[1] * xx[1]) + (wv[2] * xx[2] + wv[3] * xx[3])) +
+                          ((wv[4] * xx[4] + wv[5] * xx[5]) + (wv[6] * xx[6] + wv[7] * xx[7]));
+      }
+    }
+  }
+  // after the halvings, lane group g = lane / 8 holds sums b5 * NS/2 + b4 * NS/4 + b3 * NS/8 + i
+  // (b5 b4 b3 the bits of g); the butterfly completes them over the group's 8 lanes
+  float h1[NS / 2], h2[NS / 4], h3[NS / 8];
+  halve<NS / 2>(acc, h1, lane, 32);
+  halve<NS / 4>(h1, h2, lane, 16);
+  halve<NS / 8>(h2, h3, lane, 8);
+#pragma unroll
+  for (int i = 0; i < NS / 8; ++i)
+#pragma unroll
+    for (int o = 4; o >= 1; o >>= 1) h3[i] += __shfl_xor(h3[i], o, kWave);
+  if ((lane & 7) == 0) {
+    const int g = lane >> 3;
+    const int base = ((g >> 2) & 1) * (NS / 2) + ((g >> 1) & 1) * (NS / 4) + (g & 1) * (NS / 8);
+#pragma unroll
+    for (int i = 0; i < NS / 8; ++i) red[wave][base + i] = h3[i];
   }
   __syncthreads();
-  float acc[kGemvRows][3];
-#pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
-#pragma unroll
-    for (int v = 0; v < 3; ++v) acc[r][v] = 0.f;
-#pragma unroll
-  for (int i = 0; i < kGemvChunks; ++i) {
-    const int c = (i * 64 + lane) * 8;
-    if (c >= k) break;
-#pragma unroll
-    for (int v = 0; v < 3; ++v) {
-      if (v < nvec) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(xs + v * k + c);
-        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(xs + v * k + c + 4);
-#pragma unroll
-        for (int r = 0; r < kGemvRows; ++r) {
-          if (row0 + r < rows) {
-            float wv[8];
-            Load16<TW>::unpack(wv, raw[r][i]);
-            acc[r][v] += ((wv[0] * x0.x + wv[1] * x0.y) + (wv[2] * x0.z + wv[3] * x0.w)) +
-                         ((wv[4] * x1.x + wv[5] * x1.y) + (wv[6] * x1.z + wv[7] * x1.w));
-          }
-        }
-      }
-    }
+  if (t < NS) {
+    const int r = t / 3, v = t - 3 * r;
+    if (v < nvec && row0 + r < rows)
+      y[(size_t)v * ldy + row0 + r] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
   }
-#pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
-#pragma unroll
-    for (int v = 0; v < 3; ++v) {
-      if (v < nvec) {
-        const float t = wave_sum(acc[r][v]);
-        if (lane == 0 && row0 + r < rows) y[(size_t)v * ldy + row0 + r] = t;
-      }
-    }
 }
 
 template <typename TW>
 hipError_t launch_gemv(float *y, const TW *w, int rows, int k, const float *x, int nvec,
                        int silu_in, hipStream_t s, int ldy) {
-  const size_t lds = sizeof(float) * nvec * k;
-  const dim3 grid((rows + 4 * kGemvRows - 1) / (4 * kGemvRows));
+  const dim3 grid((rows + kGemvRows - 1) / kGemvRows);
   if (silu_in)
-    k_gemv<TW, true><<<grid, 256, lds, s>>>(y, w, rows, k, x, nvec, ldy);
+    k_gemv<TW, true><<<grid, 256, 0, s>>>(y, w, rows, k, x, nvec, ldy);
   else
-    k_gemv<TW, false><<<grid, 256, lds, s>>>(y, w, rows, k, x, nvec, ldy);
+    k_gemv<TW, false><<<grid, 256, 0, s>>>(y, w, rows, k, x, nvec, ldy);
   return hipGetLastError();
 }
 
 hipError_t gemv(float *y, const void *w, int w_type, int rows, int k, const float *x, int nvec,
                 int silu_in, hipStream_t s, int ldy) {
-  if (nvec < 1 || nvec > 3 || k % 8 || k > 512 * kGemvChunks) return hipErrorInvalidValue;
+  if (nvec < 1 || nvec > 3 || k % 8 || k > 4096) return hipErrorInvalidValue;
   if (ldy == 0) ldy = rows;
   if (ldy < rows) return hipErrorInvalidValue;
   switch (w_type) {
