@@ -267,16 +267,14 @@ class WeightSet:
 # Inferenzlatenz").
 # reading: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
 # value 448; no infinities).  One scale per row: per output feature for a weight, per token
-# for an activation; scale = max|row| / 448 is the dequantization factor, and the codes are
-# value * (448 / max|row|) clamped to +-448 and rounded to the nearest E4M3 value, ties to
-# even mantissa (a multiply by one reciprocal per row rather than a division per value); a
-# row of zeros has scale 0 and codes 0.  Scale, reciprocal and products are formed in fp32
-# (the kernel's precision) so that both sides take the same rounding decisions; for the same
-# reason the input of the second projection,
-# which the kernel holds in fp16, is rounded to fp16 before it is quantized (the LayerNorm
-# output is quantized from fp32).  A projection y = x W^T then equals
-# scale_x scale_w sum_k code_x code_w.  Only the two big projections of every block (W1, W2)
-# and their inputs (the modulated LayerNorm output and [attention || SwiGLU]) use it.
+# for an activation.  scale = max|row| / 448 is the dequantization factor, and each code is
+# the E4M3 value nearest to value / scale = value * 448 / max|row| (ties to even mantissa);
+# a row of zeros has scale 0 and codes 0.  Everything here is float64: the quotient of a
+# value with at most 24 significant bits is correctly rounded and never lands within one
+# double rounding of an E4M3 tie unless it is the tie, so the codes are those of the exact
+# quotient.  A projection y = x W^T then equals scale_x scale_w sum_k code_x code_w.  Only
+# the two big projections of every block (W1, W2) and their inputs (the modulated LayerNorm
+# output and [attention || SwiGLU]) use it.
 # ----------------------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -323,22 +321,21 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return s * mag
 
 
-def quantize_rows_fp8(x: np.ndarray, precision=np.float32):
-    """(codes uint8 [rows, cols], scales float32 [rows]) of the row-wise E4M3 quantization of
-    x rounded to `precision` (np.float32 or np.float16; round to nearest even)."""
-    x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
-    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
-    top = np.float32(E4M3_MAX)
-    scale = (amax / top).astype(np.float32)
-    recip = np.where(amax > 0, top / np.where(amax > 0, amax, np.float32(1)), np.float32(0)).astype(np.float32)
-    q = np.clip((x32 * recip[:, None]).astype(np.float32), -top, top)
-    return e4m3_encode(e4m3_round(q.astype(np.float64))), scale
+def quantize_rows_fp8(x: np.ndarray):
+    """(codes uint8 [rows, cols], scales float64 [rows]) of the row-wise E4M3 quantization of
+    x: scale = max|row| / 448, code = nearest E4M3 value of x * 448 / max|row|."""
+    x = np.asarray(x, np.float64)
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    live = amax > 0
+    q = np.zeros_like(x)
+    q[live] = x[live] * E4M3_MAX / amax[live, None]
+    return e4m3_encode(e4m3_round(q)), amax / E4M3_MAX
 
 
-def fp8_round_rows(x: np.ndarray, precision=np.float32) -> np.ndarray:
+def fp8_round_rows(x: np.ndarray) -> np.ndarray:
     """The values a row-wise E4M3 operand stands for: code * scale, per row (float64)."""
-    codes, scale = quantize_rows_fp8(x, precision)
-    return e4m3_decode(codes) * scale.astype(np.float64)[:, None]
+    codes, scale = quantize_rows_fp8(x)
+    return e4m3_decode(codes) * scale[:, None]
 
 
 def quantize_weights_fp8(sets: list[WeightSet]) -> list[WeightSet]:
@@ -370,9 +367,8 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     returns [len(rows), D].  Used to check sampled rows at full size.
 
     act_fp8: the inputs of the two projections (the modulated LayerNorm output, and
-    [attention || SwiGLU] rounded to fp16) go through the row-wise E4M3 quantization first
-    (the fp8r path; the weights are expected in their E4M3 values already,
-    quantize_weights_fp8)."""
+    [attention || SwiGLU]) go through the row-wise E4M3 quantization first (the fp8r path;
+    the weights are expected in their E4M3 values already, quantize_weights_fp8)."""
     n, d = x.shape
     nh, hd, f = dims.heads, dims.head_dim, dims.mlp_hidden
     seg = segment_ids(*segs)
@@ -428,7 +424,7 @@ def block_forward(x: np.ndarray, segs: tuple[int, int, int], sets: list[WeightSe
     m = silu(g[rows]) * u[rows]
     cat = np.concatenate([o.reshape(rows.shape[0], d), m], axis=1)
     if act_fp8:
-        cat = fp8_round_rows(cat, np.float16)
+        cat = fp8_round_rows(cat)
     out = x[rows].copy()
     for s in range(3):
         sel = seg[rows] == s
@@ -564,6 +560,7 @@ class Model:
     txt_in: np.ndarray | None = None        # [D, 8 * 2560]  text-feature projection
     double_wiring: int = 0                  # FLUX.2 double blocks: 0 parallel, 1 sequential
     fp8: bool = False                       # row-wise E4M3 block projections (fp8r)
+    block_mods: list | None = None          # [b][set]: each block's own modulation projections
 
 
 # ----------------------------------------------------------------------------------------
@@ -622,7 +619,11 @@ def forward(model: Model, lat: np.ndarray, txt: np.ndarray, grid, t: float,
         conds = cond_rows(model.arch, t, model.temb_l1, model.temb_l2)
     for b in range(model.n_stream + model.n_shared):
         kind, sos, mask = block_plan(model.arch, b, model.n_stream)
-        mods = segment_mods(model.mods[kind], sos, conds)
+        # reading: one modulation projection per (block kind, weight set), shared by the blocks
+        # of that kind, unless the model gives each block its own (block_mods); the pages tie
+        # scale, shift and gate to the timestep embedding without fixing which
+        mods = segment_mods(model.mods[kind] if model.block_mods is None else model.block_mods[b],
+                            sos, conds)
         if block_hook is not None:
             block_hook(b, x)
         if model.arch == ARCH_FLUX2 and kind == 0 and model.double_wiring:

@@ -613,6 +613,35 @@ def test_flow_map_cond_rows():
         assert not np.allclose(other[1], fm[1])
 
 
+def test_forward_per_block_modulation():
+    """Per-block modulation projections that alias the shared ones give the shared model's
+    velocity exactly; with every block's gate rows zero the stack is the identity, so the
+    velocity is the output head on the embedded latents; distinct projections change it."""
+    r = rng(43)
+    for arch in (O.ARCH_FLUX2, O.ARCH_FLUX3):
+        m = tiny_model(arch, r)
+        lat = r.normal(size=(4, TINY.in_channels))
+        txt = r.normal(size=(3, TINY.hidden))
+        v_shared = O.forward(m, lat, txt, (2, 2), 0.6)
+        m.block_mods = [m.mods[O.block_plan(arch, b, m.n_stream)[0]] for b in range(m.n_stream + m.n_shared)]
+        np.testing.assert_array_equal(O.forward(m, lat, txt, (2, 2), 0.6), v_shared)
+        d = TINY.hidden
+        zero_gate = []
+        for sets in m.block_mods:
+            zs = []
+            for w in sets:
+                w = w.copy()
+                w[2 * d:3 * d] = 0.0
+                zs.append(w)
+            zero_gate.append(zs)
+        m.block_mods = zero_gate
+        cond_img = O.cond_rows(arch, 0.6, m.temb_l1, m.temb_l2)[1]
+        want = O.final_layer(lat @ m.img_in.T, cond_img, m.final_mod, m.final_out, TINY.ln_eps)
+        np.testing.assert_allclose(O.forward(m, lat, txt, (2, 2), 0.6), want, rtol=0, atol=1e-12)
+        m.block_mods = [[r.normal(0, 0.05, w.shape) for w in sets] for sets in m.block_mods]
+        assert not np.allclose(O.forward(m, lat, txt, (2, 2), 0.6), v_shared)
+
+
 def test_flow_map_forward():
     """A flow-map model with a zero target MLP is the plain model; it needs the target time;
     with a real target MLP the velocity depends on the target time."""
@@ -691,15 +720,28 @@ def test_noise_distribution_and_prefix():
 
 # ------------------------------------------------------------------ row-wise FP8 (fp8r)
 
-def torch_fp8_rows(X, precision=torch.float32):
-    """Row-wise E4M3 values through torch's float8_e4m3fn conversion (round to nearest even),
-    independent of the oracle's rounding code; X is rounded to `precision` first."""
-    X32 = X.to(precision).to(torch.float32)
-    amax = X32.abs().amax(dim=1, keepdim=True)
-    s = amax / 448.0
-    r = torch.where(amax > 0, 448.0 / torch.where(amax > 0, amax, torch.ones_like(amax)), torch.zeros_like(amax))
-    q = torch.clamp(X32 * r, -448.0, 448.0)
-    return q.to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
+def _e4m3_ties():
+    """Midpoints of neighbouring non-negative E4M3 values (from the decoded code table)."""
+    grid = np.unique(O.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    return (grid[:-1] + grid[1:]) / 2
+
+
+def torch_fp8_rows(X):
+    """Row-wise E4M3 values through torch's float8_e4m3fn conversion of the float64 quotients
+    X * 448 / max|row| (round to nearest even), independent of the oracle's rounding code.
+    torch converts float64 through fp32, which can move a quotient exactly onto a tie of two
+    E4M3 values; there the fp32 value is nudged one fp32 step toward the true quotient first,
+    so torch rounds it to the side the quotient lies on."""
+    X = X.to(torch.float64)
+    amax = X.abs().amax(dim=1, keepdim=True)
+    safe = torch.where(amax > 0, amax, torch.ones_like(amax))
+    q = torch.where(amax > 0, X * 448.0 / safe, torch.zeros_like(X))
+    q32 = q.to(torch.float32)
+    ties = torch.tensor(_e4m3_ties())
+    on_tie = torch.isin(q32.abs().to(torch.float64), ties) & (q32.to(torch.float64) != q)
+    toward = torch.where(q > q32.to(torch.float64), torch.tensor(math.inf), torch.tensor(-math.inf))
+    q32 = torch.where(on_tie, torch.nextafter(q32, toward.to(torch.float32)), q32)
+    return q32.to(torch.float8_e4m3fn).to(torch.float64) * (amax / 448.0)
 
 
 def _e4m3_torch(v):
@@ -742,7 +784,7 @@ def test_quantize_rows_fp8_properties():
     x = r.normal(size=(6, 300)) * np.array([1e-3, 1, 50, 3e4, 1, 1])[:, None]
     x[4] = 0.0
     codes, scale = O.quantize_rows_fp8(x)
-    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    assert codes.dtype == np.uint8 and scale.dtype == np.float64
     # the largest magnitude of each row lands on +-448; a zero row has scale 0 and codes 0
     for i in (0, 1, 2, 3, 5):
         j = np.argmax(np.abs(x[i]))
@@ -751,13 +793,70 @@ def test_quantize_rows_fp8_properties():
     # a power-of-two factor changes the scale only
     c2, s2 = O.quantize_rows_fp8(x * 2.0 ** 7)
     np.testing.assert_array_equal(c2, codes)
-    np.testing.assert_array_equal(s2, scale * np.float32(2.0 ** 7))
+    np.testing.assert_array_equal(s2, scale * 2.0 ** 7)
     # each value is within half an E4M3 step (relative 2^-4, or 2^-10 of the scale) of x
     xr = O.fp8_round_rows(x)
-    sc = scale.astype(np.float64)[:, None]
-    bound = np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6)
+    sc = scale[:, None]
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-12)
     assert np.all(np.abs(xr - x) <= bound)
     np.testing.assert_array_equal(xr, torch_fp8_rows(torch.tensor(x)).numpy())
+
+
+def _nearest_e4m3_exact(q):
+    """Code of the E4M3 value nearest to the exact rational q (|q| <= 448) by brute force over
+    the code table, ties to the code with the even mantissa bit."""
+    from fractions import Fraction
+    mag = abs(q)
+    best = None
+    for c in range(0x7F):
+        v = Fraction(float(O.e4m3_decode(np.array([c], np.uint8))[0]))
+        key = (abs(v - mag), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    code = best[1]
+    return code | (0x80 if q < 0 and code else 0)
+
+
+def test_quantize_rows_fp8_matches_exact_rational_rounding():
+    """Codes equal the E4M3 rounding of the exact quotient value * 448 / max|row| (computed in
+    rational arithmetic), including quotients that are exactly ties and quotients a few fp32
+    steps on either side of a tie; scales equal max|row| / 448 correctly rounded."""
+    from fractions import Fraction
+    r = rng(74)
+    ties = _e4m3_ties()
+    rows = []
+    rows.append(r.normal(size=40).astype(np.float32))                 # random values
+    t = r.choice(ties, 40) * r.choice([-1, 1], 40)                    # exact ties, max 448
+    t[0] = 448.0
+    rows.append(t.astype(np.float32))
+    amax = np.float32(3.5)                                            # ties after a 2^7 scale
+    t2 = (r.choice(ties[ties < 440], 40) * (3.5 / 448)).astype(np.float32)
+    t2[0] = amax
+    rows.append(t2)
+    for sgn in (-1, 1):                                               # near ties, both sides
+        near = r.choice(ties[ties < 440], 40) * (1 + sgn * 3 * 2.0 ** -23)
+        near[0] = 448.0
+        rows.append(near.astype(np.float32))
+    # a generic row maximum: the quotients of the fp32 values nearest tie * max / 448 lie
+    # within an fp32 rounding of the tie without being on it
+    am = np.float64(np.float32(1000.123))
+    hz = (r.choice(ties[(ties < 440) & (ties > 2.0 ** -5)], 40) * r.choice([-1, 1], 40) * am / 448)
+    hz = hz.astype(np.float32).astype(np.float64)
+    hz[0] = am
+    q = hz * 448 / am
+    q32 = q.astype(np.float32).astype(np.float64)
+    assert np.sum(np.isin(np.abs(q32), ties) & (q32 != q)) > 20
+    rows.append(hz.astype(np.float32))
+    x = np.stack(rows).astype(np.float64)
+    codes, scale = O.quantize_rows_fp8(x)
+    for i in range(x.shape[0]):
+        am = Fraction(float(np.max(np.abs(x[i]))))
+        assert scale[i] == float(am / 448)
+        for j in range(x.shape[1]):
+            qv = Fraction(float(x[i, j])) * 448 / am
+            assert codes[i, j] == _nearest_e4m3_exact(qv), (i, j, float(qv))
+    # torch's conversion (with its fp32 step moved off the ties it creates) agrees
+    np.testing.assert_array_equal(O.fp8_round_rows(x), torch_fp8_rows(torch.tensor(x)).numpy())
 
 
 def test_fp8_projection_error_bound():
@@ -788,13 +887,13 @@ def test_fp8_block_matches_library_composition(sequential):
         mods6 = [np.concatenate([a, b]) for a, b in zip(rand_mods(r, dims), rand_mods(r, dims))]
         got = O.block_forward_sequential(x, segs, q_or, sos, mods6, pos, O.MASK_FULL, dims, act_fp8=True)
         ref = torch_sequential_block(x, segs, q_t, sos, mods6, pos, O.MASK_FULL, dims, act=torch_fp8_rows,
-                                     act2=lambda t: torch_fp8_rows(t, torch.float16))
+                                     act2=torch_fp8_rows)
         plain = O.block_forward_sequential(x, segs, sets, sos, mods6, pos, O.MASK_FULL, dims)
     else:
         mods = rand_mods(r, dims)
         got = O.block_forward(x, segs, q_or, sos, mods, pos, O.MASK_FULL, dims, act_fp8=True)
         ref = torch_block(x, segs, q_t, sos, mods, pos, O.MASK_FULL, dims, act=torch_fp8_rows,
-                          act2=lambda t: torch_fp8_rows(t, torch.float16))
+                          act2=torch_fp8_rows)
         plain = O.block_forward(x, segs, sets, sos, mods, pos, O.MASK_FULL, dims)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
     # the E4M3 rounding is visible but small against the unquantized block
@@ -802,11 +901,19 @@ def test_fp8_block_matches_library_composition(sequential):
     assert 1e-3 < d < 0.2
 
 
-def _per_tensor_quantize(x, precision=np.float32):
-    x32 = np.asarray(x, np.float64).astype(precision).astype(np.float32)
-    amax = np.float32(np.max(np.abs(x32)))
-    q = np.clip((x32 * (np.float32(448.0) / amax)).astype(np.float32), -448, 448)
-    return O.e4m3_encode(O.e4m3_round(q.astype(np.float64))), np.full(x32.shape[0], amax / np.float32(448), np.float32)
+def _per_tensor_quantize(x):
+    x = np.asarray(x, np.float64)
+    amax = np.max(np.abs(x))
+    return O.e4m3_encode(O.e4m3_round(x * 448.0 / amax)), np.full(x.shape[0], amax / 448.0)
+
+
+def _fp32_reciprocal_quantize(x):
+    """The quotient formed in fp32 as value * fp32(448 / max) (two fp32 roundings)."""
+    x32 = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    rcp = np.where(amax > 0, np.float32(448.0) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    q = (x32 * rcp[:, None]).astype(np.float32).astype(np.float64)
+    return O.e4m3_encode(O.e4m3_round(q)), amax.astype(np.float64) / 448.0
 
 
 def _wrong_layer_norm(x, eps):
@@ -857,6 +964,11 @@ def test_pins_catch_planted_slips(monkeypatch):
     monkeypatch.setattr(O, "quantize_rows_fp8", _per_tensor_quantize)
     with pytest.raises(AssertionError):
         test_fp8_block_matches_library_composition(False)
+    monkeypatch.undo()
+    # the quotient rounded through fp32 before its E4M3 rounding
+    monkeypatch.setattr(O, "quantize_rows_fp8", _fp32_reciprocal_quantize)
+    with pytest.raises(AssertionError):
+        test_quantize_rows_fp8_matches_exact_rational_rounding()
     monkeypatch.undo()
     # guidance with the branches swapped
     monkeypatch.setattr(O, "guided_velocity", lambda vc, vu, g: vc + g * (vu - vc))
