@@ -16,7 +16,9 @@
  *     Pointers marked "host" are read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is queued
  *     asynchronously on it; nothing synchronises unless DIT_DEBUG_SYNC=1 is set in the
- *     environment, which synchronises and checks after every kernel.
+ *     environment at dit_ctx_create, which synchronises and checks after every kernel, and
+ *     checks what each launch of a block or forward wrote for saturated fp16 values and
+ *     NaN / Inf (DIT_ENUMERIC).
  *   - One context serves one stream at a time: calls that overlap on one context race on
  *     its workspace.
  *   - DIT_ATTN_GRID=<n> in the environment at dit_ctx_create (0, or a multiple of 8 up to
@@ -24,7 +26,8 @@
  *     (default: the device's compute units; 0 = one workgroup per 256-query tile and head).
  *     Other values make dit_ctx_create fail with DIT_EINVAL.
  *   - Row-major everywhere.  "D" = hidden, "C" = in_channels, N = n_txt + n_img + n_ref.
- *   - Return values: 0 on success, or DIT_EINVAL / DIT_ENOMEM / DIT_EHIP / DIT_EUNSUPPORTED;
+ *   - Return values: 0 on success, or DIT_EINVAL / DIT_ENOMEM / DIT_EHIP / DIT_EUNSUPPORTED /
+ *     DIT_ENUMERIC;
  *     dit_ctx_create returns NULL on failure.  dit_get_error() then describes the failure.
  *     Faults of queued kernels surface at a later call or synchronisation.
  */
@@ -73,8 +76,14 @@ enum { DIT_FLUX2 = 0, DIT_FLUX3 = 1 };
 /* attention masks: DEFAULT = the block kind's own (per-mode: SEGMENT, others: FULL) */
 enum { DIT_MASK_DEFAULT = -1, DIT_MASK_FULL = 0, DIT_MASK_SEGMENT = 1 };
 
-/* error codes */
-enum { DIT_OK = 0, DIT_EINVAL = -1, DIT_ENOMEM = -2, DIT_EHIP = -3, DIT_EUNSUPPORTED = -4 };
+/* error codes.  DIT_ENUMERIC comes only with DIT_DEBUG_SYNC=1: after every launch the library
+ * counts, in what that launch wrote, the fp16 values at +-65504 (saturated conversions; the
+ * saturating conversion also maps NaN there) and the NaN / Inf values, and fails the call at the
+ * first launch that produced any, naming the block and the launch (the C library's error
+ * reporting: NULL / negative return and a message, hakusoku FLUX.2-klein-4B article,
+ * "エラーハンドリング"). */
+enum { DIT_OK = 0, DIT_EINVAL = -1, DIT_ENOMEM = -2, DIT_EHIP = -3, DIT_EUNSUPPORTED = -4,
+       DIT_ENUMERIC = -5 };
 
 typedef struct {
   int arch;             /* DIT_FLUX2 or DIT_FLUX3 */
@@ -116,10 +125,17 @@ typedef struct {
  *   txt_in      [D, txt_feat_dim]   text-feature projection (txt_feat_dim > 0 only)
  *   final.mod   [2D, D]      output-head modulation (shift || scale)
  *   final.out   [C, D]       output projection to the velocity
- *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) of stream blocks, per set;
- *               [6D, D] with double_wiring = 1: (shift || scale || gate) of the attention
- *               half, then of the MLP half
- *   mod.1.s0    [3D, D]      modulation of shared (single / joint) blocks
+ *   mod.0.s{s}  [3D, D]      modulation (shift || scale || gate) shared by the stream blocks,
+ *               per set; [6D, D] with double_wiring = 1: (shift || scale || gate) of the
+ *               attention half, then of the MLP half
+ *   mod.1.s0    [3D, D]      modulation shared by the shared (single / joint) blocks
+ *   blk{b}.s{s}.mod  [3D, D] (or [6D, D] as above)  block b's own modulation of set s; when
+ *               given it replaces the shared mod.{kind}.s{s} for that block.  The pages tie
+ *               scale, shift and gate to the timestep embedding without saying whether each
+ *               block has its own projection ("FLUX.3 Image Klein in Diffusers", section
+ *               "Modulation pro Token-Typ, Flow-Map-Destillation und 4D-RoPE"); both forms are
+ *               data.  Entries may alias: entries whose data pointer (and dtype) is the same
+ *               are uploaded and computed once.  A shared entry that no block uses is an error.
  *   blk{b}.s{s}.w1 [3D+2F, D]  rows Q | K | V | gate | up (head-major Q, K, V)
  *   blk{b}.s{s}.w2 [D, D+F]    output projection of [attention || SwiGLU]
  *   blk{b}.s{s}.qn, .kn [128]  query / key RMSNorm scales
@@ -144,11 +160,12 @@ void dit_ctx_free(dit_ctx *ctx);
 /* One transformer block in place on the residual stream.
  *   x     dev fp32 [N, D], in/out; rows ordered text || image || reference
  *   pos   dev fp32 [N, 4] RoPE coordinates (t, h, w, l) per token
- *   cond  dev fp32 [3, D] conditioning vector per segment (text, image, reference);
- *         rows of empty segments are ignored but must be readable
+ *   cond  dev fp32 [n_seg, D]: one conditioning vector per non-empty segment, in the order
+ *         text, image, reference (n_seg = number of n_txt, n_img, n_ref that are > 0)
  *   mask  DIT_MASK_DEFAULT / FULL / SEGMENT
  * Computes x <- x + gate_s * ([attention || SwiGLU](LN(x) * (1 + scale_s) + shift_s) W2^T)
- * with (shift, scale, gate)_s = mod.{kind}.s{set(s)} . SiLU(cond[s])
+ * with (shift, scale, gate)_s = W_mod . SiLU(cond row of s), W_mod the block's modulation
+ * projection of the segment's weight set
  * ("FLUX.3 Image Klein in Diffusers": parallel attention and SwiGLU MLP on one normalised
  * input, QK RMSNorm, adaLN from the timestep embedding, 4D RoPE).  Double blocks of a
  * double_wiring = 1 model run the two halves in sequence instead:
@@ -289,8 +306,9 @@ int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8
 /* Workspace buffer of the last call, for inspection after the stream has finished:
  * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
  * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32
- * [2][3][3][R]: kind, set, segment, shift || scale || gate, R = 3D, or 6D with
- * double_wiring = 1, whose stream-block rows hold both halves), "x" (fp32 [N, D], the
+ * [M][3][R]: distinct modulation projection in order of first use (blocks in order, sets in
+ * order), conditioning row, shift || scale || gate; R = 3D, or 6D with double_wiring = 1,
+ * whose stream-block rows hold both halves), "x" (fp32 [N, D], the
  * residual stream of dit_forward / dit_denoise after the last block).  *dtype receives
  * the element type (compute type for xm, qkv, cat; DIT_F32 for mod and x; with DIT_FP8, xm
  * holds E4M3 codes (DIT_FP8) and qkv, cat are DIT_F16); *row_stride the

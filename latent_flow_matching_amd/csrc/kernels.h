@@ -132,5 +132,9 @@ hipError_t philox_normal(float *dst, int64_t n, uint64_t seed, hipStream_t s);
 hipError_t noise_mix(float *x, const float *noise, int64_t n, float t, hipStream_t s);
 // y[r][:] += v for rows r < nrows of d floats
 hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s);
+// Debug guard: cnt[0] += values of the rows x cols buffer p (row stride ld, element type
+// OP_F32 / OP_BF16 / OP_F16) at the fp16 limit +-65504 (fp16 only), cnt[1] += NaN / Inf values.
+hipError_t count_nonfinite(unsigned *cnt, const void *p, int type, int rows, int cols, int ld,
+                           hipStream_t s);
 
 }  // namespace dit

@@ -3,6 +3,9 @@
 //   GEMV for timestep MLP and modulation, timestep embedding, Philox noise.
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -743,6 +746,44 @@ __global__ void k_add_row(float *y, int nrows, int d, const float *v) {
 hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s) {
   if (nrows <= 0 || d <= 0) return hipSuccess;
   k_add_row<<<(d + 255) / 256, 256, 0, s>>>(y, nrows, d, v);
+  return hipGetLastError();
+}
+
+// Debug guard: over rows x cols of a buffer (row stride ld), cnt[0] += fp16 values at the limit
+// +-65504 (where the saturating conversion puts out-of-range values, and NaN), cnt[1] += NaN or
+// infinite values.  A grid-stride loop; one atomic per wave.
+template <typename T>
+__global__ void k_count_nonfinite(const T *p, int rows, int cols, int ld, unsigned *cnt) {
+  unsigned sat = 0, bad = 0;
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i - r * cols;
+    const float v = to_f32(p[r * ld + c]);
+    if (!__builtin_isfinite(v)) ++bad;
+    else if (std::is_same<T, f16>::value && fabsf(v) >= 65504.f) ++sat;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    sat += __shfl_xor(sat, o, kWave);
+    bad += __shfl_xor(bad, o, kWave);
+  }
+  if ((threadIdx.x & 63) == 0 && (sat | bad)) {
+    atomicAdd(cnt, sat);
+    atomicAdd(cnt + 1, bad);
+  }
+}
+
+hipError_t count_nonfinite(unsigned *cnt, const void *p, int type, int rows, int cols, int ld,
+                           hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int64_t total = (int64_t)rows * cols;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+  switch (type) {
+    case OP_F32: k_count_nonfinite<float><<<blocks, 256, 0, s>>>((const float *)p, rows, cols, ld, cnt); break;
+    case OP_BF16: k_count_nonfinite<bf16><<<blocks, 256, 0, s>>>((const bf16 *)p, rows, cols, ld, cnt); break;
+    case OP_F16: k_count_nonfinite<f16><<<blocks, 256, 0, s>>>((const f16 *)p, rows, cols, ld, cnt); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <map>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -68,7 +70,11 @@ struct dit_ctx {
     float *s1 = nullptr, *s2 = nullptr;  // DIT_FP8: one scale per row of w1, w2
   };
   std::vector<std::vector<Set>> blk;
-  void *mod[2][3] = {{nullptr}};
+  // Modulation projections: the distinct device tensors (weight-table entries that name the
+  // same host data share one), their row counts, and which one serves each (block, set).
+  std::vector<void *> modw;
+  std::vector<int> modw_rows;
+  std::vector<std::vector<int>> mod_of;
   void *img_in = nullptr, *temb1 = nullptr, *temb2 = nullptr, *fmod = nullptr, *fout = nullptr;
   void *fout_pad = nullptr;  // 16-bit paths: final.out with zero rows up to a multiple of 256
   void *ttgt1 = nullptr, *ttgt2 = nullptr;  // flow-map target-time MLP
@@ -82,7 +88,7 @@ struct dit_ctx {
   void *vt = nullptr;        // [H][128][ldv] (16-bit paths)
   float *pos = nullptr;      // [rows_alloc][4]
   float *cs = nullptr;       // [rows_alloc][128]
-  float *modbuf = nullptr;   // [2][3][3][mod_ld()]
+  float *modbuf = nullptr;   // [modw.size()][3][mod_ld()]: one vector per cond row
   float *cond = nullptr;     // [3][D]
   float *temb_e = nullptr;   // [4][time_dim]: the three segment times, then the target time
   float *temb_h = nullptr;   // [4][D]
@@ -95,6 +101,7 @@ struct dit_ctx {
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
   int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 6)] per-unit piece counters
   float *gemm_part = nullptr;  // [lean_grid][gemm_part_floats] split-K partial tiles
+  unsigned *guard_cnt = nullptr;  // DIT_DEBUG_SYNC guard: (values at the fp16 limit, NaN/Inf)
   // DIT_FP8 workspace: E4M3 copy of cat, row scales of xm (codes in xm) and of cat's halves
   uint8_t *cat8 = nullptr;     // [rows_alloc][D+F]
   float *xs = nullptr, *cs_a = nullptr, *cs_b = nullptr;  // [rows_alloc] each
@@ -122,7 +129,6 @@ struct dit_ctx {
   size_t esz() const { return op == OP_F32 ? 4 : 2; }
   int nblocks() const { return cfg.n_stream_blocks + cfg.n_shared_blocks; }
   int kind(int b) const { return b < cfg.n_stream_blocks ? 0 : 1; }
-  int nsets_kind(int k) const { return k == 0 ? (cfg.arch == DIT_FLUX2 ? 2 : 3) : 1; }
   void set_of_seg(int k, int out[3]) const {
     if (k == 1) {
       out[0] = out[1] = out[2] = 0;
@@ -134,10 +140,10 @@ struct dit_ctx {
   }
   // sequentially wired double blocks carry two (shift, scale, gate) triples per vector
   bool seq_block(int k) const { return k == 0 && cfg.double_wiring; }
-  int mod_rows(int k) const { return (seq_block(k) ? 6 : 3) * D(); }
   int mod_ld() const { return (cfg.double_wiring ? 6 : 3) * D(); }
-  float *mod_vec(int k, int set, int seg) const {
-    return modbuf + ((size_t)(k * 3 + set) * 3 + seg) * mod_ld();
+  // (shift, scale, gate) of block b's weight set `set` for conditioning row `row`
+  float *mod_vec(int b, int set, int row) const {
+    return modbuf + ((size_t)mod_of[b][set] * 3 + row) * mod_ld();
   }
 };
 
@@ -184,6 +190,28 @@ void prof_end(dit_ctx *ctx, int e, int cls, double flops, double bytes, hipStrea
     DIT_CHECK(call, what);                                      \
     prof_end(ctx, pe_, cls, flops, bytes, stream);              \
   } while (0)
+
+// DIT_DEBUG_SYNC guard, after a launch that wrote rows x cols of p (row stride ld, element type
+// type): counts the fp16 values at +-65504 (the saturating conversion puts out-of-range values,
+// and NaN, there) and the NaN / Inf values, and fails the call with DIT_ENUMERIC if there are any.
+int guard(dit_ctx *ctx, int block, const char *what, const void *p, int type, int rows, int cols,
+          int ld, hipStream_t stream) {
+  if (!ctx->debug_sync || rows <= 0 || cols <= 0) return 0;
+  unsigned h[2] = {0, 0};
+  hipError_t e = hipMemsetAsync(ctx->guard_cnt, 0, sizeof h, stream);
+  if (e == hipSuccess) e = count_nonfinite(ctx->guard_cnt, p, type, rows, cols, ld, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h, ctx->guard_cnt, sizeof h, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "debug guard");
+  if (h[0] || h[1]) {
+    char where[32] = "";
+    if (block >= 0) snprintf(where, sizeof where, "block %d, ", block);
+    return fail(DIT_ENUMERIC,
+                "DIT_DEBUG_SYNC guard: %s%s: %u values at the fp16 limit +-65504 (saturated "
+                "conversions, or NaN) and %u NaN/Inf values", where, what, h[0], h[1]);
+  }
+  return 0;
+}
 
 int dalloc(dit_ctx *ctx, void **p, size_t bytes) {
   if (bytes == 0) bytes = 256;
@@ -346,11 +374,18 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   }
   if (c.txt_feat_dim > 0) want["txt_in"] = (int64_t)D * c.txt_feat_dim;
   const int nsets0 = c.arch == DIT_FLUX2 ? 2 : 3;
-  if (c.n_stream_blocks > 0)
-    for (int s = 0; s < nsets0; ++s)
-      want["mod.0.s" + std::to_string(s)] = (int64_t)(c.double_wiring ? 6 : 3) * D * D;
-  if (c.n_shared_blocks > 0) want["mod.1.s0"] = (int64_t)3 * D * D;
   const int nb = c.n_stream_blocks + c.n_shared_blocks;
+  // Modulation: each (block, set) takes its own blk{b}.s{s}.mod, or else the projection its
+  // block kind shares, mod.{kind}.s{s}; entries may name the same host data (aliases).
+  std::unordered_map<std::string, int64_t> optional;
+  auto mod_numel = [&](int kind) { return (int64_t)(kind == 0 && c.double_wiring ? 6 : 3) * D * D; };
+  if (c.n_stream_blocks > 0)
+    for (int s = 0; s < nsets0; ++s) optional["mod.0.s" + std::to_string(s)] = mod_numel(0);
+  if (c.n_shared_blocks > 0) optional["mod.1.s0"] = mod_numel(1);
+  for (int b = 0; b < nb; ++b)
+    for (int s = 0; s < (b < c.n_stream_blocks ? nsets0 : 1); ++s)
+      optional["blk" + std::to_string(b) + ".s" + std::to_string(s) + ".mod"] =
+          mod_numel(b < c.n_stream_blocks ? 0 : 1);
   for (int b = 0; b < nb; ++b) {
     const int ns = b < c.n_stream_blocks ? nsets0 : 1;
     for (int s = 0; s < ns; ++s) {
@@ -369,8 +404,11 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
     }
     auto it = want.find(w[i].name);
     if (it == want.end()) {
-      fail(DIT_EINVAL, "unknown weight '%s'", w[i].name);
-      return nullptr;
+      it = optional.find(w[i].name);
+      if (it == optional.end()) {
+        fail(DIT_EINVAL, "unknown weight '%s'", w[i].name);
+        return nullptr;
+      }
     }
     if (have.count(w[i].name)) {
       fail(DIT_EINVAL, "weight '%s' given twice", w[i].name);
@@ -390,6 +428,31 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   for (auto &kv : want)
     if (!have.count(kv.first)) {
       fail(DIT_EINVAL, "missing weight '%s'", kv.first.c_str());
+      return nullptr;
+    }
+  // the modulation source of every (block, set), and no shared entry left unused
+  std::vector<std::vector<const dit_tensor *>> mod_src(nb);
+  std::unordered_map<std::string, bool> shared_used;
+  for (int b = 0; b < nb; ++b) {
+    const int kind = b < c.n_stream_blocks ? 0 : 1;
+    for (int s = 0; s < (kind == 0 ? nsets0 : 1); ++s) {
+      const std::string own = "blk" + std::to_string(b) + ".s" + std::to_string(s) + ".mod";
+      const std::string shared = "mod." + std::to_string(kind) + ".s" + std::to_string(s);
+      if (have.count(own)) {
+        mod_src[b].push_back(have[own]);
+      } else if (have.count(shared)) {
+        mod_src[b].push_back(have[shared]);
+        shared_used[shared] = true;
+      } else {
+        fail(DIT_EINVAL, "missing weight '%s' (or the shared '%s')", own.c_str(), shared.c_str());
+        return nullptr;
+      }
+    }
+  }
+  for (auto &kv : have)
+    if (kv.first.rfind("mod.", 0) == 0 && !shared_used.count(kv.first)) {
+      fail(DIT_EINVAL, "weight '%s' is used by no block (each has its own blk{b}.s{s}.mod)",
+           kv.first.c_str());
       return nullptr;
     }
 
@@ -459,12 +522,26 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   if (c.txt_feat_dim > 0) rc = rc ? rc : up(&ctx->txt_in, "txt_in", false);
   rc = rc ? rc : up(&ctx->fmod, "final.mod", false);
   rc = rc ? rc : up(&ctx->fout, "final.out", false);
-  for (int k = 0; k < 2 && !rc; ++k) {
-    if ((k == 0 && c.n_stream_blocks == 0) || (k == 1 && c.n_shared_blocks == 0)) continue;
-    for (int s = 0; s < ctx->nsets_kind(k) && !rc; ++s) {
-      std::string n = "mod." + std::to_string(k) + ".s" + std::to_string(s);
-      rc = up(&ctx->mod[k][s], n.c_str(), false);
-    }
+  {
+    // one device copy per distinct host tensor (same data pointer and element type)
+    std::map<std::pair<const void *, int>, int> by_data;
+    ctx->mod_of.resize(nb);
+    for (int b = 0; b < nb && !rc; ++b)
+      for (const dit_tensor *t : mod_src[b]) {
+        const auto key = std::make_pair(t->data, t->dtype);
+        auto f = by_data.find(key);
+        if (f != by_data.end()) {
+          ctx->mod_of[b].push_back(f->second);
+          continue;
+        }
+        void *dst = nullptr;
+        rc = upload(ctx, &dst, *t, false);
+        if (rc) break;
+        by_data[key] = (int)ctx->modw.size();
+        ctx->mod_of[b].push_back((int)ctx->modw.size());
+        ctx->modw.push_back(dst);
+        ctx->modw_rows.push_back((int)(t->numel / D));
+      }
   }
   ctx->blk.resize(nb);
   for (int b = 0; b < nb && !rc; ++b) {
@@ -496,13 +573,14 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   if (ctx->op != OP_F32) rc = rc ? rc : dalloc(ctx, &ctx->vt, (size_t)c.heads * 128 * ctx->ldv * es);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->pos, R * 4 * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs, R * 128 * 4);
-  rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (size_t)2 * 3 * 3 * ctx->mod_ld() * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (ctx->modw.size() + 1) * 3 * ctx->mod_ld() * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cond, (size_t)3 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_e, (size_t)4 * T * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->temb_h, (size_t)4 * D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->tgt, (size_t)D * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->noise, (size_t)c.max_tokens * C * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->fmodv, (size_t)3 * 2 * D * 4);
+  rc = rc ? rc : dalloc(ctx, (void **)&ctx->guard_cnt, 2 * sizeof(unsigned));
   if (ctx->op != OP_F32 && ctx->lean_grid > 0) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_part,
                           (size_t)2 * ctx->lean_grid * attn_part_floats * 4);
@@ -547,12 +625,14 @@ Segs make_segs(int n_txt, int n_img, int n_ref, int nseq = 1) {
   return Segs{n_txt, n_txt + n_img, per * nseq, per};
 }
 
-// mod[kind][set][seg] = W_mod[kind][set] . SiLU(cond[seg]) for every set of the kind
-int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) {
+// Modulation vectors of the listed distinct projections i: slot (i, r) = W_mod[i] . SiLU(cond[r])
+// for every conditioning row r < ncond.
+int compute_mods(dit_ctx *ctx, const std::vector<int> &which, const float *cond, int ncond,
+                 hipStream_t stream) {
   const int D = ctx->D();
-  for (int s = 0; s < ctx->nsets_kind(kind); ++s)
-    DIT_CHECK(gemv(ctx->mod_vec(kind, s, 0), ctx->mod[kind][s], ctx->op, ctx->mod_rows(kind), D, cond, 3, 1,
-                   stream, ctx->mod_ld()),
+  for (int i : which)
+    DIT_CHECK(gemv(ctx->modbuf + (size_t)i * 3 * ctx->mod_ld(), ctx->modw[i], ctx->op, ctx->modw_rows[i], D,
+                   cond, ncond, 1, stream, ctx->mod_ld()),
               "modulation gemv");
   return 0;
 }
@@ -564,7 +644,8 @@ int compute_mods(dit_ctx *ctx, int kind, const float *cond, hipStream_t stream) 
 // LayerNorm with the second (shift, scale) and the MLP half (linear1 over the gate/up
 // rows, linear2 over W2's last F columns, gate 2).  With DIT_FP8 the LayerNorm writes E4M3
 // codes with row scales, and linear2's input is quantized per token before its GEMM.
-int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stream) {
+// mrow[s]: the conditioning row whose modulation vectors segment s uses.
+int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, const int mrow[3], hipStream_t stream) {
   const dit_config &c = ctx->cfg;
   const int D = ctx->D(), F = ctx->F();
   const int kind = ctx->kind(b);
@@ -574,7 +655,7 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   ctx->set_of_seg(kind, sos);
   const float *mseg[3], *gate[3], *qn[3], *kn[3], *mseg2[3], *gate2[3];
   for (int s = 0; s < 3; ++s) {
-    mseg[s] = ctx->mod_vec(kind, sos[s], s);
+    mseg[s] = ctx->mod_vec(b, sos[s], mrow[s]);
     gate[s] = mseg[s] + 2 * D;
     mseg2[s] = mseg[s] + 3 * D;   // second triple: sequential blocks only
     gate2[s] = mseg2[s] + 2 * D;
@@ -588,12 +669,18 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   const bool mfma = ctx->op != OP_F32;
   const double es_d = (double)es;
 
+  // debug guard on what a launch wrote (DIT_DEBUG_SYNC=1 only)
+  auto chk = [&](const char *what, const void *p, int type, int rows, int cols, int ld) {
+    return guard(ctx, b, what, p, type, rows, cols, ld, stream);
+  };
+  if (int rc = chk("input residual x", x, OP_F32, N, D, D)) return rc;
   auto ln = [&](const float *const ms[3]) -> int {
     DIT_TIMED(P_LN, 0.0, (double)N * D * (4.0 + (double)ex),
               ln_modulate(ctx->xm, f8 ? OP_FP8 : ctx->op, D, x, D, N, 0, D, c.ln_eps, ms, sg, stream,
                           ctx->xs),
               "ln_modulate");
-    return 0;
+    if (f8) return chk("ln_modulate -> E4M3 row scales", ctx->xs, OP_F32, N, 1, 1);
+    return chk("ln_modulate -> xm", ctx->xm, ctx->op, N, D, D);
   };
   auto gemm = [&](const GemmArgs &ga, int epi) -> hipError_t {
     if (f8) return gemm_fp8(ga, epi, stream);
@@ -636,12 +723,17 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   a1.cat_off = D;
   a1.xs = ctx->xs;
   DIT_TIMED(P_LINEAR1, 2.0 * N * D * (double)a1.n, 0.0, gemm(a1, EPI_QKV_SWIGLU), "linear1");
+  if (int rc = chk("linear1 -> q, k, v", ctx->qkv, ctx->op, N, 3 * D, 3 * D)) return rc;
+  if (!seq)
+    if (int rc = chk("linear1 -> SwiGLU output", (const char *)ctx->cat + (size_t)D * es, ctx->op, N, F, D + F))
+      return rc;
 
   // bytes: q, k read + written, V read + V^T written, one cos/sin row per token
   DIT_TIMED(P_QKNORM, 0.0, (double)N * (6.0 * D * es_d + 512.0),
             qk_norm_rope(ctx->qkv, ctx->op, 3 * D, D, c.heads, ctx->vt, ctx->ldv, ctx->cs, N, qn,
                          kn, sg, c.rms_eps, stream),
             "qk_norm_rope");
+  if (int rc = chk("qk_norm_rope -> q, k", ctx->qkv, ctx->op, N, 2 * D, 3 * D)) return rc;
 
   AttnArgs at = {};
   at.qkv = ctx->qkv;
@@ -675,15 +767,18 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
     DIT_TIMED(P_ATTN, fla, 0.0, attention_mfma(at, ctx->op, stream), "attention");
   else
     DIT_TIMED(P_ATTN, fla, 0.0, attention_f32(at, stream), "attention");
+  if (int rc = chk("attention -> output", ctx->cat, ctx->op, N, D, D + F)) return rc;
 
   // linear2 with the gated residual over k columns of cat starting at column k0 (W2 columns
   // k0 .. k0 + k of its D + F); with DIT_FP8 those columns are quantized first, scales in xsc
   auto linear2 = [&](int k0, int k, const float *const gt[3], float *xsc) -> int {
-    if (f8)
+    if (f8) {
       DIT_TIMED(P_QUANT, 0.0, (double)N * k * 3.0,
                 quant_rows_fp8(ctx->cat8 + k0, D + F, xsc, (const uint16_t *)ctx->cat + k0, OP_F16, D + F, N, k,
                                stream),
                 "fp8 quantization");
+      if (int rc = chk("E4M3 quantization -> row scales", xsc, OP_F32, N, 1, 1)) return rc;
+    }
     GemmArgs a2 = {};
     for (int i = 0; i < ng; ++i) {
       a2.g[i] = g2[i];
@@ -704,7 +799,7 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
     a2.xs = xsc;
     ctx->split_k(&a2);
     DIT_TIMED(P_LINEAR2, 2.0 * N * (double)k * D, 0.0, gemm(a2, EPI_RESID), "linear2");
-    return 0;
+    return chk("linear2 -> residual x", x, OP_F32, N, D, D);
   };
   if (!seq) return linear2(0, D + F, gate, ctx->cs_a);
 
@@ -719,6 +814,8 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, hipStream_t stre
   am.n = 2 * F;
   am.split = 0;
   DIT_TIMED(P_LINEAR1, 2.0 * N * D * (2.0 * F), 0.0, gemm(am, EPI_QKV_SWIGLU), "linear1");
+  if (int rc = chk("linear1 -> SwiGLU output", (const char *)ctx->cat + (size_t)D * es, ctx->op, N, F, D + F))
+    return rc;
   return linear2(D, F, gate2, ctx->cs_b);
 }
 
@@ -752,10 +849,9 @@ int prepare_conditioning(dit_ctx *ctx, double t, double t_target, hipStream_t st
               "target temb l2");
     DIT_CHECK(add_row(ctx->cond, 3, D, ctx->tgt, stream), "target time");
   }
-  if (c.n_stream_blocks > 0)
-    if (int rc = compute_mods(ctx, 0, ctx->cond, stream)) return rc;
-  if (c.n_shared_blocks > 0)
-    if (int rc = compute_mods(ctx, 1, ctx->cond, stream)) return rc;
+  std::vector<int> all(ctx->modw.size());
+  for (size_t i = 0; i < all.size(); ++i) all[i] = (int)i;
+  if (int rc = compute_mods(ctx, all, ctx->cond, 3, stream)) return rc;
   DIT_CHECK(gemv(ctx->fmodv, ctx->fmod, ctx->op, 2 * D, D, ctx->cond, 3, 1, stream), "final modulation");
   return 0;
 }
@@ -840,8 +936,10 @@ int run_forward(dit_ctx *ctx, const float *lat, const Req &rq, double t, double 
     DIT_TIMED(P_EMBED, fle, 0.0, gemm_simple(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
   else
     DIT_TIMED(P_EMBED, fle, 0.0, gemm_mfma(ae, EPI_STORE_F32, ctx->op, stream), "img_in");
+  if (int rc = guard(ctx, -1, "img_in -> residual x", ctx->x, OP_F32, sg.n, D, D, stream)) return rc;
+  const int rows3[3] = {0, 1, 2};
   for (int b = 0; b < ctx->nblocks(); ++b)
-    if (int rc = run_block(ctx, b, ctx->x, sg, DIT_MASK_DEFAULT, stream)) return rc;
+    if (int rc = run_block(ctx, b, ctx->x, sg, DIT_MASK_DEFAULT, rows3, stream)) return rc;
   // output head on the image rows of each sequence
   const float *fm = ctx->fmodv + 2 * D;  // image segment's (shift, scale)
   const float *fms[3] = {fm, fm, fm};
@@ -871,6 +969,8 @@ int run_forward(dit_ctx *ctx, const float *lat, const Req &rq, double t, double 
       af.n_store = C;
       DIT_TIMED(P_FINAL, flf, 0.0, gemm_mfma(af, EPI_STORE_F32, ctx->op, stream), "final projection");
     }
+    if (int rc = guard(ctx, -1, "output head -> velocity / latents", out, OP_F32, n_img, C, C, stream))
+      return rc;
   }
   return 0;
 }
@@ -963,8 +1063,15 @@ extern "C" int dit_block_forward(dit_ctx *ctx, int block, float *x, int n_txt, i
   hipStream_t stream = (hipStream_t)stream_;
   const Segs sg = make_segs(n_txt, n_img, n_ref);
   DIT_CHECK(rope_table(ctx->cs, pos, sg.n, ctx->cfg.rope_theta, stream), "rope_table");
-  if (int rc = compute_mods(ctx, ctx->kind(block), cond, stream)) return rc;
-  return run_block(ctx, block, x, sg, mask, stream);
+  // one conditioning row per non-empty segment, in the order text, image, reference
+  const int count[3] = {n_txt, n_img, n_ref};
+  int mrow[3], n_cond = 0;
+  for (int s = 0; s < 3; ++s) mrow[s] = count[s] > 0 ? n_cond++ : 0;
+  std::vector<int> which;
+  for (int i : ctx->mod_of[block])
+    if (std::find(which.begin(), which.end(), i) == which.end()) which.push_back(i);
+  if (int rc = compute_mods(ctx, which, cond, n_cond, stream)) return rc;
+  return run_block(ctx, block, x, sg, mask, mrow, stream);
 }
 
 extern "C" int dit_forward(dit_ctx *ctx, const float *lat, const float *ref_lat, const float *txt,
@@ -1185,7 +1292,7 @@ extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dty
   if (!strcmp(name, "xm")) return ret(ctx->xm, ctx->fp8 ? DIT_FP8 : dt, D);
   if (!strcmp(name, "qkv")) return ret(ctx->qkv, dt, 3 * D);
   if (!strcmp(name, "cat")) return ret(ctx->cat, dt, D + F);
-  if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, ctx->mod_ld());
+  if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, ctx->mod_ld());  // [M][3][R]
   if (!strcmp(name, "x")) return ret(ctx->x, DIT_F32, D);
   return nullptr;
 }

@@ -20,7 +20,7 @@ DIT_F32, DIT_BF16, DIT_F16, DIT_FP8 = 0, 1, 2, 3
 COMPUTE = {"f32": DIT_F32, "bf16": DIT_BF16, "f16": DIT_F16, "fp8": DIT_FP8}
 DIT_FLUX2, DIT_FLUX3 = 0, 1
 DIT_MASK_DEFAULT, DIT_MASK_FULL, DIT_MASK_SEGMENT = -1, 0, 1
-DIT_OK, DIT_EINVAL, DIT_ENOMEM, DIT_EHIP, DIT_EUNSUPPORTED = 0, -1, -2, -3, -4
+DIT_OK, DIT_EINVAL, DIT_ENOMEM, DIT_EHIP, DIT_EUNSUPPORTED, DIT_ENUMERIC = 0, -1, -2, -3, -4, -5
 
 
 class DitConfig(ctypes.Structure):

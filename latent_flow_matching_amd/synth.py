@@ -49,6 +49,7 @@ class ModelConfig:
     txt_feat_dim: int = 0        # > 0: text features of this width are projected by txt_in
     flow_map: bool = False       # timestep-distilled model with a target-time embedding
     double_wiring: bool = False  # FLUX.2 double blocks: attention, then MLP (own LN and gate)
+    mod_per_block: bool = False  # every block has its own modulation projections (blk{b}.s{s}.mod)
 
     @property
     def n_blocks(self) -> int:
@@ -170,9 +171,17 @@ def weight_specs(cfg: ModelConfig):
     for kind in (0, 1):
         if (kind == 0 and cfg.n_stream_blocks == 0) or (kind == 1 and cfg.n_shared_blocks == 0):
             continue
+        if cfg.mod_per_block:
+            continue
         for s in range(cfg.n_mod_sets(kind)):
             rows = 6 * d if (kind == 0 and cfg.double_wiring) else 3 * d
             specs.append((f"mod.{kind}.s{s}", (rows, d), "linear", (_G_MOD, kind, s)))
+    if cfg.mod_per_block:
+        for b in range(cfg.n_blocks):
+            kind = 0 if b < cfg.n_stream_blocks else 1
+            rows = 6 * d if (kind == 0 and cfg.double_wiring) else 3 * d
+            for s in range(cfg.sets_of_block(b)):
+                specs.append((f"blk{b}.s{s}.mod", (rows, d), "linear", (_G_MOD, kind, s, 1000 + b)))
     for b in range(cfg.n_blocks):
         for s in range(cfg.sets_of_block(b)):
             p = f"blk{b}.s{s}"

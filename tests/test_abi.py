@@ -59,8 +59,8 @@ def _cfg(**kw):
     return c
 
 
-def _table(cfg=TINY2, drop=None, extra=None, bad_numel=None):
-    w = S.gen_weights(cfg, bits=True)
+def _table(cfg=TINY2, drop=None, extra=None, bad_numel=None, w=None):
+    w = S.gen_weights(cfg, bits=True) if w is None else w
     if drop:
         w.pop(drop)
     if extra:
@@ -115,6 +115,55 @@ def test_bad_weight_table_rejected(lib, kw, msg):
     arr, n, keep = _table(**kw)
     assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
     assert msg in dit.last_error()
+
+
+def _no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+
+
+def test_per_block_modulation_tables_pass_the_weight_checks(lib):
+    """Each block's own blk{b}.s{s}.mod (distinct, aliased to one array, or mixed with the
+    shared names) passes every weight check: create then fails only for want of a device."""
+    from dataclasses import replace
+    _no_gpu()
+    own = S.gen_weights(replace(TINY2, mod_per_block=True), bits=True)
+    shared = S.gen_weights(TINY2, bits=True)
+    aliased = {k: v for k, v in shared.items() if not k.startswith("mod.")}
+    aliased.update({"blk0.s0.mod": shared["mod.0.s0"], "blk0.s1.mod": shared["mod.0.s0"],
+                    "blk1.s0.mod": shared["mod.1.s0"]})
+    mixed = dict(shared)
+    mixed.pop("mod.1.s0")
+    mixed["blk1.s0.mod"] = own["blk1.s0.mod"]
+    for w in (own, aliased, mixed):
+        arr, n, keep = _table(w=w)
+        assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+        assert "no HIP device" in dit.last_error(), dit.last_error()
+
+
+def test_modulation_table_rules(lib):
+    from dataclasses import replace
+    own = S.gen_weights(replace(TINY2, mod_per_block=True), bits=True)
+    shared = S.gen_weights(TINY2, bits=True)
+    # a shared projection that no block uses
+    w = dict(own)
+    w["mod.1.s0"] = shared["mod.1.s0"]
+    arr, n, keep = _table(w=w)
+    assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+    assert "'mod.1.s0' is used by no block" in dit.last_error()
+    # neither the block's own projection nor the shared one
+    w = dict(own)
+    w.pop("blk1.s0.mod")
+    arr, n, keep = _table(w=w)
+    assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+    assert "missing weight 'blk1.s0.mod' (or the shared 'mod.1.s0')" in dit.last_error()
+    # a block's own projection of the wrong size
+    w = dict(own)
+    w["blk0.s1.mod"] = w["blk0.s1.mod"][:-1]
+    arr, n, keep = _table(w=w)
+    assert not lib.dit_ctx_create(ctypes.byref(_cfg()), arr, n)
+    assert "'blk0.s1.mod' has" in dit.last_error()
 
 
 def test_no_device_is_an_error_not_a_fallback(lib):

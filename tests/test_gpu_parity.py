@@ -1,8 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
 
-Bars: max|gpu - oracle| <= 2e-2 * RMS(oracle) for bf16 paths, <= 1e-4 * RMS(oracle) for the
-fp32 path.  Small shapes compare every element; the full benchmark shapes compare sampled
-rows (the oracle computes those rows one by one over all keys).
+Bars: max|gpu - oracle| <= 2e-2 * RMS(oracle) for 16-bit paths, <= 1e-4 * RMS(oracle) for the
+fp32 path, on block outputs, velocities and latent updates; block tests also hold the block
+update (output - input) to its own bar (helpers.tol_update), since at small width the update
+is under 1% of the output.  Every test compares every element, the full benchmark shapes
+included; a few variant tests at full width compare sampled rows (the oracle computes those
+rows over all keys).
 """
 from dataclasses import replace
 
@@ -12,7 +15,8 @@ import pytest
 from latent_flow_matching_amd import synth as S
 from oracle import dit_oracle as O
 from tests.helpers import (BF16_TOL, F32_TOL, TINY2, TINY3, dims_of, f64, gpu_weights,
-                           oracle_block, oracle_mod_sets, oracle_model, oracle_sets, rel_err, tol)
+                           mod_names, oracle_block, oracle_block_mod_sets, oracle_model, oracle_sets,
+                           rel_err, seg_cond, tol, tol_update, update_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +54,7 @@ def oracle_stages(cfg, w, b, x, segs, pos, cond):
     dims = dims_of(cfg)
     d, f, nh = cfg.hidden, cfg.mlp_hidden, cfg.heads
     kind, sos, mask = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
-    mods = O.segment_mods(oracle_mod_sets(cfg, w, kind), sos, [f64(c) for c in cond])
+    mods = O.segment_mods(oracle_block_mod_sets(cfg, w, b), sos, [f64(c) for c in cond])
     sets = oracle_sets(cfg, w, b)
     seg = O.segment_ids(*segs)
     n = seg.shape[0]
@@ -106,7 +110,7 @@ def run_block(cfg, b, n_txt, grid, ref_grid=None, mask=None, rows=None, seed=0, 
     pos = O.positions(n_txt, grid, (ref_grid,) if ref_grid else ())
     xt = dev(x)
     print(f"[block] arch={cfg.arch} b={b} segs={segs} compute={cfg.compute} D={cfg.hidden}", flush=True)
-    ctx.block_forward(b, xt, n_txt, n_img, n_ref, dev(pos), dev(cond),
+    ctx.block_forward(b, xt, n_txt, n_img, n_ref, dev(pos), dev(seg_cond(cond, segs)),
                       dit.DIT_MASK_DEFAULT if mask is None else mask)
     torch.cuda.synchronize()
     got = xt.cpu().numpy()
@@ -114,9 +118,8 @@ def run_block(cfg, b, n_txt, grid, ref_grid=None, mask=None, rows=None, seed=0, 
     if rows is not None:
         got = got[rows]
     err = rel_err(got, ref)
-    derr = rel_err(got - x[rows if rows is not None else slice(None)],
-                   ref - f64(x[rows if rows is not None else slice(None)]))
-    print(f"    out err {err:.3e}  delta err {derr:.3e}", flush=True)
+    derr = update_err(got, ref, x[rows if rows is not None else slice(None)])
+    print(f"    out err {err:.3e}  update err {derr:.3e}", flush=True)
     if stages and rows is None and err > tol(cfg) / 4:
         print("    stages:", {k: f"{v:.2e}" for k, v in stage_report(ctx, cfg, w, b, x, segs, pos, cond).items()},
               flush=True)
@@ -135,8 +138,8 @@ F32 = [replace(TINY2, bf16=False, compute="f32"), replace(TINY3, bf16=False, com
 @pytest.mark.parametrize("b", [0, 1], ids=["stream_block", "shared_block"])
 def test_block_tiny_ragged(cfg, b):
     """Ragged segments spanning several GEMM / attention tiles, all three streams."""
-    err, _ = run_block(cfg, b, 77, (13, 11), (9, 10))
-    assert err <= tol(cfg, full_width=False)
+    err, derr = run_block(cfg, b, 77, (13, 11), (9, 10))
+    assert err <= tol(cfg) and derr <= tol_update(cfg)
 
 
 @pytest.mark.parametrize("segs", [(1, (1, 1), None), (0, (3, 5), None), (300, (2, 2), None),
@@ -145,15 +148,15 @@ def test_block_tiny_edge_shapes(segs):
     n_txt, grid, ref = segs
     for cfg in (TINY2, TINY3):
         for b in (0, 1):
-            err, _ = run_block(cfg, b, n_txt, grid, ref, max_tokens=600, stages=False)
-            assert err <= BF16_TOL
+            err, derr = run_block(cfg, b, n_txt, grid, ref, max_tokens=600, stages=False)
+            assert err <= BF16_TOL and derr <= tol_update(cfg)
 
 
 def test_single_block_fp32_32txt_16img():
     """One single-stream block, 32 text + 16 image tokens, fp32, full model width."""
     wl = S.WORKLOADS["single_block_fp32_32txt_16img"]
     err, derr = run_block(wl.model, 0, wl.n_txt, wl.grid)
-    assert err <= F32_TOL and derr <= 10 * F32_TOL
+    assert err <= F32_TOL and derr <= tol_update(wl.model)
 
 
 @pytest.mark.parametrize("compute", ["f16", "bf16"])
@@ -162,14 +165,14 @@ def test_double_block_bf16_128txt_256img(compute):
     wl = S.WORKLOADS["double_block_bf16_128txt_256img"]
     cfg = replace(wl.model, compute=compute)
     err, derr = run_block(cfg, 0, wl.n_txt, wl.grid)
-    assert err <= tol(cfg)
+    assert err <= tol(cfg, full_width=True) and derr <= tol_update(cfg)
 
 
 def test_mask_override_segment_equals_separate_streams():
     """A shared block run with the block-diagonal mask equals the oracle's masked block."""
     from latent_flow_matching_amd import dit
-    err, _ = run_block(TINY3, 1, 40, (6, 7), (5, 5), mask=dit.DIT_MASK_SEGMENT)
-    assert err <= BF16_TOL
+    err, derr = run_block(TINY3, 1, 40, (6, 7), (5, 5), mask=dit.DIT_MASK_SEGMENT)
+    assert err <= BF16_TOL and derr <= tol_update(TINY3)
 
 
 # ----------------------------------------------------------------- whole forward / denoise
@@ -191,7 +194,7 @@ def _forward_case(cfg, n_txt, grid, ref_grid, t):
 def test_forward_tiny(cfg):
     err = _forward_case(cfg, 50, (9, 7), (6, 5) if cfg.arch == S.ARCH_FLUX3 else None, 0.75)
     print(f"forward err {err:.3e}")
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 @pytest.mark.parametrize("cfg", [TINY2, TINY3], ids=["flux2", "flux3"])
@@ -211,6 +214,58 @@ def test_denoise_tiny(cfg):
     err = rel_err(lat.cpu().numpy() - f64(noise), want - f64(noise))
     print(f"denoise update err {err:.3e}")
     assert err <= BF16_TOL
+
+
+# ----------------------------------------------------------------- per-block modulation projections
+
+@pytest.mark.parametrize("cfg", [replace(TINY2, n_stream_blocks=2, n_shared_blocks=2, mod_per_block=True),
+                                 replace(TINY3, n_stream_blocks=2, n_shared_blocks=2, mod_per_block=True)],
+                         ids=["flux2", "flux3"])
+def test_forward_per_block_modulation_matches_oracle(cfg):
+    """Every block with its own modulation projections (blk{b}.s{s}.mod) against the oracle
+    model with per-block projections."""
+    err = _forward_case(cfg, 50, (9, 7), (6, 5) if cfg.arch == S.ARCH_FLUX3 else None, 0.75)
+    print(f"per-block modulation forward err {err:.3e}")
+    assert err <= tol(cfg)
+
+
+def test_per_block_modulation_aliasing_equals_shared():
+    """A table whose per-block entries all name the shared projections' data (aliases) gives
+    bitwise the velocity of the table with the shared names, and a block call on one cond row
+    per non-empty segment matches too."""
+    from latent_flow_matching_amd import dit
+    cfg = replace(TINY3, n_stream_blocks=2, n_shared_blocks=2)
+    w = gpu_weights(cfg, S.gen_weights(cfg))
+    per_block = {k: v for k, v in w.items() if not k.startswith("mod.")}
+    for b in range(cfg.n_blocks):
+        kind = 0 if b < cfg.n_stream_blocks else 1
+        for s_ in range(cfg.sets_of_block(b)):
+            per_block[f"blk{b}.s{s_}.mod"] = w[f"mod.{kind}.s{s_}"]   # the same array
+    _CTX.clear()
+    grid, ref_grid = (6, 5), (4, 4)
+    lat = dev(S.gen_latents(30, cfg.in_channels))
+    ref = dev(S.gen_latents(16, cfg.in_channels, key=(1,)))
+    txt = dev(S.gen_text(24, cfg.hidden))
+    outs = []
+    for table in (w, per_block):
+        ctx = dit.DiT(cfg, table, 256)
+        v = torch.empty((30, cfg.in_channels), device="cuda")
+        ctx.forward(lat, txt, grid, 0.5, v, ref, ref_grid)
+        x = dev(S.gen_tokens(70, cfg.hidden))
+        cond = S.gen_cond(3, cfg.hidden)
+        ctx.block_forward(3, x, 24, 30, 16, dev(O.positions(24, grid, (ref_grid,))), dev(cond))
+        torch.cuda.synchronize()
+        outs.append((v.cpu().numpy(), x.cpu().numpy()))
+        ctx.close()
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_block_forward_takes_one_cond_row_per_present_segment():
+    """With the image segment empty, the two cond rows given are those of the text and the
+    reference segments: the block matches the oracle fed those rows."""
+    cfg = TINY3
+    err, derr = run_block(cfg, 1, 40, (0, 0), (5, 6))
+    assert err <= tol(cfg) and derr <= tol_update(cfg)
 
 
 # ----------------------------------------------------------------- several references, image-to-image
@@ -236,7 +291,7 @@ def test_forward_several_references_matches_oracle(cfg):
                      f64(ref), list(REF_GRIDS))
     err = rel_err(v.cpu().numpy(), want)
     print(f"several references err {err:.3e}")
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 REF_GRIDS_MAX = [(2, 3), (3, 2), (1, 4), (4, 1), (2, 2), (1, 1), (3, 3), (2, 5), (1, 2), (2, 1)]
@@ -259,7 +314,7 @@ def test_forward_ten_references_matches_oracle(cfg):
                      list(REF_GRIDS_MAX))
     err = rel_err(v.cpu().numpy(), want)
     print(f"    ten references err {err:.3e}", flush=True)
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 @pytest.mark.parametrize("seeded", [True, False], ids=["seeded_noise", "given_noise"])
@@ -349,7 +404,7 @@ def test_text_features_match_oracle(cfg, n_txt):
     want = O.project_text(f64(feat), f64(w["txt_in"]))
     err = rel_err(out.cpu().numpy(), want)
     print(f"text features err {err:.3e}")
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 @pytest.mark.parametrize("cfg", FM, ids=["f16", "bf16", "f32"])
@@ -368,7 +423,7 @@ def test_forward_flow_matches_oracle(cfg):
                      f64(ref), ref_grid, t_target=0.5)
     err = rel_err(v.cpu().numpy(), want)
     print(f"flow-map forward err {err:.3e}")
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 def test_denoise_flow_map_matches_oracle():
@@ -442,7 +497,7 @@ def test_forward_cfg_matches_oracle(cfg, guidance):
     got = v.cpu().numpy().astype(np.float64)
     rms = lambda a: float(np.sqrt(np.mean(a * a)))
     err = float(np.max(np.abs(got - want)))
-    bound = tol(cfg, full_width=False) * (abs(guidance) * rms(vc) + abs(1 - guidance) * rms(vu))
+    bound = tol(cfg) * (abs(guidance) * rms(vc) + abs(1 - guidance) * rms(vu))
     print(f"    forward_cfg max err {err:.3e}, bound {bound:.3e} (rel to RMS(v) {err / rms(want):.3e})",
           flush=True)
     assert err <= bound
@@ -584,8 +639,8 @@ def test_attention_equal_shares_match_oracle(case, monkeypatch):
     monkeypatch.setenv("DIT_ATTN_GRID", str(lean_grid))
     _CTX.clear()
     try:
-        err, _ = run_block(cfg, b, n_txt, grid, ref_grid, max_tokens=n + 1)
-        assert err <= tol(cfg, full_width=False)
+        err, derr = run_block(cfg, b, n_txt, grid, ref_grid, max_tokens=n + 1)
+        assert err <= tol(cfg) and derr <= tol_update(cfg)
         ctx, _ = context(cfg, n + 1)
         x = S.gen_tokens(n, cfg.hidden, key=(5,))
         cond = S.gen_cond(3, cfg.hidden)
@@ -593,7 +648,7 @@ def test_attention_equal_shares_match_oracle(case, monkeypatch):
         outs = []
         for _ in range(2):
             xt = dev(x)
-            ctx.block_forward(b, xt, segs[0], segs[1], segs[2], dev(pos), dev(cond))
+            ctx.block_forward(b, xt, segs[0], segs[1], segs[2], dev(pos), dev(seg_cond(cond, segs)))
             torch.cuda.synchronize()
             outs.append(xt.cpu().numpy())
         assert np.array_equal(outs[0], outs[1])
@@ -644,15 +699,15 @@ def test_sequential_block_matches_oracle(cfg, b, segs):
     W1 and W2 used in halves) against the oracle's sequential block; the single block of the
     same model keeps the parallel form."""
     n_txt, grid, ref_grid = segs
-    err, _ = run_block(cfg, b, n_txt, grid, ref_grid, stages=False)
-    assert err <= tol(cfg)
+    err, derr = run_block(cfg, b, n_txt, grid, ref_grid, stages=False)
+    assert err <= tol(cfg) and derr <= tol_update(cfg)
 
 
 @pytest.mark.parametrize("cfg", SEQ, ids=["f16", "bf16", "f32"])
 def test_sequential_forward_matches_oracle(cfg):
     err = _forward_case(cfg, 50, (9, 7), (6, 5), 0.75)
     print(f"sequential forward err {err:.3e}")
-    assert err <= tol(cfg, full_width=False)
+    assert err <= tol(cfg)
 
 
 def test_sequential_denoise_cfg_matches_oracle():
@@ -689,8 +744,8 @@ def test_sequential_block_full_width_sampled_rows(n_img, grid):
     linear2 halves fill few compute units and run as k-slices over their column ranges of W2."""
     cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1, double_wiring=True)
     n = 512 + n_img
-    err, _ = run_block(cfg, 0, 512, grid, rows=_rows(n), max_tokens=n, stages=False)
-    assert err <= BF16_TOL
+    err, derr = run_block(cfg, 0, 512, grid, rows=_rows(n), max_tokens=n, stages=False)
+    assert err <= BF16_TOL and derr <= tol_update(cfg)
 
 
 def test_forward_cfg_full_width_matches_oracle():
@@ -717,57 +772,33 @@ def test_forward_cfg_full_width_matches_oracle():
     assert err <= bound
 
 
-def test_sequential_fp8_block_full_width_sampled_rows():
-    """The sequentially wired double block on the E4M3 path at full width, 512 + 4096 tokens:
-    each half quantizes its own inputs (bars for the compounded code flips of this wiring)."""
-    from tests.helpers import FP8_SEQ_UPDATE_MAX_TOL, FP8_SEQ_UPDATE_RMS_TOL
-    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1, double_wiring=True,
-                  compute="fp8")
-    n = 512 + 4096
-    rows = _rows(n)
-    ctx, w = context(cfg, n)
-    x = S.gen_tokens(n, cfg.hidden, key=(0,))
-    cond = S.gen_cond(3, cfg.hidden)
-    pos = O.positions(512, (64, 64), ())
-    xt = dev(x)
-    from latent_flow_matching_amd import dit
-    print("[block] sequential fp8 full width 512+4096", flush=True)
-    ctx.block_forward(0, xt, 512, 4096, 0, dev(pos), dev(cond), dit.DIT_MASK_DEFAULT)
-    torch.cuda.synchronize()
-    got = xt.cpu().numpy()[rows].astype(np.float64)
-    ref = oracle_block(cfg, w, 0, x, (512, 4096, 0), pos, cond, rows=rows)
-    u_got, u_ref = got - f64(x[rows]), ref - f64(x[rows])
-    rms_u = float(np.sqrt(np.mean(u_ref ** 2)))
-    e_rms = float(np.sqrt(np.mean((u_got - u_ref) ** 2))) / rms_u
-    e_max = float(np.max(np.abs(u_got - u_ref))) / rms_u
-    print(f"    update error: RMS {e_rms:.3e} (bar {FP8_SEQ_UPDATE_RMS_TOL}), max {e_max:.3e} "
-          f"(bar {FP8_SEQ_UPDATE_MAX_TOL})", flush=True)
-    assert e_rms <= FP8_SEQ_UPDATE_RMS_TOL and e_max <= FP8_SEQ_UPDATE_MAX_TOL
-
-
-# ----------------------------------------------------------------- full benchmark shapes, sampled rows
-
 def _rows(n, k=24, seed=0):
     r = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, n - 1], r.choice(n, k, replace=False)]))
 
 
+# ----------------------------------------------------------------- full benchmark shapes, every element
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("b", [0, 1], ids=["double", "single"])
-def test_flux2_block_1024px_sampled_rows(b):
-    """FLUX.2 double / single block at 512 text + 4096 image tokens (1024x1024 px)."""
+def test_flux2_block_512txt_4096img_every_element(b):
+    """FLUX.2 double / single block at 512 text + 4096 image tokens (1024x1024 px), in the
+    launch configuration the benchmark times: every element of the output and of the update."""
     cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
     n = 512 + 4096
-    err, _ = run_block(cfg, b, 512, (64, 64), rows=_rows(n), max_tokens=n)
-    assert err <= BF16_TOL
+    err, derr = run_block(cfg, b, 512, (64, 64), max_tokens=n, stages=False)
+    assert err <= BF16_TOL and derr <= tol_update(cfg)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("b", [0, 1], ids=["per_mode", "joint"])
-def test_flux3_block_1024px_ref_sampled_rows(b):
-    """FLUX.3 per-mode / joint block at 512 text + 4096 image + 4096 reference tokens."""
+def test_flux3_block_512txt_4096img_4096ref_every_element(b):
+    """FLUX.3 per-mode / joint block at 512 text + 4096 image + 4096 reference tokens: every
+    element of the output and of the update."""
     cfg = replace(S.FLUX3_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
     n = 512 + 4096 + 4096
-    err, _ = run_block(cfg, b, 512, (64, 64), (64, 64), rows=_rows(n), max_tokens=n)
-    assert err <= BF16_TOL
+    err, derr = run_block(cfg, b, 512, (64, 64), (64, 64), max_tokens=n, stages=False)
+    assert err <= BF16_TOL and derr <= tol_update(cfg)
 
 
 # ----------------------------------------------------------------- whole stack, teacher-forced per block
@@ -778,7 +809,7 @@ _STACK_WL = S.WORKLOADS["flux2_stack_512txt_1024img_4step"]
 @pytest.fixture(scope="module")
 def flux2_stack_run():
     """All 25 FLUX.2 blocks at 512 text + 1024 image tokens (512x512 px) run on the GPU in
-    order; each block's input (the previous GPU block's output) and sampled output rows."""
+    order; each block's input (the previous GPU block's output) and output."""
     from latent_flow_matching_amd import dit
     wl = _STACK_WL
     cfg = wl.model
@@ -789,32 +820,33 @@ def flux2_stack_run():
     x0 = S.gen_tokens(n, cfg.hidden, key=(7,))
     cond = S.gen_cond(3, cfg.hidden)
     pos = O.positions(wl.n_txt, wl.grid)
-    rows = _rows(n, k=14, seed=3)
     xt = dev(x0)
     ins, outs = [], []
     for b in range(cfg.n_blocks):
         ins.append(xt.cpu().numpy())
-        ctx.block_forward(b, xt, *segs, dev(pos), dev(cond))
+        ctx.block_forward(b, xt, *segs, dev(pos), dev(seg_cond(cond, segs)))
         torch.cuda.synchronize()
-        outs.append(xt.cpu().numpy()[rows])
+        outs.append(xt.cpu().numpy())
     ctx.close()
-    return cfg, segs, pos, cond, rows, ins, outs
+    return cfg, segs, pos, cond, ins, outs
+
+
+def _stack_block(cfg, segs, pos, cond, ins, outs, b):
+    w = S.gen_block_weights(cfg, b)
+    w.update(S.gen_weights(cfg, names=mod_names(cfg, b)))
+    x = ins[b]
+    ref = oracle_block(cfg, w, b, x, segs, pos, cond)
+    err = rel_err(outs[b], ref)
+    derr = update_err(outs[b], ref, x)
+    print(f"block {b}: out err {err:.3e}  update err {derr:.3e}", flush=True)
+    assert err <= BF16_TOL and derr <= tol_update(cfg)
 
 
 @pytest.mark.parametrize("b", range(_STACK_WL.model.n_blocks))
 def test_flux2_stack_512txt_1024img_per_block(flux2_stack_run, b):
-    """Teacher-forced stack parity: the oracle block runs on the GPU's own input to block b,
-    sampled output rows compared (full attention over all keys for those rows)."""
-    cfg, segs, pos, cond, rows, ins, outs = flux2_stack_run
-    kind, _, _ = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
-    w = S.gen_block_weights(cfg, b)
-    w.update(S.gen_weights(cfg, names={f"mod.{kind}.s{s}" for s in range(cfg.n_mod_sets(kind))}))
-    x = ins[b]
-    ref = oracle_block(cfg, w, b, x, segs, pos, cond, rows=rows)
-    err = rel_err(outs[b], ref)
-    derr = rel_err(outs[b] - x[rows], ref - f64(x[rows]))
-    print(f"block {b}: out err {err:.3e}  delta err {derr:.3e}", flush=True)
-    assert err <= BF16_TOL
+    """Teacher-forced stack parity: the oracle block runs on the GPU's own input to block b;
+    every element of the block's output and update is compared."""
+    _stack_block(*flux2_stack_run, b)
 
 
 @pytest.fixture(scope="module")
@@ -831,28 +863,75 @@ def flux3_stack_run():
     x0 = S.gen_tokens(n, cfg.hidden, key=(8,))
     cond = S.gen_cond(3, cfg.hidden)
     pos = O.positions(n_txt, grid, (ref_grid,))
-    rows = _rows(n, k=14, seed=4)
     xt = dev(x0)
     ins, outs = [], []
     for b in range(cfg.n_blocks):
         ins.append(xt.cpu().numpy())
-        ctx.block_forward(b, xt, *segs, dev(pos), dev(cond))
+        ctx.block_forward(b, xt, *segs, dev(pos), dev(seg_cond(cond, segs)))
         torch.cuda.synchronize()
-        outs.append(xt.cpu().numpy()[rows])
+        outs.append(xt.cpu().numpy())
     ctx.close()
-    return cfg, segs, pos, cond, rows, ins, outs
+    return cfg, segs, pos, cond, ins, outs
 
 
 @pytest.mark.parametrize("b", range(S.FLUX3_KLEIN.n_blocks))
 def test_flux3_stack_128txt_256img_256ref_per_block(flux3_stack_run, b):
     """Teacher-forced FLUX.3 stack parity, per block, on the GPU's own block inputs."""
-    cfg, segs, pos, cond, rows, ins, outs = flux3_stack_run
-    kind, _, _ = O.block_plan(cfg.arch, b, cfg.n_stream_blocks)
-    w = S.gen_block_weights(cfg, b)
-    w.update(S.gen_weights(cfg, names={f"mod.{kind}.s{s}" for s in range(cfg.n_mod_sets(kind))}))
-    x = ins[b]
-    ref = oracle_block(cfg, w, b, x, segs, pos, cond, rows=rows)
-    err = rel_err(outs[b], ref)
-    derr = rel_err(outs[b] - x[rows], ref - f64(x[rows]))
-    print(f"block {b}: out err {err:.3e}  delta err {derr:.3e}", flush=True)
+    _stack_block(*flux3_stack_run, b)
+
+
+# ----------------------------------------------------------------- whole FLUX.2 model at 512x512 px
+
+@pytest.fixture(scope="module")
+def flux2_model_512px():
+    """The full 25-block FLUX.2 model at 512 text + 1024 image tokens: a library context and
+    the oracle's model of the same seeded weights."""
+    from latent_flow_matching_amd import dit
+    wl = _STACK_WL
+    cfg = wl.model
+    _CTX.clear()
+    w32 = S.gen_weights(cfg)
+    ctx = dit.DiT(cfg, gpu_weights(cfg, w32), max_tokens=wl.n_tokens)
+    m = oracle_model(cfg, w32)
+    del w32
+    yield wl, cfg, ctx, m
+    ctx.close()
+
+
+@pytest.mark.timeout(900)
+def test_flux2_forward_512txt_1024img_25_blocks(flux2_model_512px):
+    """One transformer call of the whole 25-block stack (5 double + 20 single) at 512 text +
+    1024 image tokens against the oracle's forward: every element of the velocity."""
+    wl, cfg, ctx, m = flux2_model_512px
+    lat = S.gen_latents(wl.n_img, cfg.in_channels)
+    txt = S.gen_text(wl.n_txt, cfg.hidden)
+    v = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
+    print("[forward] FLUX.2 25 blocks, 512+1024 tokens, t=0.75", flush=True)
+    ctx.forward(dev(lat), dev(txt), wl.grid, 0.75, v)
+    torch.cuda.synchronize()
+    want = O.forward(m, f64(lat), f64(txt), wl.grid, float(np.float32(0.75)))
+    err = rel_err(v.cpu().numpy(), want)
+    print(f"    25-block forward err {err:.3e}", flush=True)
     assert err <= BF16_TOL
+
+
+@pytest.mark.timeout(1800)
+def test_flux2_denoise_512txt_1024img_4step_reported(flux2_model_512px):
+    """The 4-step Euler loop of the whole stack at 512 text + 1024 image tokens from seeded
+    noise, against the oracle's loop.  Errors compound over 100 block calls, so this is
+    reported (printed); the assertion only guards against gross failure."""
+    wl, cfg, ctx, m = flux2_model_512px
+    seed = 11
+    txt = S.gen_text(wl.n_txt, cfg.hidden)
+    lat = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
+    print("[denoise] FLUX.2 25 blocks, 512+1024 tokens, 4 Euler steps", flush=True)
+    ctx.denoise(lat, dev(txt), wl.grid, 4, seed)
+    torch.cuda.synchronize()
+    noise = O.noise(wl.n_img * cfg.in_channels, seed).reshape(wl.n_img, cfg.in_channels)
+    want = O.denoise(m, noise, f64(txt), wl.grid, 4)
+    got = lat.cpu().numpy().astype(np.float64)
+    err = rel_err(got - noise, want - noise)
+    rms = float(np.sqrt(np.mean((got - want) ** 2)) / np.sqrt(np.mean((want - noise) ** 2)))
+    print(f"    REPORTED 4-step denoise, 25 blocks, 512+1024 tokens: latent update max err / RMS "
+          f"{err:.3e}, RMS err / RMS {rms:.3e}", flush=True)
+    assert err <= 0.5
