@@ -84,11 +84,12 @@ def cpu_baseline(wl, cfg):
         x = O.block_forward(x, segs, sets, sos, mods, pos, mask, dims, act_fp8=fp8)
         dt += time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model, nproc = host_cpu()
     return {"value": len(blocks) * n / dt, "unit": "block tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": f"blocks {', '.join(map(str, blocks))} of the stack in sequence at "
                       f"{'+'.join(str(s) for s in segs if s)} tokens, all rows, float64 "
-                      f"NumPy/OpenBLAS, {dt:.1f} s of oracle time"
+                      f"NumPy with {threads} BLAS threads, {dt:.1f} s of oracle time"
                       + ("; row-wise E4M3 projections" if fp8 else "")
                       + ("; with guidance the oracle runs each branch as such a sequence"
                          if wl.guidance is not None else "")}
@@ -175,6 +176,19 @@ def summarize_rocprof(args):
             lines.append(f"| {cls} | `{short[:70]}` | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                          f"{float(r['TotalDurationNs']) / total:.3f} |")
+        per_class = {}
+        for r in rows:
+            cls = _kernel_class(r["Name"])
+            if cls is None:
+                continue
+            c = per_class.setdefault(cls, [0.0, 0])
+            c[0] += float(r["TotalDurationNs"])
+            c[1] += int(r["Calls"])
+        tj = {"workload": wl, "compute": args.compute, "sources_sha256": all_sources_sha256(),
+              "avg_us": {k: round(v[0] / v[1] / 1e3, 2) for k, v in sorted(per_class.items())}}
+        lines += ["", "Average launch duration per kernel class, read by bench.py for "
+                  "`roofline.trace_avg_launch_us` while the library's sources hash to the same "
+                  "value:", "", "trace_json: " + json.dumps(tj)]
         out = os.path.join(PROFILES, f"kernel_trace_{wl}{sfx}.md")
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -265,6 +279,174 @@ def summarize_rocprof(args):
         print(f"wrote {out}")
 
 
+def all_sources_sha256():
+    """Hash of every kernel and runtime source of the library (what a kernel trace measured)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "latent_flow_matching_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_trace_avg(kernel, workload, compute):
+    """Average duration (us) of `kernel` in the committed rocprofv3 trace of this workload, or
+    None when there is none or the library's sources have changed since it was taken."""
+    path = os.path.join(PROFILES, f"kernel_trace_{workload}" + ("_fp8" if compute == "fp8" else "") + ".md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"^trace_json: (\{.*\})$", f.read(), re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("sources_sha256") != all_sources_sha256():
+        return None
+    return d.get("avg_us", {}).get(kernel), path
+
+
+def host_cpu():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return model, nproc
+
+
+def make_context(cfg, max_tokens):
+    from latent_flow_matching_amd import dit, synth as S
+    t0 = time.perf_counter()
+    weights = S.gen_weights(cfg, bits=True)
+    ctx = dit.DiT(cfg, weights, max_tokens=max_tokens)
+    del weights
+    log(f"context for {cfg.arch=} {cfg.compute=} {cfg.n_blocks} blocks created in {time.perf_counter() - t0:.1f} s")
+    return ctx
+
+
+def time_stack(ctx, wl, cfg, steps, warmup, profile=True):
+    """Time `steps` full denoise calls of a stack workload on ctx (inputs resident in HBM).
+    With profile: one more untimed step with events around every launch (the per-kernel
+    breakdown), and events around the dominant kernel class during the timed steps."""
+    import torch
+
+    from latent_flow_matching_amd import synth as S
+    nseq = 1 if wl.guidance is None else 2
+    txt = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden), device="cuda")
+    txt_u = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden, seed=S.SEED_T + 7), device="cuda")
+    ref = (torch.tensor(S.gen_latents(wl.n_ref, cfg.in_channels, key=(1,)), device="cuda")
+           if wl.n_ref else None)
+    lat = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
+    ref_grid = wl.ref_grid or (0, 0)
+    feat = (torch.tensor(S.gen_normal((wl.n_txt, cfg.txt_feat_dim), S.SEED_T, (5,)), device="cuda")
+            if cfg.txt_feat_dim else None)
+
+    def step(i):
+        if feat is not None:  # the text projection runs once per image, inside the step
+            ctx.text_features(feat, txt)
+        if nseq == 2:
+            ctx.denoise_cfg(lat, txt, txt_u, wl.grid, wl.steps, wl.guidance, seed=1000 + i,
+                            ref_lat=ref, ref_grid=ref_grid)
+        else:
+            ctx.denoise(lat, txt, wl.grid, wl.steps, seed=1000 + i, ref_lat=ref, ref_grid=ref_grid)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    launches = wl.steps * (cfg.n_blocks * 7 + 8 + 4 * nseq) + 64  # room for fp8 and sequential blocks
+    prof, dom = None, None
+    if profile:
+        ctx.profile_start(launches)
+        step(warmup)
+        torch.cuda.synchronize()
+        prof = ctx.profile_stop()
+        dom = max((k for k in prof if prof[k][2] > 0), key=lambda k: prof[k][0])
+        ctx.profile_start(steps * launches, kernels=dom)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(warmup + 1 + i)
+    end.record()
+    torch.cuda.synchronize()
+    timed = ctx.profile_stop() if profile else None
+    ms = start.elapsed_time(end)
+    assert torch.isfinite(lat).all(), "non-finite latents"
+    return {"ms": ms, "steps": steps, "prof": prof, "timed": timed, "dom": dom, "nseq": nseq}
+
+
+def stack_flops(wl, cfg):
+    """GEMM + attention flops of one denoise call (all steps, both branches with guidance)."""
+    from latent_flow_matching_amd import synth as S
+    segs = (wl.n_txt, wl.n_img, wl.n_ref)
+    segs = tuple(x for x in segs if x)
+    per_mode = cfg.arch == S.ARCH_FLUX3
+    fl = (cfg.n_stream_blocks * S.flops_per_block(segs, cfg.hidden, cfg.mlp_hidden, per_mode) +
+          cfg.n_shared_blocks * S.flops_per_block(segs, cfg.hidden, cfg.mlp_hidden, False))
+    return fl * wl.steps * (1 if wl.guidance is None else 2)
+
+
+def stack_summary(wl, cfg, r, mfma_peak):
+    ms_step = r["ms"] / r["steps"]
+    tf = stack_flops(wl, cfg) / (ms_step * 1e-3) / 1e12
+    toks = wl.n_tokens * r["nseq"] * cfg.n_blocks * wl.steps / (ms_step * 1e-3)
+    out = {"ms_per_step": round(ms_step, 3), "block_tokens_per_s": round(toks, 1),
+           "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
+    if mfma_peak:
+        out["pct_measured_peak"] = round(100 * tf / mfma_peak, 2)
+    return out
+
+
+def time_block_workload(wl, steps=20, warmup=3):
+    """One block of a single-block configuration through dit_block_forward (its modulation
+    GEMVs included): us per call, and the bytes it must stream, W1 and W2 of its weight sets
+    and their modulation projections, over that time (these configurations are bound by that
+    weight stream).  The RoPE coordinates are zeros: their values do not change the work."""
+    import torch
+
+    from latent_flow_matching_amd import synth as S
+    cfg = wl.model
+    n = wl.n_tokens
+    ctx = make_context(cfg, n)
+    d, f = cfg.hidden, cfg.mlp_hidden
+    kind = 0 if cfg.n_stream_blocks else 1
+    sets = cfg.sets_of_block(0)
+    es = 4 if cfg.compute == "f32" else 2
+    wbytes = es * (sets * ((3 * d + 2 * f) * d + d * (d + f)) + cfg.n_mod_sets(kind) * 3 * d * d)
+    x = torch.tensor(S.gen_tokens(n, d), device="cuda")
+    pos = torch.zeros((n, 4), device="cuda")
+    segs = (wl.n_txt, wl.n_img, wl.n_ref)
+    cond = torch.tensor(S.gen_cond(sum(1 for v in segs if v), d), device="cuda")
+    for _ in range(warmup):
+        ctx.block_forward(0, x, *segs, pos, cond)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        ctx.block_forward(0, x, *segs, pos, cond)
+    end.record()
+    torch.cuda.synchronize()
+    ctx.close()
+    us = start.elapsed_time(end) * 1e3 / steps
+    fl = S.flops_per_block(tuple(v for v in segs if v), d, f, False)
+    return {"us_per_block": round(us, 1), "bound": "hbm", "weight_bytes": wbytes,
+            "gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "tflops": round(fl / (us * 1e-6) / 1e12, 2), "operands": cfg.compute,
+            "block": "double" if kind == 0 else "single"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +455,9 @@ def main():
     ap.add_argument("--workload", default="flux2_stack_512txt_4096img_4step")
     ap.add_argument("--compute", default="f16", choices=["f16", "bf16", "fp8"])
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--extras", default="on", choices=["on", "off"],
+                    help="also time the other configurations (bf16 operands, 512x512, FLUX.3 "
+                         "with a reference, the single double and single blocks)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration"])
     ap.add_argument("--summarize-rocprof", action="store_true")
     ap.add_argument("--trace-dir")
@@ -296,7 +481,6 @@ def main():
 
     from dataclasses import replace
 
-    import numpy as np
     import torch
 
     if args.mode == "copy-calibration":
@@ -308,61 +492,22 @@ def main():
 
     wl = S.WORKLOADS[args.workload]
     if wl.blocks != "stack":
-        raise SystemExit(f"{args.workload} is a parity configuration, not a bench workload")
+        raise SystemExit(f"{args.workload} is a single-block configuration; it is timed with the "
+                         "extras of a stack workload")
     cfg = replace(wl.model, compute=args.compute)
-    n = wl.n_tokens
-    nseq = 1 if wl.guidance is None else 2  # guidance: both branches as one batch of 2
     torch.cuda.set_device(0)
-    t0 = time.perf_counter()
-    weights = S.gen_weights(cfg, bits=True)
-    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
-    t0 = time.perf_counter()
-    ctx = dit.DiT(cfg, weights, max_tokens=n * nseq)
-    del weights
-    log(f"context created in {time.perf_counter() - t0:.1f} s")
-    txt = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden), device="cuda")
-    txt_u = torch.tensor(S.gen_text(wl.n_txt, cfg.hidden, seed=S.SEED_T + 7), device="cuda")
-    ref = (torch.tensor(S.gen_latents(wl.n_ref, cfg.in_channels, key=(1,)), device="cuda")
-           if wl.n_ref else None)
-    lat = torch.empty((wl.n_img, cfg.in_channels), device="cuda")
-    ref_grid = wl.ref_grid or (0, 0)
+    mfma = {}
+    for c in ("f16", "bf16"):
+        tf, ghz = dit.mfma_rate(c)
+        mfma[c] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3)}
+        log(f"sustained 16x16x32 MFMA rate, {c}: {tf:.1f} TFLOP/s at {ghz:.2f} GHz")
+    mpeak = mfma["bf16" if args.compute == "bf16" else "f16"]["tflops"] if args.compute != "fp8" else None
 
-    feat = (torch.tensor(S.gen_normal((wl.n_txt, cfg.txt_feat_dim), S.SEED_T, (5,)), device="cuda")
-            if cfg.txt_feat_dim else None)
-
-    def step(i):
-        if feat is not None:  # the text projection runs once per image, inside the step
-            ctx.text_features(feat, txt)
-        if nseq == 2:
-            ctx.denoise_cfg(lat, txt, txt_u, wl.grid, wl.steps, wl.guidance, seed=1000 + i,
-                            ref_lat=ref, ref_grid=ref_grid)
-        else:
-            ctx.denoise(lat, txt, wl.grid, wl.steps, seed=1000 + i, ref_lat=ref, ref_grid=ref_grid)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # one untimed step with every kernel class timed: the per-kernel breakdown, and which class
-    # dominates (the roofline kernel)
-    launches = wl.steps * (cfg.n_blocks * 7 + 8 + 4 * nseq) + 64  # room for fp8 and sequential blocks
-    ctx.profile_start(launches)
-    step(args.warmup)
-    torch.cuda.synchronize()
-    prof = ctx.profile_stop()
-    dom = max((k for k in prof if prof[k][2] > 0), key=lambda k: prof[k][0])
-    # timed steps: only the dominant class records events (two per launch)
-    ctx.profile_start(args.steps * launches, kernels=dom)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step(args.warmup + 1 + i)
-    end.record()
-    torch.cuda.synchronize()
-    prof_timed = ctx.profile_stop()
-    ms = start.elapsed_time(end)
-    assert torch.isfinite(lat).all(), "non-finite latents"
-
+    nseq = 1 if wl.guidance is None else 2
+    ctx = make_context(cfg, wl.n_tokens * nseq)
+    r = time_stack(ctx, wl, cfg, args.steps, args.warmup)
+    prof, dom, ms = r["prof"], r["dom"], r["ms"]
+    n = wl.n_tokens
     per_step_ms = ms / args.steps
     blocks = cfg.n_blocks
     block_tokens = n * nseq * blocks * wl.steps * args.steps
@@ -385,7 +530,7 @@ def main():
             e["gbs"] = round(by / (kms * 1e-3) / 1e9, 1)
         kernels[k] = e
         log(f"  {k:14s} {e}")
-    dms, dcnt, dfl, _ = prof_timed[dom]  # live, over the timed steps
+    dms, dcnt, dfl, _ = r["timed"][dom]  # live, over the timed steps
     achieved = dfl / dcnt / (dms / dcnt * 1e-3) / 1e12
     tr = load_traffic(dom, wl.name, args.compute)
     # a contraction is priced at the peak of its own operand type
@@ -394,9 +539,18 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": dpeak,
                 "unit": "TFLOP/s", "frac": round(achieved / dpeak, 4),
                 "traffic": round(tr["bytes_per_launch"]) if tr else None,
-                "flops_per_launch": dfl / dcnt, "avg_launch_us": round(dms / dcnt * 1e3, 2)}
+                "flops_per_launch": dfl / dcnt, "avg_launch_us": round(dms / dcnt * 1e3, 2),
+                "avg_launch_source": "hipEvents around every launch of this kernel in the timed steps"}
     if tr:
         roofline["traffic_source"] = "profiles/" + traffic_name(dom, wl.name, args.compute)
+    trace = load_trace_avg(dom, wl.name, args.compute)
+    if trace and trace[0]:
+        t_us = trace[0]
+        roofline["trace_avg_launch_us"] = round(t_us, 2)
+        roofline["trace_frac"] = round(dfl / dcnt / (t_us * 1e-6) / 1e12 / dpeak, 4)
+        roofline["trace_source"] = os.path.relpath(trace[1], ROOT)
+    if mpeak and dom != "fp8_quant":
+        roofline["frac_of_measured_peak"] = round(achieved / mpeak, 4)
 
     result = {
         "metric": "DiT block tokens/sec and attention+GEMM TFLOP/s (% bf16 MFMA peak)",
@@ -409,17 +563,48 @@ def main():
         "config": {"workload": wl.name, "tokens": n * nseq, "sequences": nseq,
                    "guidance": wl.guidance, "n_txt": wl.n_txt, "n_img": wl.n_img,
                    "n_ref": wl.n_ref, "blocks": blocks, "euler_steps": wl.steps,
+                   "operands": {"f16": "fp16 activations, bf16 weights held exactly in fp16",
+                                "bf16": "bf16 activations and weights",
+                                "fp8": "E4M3 row-wise block projections, the rest fp16"}[args.compute],
                    "weights": "e4m3 row-wise (from bf16)" if args.compute == "fp8" else "bf16",
                    "accumulate": "f32", "parallelism": "none"},
         "tflops": round(tflops, 1),
         "pct_peak": round(100 * tflops / peak, 2),
+        "mfma_measured": mfma,
         "kernels": kernels,
         "roofline": roofline,
     }
+    if mpeak:
+        result["pct_measured_peak"] = round(100 * tflops / mpeak, 2)
+    extras = {}
+    if args.extras == "on" and args.workload == "flux2_stack_512txt_4096img_4step" and args.compute == "f16":
+        # 512x512 px on the same model (the context's workspace covers it)
+        c3 = S.WORKLOADS["flux2_stack_512txt_1024img_4step"]
+        r3 = time_stack(ctx, c3, cfg, max(3, args.steps // 2), 2, profile=False)
+        extras[c3.name] = stack_summary(c3, cfg, r3, mpeak)
+    ctx.close()
+    if args.extras == "on" and args.workload == "flux2_stack_512txt_4096img_4step" and args.compute == "f16":
+        # the same workload with bf16 MFMA operands
+        cb = replace(cfg, compute="bf16")
+        ctx = make_context(cb, wl.n_tokens)
+        rb = time_stack(ctx, wl, cb, max(3, args.steps // 2), 2, profile=False)
+        ctx.close()
+        extras[wl.name + "_bf16_operands"] = stack_summary(wl, cb, rb, mfma["bf16"]["tflops"])
+        # FLUX.3 with one 1024x1024 reference, one step
+        c5 = S.WORKLOADS["flux3_stack_512txt_4096img_4096ref_1step"]
+        ctx = make_context(c5.model, c5.n_tokens)
+        r5 = time_stack(ctx, c5, c5.model, max(3, args.steps // 2), 2, profile=False)
+        ctx.close()
+        extras[c5.name] = stack_summary(c5, c5.model, r5, mpeak)
+        for name in ("double_block_bf16_128txt_256img", "single_block_fp32_32txt_16img"):
+            extras[name] = time_block_workload(S.WORKLOADS[name])
+    if extras:
+        result["other_workloads"] = extras
+        for k, v in extras.items():
+            log(f"  {k}: {v}")
     if args.cpu_baseline == "on":
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(wl, cfg)
-    ctx.close()
     print(json.dumps(result), flush=True)
 
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 SOURCES = ["kernels_misc.hip", "gemm_mfma.hip", "gemm_fp8.hip", "attention_mfma.hip", "simple_f32.hip",
-           "runtime.hip"]
+           "peak_probe.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # no packed-fp32 instructions in device code

@@ -396,11 +396,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
       continue;
     }
 
-    // A piece: publish (O, max, sum); the last piece of the unit to finish merges them.  The
-    // partials are written and read with device-coherent (sc1) buffer accesses: the stores
-    // write through the XCD's L2 and have completed before the piece counter is raised, and
-    // the merging loads do not hit lines another XCD's L2 may hold, so no cache-wide
-    // writeback or invalidate is needed.
+    // A piece: publish (O, max, sum); the last piece of the unit to finish merges them.
+    // Ordering, in the HIP memory model at agent scope: every wave's partial stores have
+    // completed before the workgroup barrier, the counter increment is a release (it
+    // happens after them), and the piece that sees the last count performs an acquire fence
+    // before the barrier that lets its waves read the other pieces' partials.  The partials
+    // are also written and read with device-coherent (sc1) buffer accesses, so the stores
+    // leave no dirty lines for the release's writeback.
     const __amdgpu_buffer_rsrc_t rs_part = __builtin_amdgcn_make_buffer_rsrc(
         a.part, (short)0, (int)((size_t)2 * G * kPartFloats * 4), 0x00020000);
     const int o_off = (wave * 16 * 64 + lane) * 16, ml_off = kPartO * 4 + (wave * 64 + lane) * 16;
@@ -419,9 +421,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
     const int w0 = share_owner(p, u0, G), w1 = share_owner(p, u0 + nku - 1, G);
     __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
     __syncthreads();
-    if (tid == 0)
-      merge_flag = __hip_atomic_fetch_add(a.cnt + unit, 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
+    if (tid == 0) {
+      const bool last = __hip_atomic_fetch_add(a.cnt + unit, 1, __ATOMIC_RELEASE,
+                                               __HIP_MEMORY_SCOPE_AGENT) == w1 - w0;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      merge_flag = last;
+    }
     __syncthreads();
     if (merge_flag) {
       // two passes over the pieces (at most 8, checked by the launcher): the maxima, then the

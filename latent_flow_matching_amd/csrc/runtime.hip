@@ -1280,6 +1280,42 @@ extern "C" int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, 
   return 0;
 }
 
+extern "C" int dit_mfma_rate(int compute, int iters, double *tflops, double *ghz, void *stream_) {
+  g_err.clear();
+  if ((compute != DIT_F16 && compute != DIT_BF16) || iters < 1 || iters > (1 << 24) || !tflops || !ghz)
+    return fail(DIT_EINVAL, "dit_mfma_rate: compute must be DIT_F16 or DIT_BF16, 1 <= iters <= 2^24");
+  hipStream_t stream = (hipStream_t)stream_;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "dit_mfma_rate");
+  const int blocks = 2 * cus;  // two waves on every SIMD
+  float *sink = nullptr;
+  unsigned long long *clk = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipMalloc(&sink, (size_t)blocks * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&clk, sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  unsigned long long clocks = 0;
+  float ms = 0.f;
+  if (e == hipSuccess) e = mfma_rate(compute, blocks, 1000, sink, clk, stream);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, stream);
+  if (e == hipSuccess) e = mfma_rate(compute, blocks, iters, sink, clk, stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e == hipSuccess) e = hipMemcpy(&clocks, clk, sizeof clocks, hipMemcpyDeviceToHost);
+  (void)hipFree(sink);
+  (void)hipFree(clk);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_fail(e, "dit_mfma_rate");
+  *tflops = mfma_rate_flops(blocks, iters) / (ms * 1e-3) / 1e12;
+  *ghz = (double)clocks / (ms * 1e-3) / 1e9;
+  return 0;
+}
+
 extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dtype, int64_t *row_stride) {
   if (!ctx || !name) return nullptr;
   const int D = ctx->D(), F = ctx->F();
