@@ -303,6 +303,18 @@ int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx, uint8_t *
 int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
                  const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream);
 
+/* dit_gemm_fp8 for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): same arguments, checks, return codes
+ * and result up to fp32 summation order.  It allocates nothing; in exchange, launches whose
+ * 256 x 256 tiles fill under half of the compute units cut k into slices (as the library's
+ * block projections do) whose fp32 partial tiles live in a file-scope device array of the
+ * library, 32 MiB (128 partial tiles) per device, held until the process ends.  The slice
+ * count is capped to what the array holds, so no size is rejected for want of room.  Every
+ * call on one device shares that device's array: calls that overlap on one device (several
+ * streams, several threads) race and must be serialised by the caller. */
+int dit_gemm_fp8_static(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
+                        const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream);
+
 /* Workspace buffer of the last call, for inspection after the stream has finished:
  * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
  * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32

@@ -214,7 +214,8 @@ hipError_t launch8(const GemmArgs &a, hipStream_t s) {
   int splits = 1;
   if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * total <= a.split_grid) {
     splits = min(8, min(a.split_grid / total, (a.k / BK8) / 8));
-    if (splits < 2 || (long long)splits * total > a.part_tiles) splits = 1;
+    splits = min(splits, a.part_tiles / total);  // as many partial tiles as the workspace holds
+    if (splits < 2) splits = 1;
   }
   const int grid = (total * splits + 7) / 8 * 8;
   k_gemm8<EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);

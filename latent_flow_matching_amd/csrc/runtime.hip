@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -1256,25 +1257,92 @@ extern "C" int dit_quantize_rows_fp8(const float *x, int rows, int cols, int ldx
   return 0;
 }
 
-extern "C" int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
-                            const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream) {
-  g_err.clear();
+namespace {
+
+// Arguments of the E4M3 GEMM entry points: checks, then the launch description.
+int fp8_gemm_args(GemmArgs *a, const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
+                  const float *sw, int n, int ldw, int k, float *y, int ldy) {
   if (!qx || !sx || !qw || !sw || !y || m < 0) return fail(DIT_EINVAL, "bad arguments");
   if (n < 256 || n % 256 || k < 128 || k % 128)
     return fail(DIT_EUNSUPPORTED, "dit_gemm_fp8 needs n %% 256 == 0 and k %% 128 == 0 (n %d, k %d)", n, k);
   if (ldx < k || ldx % 16 || ldw < k || ldw % 16 || ldy < n || ldy % 4)
     return fail(DIT_EINVAL, "bad strides (ldx, ldw >= k, multiples of 16; ldy >= n, multiple of 4)");
+  *a = GemmArgs{};
+  a->g[0] = GemmGroup{qx, qw, m, 0, sw};
+  a->ng = 1;
+  a->n = n;
+  a->k = k;
+  a->ldx = ldx;
+  a->ldw = ldw;
+  a->out = y;
+  a->ldo = ldy;
+  a->xs = sx;
+  return 0;
+}
+
+// The allocation-free GEMM's k-slice partial tiles: a file-scope device array (each device
+// holds its own copy until the process ends), 128 tiles of 256 x 256 fp32 = 32 MiB.  Host
+// code never uses the array's name as an address: the device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch.
+constexpr int kStaticPartTiles = 128;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float scratch[(size_t)kStaticPartTiles * gemm_part_floats];
+
+struct ScratchOfDevice {
+  float *ptr;
+  int cus;
+};
+std::mutex g_scratch_mu;
+ScratchOfDevice g_scratch[kMaxDevices] = {};
+
+int scratch_of_current_device(ScratchOfDevice *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DIT_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchOfDevice &sd = g_scratch[dev];
+  if (!sd.ptr) {
+    float *p = nullptr;
+    e = hipGetSymbolAddress((void **)&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    sd.cus = cus / 8 * 8;
+    sd.ptr = p;
+  }
+  *out = sd;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" int dit_gemm_fp8(const uint8_t *qx, const float *sx, int m, int ldx, const uint8_t *qw,
+                            const float *sw, int n, int ldw, int k, float *y, int ldy, void *stream) {
+  g_err.clear();
+  GemmArgs a;
+  if (int rc = fp8_gemm_args(&a, qx, sx, m, ldx, qw, sw, n, ldw, k, y, ldy)) return rc;
   if (m == 0) return 0;
-  GemmArgs a = {};
-  a.g[0] = GemmGroup{qx, qw, m, 0, sw};
-  a.ng = 1;
-  a.n = n;
-  a.k = k;
-  a.ldx = ldx;
-  a.ldw = ldw;
-  a.out = y;
-  a.ldo = ldy;
-  a.xs = sx;
+  hipError_t e = gemm_fp8(a, EPI_STORE_F32, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 gemm");
+  return 0;
+}
+
+extern "C" int dit_gemm_fp8_static(const uint8_t *qx, const float *sx, int m, int ldx,
+                                   const uint8_t *qw, const float *sw, int n, int ldw, int k,
+                                   float *y, int ldy, void *stream) {
+  g_err.clear();
+  GemmArgs a;
+  if (int rc = fp8_gemm_args(&a, qx, sx, m, ldx, qw, sw, n, ldw, k, y, ldy)) return rc;
+  if (m == 0) return 0;
+  ScratchOfDevice sd;
+  if (int rc = scratch_of_current_device(&sd)) return rc;
+  // k-slices for launches whose tiles fill under half of the compute units, their partial
+  // tiles in the static array (the launcher caps the slice count to what it holds)
+  a.part = sd.ptr;
+  a.part_tiles = kStaticPartTiles;
+  a.split_grid = sd.cus;
   hipError_t e = gemm_fp8(a, EPI_STORE_F32, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp8 gemm");
   return 0;

@@ -92,6 +92,8 @@ def load_library(path: str = None):
     lib.dit_quantize_rows_fp8.argtypes = [P, I, I, I, P, I, P, P]
     lib.dit_gemm_fp8.restype = I
     lib.dit_gemm_fp8.argtypes = [P, P, I, I, P, P, I, I, I, P, I, P]
+    lib.dit_gemm_fp8_static.restype = I
+    lib.dit_gemm_fp8_static.argtypes = [P, P, I, I, P, P, I, I, I, P, I, P]
     lib.dit_mfma_rate.restype = I
     lib.dit_mfma_rate.argtypes = [I, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), P]
     lib.dit_debug_buffer.restype = P
@@ -341,16 +343,16 @@ def quantize_rows_fp8(x, stream=None):
     return q, sc
 
 
-def gemm_fp8(qx, sx, qw, sw, stream=None, y=None):
-    """y = sx[:, None] * sw[None, :] * (qx . qw^T) over E4M3 codes (dit_gemm_fp8); qx must
-    have rows readable up to its row count rounded up to 256 (pass a padded tensor's view).
-    y: an output to fill, else a new one."""
+def gemm_fp8(qx, sx, qw, sw, stream=None, y=None, static=False):
+    """y = sx[:, None] * sw[None, :] * (qx . qw^T) over E4M3 codes (dit_gemm_fp8, or
+    dit_gemm_fp8_static with static=True); qx must have rows readable up to its row count
+    rounded up to 256 (pass a padded tensor's view).  y: an output to fill, else a new one."""
     import torch
     m, k = qx.shape
     n = qw.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=qx.device)
-    fn = load_library().dit_gemm_fp8
+    fn = load_library().dit_gemm_fp8_static if static else load_library().dit_gemm_fp8
     _check(fn(_ptr(qx), _ptr(sx), m, qx.stride(0), _ptr(qw), _ptr(sw), n, qw.stride(0), k, _ptr(y),
               y.stride(0), _stream(stream)))
     return y
