@@ -347,11 +347,11 @@ int dit_profile_get(dit_ctx *ctx, const char *kernel, double *ms, int64_t *launc
 /* Sustained matrix-core rate of the current device, the measured denominator beside the
  * published peak: two waves on every SIMD of every compute unit run iters x 8 independent
  * v_mfma_f32_16x16x32 of the compute type (DIT_F16 or DIT_BF16, the form the block kernels
- * use) on register operands.  *tflops = executed flops / event-timed duration; *ghz = shader
- * clocks one wave counted (s_memtime) / the same duration, the clock the chip held under that
- * load.  Allocates and frees a few bytes of device memory and synchronises the stream: a
+ * use) on register operands.  *tflops = executed flops / event-timed duration; *ghz = the
+ * clock that rate implies at one such MFMA per 16 cycles per SIMD (derived, not a counter
+ * reading).  Allocates and frees a few bytes of device memory and synchronises the stream: a
  * benchmark tool, not for use inside a timed region.  1 <= iters <= 2^24 (10^5 takes about
- * 10 ms).  DIT_EINVAL for other arguments, DIT_EHIP on a HIP failure. */
+ * 14 ms).  DIT_EINVAL for other arguments, DIT_EHIP on a HIP failure. */
 int dit_mfma_rate(int compute, int iters, double *tflops, double *ghz, void *stream);
 
 /* Thread-local description of the last failure on this thread ("" if none). */

@@ -133,10 +133,9 @@ hipError_t noise_mix(float *x, const float *noise, int64_t n, float t, hipStream
 // y[r][:] += v for rows r < nrows of d floats
 hipError_t add_row(float *y, int nrows, int d, const float *v, hipStream_t s);
 // Sustained MFMA rate probe: blocks workgroups of 4 waves each run iters x 8 independent
-// 16x16x32 MFMAs of type op (OP_F16 / OP_BF16); *clocks receives the shader clocks one wave
-// counted around its loop (sink is written only in a case that never occurs: [blocks]).
-hipError_t mfma_rate(int op, int blocks, int iters, float *sink, unsigned long long *clocks,
-                     hipStream_t s);
+// 16x16x32 MFMAs of type op (OP_F16 / OP_BF16) (sink [blocks] is written only in a case that
+// never occurs).
+hipError_t mfma_rate(int op, int blocks, int iters, float *sink, hipStream_t s);
 double mfma_rate_flops(int blocks, int iters);
 // Debug guard: cnt[0] += values of the rows x cols buffer p (row stride ld, element type
 // OP_F32 / OP_BF16 / OP_F16) at the fp16 limit +-65504 (fp16 only), cnt[1] += NaN / Inf values.

@@ -1,10 +1,8 @@
 // Sustained matrix-core rate of this device, for the benchmark's roofline denominators.
 //
 // Every wave runs chains of independent v_mfma_f32_16x16x32_{f16,bf16} (the form the GEMMs and
-// the attention use) on register operands, two waves per SIMD on every compute unit, and
-// reads the shader clock counter (s_memtime) around its loop.  The host divides the executed
-// flops by the event-timed duration (sustained TFLOP/s) and the counted clocks by the same
-// duration (the clock the chip held meanwhile).
+// the attention use) on register operands, two waves per SIMD on every compute unit.  The host
+// divides the executed flops by the event-timed duration (sustained TFLOP/s).
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +27,7 @@ template <> struct MfmaInPlace<bf16> {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_mfma_rate(float *sink, unsigned long long *clocks, int iters) {
+__global__ __launch_bounds__(256) void k_mfma_rate(float *sink, int iters) {
   typedef typename Mfma<T>::v8 V8;
   V8 a, b;
 #pragma unroll
@@ -40,31 +38,27 @@ __global__ __launch_bounds__(256) void k_mfma_rate(float *sink, unsigned long lo
   f32x4 c[kChains];
 #pragma unroll
   for (int j = 0; j < kChains; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
     for (int j = 0; j < kChains; ++j) MfmaInPlace<T>::run(c[j], a, b);
   }
   // the last MFMAs complete before their results are read (16 passes of wait)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kChains; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
   // the result is kept only so that the chains are not removed; it is never a real value
   if (s == 123456.f) sink[blockIdx.x] = s;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *clocks = t1 - t0;
 }
 
 }  // namespace
 
-hipError_t mfma_rate(int op, int blocks, int iters, float *sink, unsigned long long *clocks,
-                     hipStream_t s) {
+hipError_t mfma_rate(int op, int blocks, int iters, float *sink, hipStream_t s) {
   if (blocks < 1 || iters < 1) return hipErrorInvalidValue;
   if (op == OP_F16)
-    k_mfma_rate<f16><<<blocks, 256, 0, s>>>(sink, clocks, iters);
+    k_mfma_rate<f16><<<blocks, 256, 0, s>>>(sink, iters);
   else if (op == OP_BF16)
-    k_mfma_rate<bf16><<<blocks, 256, 0, s>>>(sink, clocks, iters);
+    k_mfma_rate<bf16><<<blocks, 256, 0, s>>>(sink, iters);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -101,7 +101,7 @@ struct dit_ctx {
   int lean_grid = 0;         // attention: one workgroup per compute unit (multiple of 8)
   float *attn_part = nullptr;  // [2 * lean_grid][attn_part_floats] partial pieces
   int *attn_cnt = nullptr;     // [heads * (max_tokens / 256 + 6)] per-unit piece counters
-  float *gemm_part = nullptr;  // [lean_grid][gemm_part_floats] split-K partial tiles
+  float *gemm_part = nullptr;  // [cus][gemm_part_floats] split-K partial tiles
   unsigned *guard_cnt = nullptr;  // DIT_DEBUG_SYNC guard: (values at the fp16 limit, NaN/Inf)
   // DIT_FP8 workspace: E4M3 copy of cat, row scales of xm (codes in xm) and of cat's halves
   uint8_t *cat8 = nullptr;     // [rows_alloc][D+F]
@@ -1359,28 +1359,24 @@ extern "C" int dit_mfma_rate(int compute, int iters, double *tflops, double *ghz
   if (e != hipSuccess) return hip_fail(e, "dit_mfma_rate");
   const int blocks = 2 * cus;  // two waves on every SIMD
   float *sink = nullptr;
-  unsigned long long *clk = nullptr;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   e = hipMalloc(&sink, (size_t)blocks * sizeof(float));
-  if (e == hipSuccess) e = hipMalloc(&clk, sizeof(unsigned long long));
   if (e == hipSuccess) e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
-  unsigned long long clocks = 0;
   float ms = 0.f;
-  if (e == hipSuccess) e = mfma_rate(compute, blocks, 1000, sink, clk, stream);  // warm-up
+  if (e == hipSuccess) e = mfma_rate(compute, blocks, 1000, sink, stream);  // warm-up
   if (e == hipSuccess) e = hipEventRecord(e0, stream);
-  if (e == hipSuccess) e = mfma_rate(compute, blocks, iters, sink, clk, stream);
+  if (e == hipSuccess) e = mfma_rate(compute, blocks, iters, sink, stream);
   if (e == hipSuccess) e = hipEventRecord(e1, stream);
   if (e == hipSuccess) e = hipEventSynchronize(e1);
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-  if (e == hipSuccess) e = hipMemcpy(&clocks, clk, sizeof clocks, hipMemcpyDeviceToHost);
   (void)hipFree(sink);
-  (void)hipFree(clk);
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   if (e != hipSuccess) return hip_fail(e, "dit_mfma_rate");
   *tflops = mfma_rate_flops(blocks, iters) / (ms * 1e-3) / 1e12;
-  *ghz = (double)clocks / (ms * 1e-3) / 1e9;
+  // one 16x16x32 MFMA (16384 flops) every 16 cycles on each of the 4 SIMDs of every CU
+  *ghz = *tflops * 1e12 / (1024.0 * 4 * cus) / 1e9;
   return 0;
 }
 

@@ -777,6 +777,30 @@ def _rows(n, k=24, seed=0):
     return np.unique(np.concatenate([[0, n - 1], r.choice(n, k, replace=False)]))
 
 
+# ----------------------------------------------------------------- determinism at full size
+
+@pytest.mark.timeout(300)
+def test_full_size_blocks_are_deterministic():
+    """At 512+4096 tokens the attention cuts units into pieces over equal shares of all compute
+    units, and which piece of a unit finishes last and merges varies from run to run; the
+    result must not: two runs of a double and a single block are bitwise equal."""
+    from latent_flow_matching_amd import dit
+    cfg = replace(S.FLUX2_KLEIN, n_stream_blocks=1, n_shared_blocks=1)
+    n = 512 + 4096
+    ctx, _ = context(cfg, n)
+    x = S.gen_tokens(n, cfg.hidden, key=(9,))
+    cond = S.gen_cond(2, cfg.hidden)
+    pos = O.positions(512, (64, 64))
+    outs = []
+    for _ in range(2):
+        xt = dev(x)
+        for b in (0, 1):
+            ctx.block_forward(b, xt, 512, 4096, 0, dev(pos), dev(cond))
+        torch.cuda.synchronize()
+        outs.append(xt.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
 # ----------------------------------------------------------------- full benchmark shapes, every element
 
 @pytest.mark.timeout(600)
