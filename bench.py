@@ -499,8 +499,9 @@ def main():
     mfma = {}
     for c in ("f16", "bf16"):
         tf, ghz = dit.mfma_rate(c)
-        mfma[c] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3)}
-        log(f"sustained 16x16x32 MFMA rate, {c}: {tf:.1f} TFLOP/s at {ghz:.2f} GHz")
+        mfma[c] = {"tflops": round(tf, 1), "implied_clock_ghz": round(ghz, 3)}
+        log(f"sustained 16x16x32 MFMA rate, {c}: {tf:.1f} TFLOP/s (implies {ghz:.2f} GHz at one "
+            f"MFMA per 16 cycles per SIMD)")
     mpeak = mfma["bf16" if args.compute == "bf16" else "f16"]["tflops"] if args.compute != "fp8" else None
 
     nseq = 1 if wl.guidance is None else 2
