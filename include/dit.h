@@ -317,7 +317,10 @@ int dit_gemm_fp8_static(const uint8_t *qx, const float *sx, int m, int ldx, cons
 
 /* Workspace buffer of the last call, for inspection after the stream has finished:
  * "xm" (LayerNorm+modulation output, [N, D]), "qkv" ([N, 3D], q and k after RMSNorm and
- * RoPE), "cat" ([N, D+F], attention output || SwiGLU output), "mod" (fp32
+ * RoPE; v only on the fp32 path), "vt" (16-bit and FP8 paths: V transposed, [H * 128 rows of
+ * one head's dim][token'], where every 32 tokens are stored in the order 0-3, 16-19, 4-7,
+ * 20-23, 8-11, 24-27, 12-15, 28-31, then zeros; NULL on the fp32 path), "cat" ([N, D+F],
+ * attention output || SwiGLU output), "mod" (fp32
  * [M][3][R]: distinct modulation projection in order of first use (blocks in order, sets in
  * order), conditioning row, shift || scale || gate; R = 3D, or 6D with double_wiring = 1,
  * whose stream-block rows hold both halves), "x" (fp32 [N, D], the

@@ -18,7 +18,7 @@
 //                 the B operand's k positions 8q..8q+7 in that order).
 // The running max is raised lazily: P is formed against the stored max unless some row's
 // max grew by more than 2^8, so O is rescaled only when that happens (P <= 256 fits fp16).
-// V is read in the transposed layout written by the QK-norm kernel, vt[h][d][token'] with the
+// V is read in the transposed layout written by linear1's epilogue, vt[h][d][token'] with the
 // tokens of every 32 reordered so that 16-byte chunk q holds tokens 4q..4q+3, 16+4q..16+4q+3:
 // the eight keys a lane multiplies in one P.V MFMA form a single chunk.  Scores are kept in the log2 domain
 // (scale * log2(e) folded into one FMA before exp2).

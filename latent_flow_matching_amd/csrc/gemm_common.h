@@ -34,16 +34,271 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // byte offset inside 
 
 constexpr int kGroupN = 4;  // feature tiles per ordering group (4 x 8 tiles per XCD round)
 
+// linear1's feature tiles in an interleaved order: head tile b's Q, K and V tiles, then its
+// share of the SwiGLU tiles, for b = 0, 1, ...  Workgroups reach the XCDs in contiguous ranges
+// of tile ids, so in plain order the Q and K tiles (whose fused epilogue costs the most) would
+// all land on the first XCDs; interleaved, every XCD gets the same mix.  Identity when there
+// are no Q / K / V columns (split == 0).
+__device__ __forceinline__ int qkv_feature_tile(int l, int n_tiles, int split) {
+  const int tq = split / (3 * BN);  // tiles of each of Q, K and V
+  if (tq == 0) return l;
+  const int tm = n_tiles - 3 * tq;  // SwiGLU tiles
+  int b = 0;
+  while (b + 1 < tq && 3 * (b + 1) + (b + 1) * tm / tq <= l) ++b;
+  const int o = l - (3 * b + b * tm / tq);
+  return o < 3 ? o * tq + b : 3 * tq + b * tm / tq + (o - 3);
+}
+
+// Bytes per row of a wave's V-transpose tile in LDS: 96 columns (three 32-token groups) of
+// 16-bit values plus 16 B, so that the four dim rows one ds_write_b16 touches (dims 4 apart)
+// start 16 banks apart.
+constexpr int kVtPitch = 208;
+constexpr int kVtLds = 128 * kVtPitch;  // per wave
+
+// Column of token t inside its aligned 32-token group of vt: 16-byte chunk q holds tokens
+// 4q..4q+3 then 16+4q..16+4q+3.
+__device__ __forceinline__ int vt_col(int u) {
+  return ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
+}
+
+// Fused part of linear1's epilogue for a wave whose 128 features are one Q, K or V head
+// (a.vt != nullptr).  Lane (r16, q4) holds dims 16 i + 4 q4 + {0..3} of token 16 j + r16.
+//   Q, K: RMSNorm over the head's 128 dims ("FLUX.3 Image Klein in Diffusers", "Entkoppelte
+//   Vorverarbeitung ...": queries and keys are RMS-normalised) -- the lane's 32 squares plus
+//   those of lanes r16 + 16, + 32, + 48 -- times the segment's weight, then the rotary
+//   embedding of adjacent pairs (2p, 2p + 1) with the token's (cos, sin) of pair p (the
+//   lane's four dims are two whole pairs), stored to qkv.
+//   V: written transposed to vt.  The wave's tokens go in halves of 64 through its own LDS
+//   tile [128 dims][96 columns] (a half touches at most three aligned 32-token groups),
+//   then out as 16-byte chunks; chunks that hold tokens outside the half or the group are
+//   written element by element, so tiles that share a chunk write disjoint bytes.  The
+//   caller has passed a workgroup barrier after the main loop's last LDS reads.
+template <typename T, int BM, int WN, int WM>
+__device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const GemmGroup &grp,
+                                                   int n0, int m0, int wn, int wm, int lane,
+                                                   f32x4 (&acc)[BN / WN / 16][BM / WM / 16],
+                                                   char *smem) {
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int FS = WTN / 16, TS = WTM / 16;
+  static_assert(WTN == 128 && WTM % 64 == 0, "one head per wave, token halves of 64");
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int dm = a.split / 3;
+  const int fw = n0 + wn * WTN;  // the wave's first feature
+  const int part = fw / dm;      // 0 Q, 1 K, 2 V
+  const int h = (fw - part * dm) >> 7;
+  const int mw = m0 + wm * WTM;  // the wave's first row in the group
+  if (mw >= grp.rows) return;
+  const int wave = wm * WN + wn;
+  if (part < 2) {
+    // Pass 1, registers only: each token's 1 / RMS from the fp32 accumulators (its 128 dims
+    // are this lane's 32 and those of lanes +16, +32, +48), and the scaled values as fp16
+    // into the wave's LDS tile [128 tokens][128 dims], 16-byte chunk c of token t at slot
+    // c ^ (t & 15) so that the 16 tokens of one write land on distinct banks.
+    char *tq = smem + wave * (128 * 256);
+#pragma unroll
+    for (int j = 0; j < TS; ++j) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ss += acc[i][j][r] * acc[i][j][r];
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      const float rs = 1.0f / sqrtf(ss * (1.0f / 128.f) + a.rms_eps);
+      const int t = j * 16 + r16;
+#pragma unroll
+      for (int i = 0; i < FS; ++i) {
+        const int c = 2 * i + (q4 >> 1);  // 16-byte chunk of dims 16 i + 4 q4 ..
+        f16x4 v = {(f16)(acc[i][j][0] * rs), (f16)(acc[i][j][1] * rs), (f16)(acc[i][j][2] * rs),
+                   (f16)(acc[i][j][3] * rs)};
+        *reinterpret_cast<f16x4 *>(tq + t * 256 + ((c ^ (t & 15)) << 4) + (q4 & 1) * 8) = v;
+      }
+    }
+    // Pass 2, after the accumulators' last use: lane (c = lane % 16) takes dims 8c .. 8c + 7
+    // (pairs 4c .. 4c + 3: axis c / 4, frequencies j0 = 4 (c % 4) .. j0 + 3) of tokens
+    // lane / 16 + 4k.  It multiplies by the segment's weights and rotates each pair by
+    // angle = pos * freq_j, taken in revolutions: x = pos * hi_j is exact for integer positions,
+    // so r = (x - rint(x)) + pos * lo_j keeps the angle's precision within half a turn, where
+    // the hardware sine and cosine are accurate.  The positions of all 32 tokens are loaded
+    // at once; 16 lanes store one token's 256-byte head row.
+    const int c = lane & 15, tl = lane >> 4;
+    const int mlast = min(mw + WTM, grp.rows) - 1;
+    const int seg0 = segment_of(grp.out_row0 + mw, a.b1, a.b2, a.per);
+    const bool one_seg = seg0 == segment_of(grp.out_row0 + mlast, a.b1, a.b2, a.per);
+    const float *const *wsel = part == 0 ? a.qn : a.kn;
+    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(wsel[seg0] + 8 * c);
+    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(wsel[seg0] + 8 * c + 4);
+    const f32x4 fh = *reinterpret_cast<const f32x4 *>(a.rope_fr + 4 * (c & 3));
+    const f32x4 fl = *reinterpret_cast<const f32x4 *>(a.rope_fr + 16 + 4 * (c & 3));
+    constexpr int NT4 = WTM / 4;  // tokens per lane
+    float pv[NT4];
+#pragma unroll
+    for (int k = 0; k < NT4; ++k) {
+      const int tok = grp.out_row0 + min(mw + tl + 4 * k, grp.rows - 1);
+      pv[k] = a.rope_pos[(size_t)tok * 4 + (c >> 2)];
+    }
+    constexpr int KB = 8;
+#pragma unroll
+    for (int k0 = 0; k0 < NT4; k0 += KB) {
+      f16x8 hv[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int t = tl + 4 * (k0 + k);
+        hv[k] = *reinterpret_cast<const f16x8 *>(tq + t * 256 + ((c ^ (t & 15)) << 4));
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int t = tl + 4 * (k0 + k), m = mw + t;
+        if (m >= grp.rows) continue;
+        const int tok = grp.out_row0 + m;
+        f32x4 wa = w0, wb = w1;
+        if (!one_seg) {
+          const float *wr = wsel[segment_of(tok, a.b1, a.b2, a.per)] + 8 * c;
+          wa = *reinterpret_cast<const f32x4 *>(wr);
+          wb = *reinterpret_cast<const f32x4 *>(wr + 4);
+        }
+        const float y[8] = {(float)hv[k][0] * wa.x, (float)hv[k][1] * wa.y, (float)hv[k][2] * wa.z,
+                            (float)hv[k][3] * wa.w, (float)hv[k][4] * wb.x, (float)hv[k][5] * wb.y,
+                            (float)hv[k][6] * wb.z, (float)hv[k][7] * wb.w};
+        const float p = pv[k0 + k];
+        typename Mfma<T>::v8 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = p * fh[q];
+          const float r = (x - __builtin_rintf(x)) + p * fl[q];
+          const float co = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
+          o[2 * q] = from_f32<T>(y[2 * q] * co - y[2 * q + 1] * sn);
+          o[2 * q + 1] = from_f32<T>(y[2 * q] * sn + y[2 * q + 1] * co);
+        }
+        *reinterpret_cast<typename Mfma<T>::v8 *>(reinterpret_cast<T *>(a.qkv) +
+                                                  (size_t)tok * a.ldq + fw + 8 * c) = o;
+      }
+    }
+    return;
+  }
+  char *tile = smem + wave * kVtLds;
+  T *vb = reinterpret_cast<T *>(a.vt) + (size_t)h * 128 * a.ldv;
+  const int tw0 = grp.out_row0 + mw;        // the wave's first token
+  const int gend = grp.out_row0 + grp.rows;  // the group's end
+#pragma unroll
+  for (int hf = 0; hf < WTM / 64; ++hf) {
+    const int t0 = tw0 + 64 * hf, g0 = t0 & ~31;
+    if (t0 >= gend) break;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = t0 + 16 * jj + r16 - g0;
+      const int col = (c & ~31) + vt_col(c & 31);
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<T *>(tile + (16 * i + 4 * q4 + r) * kVtPitch + col * 2) =
+              from_f32<T>(acc[i][4 * hf + jj][r]);
+    }
+    // (a wave's LDS operations complete in order: its reads below see its writes above)
+    // Lane (ch = lane % 16, of which 12 are used) copies chunk ch of dim rows lane / 16 + 4k:
+    // whether that chunk lies wholly in this half is the same for every row.
+    const int t1 = min(t0 + 64, gend);
+    const int ch = lane & 15, dl = lane >> 4;
+    const int ta = g0 + (ch >> 2) * 32 + (ch & 3) * 4;  // tokens ta.., ta + 16.. of the chunk
+    const bool any = ch < 12 && ta + 19 >= t0 && ta < t1;
+    const bool whole = any && ta >= t0 && ta + 19 < t1;
+    const char *src = tile + dl * kVtPitch + ch * 16;
+    T *dst = vb + (size_t)dl * a.ldv + g0 + ch * 8;
+    if (whole) {
+#pragma unroll
+      for (int k0 = 0; k0 < 32; k0 += 8) {
+        u32x4 cv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          cv[k] = *reinterpret_cast<const u32x4 *>(src + (k0 + k) * 4 * kVtPitch);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          *reinterpret_cast<u32x4 *>(dst + (size_t)(k0 + k) * 4 * a.ldv) = cv[k];
+      }
+    } else if (any) {  // shared with the neighbouring half, wave or group: element by element
+#pragma unroll 1
+      for (int k = 0; k < 32; ++k) {
+        const uint16_t *sv = reinterpret_cast<const uint16_t *>(src + k * 4 * kVtPitch);
+        uint16_t *dv = reinterpret_cast<uint16_t *>(dst + (size_t)k * 4 * a.ldv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = ta + (e < 4 ? e : e + 12);
+          if (t >= t0 && t < t1) dv[e] = sv[e];
+        }
+      }
+    }
+  }
+  // the tile holding the last token also writes the zeros past it (this head, wm == 0 wave)
+  if (wm == 0 && gend == a.n_tok && m0 + BM >= grp.rows) {
+    const int z0 = a.n_tok & ~31, z1 = (a.n_tok / 64 + 2) * 64;
+    const int nch = (z1 - z0) / 8;
+    for (int k = lane; k < 128 * nch; k += 64) {
+      const int d = k / nch, ch = k - d * nch;
+      const int ta = z0 + (ch >> 2) * 32 + (ch & 3) * 4;
+      T *dst = vb + (size_t)d * a.ldv + z0 + ch * 8;
+      if (ta >= a.n_tok) {
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (ta + (e < 4 ? e : e + 12) >= a.n_tok) reinterpret_cast<uint16_t *>(dst)[e] = 0;
+      }
+    }
+  }
+}
+
 // Epilogue: lane owns token (lane & 15) and features 4 (lane >> 4) + {0..3} of every 16x16
-// sub-tile.
+// sub-tile.  smem: the workgroup's LDS (at least 4 x kVtLds bytes), used by the fused
+// Q / K / V epilogue, which every wave of a workgroup takes or none does.
 template <typename T, int BM, int WN, int WM, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp, int n0, int m0,
                                          int wn, int wm, int lane,
-                                         f32x4 (&acc)[BN / WN / 16][BM / WM / 16]) {
+                                         f32x4 (&acc)[BN / WN / 16][BM / WM / 16], char *smem) {
   constexpr int WTN = BN / WN, WTM = BM / WM;
   constexpr int FS = WTN / 16, TS = WTM / 16;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int fbase = n0 + wn * WTN + 4 * q4;
+  if constexpr (EPI == EPI_QKV_SWIGLU) {
+    if (a.vt != nullptr && n0 < a.split) {
+      __syncthreads();  // every wave's last fragment reads are done before LDS is reused
+      epilogue_qkv_heads<T, BM, WN, WM>(a, grp, n0, m0, wn, wm, lane, acc, smem);
+      return;
+    }
+  }
+  if constexpr (EPI == EPI_RESID) {
+    // Gated residual.  One wave per SIMD leaves load latency exposed: the gate is loaded once
+    // when the wave's rows share a segment, so each token sub-tile's eight x loads go out
+    // together and cost one round trip.
+    const int mw = m0 + wm * WTM;  // the wave's first row in the group
+    if (mw >= grp.rows) return;
+    const int mlast = min(mw + WTM, grp.rows) - 1;
+    const int seg0 = segment_of(grp.out_row0 + mw, a.b1, a.b2, a.per);
+    if (seg0 == segment_of(grp.out_row0 + mlast, a.b1, a.b2, a.per)) {
+      f32x4 g[FS];
+#pragma unroll
+      for (int i = 0; i < FS; ++i)
+        g[i] = *reinterpret_cast<const f32x4 *>(a.gate[seg0] + fbase + i * 16);
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const int m = mw + j * 16 + r16;
+        if (m >= grp.rows) continue;
+        float *xr = a.x + (size_t)(grp.out_row0 + m) * a.ldres + fbase;
+        f32x4 xv[FS];
+#pragma unroll
+        for (int i = 0; i < FS; ++i) xv[i] = *reinterpret_cast<const f32x4 *>(xr + i * 16);
+#pragma unroll
+        for (int i = 0; i < FS; ++i) {
+          xv[i].x += g[i].x * acc[i][j][0];
+          xv[i].y += g[i].y * acc[i][j][1];
+          xv[i].z += g[i].z * acc[i][j][2];
+          xv[i].w += g[i].w * acc[i][j][3];
+          *reinterpret_cast<f32x4 *>(xr + i * 16) = xv[i];
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < TS; ++j) {
     const int m = m0 + wm * WTM + j * 16 + r16;  // row inside the group
@@ -103,6 +358,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
         }
     }
   }
+}
+
+// Host check of the fused Q / K / V epilogue's shape: whole 256-feature tiles per Q, K and V
+// region, and the table, weights and output it reads and writes.
+inline bool fused_heads_ok(const GemmArgs &a, int epi) {
+  if (epi != EPI_QKV_SWIGLU || a.vt == nullptr) return true;
+  if (a.split % 3 || (a.split / 3) % BN || a.split > a.n || !a.qkv) return false;
+  if (!a.rope_pos || !a.rope_fr) return false;
+  if (a.n_tok < 0 || a.ldv < (a.n_tok / 64 + 2) * 64) return false;
+  for (int s = 0; s < 3; ++s)
+    if (!a.qn[s] || !a.kn[s]) return false;
+  return true;
 }
 
 // Barrier for LDS hand-over only: global loads stay in flight across it (a workgroup fence

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
   const int first_n = group * kGroupN;
   const int gsize = min(n_tiles - first_n, kGroupN);
   const int rem = lid - group * in_group;
-  const int tile_n = first_n + rem % gsize;
+  const int tile_n = EPI == EPI_QKV_SWIGLU ? qkv_feature_tile(first_n + rem % gsize, n_tiles, a.split)
+                                          : first_n + rem % gsize;
   const int mt = rem / gsize;
   int gi = 0;
 #pragma unroll
@@ -197,7 +198,8 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
       for (int j = 0; j < TS; ++j) pp[(i * TS + j) * 64] = acc[i][j];
     return;
   }
-  epilogue<f16, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
+  static_assert(2 * STAGE >= 4 * kVtLds, "LDS for the fused V transpose");
+  epilogue<f16, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
 template <int EPI>
@@ -230,6 +232,7 @@ hipError_t launch8(const GemmArgs &a, hipStream_t s) {
 
 hipError_t gemm_fp8(const GemmArgs &a, int epi, hipStream_t s) {
   if (a.n % BN || a.k % BK8 || a.ng < 1 || a.ng > kMaxGroups || !a.xs) return hipErrorInvalidValue;
+  if (!fused_heads_ok(a, epi)) return hipErrorInvalidValue;
   if (a.ldx % 16 || (a.ldw > 0 ? a.ldw : a.k) % 16) return hipErrorInvalidValue;
   for (int i = 0; i < a.ng; ++i)
     if (!a.g[i].ws) return hipErrorInvalidValue;

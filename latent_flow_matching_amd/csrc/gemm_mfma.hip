@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   const int first_n = group * kGroupN;
   const int gsize = min(n_tiles - first_n, kGroupN);
   const int rem = lid - group * in_group;
-  const int tile_n = first_n + rem % gsize;
+  const int tile_n = EPI == EPI_QKV_SWIGLU ? qkv_feature_tile(first_n + rem % gsize, n_tiles, a.split)
+                                          : first_n + rem % gsize;
   const int mt = rem / gsize;
   int gi = 0;
 #pragma unroll
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
       for (int j = 0; j < TS; ++j) pp[(i * TS + j) * 64] = acc[i][j];
     return;
   }
-  epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc);
+  static_assert(2 * STAGE >= 4 * kVtLds, "LDS for the fused V transpose");
+  epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
 template <typename T, int EPI>
@@ -270,6 +272,7 @@ hipError_t dispatch(const GemmArgs &a, int epi, hipStream_t s) {
 
 hipError_t gemm_mfma(const GemmArgs &a, int epi, int op, hipStream_t s) {
   if (a.n % BN || a.k % BK || a.ng < 1 || a.ng > kMaxGroups) return hipErrorInvalidValue;
+  if (!fused_heads_ok(a, epi)) return hipErrorInvalidValue;
   if (op == OP_BF16) return dispatch<bf16>(a, epi, s);
   if (op == OP_F16) return dispatch<f16>(a, epi, s);
   return hipErrorInvalidValue;

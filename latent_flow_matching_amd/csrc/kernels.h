@@ -46,7 +46,18 @@ struct GemmArgs {
   float *out; int ldo; int accumulate; float alpha; int n_store;
   // EPI_QKV_SWIGLU
   void *qkv; int ldq; int split; void *cat; int ldc; int cat_off;
-  // EPI_RESID
+  // EPI_QKV_SWIGLU, 16-bit and FP8 GEMMs, when vt != nullptr (split = 3 x 128-dim heads of
+  // d_model = split / 3 each, and split % 256 == 0): each Q and K head is RMS-normalised with
+  // the weights qn / kn of its token's segment (segments by b1, b2, per below) and rotated by
+  // the 4D RoPE angles pos[token][axis] * freq_j, axis = pair / 16, j = pair % 16, then stored
+  // to qkv; rope_fr holds freq_j / (2 pi) split as hi[16] (12 significant bits, so that an
+  // integer position up to 4096 times hi is exact in fp32) then lo[16] = the remainder.
+  // V is not stored to qkv but written transposed to vt [head][128][ldv] (the attention's
+  // layout: in every 32 tokens, 16-byte chunk q holds tokens 4q..4q+3 and 16+4q..16+4q+3),
+  // with zeros for the tokens in [n_tok, (n_tok / 64 + 2) * 64).
+  void *vt; int ldv; int n_tok; const float *rope_pos; const float *rope_fr;
+  const float *qn[3]; const float *kn[3]; float rms_eps;
+  // EPI_RESID (b1, b2, per also give the segments of the fused Q / K norm)
   float *x; int ldres; const float *gate[3]; int b1, b2, per;
   // Split K (EPI_RESID and EPI_STORE_F32): when the tiles fill under half of split_grid
   // compute units and k is long, each tile's k-tiles are cut into S slices; every slice stores
@@ -112,9 +123,9 @@ hipError_t rope_table(float *cs, const float *pos, int n, float theta, hipStream
 hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx, int rows,
                        int row0, int d, float eps, const float *const mod_seg[3], Segs segs,
                        hipStream_t s, float *out_scale = nullptr);
-// q, k of every (token, head): RMSNorm with the segment's scale, then RoPE, in place;
-// 16-bit paths also write V transposed into vt (and zeros for columns [n, n+64)).
-hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, void *vt, int ldv,
+// q, k of every (token, head): RMSNorm with the segment's scale, then RoPE, in place (fp32
+// path; the 16-bit and FP8 paths fuse this into linear1's epilogue).
+hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads,
                         const float *cs, int n, const float *const qn[3],
                         const float *const kn[3], Segs segs, float eps, hipStream_t s);
 // dst[i] = src[i] rounded to the 16-bit type (OP_BF16 / OP_F16), i < n

@@ -206,10 +206,9 @@ hipError_t ln_modulate(void *out, int out_type, int ldo, const float *x, int ldx
 // scale ("FLUX.3 Image Klein in Diffusers", "Entkoppelte Vorverarbeitung ...": queries and
 // keys are RMS-normalised before attention), then the 4D rotary embedding: lane p rotates
 // the adjacent pair (2p, 2p+1) by the angle of axis p/16, frequency index p%16.
-// The 16-bit paths also write V transposed, vt[h][d][token'], the layout the attention
-// kernel's P.V product reads (keys contiguous; token' reorders every 32 tokens so that
-// 16-byte chunk q holds tokens 4q..4q+3, 16+4q..16+4q+3), with zeros for the 64 columns past n.
-// Grid: (ceil(n/64) + 1 token tiles, heads); 4 waves, each 16 tokens of the tile.
+// The fp32 path runs this kernel; the 16-bit and FP8 paths do the same work in linear1's
+// epilogue (gemm_common.h), which also writes V transposed for the attention kernel.
+// Grid: (ceil(n/64) token tiles, heads); 4 waves, each 16 tokens of the tile.
 // ------------------------------------------------------------------------------------------
 template <typename T> struct Pair;
 template <> struct Pair<float> {
@@ -219,8 +218,8 @@ template <> struct Pair<float> {
   static __device__ float2 make(float a, float b) { return make_float2(a, b); }
 };
 template <typename T>
-__global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_model, T *vt,
-                                                       int ldv, const float *cs, int n,
+__global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_model,
+                                                       const float *cs, int n,
                                                        const float *qn0, const float *qn1,
                                                        const float *qn2, const float *kn0,
                                                        const float *kn1, const float *kn2,
@@ -257,142 +256,14 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(T *qkv, int ldq, int d_mod
   }
 }
 
-// 16-bit path: each lane owns 8 consecutive dims of one (token, head) row (16-byte loads and
-// stores; its four RoPE pairs stay in the lane), 16 lanes per row, so a wave handles 4 tokens
-// at once and reduces the sum of squares with 4 xor-shuffles inside its 16-lane group.  All
-// loads (V of the workgroup's 64 tokens, then q, k and the RoPE table of the wave's 16 tokens)
-// are issued before any arithmetic.  The workgroup then writes V transposed into vt (zeros
-// past n): the P.V operand layout of the attention kernel.
-template <typename T>
-__global__ __launch_bounds__(256) void k_qk_norm_rope16(T *qkv, int ldq, int d_model, T *vt,
-                                                         int ldv, const float *cs, int n,
-                                                         const float *qn0, const float *qn1,
-                                                         const float *qn2, const float *kn0,
-                                                         const float *kn1, const float *kn2,
-                                                         int b1, int b2, int per, float eps) {
-  typedef typename Mfma<T>::v8 V8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, t0 = blockIdx.x * 64;
-  const int sub = lane >> 4, c8 = (lane & 15) * 8;
-  // V of the workgroup's 64 tokens (16-byte chunk c of row c / 16), loaded first so that its
-  // latency overlaps the q/k work; written transposed after it (zeros past n)
-  u32x4 vv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = threadIdx.x + 256 * j, tok = t0 + (c >> 4);
-    vv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (vt != nullptr && tok < n)
-      vv[j] = *reinterpret_cast<const u32x4 *>(qkv + (size_t)tok * ldq + 2 * d_model + h * 128 +
-                                               (c & 15) * 8);
-  }
-  V8 qv[4], kv[4];
-  f32x4 ca[4], cb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = t0 + wave * 16 + i * 4 + sub;
-    if (tok < n) {
-      const T *qp = qkv + (size_t)tok * ldq + h * 128 + c8;
-      qv[i] = *reinterpret_cast<const V8 *>(qp);
-      kv[i] = *reinterpret_cast<const V8 *>(qp + d_model);
-      const float *cp = cs + (size_t)tok * 128 + c8;  // (cos, sin) of pairs c8/2 .. c8/2 + 3
-      ca[i] = *reinterpret_cast<const f32x4 *>(cp);
-      cb[i] = *reinterpret_cast<const f32x4 *>(cp + 4);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[i][e] = kv[i][e] = (T)0.f;
-      ca[i] = cb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = t0 + wave * 16 + i * 4 + sub;
-    float q[8], k[8];
-    float sq = 0.f, sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      q[e] = (float)qv[i][e];
-      k[e] = (float)kv[i][e];
-      sq += q[e] * q[e];
-      sk += k[e] * k[e];
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) {  // sum over the 16 lanes of this row
-      sq += __shfl_xor(sq, m, 16);
-      sk += __shfl_xor(sk, m, 16);
-    }
-    if (tok >= n) continue;
-    const int seg = segment_of(tok, b1, b2, per);
-    const float *qn = (seg == 0 ? qn0 : (seg == 1 ? qn1 : qn2)) + c8;
-    const float *kn = (seg == 0 ? kn0 : (seg == 1 ? kn1 : kn2)) + c8;
-    const float rq = 1.0f / sqrtf(sq * (1.0f / 128.f) + eps);
-    const float rk = 1.0f / sqrtf(sk * (1.0f / 128.f) + eps);
-    const f32x4 wq0 = *reinterpret_cast<const f32x4 *>(qn), wq1 = *reinterpret_cast<const f32x4 *>(qn + 4);
-    const f32x4 wk0 = *reinterpret_cast<const f32x4 *>(kn), wk1 = *reinterpret_cast<const f32x4 *>(kn + 4);
-    const float wq[8] = {wq0.x, wq0.y, wq0.z, wq0.w, wq1.x, wq1.y, wq1.z, wq1.w};
-    const float wk[8] = {wk0.x, wk0.y, wk0.z, wk0.w, wk1.x, wk1.y, wk1.z, wk1.w};
-    const float cv[8] = {ca[i].x, ca[i].y, ca[i].z, ca[i].w, cb[i].x, cb[i].y, cb[i].z, cb[i].w};
-    V8 qo, ko;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float c = cv[2 * p], sn = cv[2 * p + 1];
-      const float qa = q[2 * p] * rq * wq[2 * p], qb = q[2 * p + 1] * rq * wq[2 * p + 1];
-      const float ka = k[2 * p] * rk * wk[2 * p], kb = k[2 * p + 1] * rk * wk[2 * p + 1];
-      qo[2 * p] = from_f32<T>(qa * c - qb * sn);
-      qo[2 * p + 1] = from_f32<T>(qa * sn + qb * c);
-      ko[2 * p] = from_f32<T>(ka * c - kb * sn);
-      ko[2 * p + 1] = from_f32<T>(ka * sn + kb * c);
-    }
-    T *qp = qkv + (size_t)tok * ldq + h * 128 + c8;
-    *reinterpret_cast<V8 *>(qp) = qo;
-    *reinterpret_cast<V8 *>(qp + d_model) = ko;
-  }
-  if (vt == nullptr) return;
-  // V transpose through LDS: tile [64 tokens][128 dims] with a 130-element (65-dword) pitch,
-  // so the eight rows one read instruction touches fall in distinct banks
-  constexpr int kPitch = 130;
-  __shared__ __attribute__((aligned(16))) T tile[64 * kPitch];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = threadIdx.x + 256 * j, r = c >> 4, ch = c & 15;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[r * kPitch + ch * 8]);  // 4-byte aligned
-    dst[0] = vv[j].x;
-    dst[1] = vv[j].y;
-    dst[2] = vv[j].z;
-    dst[3] = vv[j].w;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < 128 * 8; c += 256) {
-    // eight consecutive lanes write the 128 contiguous bytes (64 keys) of one dim's row
-    const int d = c >> 3, ch = c & 7;
-    V8 o;
-    // within every 32 tokens, chunk q (8 columns) holds tokens 4q..4q+3 and 16+4q..16+4q+3:
-    // the eight keys one attention lane multiplies in a P.V MFMA, contiguous
-    const int base = (ch >> 2) * 32 + (ch & 3) * 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = tile[(base + (e < 4 ? e : e + 12)) * kPitch + d];
-    *reinterpret_cast<V8 *>(vt + ((size_t)h * 128 + d) * ldv + t0 + ch * 8) = o;
-  }
-}
-
-hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads, void *vt, int ldv,
+hipError_t qk_norm_rope(void *qkv, int type, int ldq, int d_model, int heads,
                         const float *cs, int n, const float *const qn[3],
                         const float *const kn[3], Segs segs, float eps, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  dim3 grid(n / 64 + 2, heads);  // covers [0, n + 64) for the V transpose
   switch (type) {
-    case OP_BF16:
-      k_qk_norm_rope16<bf16><<<grid, 256, 0, s>>>((bf16 *)qkv, ldq, d_model, (bf16 *)vt, ldv, cs, n,
-                                                qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
-                                                segs.b2, segs.per, eps);
-      break;
-    case OP_F16:
-      k_qk_norm_rope16<f16><<<grid, 256, 0, s>>>((f16 *)qkv, ldq, d_model, (f16 *)vt, ldv, cs, n,
-                                               qn[0], qn[1], qn[2], kn[0], kn[1], kn[2], segs.b1,
-                                               segs.b2, segs.per, eps);
-      break;
     case OP_F32:
       k_qk_norm_rope<float><<<dim3((n + 63) / 64, heads), 256, 0, s>>>(
-          (float *)qkv, ldq, d_model, nullptr, 0, cs, n, qn[0], qn[1], qn[2], kn[0], kn[1], kn[2],
+          (float *)qkv, ldq, d_model, cs, n, qn[0], qn[1], qn[2], kn[0], kn[1], kn[2],
           segs.b1, segs.b2, segs.per, eps);
       break;
     default:

@@ -3,8 +3,9 @@
 //
 // Launch sequence of one block (all on the caller's stream):
 //   ln_modulate      x (fp32) -> xm                 LayerNorm + adaLN (shift, scale)
-//   linear1          xm . W1^T -> qkv, cat[:, D:]   fused QKV + SwiGLU epilogue
-//   qk_norm_rope     qkv in place (+ V^T)           QK RMSNorm + 4D RoPE
+//   linear1          xm . W1^T -> qkv, V^T,         fused QKV (with QK RMSNorm + 4D RoPE and
+//                    cat[:, D:]                     the V transpose) + SwiGLU epilogue
+//   qk_norm_rope     qkv in place                   QK RMSNorm + 4D RoPE (fp32 path only)
 //   attention        qkv, V^T -> cat[:, :D]         softmax attention (full or per stream)
 //   linear2          cat . W2^T -> x += gate * .    gated residual
 // Stream blocks (double / per-mode) run the two projections as row groups with one weight
@@ -88,6 +89,8 @@ struct dit_ctx {
   void *cat = nullptr;       // [rows_alloc][D+F]
   void *vt = nullptr;        // [H][128][ldv] (16-bit paths)
   float *pos = nullptr;      // [rows_alloc][4]
+  const float *rope_pos = nullptr;  // positions of the call in flight (pos, or the caller's)
+  float *rope_fr = nullptr;  // [32]: RoPE frequency / (2 pi), 12-bit high parts then remainders
   float *cs = nullptr;       // [rows_alloc][128]
   float *modbuf = nullptr;   // [modw.size()][3][mod_ld()]: one vector per cond row
   float *cond = nullptr;     // [3][D]
@@ -573,6 +576,24 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
   rc = rc ? rc : dalloc(ctx, &ctx->cat, R * (D + F) * es);
   if (ctx->op != OP_F32) rc = rc ? rc : dalloc(ctx, &ctx->vt, (size_t)c.heads * 128 * ctx->ldv * es);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->pos, R * 4 * 4);
+  if (!rc) {
+    // RoPE frequencies theta^(-2j / 32) in revolutions per unit position, each split into a
+    // 12-significant-bit part (exact products with integer positions up to 4096) and the rest
+    float fr[32];
+    for (int j = 0; j < 16; ++j) {
+      const double f = exp(-log((double)c.rope_theta) * (2.0 * j) / 32.0) / (2.0 * M_PI);
+      int e = 0;
+      const double m = frexp(f, &e);  // f = m 2^e, 0.5 <= m < 1
+      const double hi = ldexp(nearbyint(m * 4096.0) / 4096.0, e);
+      fr[j] = (float)hi;
+      fr[16 + j] = (float)(f - hi);
+    }
+    rc = dalloc(ctx, (void **)&ctx->rope_fr, sizeof(fr));
+    if (!rc) {
+      hipError_t e = hipMemcpy(ctx->rope_fr, fr, sizeof(fr), hipMemcpyHostToDevice);
+      if (e != hipSuccess) rc = hip_fail(e, "upload of the RoPE frequencies");
+    }
+  }
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cs, R * 128 * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->modbuf, (ctx->modw.size() + 1) * 3 * ctx->mod_ld() * 4);
   rc = rc ? rc : dalloc(ctx, (void **)&ctx->cond, (size_t)3 * D * 4);
@@ -723,18 +744,41 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, const int mrow[3
   a1.ldc = D + F;
   a1.cat_off = D;
   a1.xs = ctx->xs;
+  // MFMA paths: QK RMSNorm + RoPE and the V transpose run in linear1's epilogue
+  if (mfma) {
+    a1.vt = ctx->vt;
+    a1.ldv = ctx->ldv;
+    a1.n_tok = N;
+    a1.rope_pos = ctx->rope_pos;
+    a1.rope_fr = ctx->rope_fr;
+    for (int s = 0; s < 3; ++s) {
+      a1.qn[s] = qn[s];
+      a1.kn[s] = kn[s];
+    }
+    a1.rms_eps = c.rms_eps;
+    a1.b1 = sg.b1;
+    a1.b2 = sg.b2;
+    a1.per = sg.per;
+  }
   DIT_TIMED(P_LINEAR1, 2.0 * N * D * (double)a1.n, 0.0, gemm(a1, EPI_QKV_SWIGLU), "linear1");
-  if (int rc = chk("linear1 -> q, k, v", ctx->qkv, ctx->op, N, 3 * D, 3 * D)) return rc;
+  if (mfma) {
+    if (int rc = chk("linear1 -> q, k (normalised, rotated)", ctx->qkv, ctx->op, N, 2 * D, 3 * D)) return rc;
+    if (int rc = chk("linear1 -> V^T", ctx->vt, ctx->op, D, N, ctx->ldv)) return rc;
+  } else {
+    if (int rc = chk("linear1 -> q, k, v", ctx->qkv, ctx->op, N, 3 * D, 3 * D)) return rc;
+  }
   if (!seq)
     if (int rc = chk("linear1 -> SwiGLU output", (const char *)ctx->cat + (size_t)D * es, ctx->op, N, F, D + F))
       return rc;
 
-  // bytes: q, k read + written, V read + V^T written, one cos/sin row per token
-  DIT_TIMED(P_QKNORM, 0.0, (double)N * (6.0 * D * es_d + 512.0),
-            qk_norm_rope(ctx->qkv, ctx->op, 3 * D, D, c.heads, ctx->vt, ctx->ldv, ctx->cs, N, qn,
-                         kn, sg, c.rms_eps, stream),
-            "qk_norm_rope");
-  if (int rc = chk("qk_norm_rope -> q, k", ctx->qkv, ctx->op, N, 2 * D, 3 * D)) return rc;
+  if (!mfma) {
+    // bytes: q, k read + written, one cos/sin row per token
+    DIT_TIMED(P_QKNORM, 0.0, (double)N * (4.0 * D * es_d + 512.0),
+              qk_norm_rope(ctx->qkv, ctx->op, 3 * D, D, c.heads, ctx->cs, N, qn, kn, sg,
+                           c.rms_eps, stream),
+              "qk_norm_rope");
+    if (int rc = chk("qk_norm_rope -> q, k", ctx->qkv, ctx->op, N, 2 * D, 3 * D)) return rc;
+  }
 
   AttnArgs at = {};
   at.qkv = ctx->qkv;
@@ -903,7 +947,9 @@ int run_forward(dit_ctx *ctx, const float *lat, const Req &rq, double t, double 
     DIT_CHECK(fill_positions(ctx->pos + (size_t)qs * per * 4, n_txt, gh, gw, rq.grids, rq.n_refs,
                              stream),
               "positions");
-  DIT_CHECK(rope_table(ctx->cs, ctx->pos, sg.n, c.rope_theta, stream), "rope_table");
+  if (ctx->op == OP_F32)  // the MFMA paths rotate in linear1's epilogue, from the positions
+    DIT_CHECK(rope_table(ctx->cs, ctx->pos, sg.n, c.rope_theta, stream), "rope_table");
+  ctx->rope_pos = ctx->pos;
   // sequence: text embeddings as they are, latents through the input projection
   for (int qs = 0; qs < nseq; ++qs)
     DIT_CHECK(copy_rows_f32(ctx->x + (size_t)qs * per * D, D, txt[qs], D, n_txt, D, stream),
@@ -1063,7 +1109,9 @@ extern "C" int dit_block_forward(dit_ctx *ctx, int block, float *x, int n_txt, i
   if (int rc = check_tokens(ctx, n_txt, n_img, n_ref)) return rc;
   hipStream_t stream = (hipStream_t)stream_;
   const Segs sg = make_segs(n_txt, n_img, n_ref);
-  DIT_CHECK(rope_table(ctx->cs, pos, sg.n, ctx->cfg.rope_theta, stream), "rope_table");
+  if (ctx->op == OP_F32)
+    DIT_CHECK(rope_table(ctx->cs, pos, sg.n, ctx->cfg.rope_theta, stream), "rope_table");
+  ctx->rope_pos = pos;
   // one conditioning row per non-empty segment, in the order text, image, reference
   const int count[3] = {n_txt, n_img, n_ref};
   int mrow[3], n_cond = 0;
@@ -1391,6 +1439,7 @@ extern "C" const void *dit_debug_buffer(dit_ctx *ctx, const char *name, int *dty
   };
   if (!strcmp(name, "xm")) return ret(ctx->xm, ctx->fp8 ? DIT_FP8 : dt, D);
   if (!strcmp(name, "qkv")) return ret(ctx->qkv, dt, 3 * D);
+  if (!strcmp(name, "vt")) return ctx->vt ? ret(ctx->vt, dt, ctx->ldv) : nullptr;
   if (!strcmp(name, "cat")) return ret(ctx->cat, dt, D + F);
   if (!strcmp(name, "mod")) return ret(ctx->modbuf, DIT_F32, ctx->mod_ld());  // [M][3][R]
   if (!strcmp(name, "x")) return ret(ctx->x, DIT_F32, D);

@@ -69,7 +69,8 @@ def oracle_stages(cfg, w, b, x, segs, pos, cond):
             continue
         sh, sc, _ = O.split_modulation(mods[s], d)
         xm[sel] = y[sel] * (1 + sc) + sh
-        h[sel] = xm[sel] @ sets[sos[s]].w1.T
+        xin = O.fp8_round_rows(xm[sel]) if cfg.compute == "fp8" else xm[sel]
+        h[sel] = xin @ sets[sos[s]].w1.T
         qn[sel] = O.rms_norm(h[sel, :d].reshape(-1, nh, 128), sets[sos[s]].qn, cfg.rms_eps)
         kn[sel] = O.rms_norm(h[sel, d:2 * d].reshape(-1, nh, 128), sets[sos[s]].kn, cfg.rms_eps)
     ang = O.rope_angles(f64(pos), cfg.rope_theta)
@@ -82,6 +83,19 @@ def oracle_stages(cfg, w, b, x, segs, pos, cond):
     return dict(xm=xm, q=q, k=k, v=v, o=o, m=m, mods=mods)
 
 
+def vt_column(t):
+    """Column of token t in the transposed V buffer: every 32 tokens are stored in 16-byte
+    chunks of tokens (4q..4q+3, 16+4q..16+4q+3), q = 0..3."""
+    u = t % 32
+    return t - u + (u % 16) // 4 * 8 + u // 16 * 4 + u % 4
+
+
+def vt_tokens(ctx, d, n):
+    """V [n, d] read back from the transposed buffer."""
+    vt = ctx.debug_buffer("vt", d).cpu().numpy()
+    return vt[:, [vt_column(t) for t in range(n)]].T
+
+
 def stage_report(ctx, cfg, w, b, x, segs, pos, cond):
     n = sum(segs)
     d = cfg.hidden
@@ -89,8 +103,9 @@ def stage_report(ctx, cfg, w, b, x, segs, pos, cond):
     qkv = ctx.debug_buffer("qkv", n).cpu().numpy()
     cat = ctx.debug_buffer("cat", n).cpu().numpy()
     xm = ctx.debug_buffer("xm", n).cpu().numpy()
+    v = qkv[:, 2 * d:] if cfg.compute == "f32" else vt_tokens(ctx, d, n)
     rep = {"xm": rel_err(xm, st["xm"]), "q": rel_err(qkv[:, :d], st["q"]),
-           "k": rel_err(qkv[:, d:2 * d], st["k"]), "v": rel_err(qkv[:, 2 * d:], st["v"]),
+           "k": rel_err(qkv[:, d:2 * d], st["k"]), "v": rel_err(v, st["v"]),
            "attn": rel_err(cat[:, :d], st["o"]), "swiglu": rel_err(cat[:, d:], st["m"])}
     return rep
 
@@ -140,6 +155,42 @@ def test_block_tiny_ragged(cfg, b):
     """Ragged segments spanning several GEMM / attention tiles, all three streams."""
     err, derr = run_block(cfg, b, 77, (13, 11), (9, 10))
     assert err <= tol(cfg) and derr <= tol_update(cfg)
+
+
+@pytest.mark.parametrize("cfg", [TINY2, TINY3] + C16,
+                         ids=["flux2_f16", "flux3_f16", "flux2_bf16", "flux3_bf16"])
+def test_fused_qk_norm_rope_and_v_transpose(cfg):
+    """linear1's epilogue: normalised and rotated q, k and the transposed V, stage by stage,
+    with segment boundaries off the 32-token grid (77 text tokens); then a smaller call on the
+    same context, whose V^T columns past its last token must read exactly zero although the
+    first call wrote values there.  The E4M3 path runs the same epilogue after its scaling;
+    its stages are not compared here because a weight code that the library's fp32 quantizer
+    puts on the other side of a near tie (about 1 in 10^4 of these bf16 weights) moves every
+    output of its feature by up to a few percent of RMS at this width -- its block tests
+    hold it to the error model's bars instead."""
+    from latent_flow_matching_amd import dit
+    ctx, w = context(cfg, 700)
+    d = cfg.hidden
+    bar = tol(cfg)
+    for segs, grid, ref in (((77, 117, 99), (9, 13), (9, 11)), ((40, 30, 0), (5, 6), None)):
+        n = sum(segs)
+        x = S.gen_tokens(n, d, key=(n,))
+        cond = S.gen_cond(3, d)
+        pos = O.positions(segs[0], grid, (ref,) if ref else ())
+        for b in (0, 1):
+            ctx.block_forward(b, dev(x), segs[0], segs[1], segs[2], dev(pos),
+                              dev(seg_cond(cond, segs)), dit.DIT_MASK_DEFAULT)
+            torch.cuda.synchronize()
+            st = oracle_stages(cfg, w, b, x, segs, pos, cond)
+            qkv = ctx.debug_buffer("qkv", n).cpu().numpy()
+            eq, ek = rel_err(qkv[:, :d], st["q"]), rel_err(qkv[:, d:2 * d], st["k"])
+            ev = rel_err(vt_tokens(ctx, d, n), st["v"])
+            print(f"[fused] {cfg.compute} arch={cfg.arch} b={b} segs={segs} q {eq:.2e} k {ek:.2e} "
+                  f"v {ev:.2e}", flush=True)
+            assert max(eq, ek, ev) <= bar
+            vt = ctx.debug_buffer("vt", d).cpu().numpy()
+            tail = [vt_column(t) for t in range(n, (n // 64 + 2) * 64)]
+            assert not np.any(vt[:, tail]), "V^T past the last token is not zero"
 
 
 @pytest.mark.parametrize("segs", [(1, (1, 1), None), (0, (3, 5), None), (300, (2, 2), None),
