@@ -31,15 +31,24 @@ constexpr int BK = 64;   // k per LDS stage
 // after each MFMA, so the LDS and global latencies sit under MFMAs.  Token rows, which miss L2
 // more often than weight rows under the grouped tile order, get two staging sets and so two
 // k-tiles of latency cover.
-template <typename T, int EPI>
+//
+// BM (token rows per tile) is 256 or 224: 224-row tiles (7 token sub-tiles per wave) let a
+// launch whose 256-row tiles would leave many compute units idle in its last round fill them
+// (linear2 at 4608 tokens: 12 x 18 = 216 tiles of 256 rows for 256 compute units, 12 x 21 =
+// 252 of 224 rows).  The schedule below is written for any TS; with TS = 8 it is the
+// 256-row kernel's.
+template <typename T, int EPI, int BM>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_tiles_total,
                                                   int total_tiles, int splits) {
-  constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
-  constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
-  constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 sub-tiles of 16 x 16
-  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 16-byte loads per thread
+  constexpr int WN = 2, WM = 2, NT = 256;
+  constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128 (or 128 x 112)
+  constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 (or 8 x 7) sub-tiles of 16 x 16
+  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 (or 8 + 7) 16-byte loads per thread
   constexpr int KS = BK / 32;                  // 2 k-steps of 32 per k-tile
-  constexpr int STAGE = (BN + BM) * BK * 2;    // 64 KB
+  constexpr int STAGE = (BN + BM) * BK * 2;    // 64 KB (or 60 KB)
+  constexpr int NK = FS * TS;                  // MFMAs per k-step
+  constexpr int NMEM = 3 * (FS + TS);          // memory operations placed before the barrier
+  static_assert(BM % 32 == 0 && LA == FS && LB == TS, "tile shape");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   typedef typename Mfma<T>::v8 V8;
 
@@ -142,11 +151,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   };
 
   // single operations, so the loop below can fix their order exactly
-  auto mma_one = [&](int ks, int idx) {  // idx = 8 i + j
-    acc[idx >> 3][idx & 7] =
-        Mfma<T>::mma16(fr[ks][idx >> 3], fr[ks][FS + (idx & 7)], acc[idx >> 3][idx & 7]);
+  auto mma_one = [&](int ks, int idx) {  // idx = TS i + j
+    acc[idx / TS][idx % TS] =
+        Mfma<T>::mma16(fr[ks][idx / TS], fr[ks][FS + idx % TS], acc[idx / TS][idx % TS]);
   };
-  auto read_one = [&](int stage, int ks, int f) {  // f < 8: weight rows, else token rows
+  auto read_one = [&](int stage, int ks, int f) {  // f < FS: weight rows, else token rows
     const char *As = smem + stage * STAGE;
     const char *Bs = As + BN * 128;
     const int ch = ks * 4 + q4;
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
     else
       fr[ks][f] = *reinterpret_cast<const V8 *>(Bs + swz(wm * WTM + (f - FS) * 16 + r16, ch));
   };
-  auto write_one = [&](int stage, int i, const u32x4 (&rb)[LB]) {  // i < 8: weights
+  auto write_one = [&](int stage, int i, const u32x4 (&rb)[LB]) {  // i < LA: weights
     char *As = smem + stage * STAGE;
     char *Bs = As + BN * 128;
     if (i < LA)
@@ -179,17 +188,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   // Order of the fragment reads: k-step 1 of the tile reads its token sub-tiles first (every
   // MFMA row needs all of them), the next tile's k-step 0 reads weight sub-tile 0, the token
   // sub-tiles, then the other weight sub-tiles (the order its first MFMAs use them).
-  auto frag_k1 = [](int r) { return r < 8 ? 8 + r : r - 8; };
-  auto frag_k0 = [](int r) { return r == 0 ? 0 : (r <= 8 ? 7 + r : r - 8); };
+  auto frag_k1 = [](int r) { return r < TS ? FS + r : r - TS; };
+  auto frag_k0 = [](int r) { return r == 0 ? 0 : (r <= TS ? FS - 1 + r : r - TS); };
   // one k-tile; rb holds the token rows of tile kt+1 and receives those of tile kt+3
   auto ktile = [&](int kt, u32x4 (&rb)[LB]) {
     const int cur = kt & 1;
     const int na = min(kt + 2, KT - 1), nb = min(kt + 3, KT - 1);  // clamped: repeats harmless
-    // before the barrier: 96 MFMAs (k-step 0, half of k-step 1); after every second one comes
-    // in turn a fragment read of k-step 1, an LDS write of tile kt+1 or a global load
+    // before the barrier: 2 NMEM MFMAs (k-step 0 and part of k-step 1; 96 of 128 for 256-row
+    // tiles); after every second one comes in turn a fragment read of k-step 1, an LDS write
+    // of tile kt+1 or a global load
 #pragma unroll
-    for (int m = 0; m < 96; ++m) {
-      mma_one(m >> 6, m & 63);
+    for (int m = 0; m < 2 * NMEM; ++m) {
+      mma_one(m / NK, m % NK);
       if ((m & 1) == 0) {
         const int q = m >> 1, r = q / 3;
         if (q % 3 == 0) read_one(cur, 1, frag_k1(r));
@@ -199,12 +209,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_sync();  // tile kt+1 written by every wave; tile kt's reads done
-    // after the barrier: the other 32 MFMAs of k-step 1, every second one after a read of
-    // tile kt+1's k-step 0
+    // after the barrier: the other MFMAs of k-step 1 (32 for 256-row tiles), the reads of
+    // tile kt+1's k-step 0 spread evenly before them (every second one for 256-row tiles)
+    constexpr int NPOST = 2 * NK - 2 * NMEM, NR = FS + TS;
 #pragma unroll
-    for (int m = 96; m < 128; ++m) {
-      if ((m & 1) == 0) read_one(cur ^ 1, 0, frag_k0((m - 96) >> 1));
-      mma_one(1, m & 63);
+    for (int m = 0; m < NPOST; ++m) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if (r * NPOST / NR == m) read_one(cur ^ 1, 0, frag_k0(r));
+      mma_one(1, NK - NPOST + m);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -233,13 +246,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
   epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
+// Token-tile bounds of the row groups for tile height bm; returns the number of token tiles.
+int tile_bounds(const GemmArgs &a, int bm, TileBounds *tb) {
+  *tb = TileBounds{};
+  for (int i = 0; i < kMaxGroups; ++i)
+    tb->t[i + 1] = tb->t[i] + (i < a.ng ? (a.g[i].rows + bm - 1) / bm : 0);
+  return tb->t[kMaxGroups];
+}
+
 template <typename T, int EPI>
 hipError_t launch(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 256;
-  TileBounds tb = {};
-  for (int i = 0; i < kMaxGroups; ++i)
-    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
-  const int m_tiles = tb.t[kMaxGroups];
+  TileBounds tb;
+  const int m_tiles = tile_bounds(a, 256, &tb);
   if (m_tiles == 0) return hipSuccess;
   const int total = m_tiles * (a.n / BN);
   // k-slices: only for tiles that fill under half of the compute units, with at least 8
@@ -249,8 +267,22 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
     splits = min(8, min(a.split_grid / total, (a.k / BK) / 8));
     if (splits < 2 || (long long)splits * total > a.part_tiles) splits = 1;
   }
+  if constexpr (EPI == EPI_RESID) {
+    // 224-row tiles when the rounds of tiles over the compute units times the tile height
+    // (the time, up to the tiles' own efficiency) come out lower
+    if (splits == 1 && a.cus > 0) {
+      TileBounds tb7;
+      const int m7 = tile_bounds(a, 224, &tb7), total7 = m7 * (a.n / BN);
+      const long long t256 = (long long)((total + a.cus - 1) / a.cus) * 256;
+      const long long t224 = (long long)((total7 + a.cus - 1) / a.cus) * 224;
+      if (t224 < t256) {
+        k_gemm<T, EPI, 224><<<(total7 + 7) / 8 * 8, 256, 0, s>>>(a, tb7, m7, total7, 1);
+        return hipGetLastError();
+      }
+    }
+  }
   const int grid = (total * splits + 7) / 8 * 8;
-  k_gemm<T, EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
+  k_gemm<T, EPI, 256><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
   if (splits > 1) {
     if constexpr (EPI != EPI_QKV_SWIGLU)
       k_gemm_reduce<EPI><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);

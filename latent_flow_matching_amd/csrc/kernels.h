@@ -64,6 +64,9 @@ struct GemmArgs {
   // its fp32 partial tile to part (room for part_tiles tiles of 256 x 256), and a second kernel
   // adds the slices in slice order and applies the epilogue.  split_grid = 0: never.
   float *part; int part_tiles; int split_grid;
+  // Compute units of the device (EPI_RESID on the 16-bit GEMM: picks 224-row token tiles when
+  // they fill the device in fewer tile-heights; 0: always 256-row tiles)
+  int cus;
   // FP8 GEMM: scale of each input row, indexed by token (out_row0 + row)
   const float *xs;
 };

@@ -128,6 +128,7 @@ struct dit_ctx {
     a->part = gemm_part;
     a->part_tiles = gemm_part ? cus : 0;
     a->split_grid = gemm_part ? cus : 0;
+    a->cus = cus;
   }
   int F() const { return cfg.mlp_hidden; }
   size_t esz() const { return op == OP_F32 ? 4 : 2; }
