@@ -33,13 +33,14 @@ GEMM_SOURCES = {"f16": ("gemm_mfma.hip", "gemm_common.h"), "bf16": ("gemm_mfma.h
                 "fp8": ("gemm_fp8.hip", "gemm_common.h")}
 COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
 # rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
-# (patterns match the mangled names rocprofv3 prints: the epilogue is the last template argument)
-KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8)?I.*Li1EEEv|k_gemm8<1>"),
-                  ("linear2", r"k_gemm(?:_v3|_mfma|8)?I.*Li2EEEv|k_gemm8<2>"),
+# (patterns match the mangled names rocprofv3 prints: the epilogue is the template argument
+# after the operand type, followed by the token-tile height on the 16-bit GEMM)
+KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8)?I.*Li1E(?:Li\d+E)?EEv|k_gemm8<1>"),
+                  ("linear2", r"k_gemm(?:_v3|_mfma|8)?I.*Li2E(?:Li\d+E)?EEv|k_gemm8<2>"),
                   ("fp8_quant", r"k_quant_rows"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
                   ("ln_modulate", r"k_ln_modulate"),
-                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8)?I.*Li0EEEv|k_to_half"),
+                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8)?I.*Li0E(?:Li\d+E)?EEv|k_to_half"),
                   ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
 
 
@@ -542,6 +543,10 @@ def main():
                 "traffic": round(tr["bytes_per_launch"]) if tr else None,
                 "flops_per_launch": dfl / dcnt, "avg_launch_us": round(dms / dcnt * 1e3, 2),
                 "avg_launch_source": "hipEvents around every launch of this kernel in the timed steps"}
+    if dom == "linear1" and args.compute != "f32":
+        # the launch also runs QK-RMSNorm, RoPE and the V transpose in its epilogue; the flops
+        # counted are the projection's only
+        roofline["epilogue_includes"] = "SwiGLU, QK-RMSNorm + RoPE, V transpose (not in flops_per_launch)"
     if tr:
         roofline["traffic_source"] = "profiles/" + traffic_name(dom, wl.name, args.compute)
     trace = load_trace_avg(dom, wl.name, args.compute)
