@@ -496,11 +496,14 @@ hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
   p.iters = p.iters_head * a.heads;
   int grid = (p.total + 7) / 8 * 8;
   const int lg = a.lean_grid / 8 * 8;
-  // Equal shares when one unit per workgroup would leave over a tenth of the last round
-  // idle.  A share of iters / lg iterations cuts a unit into at most ceil(nk / share) + 1
-  // pieces, which the merge supports up to 8; shares under 8 key tiles are not worth a merge.
+  // Equal shares when they beat one unit per workgroup: that takes `rounds` unit-times, equal
+  // shares take total / lg of them plus the cost of pieces and merges, about a fifth in the
+  // block (measured: 272-276 against 264-267 us for 432 units at 4608 tokens, 894 against
+  // 1009 us for 816 units at 8704).  A share of iters / lg iterations cuts a unit into at
+  // most ceil(nk / share) + 1 pieces, which the merge supports up to 8; shares under 8 key
+  // tiles are not worth a merge.
   const long long rounds = (p.total + lg - 1) / (lg > 0 ? lg : 1);
-  if (a.part != nullptr && a.cnt != nullptr && lg > 0 && 10LL * p.total < 9LL * rounds * lg) {
+  if (a.part != nullptr && a.cnt != nullptr && lg > 0 && 6LL * p.total < 5LL * rounds * lg) {
     int nk_max = 1;
     for (int i = 0; i < kMaxGroups; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
     const int share = p.iters / lg;

@@ -663,7 +663,7 @@ def _split_plan(groups, heads, lean_grid):
     iters = sum(q * k for q, k in zip(q_tiles, nk)) * heads
     rounds = -(-total // lean_grid)
     share = iters // lean_grid
-    lean = 10 * total < 9 * rounds * lean_grid and share >= 8 and -(-max(nk) // share) + 1 <= 8
+    lean = 6 * total < 5 * rounds * lean_grid and share >= 8 and -(-max(nk) // share) + 1 <= 8
     return lean, -(-max(nk) // max(share, 1)) + 1
 
 
