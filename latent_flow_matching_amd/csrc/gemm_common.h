@@ -138,40 +138,51 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
       pv[k] = a.rope_pos[(size_t)tok * 4 + (c >> 2)];
     }
     constexpr int KB = 8;
+    // y = weight * (value / RMS), then the rotation of its four pairs by pos * freq
+    auto rotate = [&](const f16x8 &h, const f32x4 &wa, const f32x4 &wb, float p) {
+      const float y[8] = {(float)h[0] * wa.x, (float)h[1] * wa.y, (float)h[2] * wa.z,
+                          (float)h[3] * wa.w, (float)h[4] * wb.x, (float)h[5] * wb.y,
+                          (float)h[6] * wb.z, (float)h[7] * wb.w};
+      typename Mfma<T>::v8 o;
 #pragma unroll
-    for (int k0 = 0; k0 < NT4; k0 += KB) {
-      f16x8 hv[KB];
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int t = tl + 4 * (k0 + k);
-        hv[k] = *reinterpret_cast<const f16x8 *>(tq + t * 256 + ((c ^ (t & 15)) << 4));
+      for (int q = 0; q < 4; ++q) {
+        const float x = p * fh[q];
+        const float r = (x - __builtin_rintf(x)) + p * fl[q];
+        const float co = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
+        o[2 * q] = from_f32<T>(y[2 * q] * co - y[2 * q + 1] * sn);
+        o[2 * q + 1] = from_f32<T>(y[2 * q] * sn + y[2 * q + 1] * co);
       }
+      return o;
+    };
+    typedef typename Mfma<T>::v8 V8o;
+    if (one_seg && mw + WTM <= grp.rows) {
+      // every token of the wave in the group and in one segment: no per-token branches, so
+      // the compiler can interleave the eight tokens of a batch
+      V8o *dst = reinterpret_cast<V8o *>(reinterpret_cast<T *>(a.qkv) +
+                                         (size_t)(grp.out_row0 + mw + tl) * a.ldq + fw + 8 * c);
+      const size_t step = (size_t)4 * a.ldq / 8;  // four tokens, in 16-byte units
 #pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int t = tl + 4 * (k0 + k), m = mw + t;
+      for (int k0 = 0; k0 < NT4; k0 += KB) {
+        f16x8 hv[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const int t = tl + 4 * (k0 + k);
+          hv[k] = *reinterpret_cast<const f16x8 *>(tq + t * 256 + ((c ^ (t & 15)) << 4));
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) dst[(k0 + k) * step] = rotate(hv[k], w0, w1, pv[k0 + k]);
+      }
+    } else {
+#pragma unroll 1
+      for (int k = 0; k < NT4; ++k) {
+        const int t = tl + 4 * k, m = mw + t;
         if (m >= grp.rows) continue;
         const int tok = grp.out_row0 + m;
-        f32x4 wa = w0, wb = w1;
-        if (!one_seg) {
-          const float *wr = wsel[segment_of(tok, a.b1, a.b2, a.per)] + 8 * c;
-          wa = *reinterpret_cast<const f32x4 *>(wr);
-          wb = *reinterpret_cast<const f32x4 *>(wr + 4);
-        }
-        const float y[8] = {(float)hv[k][0] * wa.x, (float)hv[k][1] * wa.y, (float)hv[k][2] * wa.z,
-                            (float)hv[k][3] * wa.w, (float)hv[k][4] * wb.x, (float)hv[k][5] * wb.y,
-                            (float)hv[k][6] * wb.z, (float)hv[k][7] * wb.w};
-        const float p = pv[k0 + k];
-        typename Mfma<T>::v8 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x = p * fh[q];
-          const float r = (x - __builtin_rintf(x)) + p * fl[q];
-          const float co = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
-          o[2 * q] = from_f32<T>(y[2 * q] * co - y[2 * q + 1] * sn);
-          o[2 * q + 1] = from_f32<T>(y[2 * q] * sn + y[2 * q + 1] * co);
-        }
-        *reinterpret_cast<typename Mfma<T>::v8 *>(reinterpret_cast<T *>(a.qkv) +
-                                                  (size_t)tok * a.ldq + fw + 8 * c) = o;
+        const float *wr = wsel[segment_of(tok, a.b1, a.b2, a.per)] + 8 * c;
+        const f16x8 h = *reinterpret_cast<const f16x8 *>(tq + t * 256 + ((c ^ (t & 15)) << 4));
+        *reinterpret_cast<V8o *>(reinterpret_cast<T *>(a.qkv) + (size_t)tok * a.ldq + fw + 8 * c) =
+            rotate(h, *reinterpret_cast<const f32x4 *>(wr), *reinterpret_cast<const f32x4 *>(wr + 4),
+                   a.rope_pos[(size_t)tok * 4 + (c >> 2)]);
       }
     }
     return;
