@@ -81,6 +81,10 @@ struct AttnPlan {
   int iters_head, iters;    // iterations per head, in total
   int total;              // units
   int lean;               // 1: equal iteration shares over the grid; 0: one unit per workgroup
+  // lean: units [0, full) run whole, workgroup w taking units w, w + grid, ... (full is a
+  // multiple of the grid); the iterations from it_full (unit full's first) to the end are
+  // split into equal shares
+  int full, it_full;
 };
 
 struct Unit {
@@ -99,12 +103,22 @@ __device__ __forceinline__ Unit decode(const AttnPlan &p, int it) {
   u.qt = p.tb[u.g] + ql;
   return u;
 }
-// first iteration of the share of workgroup w, and the workgroup whose share holds it
+// first iteration of the share of workgroup w, and the workgroup whose share holds iteration
+// it (it >= it_full)
 __device__ __forceinline__ int share_begin(const AttnPlan &p, int w, int grid) {
-  return (int)((long long)p.iters * w / grid);
+  return p.it_full + (int)((long long)(p.iters - p.it_full) * w / grid);
 }
 __device__ __forceinline__ int share_owner(const AttnPlan &p, int it, int grid) {
-  return (int)(((long long)(it + 1) * grid + p.iters - 1) / p.iters) - 1;
+  const long long span = p.iters - p.it_full;
+  return (int)(((long long)(it - p.it_full + 1) * grid + span - 1) / span) - 1;
+}
+// first iteration of unit u (head-major, query tiles in group order)
+__device__ __forceinline__ int unit_begin(const AttnPlan &p, int u) {
+  const int hd = u / p.q_tiles, qt = u - hd * p.q_tiles;
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) g += qt >= p.tb[i];
+  return hd * p.iters_head + p.cum[g] + (qt - p.tb[g]) * p.nk[g];
 }
 
 // Partial results of a piece: O as 16 float4 per lane and wave, then (max, max, sum, sum) of the
@@ -123,20 +137,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   const int G = gridDim.x;
   const int per = G >> 3;
   const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  int it0, it1;
+  int it0, it1, n_whole = 0;  // the share (or the one unit), then whole units lid + G r, r < n_whole
   if (p.lean) {
     it0 = share_begin(p, lid, G);
     it1 = share_begin(p, lid + 1, G);
+    n_whole = p.full / G;
   } else {
     if (lid >= p.total) return;
-    const int hd = lid / p.q_tiles, qt = lid - hd * p.q_tiles;
-    int g = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxGroups; ++i) g += qt >= p.tb[i];
-    it0 = hd * p.iters_head + p.cum[g] + (qt - p.tb[g]) * p.nk[g];
-    it1 = it0 + p.nk[g];
+    it0 = unit_begin(p, lid);
+    it1 = it0 + p.nk[decode(p, it0).g];
   }
-  if (it0 >= it1) return;
+  if (it0 >= it1 && n_whole == 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -300,15 +311,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
   using I32 = std::integral_constant<int, 32>;
 
   // Pieces of this workgroup's share: a partial piece at the end of the share first (the
-  // head of a unit the next workgroup finishes), then the first piece, then whole units.
-  const Unit uf = decode(p, it0);
-  const int len_first = min(it1 - it0, p.nk[uf.g] - uf.t);
-  const Unit ul = decode(p, it1 - 1);
-  const bool last_partial = (it0 + len_first < it1) && (ul.t + 1 < p.nk[ul.g]);
-  const int len_last = last_partial ? ul.t + 1 : 0;
+  // head of a unit the next workgroup finishes), then the first piece, then the whole units
+  // inside the share; then the whole units of the full rounds.
+  int len_first = 0, len_last = 0, step = 3;
+  if (it0 < it1) {
+    const Unit uf = decode(p, it0);
+    len_first = min(it1 - it0, p.nk[uf.g] - uf.t);
+    const Unit ul = decode(p, it1 - 1);
+    const bool last_partial = (it0 + len_first < it1) && (ul.t + 1 < p.nk[ul.g]);
+    len_last = last_partial ? ul.t + 1 : 0;
+    step = last_partial ? 0 : 1;
+  }
   const int mid_end = it1 - len_last;
-  int mid = it0 + len_first;
-  int step = last_partial ? 0 : 1;
+  int mid = it0 + len_first, r_whole = 0;
   for (;;) {
     int pit, plen, slot;
     if (step == 0) {
@@ -321,12 +336,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a, AttnPlan p) {
       plen = len_first;
       slot = 2 * lid;
       step = 2;
-    } else {
-      if (mid >= mid_end) break;
+    } else if (step == 2 && mid < mid_end) {
       pit = mid;
       plen = p.nk[decode(p, mid).g];
       slot = -1;
       mid += plen;
+    } else {
+      if (r_whole >= n_whole) break;
+      pit = unit_begin(p, lid + r_whole * G);
+      plen = p.nk[decode(p, pit).g];
+      slot = -1;
+      ++r_whole;
     }
     const Unit u = decode(p, pit);
     const int nku = p.nk[u.g];
@@ -496,20 +516,34 @@ hipError_t attention_mfma(const AttnArgs &a, int op, hipStream_t s) {
   p.iters = p.iters_head * a.heads;
   int grid = (p.total + 7) / 8 * 8;
   const int lg = a.lean_grid / 8 * 8;
-  // Equal shares when they beat one unit per workgroup: that takes `rounds` unit-times, equal
-  // shares take total / lg of them plus the cost of pieces and merges, about a fifth in the
-  // block (measured: 272-276 against 264-267 us for 432 units at 4608 tokens, 894 against
-  // 1009 us for 816 units at 8704).  A share of iters / lg iterations cuts a unit into at
-  // most ceil(nk / share) + 1 pieces, which the merge supports up to 8; shares under 8 key
-  // tiles are not worth a merge.
-  const long long rounds = (p.total + lg - 1) / (lg > 0 ? lg : 1);
-  if (a.part != nullptr && a.cnt != nullptr && lg > 0 && 6LL * p.total < 5LL * rounds * lg) {
-    int nk_max = 1;
-    for (int i = 0; i < kMaxGroups; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
-    const int share = p.iters / lg;
-    if (share >= 8 && (nk_max + share - 1) / share + 1 <= 8) {
-      p.lean = 1;
-      grid = lg;
+  // One unit per workgroup leaves compute units idle in a last, partly filled round, but the
+  // chip is power-limited: the busy ones then run faster, so splitting units into pieces (with
+  // the cost of publishing and merging them) pays only when that round is mostly empty.
+  // Measured, one unit per workgroup against split: 56 against 69 us for 144 units on 256
+  // CUs (1536 tokens), 274 against 275 us for 432 (4608), 1010 against 896 us for 816 (8704),
+  // 213 against 190 us for 336 (3584).  A share of s iterations cuts a unit into at most
+  // ceil(nk / s) + 1 pieces, which the merge supports up to 8; shares under 8 key tiles are
+  // not worth a merge.
+  if (a.part != nullptr && a.cnt != nullptr && lg > 0) {
+    // Units of the full rounds run whole; the last round's units are split when they would
+    // fill under 40% of it.
+    const int full = p.total / lg * lg, rest = p.total - full;
+    if (rest > 0 && 5LL * rest < 2LL * lg) {
+      p.full = full;
+      p.it_full = 0;
+      if (full > 0) {  // first iteration of unit `full`, as unit_begin computes it
+        const int hd = full / p.q_tiles, qt = full - hd * p.q_tiles;
+        int g = 0;
+        for (int i = 1; i < kMaxGroups; ++i) g += qt >= p.tb[i];
+        p.it_full = hd * p.iters_head + p.cum[g] + (qt - p.tb[g]) * p.nk[g];
+      }
+      int nk_max = 1;
+      for (int i = 0; i < kMaxGroups; ++i) nk_max = nk_max > p.nk[i] ? nk_max : p.nk[i];
+      const int share = (p.iters - p.it_full) / lg;
+      if (share >= 8 && (nk_max + share - 1) / share + 1 <= 8) {
+        p.lean = 1;
+        grid = lg;
+      }
     }
   }
   if (op == OP_BF16)

@@ -655,23 +655,29 @@ def test_block_is_deterministic():
 # ----------------------------------------------------------------- attention split into equal shares
 
 def _split_plan(groups, heads, lean_grid):
-    """Whether the MFMA attention launch takes equal key-tile shares, and the most pieces a
-    unit is cut into: the launcher's rule restated, so each case below provably exercises it."""
+    """(split, most pieces per split unit, rounds of whole units): the launcher's rule
+    restated, so each case below provably exercises it.  Units of the full rounds run whole;
+    the rest are split into equal key-tile shares when that is expected to beat a round."""
     q_tiles = [(q1 - q0 + 255) // 256 for q0, q1, _, _ in groups]
     nk = [(k1 - k0 // 64 * 64 + 63) // 64 for _, _, k0, k1 in groups]
     total = sum(q_tiles) * heads
-    iters = sum(q * k for q, k in zip(q_tiles, nk)) * heads
-    rounds = -(-total // lean_grid)
-    share = iters // lean_grid
-    lean = 6 * total < 5 * rounds * lean_grid and share >= 8 and -(-max(nk) // share) + 1 <= 8
-    return lean, -(-max(nk) // max(share, 1)) + 1
+    full = total // lean_grid * lean_grid
+    rest = total - full
+    # iterations of the units past `full` (units head-major, query tiles in group order)
+    unit_iters = [k for _ in range(heads) for q, k in zip(q_tiles, nk) for _ in range(q)]
+    share = sum(unit_iters[full:]) // lean_grid
+    lean = (rest > 0 and 5 * rest < 2 * lean_grid and share >= 8
+            and -(-max(nk) // share) + 1 <= 8)
+    return lean, -(-max(nk) // max(share, 1)) + 1, full // lean_grid
 
 
 @pytest.mark.parametrize("case", [
-    ("flux2_single_full_mask", TINY2, 1, 300, (40, 40), None, 56),
-    ("flux2_single_full_mask_bf16", C16[0], 1, 300, (40, 40), None, 56),
-    ("flux3_per_mode_block_diagonal", TINY3, 0, 300, (40, 40), (30, 30), 16),
-    ("flux3_joint_full_mask", TINY3, 1, 300, (40, 40), (30, 30), 40),
+    ("flux2_single_full_mask", TINY2, 1, 77, (20, 20), (30, 30), 32),
+    ("flux2_single_full_mask_bf16", C16[0], 1, 77, (20, 20), (30, 30), 32),
+    ("flux3_per_mode_block_diagonal", TINY3, 0, 300, (20, 20), (40, 40), 16),
+    ("flux3_joint_full_mask", TINY3, 1, 300, (20, 20), (30, 30), 40),
+    ("flux3_joint_three_whole_rounds", TINY3, 1, 32, (40, 40), (40, 40), 8),
+    ("flux2_single_two_whole_rounds", TINY2, 1, 77, (20, 20), (40, 40), 8),
 ], ids=lambda c: c[0])
 def test_attention_equal_shares_match_oracle(case, monkeypatch):
     """Attention with a forced share count (DIT_ATTN_GRID), so that units are cut into several
@@ -685,8 +691,9 @@ def test_attention_equal_shares_match_oracle(case, monkeypatch):
         groups = [(bounds[i], bounds[i + 1], bounds[i], bounds[i + 1]) for i in range(3) if segs[i]]
     else:
         groups = [(0, n, 0, n)]
-    lean, pieces = _split_plan(groups, cfg.heads, lean_grid)
+    lean, pieces, whole_rounds = _split_plan(groups, cfg.heads, lean_grid)
     assert lean and pieces >= 2, (lean, pieces)
+    print(f"[shares] {case[0]}: pieces <= {pieces}, whole-unit rounds {whole_rounds}", flush=True)
     monkeypatch.setenv("DIT_ATTN_GRID", str(lean_grid))
     _CTX.clear()
     try:
