@@ -10,6 +10,7 @@ Prints ONE JSON line on stdout; details go to stderr.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute f16|bf16|fp8]
     (fp8: the block projections in row-wise E4M3 on the FP8 MFMA, everything else f16)
     python bench.py --mode copy-calibration      # elementwise copy of 1 GiB, for PMC scaling
+    python bench.py --mode attention-balance     # attention, split last round vs whole units
     python bench.py --summarize-rocprof DIR ...  # rocprofv3 CSVs -> profiles/*.md (CPU only)
 """
 import argparse
@@ -409,6 +410,52 @@ def stack_summary(wl, cfg, r, mfma_peak):
     return out
 
 
+def attention_balance(reps=20):
+    """Attention of a FLUX.2 double and single block at 512 text + 1024 / 4096 image tokens
+    and of a FLUX.3 joint block at 512 + 4096 + 4096 tokens, with the launcher's default
+    (whole units, the last round split when it is under 40% full) and with one workgroup per
+    unit (DIT_ATTN_GRID=0): the measurements behind that rule."""
+    from dataclasses import replace
+
+    import torch
+
+    from latent_flow_matching_amd import dit, synth as S
+    out = {}
+    for name, base, segs in (("512txt_1024img", S.FLUX2_KLEIN, (512, 1024, 0)),
+                             ("512txt_4096img", S.FLUX2_KLEIN, (512, 4096, 0)),
+                             ("512txt_4096img_4096ref_joint", S.FLUX3_KLEIN, (512, 4096, 4096))):
+        blocks = (0,) if base is S.FLUX3_KLEIN else (0, 1)
+        cfg = replace(base, n_stream_blocks=0 if base is S.FLUX3_KLEIN else 1, n_shared_blocks=1)
+        n = sum(segs)
+        w = S.gen_weights(cfg, bits=True)
+        row = {}
+        for mode, grid in (("default", None), ("whole_units", "0")):
+            if grid is None:
+                os.environ.pop("DIT_ATTN_GRID", None)
+            else:
+                os.environ["DIT_ATTN_GRID"] = grid
+            ctx = dit.DiT(cfg, w, max_tokens=n)
+            x = torch.tensor(S.gen_tokens(n, cfg.hidden), device="cuda")
+            pos = torch.zeros((n, 4), device="cuda")
+            cond = torch.tensor(S.gen_cond(sum(1 for v in segs if v), cfg.hidden), device="cuda")
+            for _ in range(3):
+                for b in blocks:
+                    ctx.block_forward(b, x, *segs, pos, cond)
+            torch.cuda.synchronize()
+            ctx.profile_start(4000, kernels="attention")
+            for _ in range(reps):
+                for b in blocks:
+                    ctx.block_forward(b, x, *segs, pos, cond)
+            torch.cuda.synchronize()
+            ms, cnt, _, _ = ctx.profile_stop()["attention"]
+            row[mode + "_us"] = round(ms / cnt * 1e3, 1)
+            ctx.close()
+        os.environ.pop("DIT_ATTN_GRID", None)
+        out[name] = row
+        log(f"  attention {name}: {row}")
+    print(json.dumps({"mode": "attention-balance", "attention": out}), flush=True)
+
+
 def time_block_workload(wl, steps=20, warmup=3):
     """One block of a single-block configuration through dit_block_forward (its modulation
     GEMVs included): us per call, and the bytes it must stream, W1 and W2 of its weight sets
@@ -459,7 +506,7 @@ def main():
     ap.add_argument("--extras", default="on", choices=["on", "off"],
                     help="also time the other configurations (bf16 operands, 512x512, FLUX.3 "
                          "with a reference, the single double and single blocks)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calibration", "attention-balance"])
     ap.add_argument("--summarize-rocprof", action="store_true")
     ap.add_argument("--trace-dir")
     ap.add_argument("--trace-cmd", default="")
@@ -487,6 +534,10 @@ def main():
     if args.mode == "copy-calibration":
         torch.cuda.set_device(0)
         copy_calibration()
+        return
+    if args.mode == "attention-balance":
+        torch.cuda.set_device(0)
+        attention_balance()
         return
 
     from latent_flow_matching_amd import dit, synth as S
