@@ -106,6 +106,44 @@ def rope_complex(x, pos, theta):
     return torch.view_as_real(xc * rot[:, None, :]).reshape(n, h, d).numpy()
 
 
+def _parameter_count(arch, n_stream, n_shared, per_block_mod=False, tied_shared=False,
+                     text_proj=0, target_time=False):
+    """Generator parameters of a model built as the oracle reads the pages: each block's
+    weight sets (block_plan) hold W1 [3D+2F, D], W2 [D, D+F] and two [128] norm scales; the
+    modulation projections [3D, D] are one per (block kind, set), or one per (block, set) with
+    per_block_mod; tied_shared makes all shared / joint blocks one set."""
+    d, f, c, hd, td = 3072, 9216, 128, 128, 256
+    per_set = (3 * d + 2 * f) * d + d * (d + f) + 2 * hd
+    mod = 3 * d * d
+    sets = [len(set(O.block_plan(arch, b, n_stream)[1])) for b in range(n_stream + n_shared)]
+    blocks = sum(sets[:n_stream]) + (1 if tied_shared else sum(sets[n_stream:]))
+    mods = sum(sets) if per_block_mod else len(set(O.block_plan(arch, 0, n_stream)[1])) + 1
+    globals_ = d * c + d * td + d * d + 2 * d * d + c * d  # img_in, cond MLP, final layer
+    globals_ += text_proj * d + (d * td + d * d if target_time else 0)
+    return blocks * per_set + mods * mod + globals_
+
+
+def test_parameter_count_fits_printed_total():
+    """Readings Q2 (modulation projections shared per block kind and weight set) and Q16 (the
+    28 joint blocks are distinct, each one set shared by the streams) against the printed
+    generator size: 5.6 billion parameters without the text encoder, 11.2 GB of bf16 weights
+    (we0.ai "FLUX 3 Image Klein" article: introduction; "Hardwareanforderungen, Quantisierung
+    und Inferenzlatenz").  Per-block projections or tied joint blocks miss it by far."""
+    kw = dict(arch=O.ARCH_FLUX3, n_stream=5, n_shared=28, text_proj=20480, target_time=True)
+    shared = _parameter_count(**kw)
+    per_block = _parameter_count(per_block_mod=True, **kw)
+    tied = _parameter_count(tied_shared=True, **kw)
+    printed = 5.6e9
+    assert abs(shared / printed - 1) < 0.05, shared
+    assert abs(2 * shared / 11.2e9 - 1) < 0.05
+    assert per_block / printed - 1 > 0.15, per_block
+    assert 1 - tied / printed > 0.5, tied
+    # FLUX.2-klein "4B" (the model name, "Flux 2 Klein: Reine C-basierte Inferenz"): the same
+    # structure with 5 double and 20 single blocks comes to about 3.8 billion
+    flux2 = _parameter_count(O.ARCH_FLUX2, 5, 20)
+    assert abs(flux2 / 4e9 - 1) < 0.1, flux2
+
+
 def test_rope_matches_complex_rotation():
     r = rng(1)
     pos = O.positions(7, (3, 3), ((2, 3),))
