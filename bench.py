@@ -376,16 +376,24 @@ def time_stack(ctx, wl, cfg, steps, warmup, profile=True):
         dom = max((k for k in prof if prof[k][2] > 0), key=lambda k: prof[k][0])
         ctx.profile_start(steps * launches, kernels=dom)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between consecutive steps as well, for the per-step median (the total is the
+    # span of the first and last events, as before)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)]
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
         step(warmup + 1 + i)
+        if i + 1 < steps:
+            marks[i].record()
     end.record()
     torch.cuda.synchronize()
     timed = ctx.profile_stop() if profile else None
     ms = start.elapsed_time(end)
+    evs = [start, *marks, end]
+    each = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     assert torch.isfinite(lat).all(), "non-finite latents"
-    return {"ms": ms, "steps": steps, "prof": prof, "timed": timed, "dom": dom, "nseq": nseq}
+    return {"ms": ms, "steps": steps, "prof": prof, "timed": timed, "dom": dom, "nseq": nseq,
+            "each_ms": each}
 
 
 def stack_flops(wl, cfg):
@@ -403,7 +411,9 @@ def stack_summary(wl, cfg, r, mfma_peak):
     ms_step = r["ms"] / r["steps"]
     tf = stack_flops(wl, cfg) / (ms_step * 1e-3) / 1e12
     toks = wl.n_tokens * r["nseq"] * cfg.n_blocks * wl.steps / (ms_step * 1e-3)
-    out = {"ms_per_step": round(ms_step, 3), "block_tokens_per_s": round(toks, 1),
+    each = sorted(r["each_ms"])
+    out = {"ms_per_step": round(ms_step, 3), "ms_per_step_median": round(each[len(each) // 2], 3),
+           "block_tokens_per_s": round(toks, 1),
            "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
     if mfma_peak:
         out["pct_measured_peak"] = round(100 * tf / mfma_peak, 2)
@@ -478,17 +488,19 @@ def time_block_workload(wl, steps=20, warmup=3):
     cond = torch.tensor(S.gen_cond(sum(1 for v in segs if v), d), device="cuda")
     for _ in range(warmup):
         ctx.block_forward(0, x, *segs, pos, cond)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         ctx.block_forward(0, x, *segs, pos, cond)
-    end.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     ctx.close()
-    us = start.elapsed_time(end) * 1e3 / steps
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
+    each = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
     fl = S.flops_per_block(tuple(v for v in segs if v), d, f, False)
-    return {"us_per_block": round(us, 1), "bound": "hbm", "weight_bytes": wbytes,
+    return {"us_per_block": round(us, 1), "us_per_block_median": round(each[steps // 2], 1),
+            "bound": "hbm", "weight_bytes": wbytes,
             "gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "tflops": round(fl / (us * 1e-6) / 1e12, 2), "operands": cfg.compute,
@@ -615,6 +627,8 @@ def main():
         "unit": "block tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(per_step_ms, 3),
+        "ms_per_step_median": round(sorted(r["each_ms"])[args.steps // 2], 3),
+        "ms_each_step": [round(v, 3) for v in r["each_ms"]],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": args.compute, "data": "synthetic",
         "config": {"workload": wl.name, "tokens": n * nseq, "sequences": nseq,
