@@ -123,7 +123,7 @@ struct dit_ctx {
   int prof_next = 0;
 
   int D() const { return cfg.hidden; }
-  // lets an MFMA GEMM cut long k into slices when its tiles fill too few compute units
+  // lets a GEMM cut long k into slices when its tiles fill too few compute units
   void split_k(GemmArgs *a) const {
     a->part = gemm_part;
     a->part_tiles = gemm_part ? cus : 0;
@@ -610,7 +610,7 @@ extern "C" dit_ctx *dit_ctx_create(const dit_config *cfg, const dit_tensor *w, i
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->attn_cnt,
                           (size_t)c.heads * (c.max_tokens / 256 + kMaxGroups) * 4);
   }
-  if (ctx->op != OP_F32 && ctx->cus > 0)
+  if (ctx->cus > 0)
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->gemm_part, (size_t)ctx->cus * gemm_part_floats * 4);
   if (ctx->fp8) {
     rc = rc ? rc : dalloc(ctx, (void **)&ctx->cat8, R * (D + F));
@@ -760,6 +760,8 @@ int run_block(dit_ctx *ctx, int b, float *x, Segs sg, int mask, const int mrow[3
     a1.b1 = sg.b1;
     a1.b2 = sg.b2;
     a1.per = sg.per;
+  } else {
+    ctx->split_k(&a1);  // the fp32 GEMM cuts k into slices when its tiles are few
   }
   DIT_TIMED(P_LINEAR1, 2.0 * N * D * (double)a1.n, 0.0, gemm(a1, EPI_QKV_SWIGLU), "linear1");
   if (mfma) {

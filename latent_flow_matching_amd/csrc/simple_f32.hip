@@ -2,7 +2,9 @@
 //   * gemm_simple: LDS-tiled FMA GEMM with fp32 activations and fp32 or bf16 weights.  It
 //     runs every GEMM of the fp32 compute path and, in both paths, the two small
 //     projections with 128-wide latents (img_in, final.out), whose inputs are the caller's
-//     unpadded fp32 latents.
+//     unpadded fp32 latents.  Launches with few tiles cut k into slices (a second kernel
+//     adds them in a fixed order), so that few tokens still stream the weights through
+//     the whole device.
 //   * attention_f32: the fp32 path's softmax attention, one wave per (query, head), online
 //     softmax over 64-key chunks.
 #include <math.h>
@@ -21,46 +23,11 @@ struct TileStarts {
   int t[kMaxGroups + 1];
 };
 
-template <typename TW, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, int m_tiles_total) {
-  __shared__ float ws[TK][TN + 4];
-  __shared__ float xs[TK][TM + 4];
-  const int tile_n = blockIdx.x / m_tiles_total;
-  const int mt = blockIdx.x - tile_n * m_tiles_total;
-  int gi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
-  const int lmt = mt - tb.t[gi];
-  const GemmGroup grp = a.g[gi];
-  const int n0 = tile_n * TN, m0 = lmt * TM;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const TW *W = reinterpret_cast<const TW *>(grp.w);
-  const float *X = reinterpret_cast<const float *>(grp.x);
-  const int lr = tid >> 2, lk = (tid & 3) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < a.k; k0 += TK) {
-    const TW *wp = W + (size_t)(n0 + lr) * (a.ldw > 0 ? a.ldw : a.k) + k0 + lk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ws[lk + e][lr] = to_f32(wp[e]);
-    const int xr = m0 + lr;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      xs[lk + e][lr] = xr < grp.rows ? X[(size_t)xr * a.ldx + k0 + lk + e] : 0.f;
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < TK; ++kk) {
-      float wv[4], xv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = ws[kk][tx + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = xs[kk][ty + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += wv[i] * xv[j];
-    }
-    __syncthreads();
-  }
+// The epilogue of one 64 x 64 tile: thread (tx, ty) holds features n0 + tx + 16 i of tokens
+// m0 + ty + 16 j (rows inside the group).
+template <int EPI>
+__device__ __forceinline__ void simple_epilogue(const GemmArgs &a, const GemmGroup &grp, int n0,
+                                                int m0, int tx, int ty, const float (&acc)[4][4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + ty + 16 * j;
@@ -94,6 +61,103 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, 
   }
 }
 
+// Tile coordinates of workgroup tile `lt` (feature tile major, then the groups' token tiles).
+struct SimpleTile {
+  int gi, n0, m0;
+};
+__device__ __forceinline__ SimpleTile simple_tile(const TileStarts &tb, int m_tiles_total, int lt) {
+  const int tile_n = lt / m_tiles_total;
+  const int mt = lt - tile_n * m_tiles_total;
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
+  return SimpleTile{gi, tile_n * TN, (mt - tb.t[gi]) * TM};
+}
+
+// k-slices: workgroup (tile, slice) takes the slice's TK-steps [kt0, kt1) of the tile's k;
+// with splits > 1 it stores its 64 x 64 partial sums to a.part ([slice][tile][m][n]), and
+// k_gemm_simple_reduce adds the slices in slice order and applies the epilogue.
+template <typename TW, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, int m_tiles_total,
+                                                     int splits) {
+  __shared__ float ws[TK][TN + 4];
+  __shared__ float xs[TK][TM + 4];
+  const int lt = blockIdx.x / splits, slice = blockIdx.x - lt * splits;
+  const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
+  const GemmGroup grp = a.g[st.gi];
+  const int n0 = st.n0, m0 = st.m0;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const TW *W = reinterpret_cast<const TW *>(grp.w);
+  const float *X = reinterpret_cast<const float *>(grp.x);
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int kt_all = a.k / TK;
+  const int kt0 = (int)((long long)kt_all * slice / splits);
+  const int kt1 = (int)((long long)kt_all * (slice + 1) / splits);
+  // the next k-step's operands load into registers while the current one multiplies
+  const TW *wrow = W + (size_t)(n0 + lr) * (a.ldw > 0 ? a.ldw : a.k) + lk;
+  const int xrow = m0 + lr;
+  const float *xp = X + (size_t)xrow * a.ldx + lk;
+  float wn[4], xn[4];
+  auto fetch = [&](int kt) {
+    const int k0 = kt * TK;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wn[e] = to_f32(wrow[k0 + e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xn[e] = xrow < grp.rows ? xp[k0 + e] : 0.f;
+  };
+  float acc[4][4] = {};
+  if (kt0 < kt1) fetch(kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ws[lk + e][lr] = wn[e];
+      xs[lk + e][lr] = xn[e];
+    }
+    __syncthreads();
+    if (kt + 1 < kt1) fetch(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float wv[4], xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = ws[kk][tx + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = xs[kk][ty + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += wv[i] * xv[j];
+    }
+    __syncthreads();
+  }
+  if (splits > 1) {
+    const int tiles = gridDim.x / splits;
+    float *pp = a.part + ((size_t)slice * tiles + lt) * (TM * TN);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[(ty + 16 * j) * TN + tx + 16 * i] = acc[i][j];
+    return;
+  }
+  simple_epilogue<EPI>(a, grp, n0, m0, tx, ty, acc);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_simple_reduce(GemmArgs a, TileStarts tb,
+                                                            int m_tiles_total, int splits) {
+  const int lt = blockIdx.x, tiles = gridDim.x;
+  const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int s = 0; s < splits; ++s) {
+    const float *pp = a.part + ((size_t)s * tiles + lt) * (TM * TN);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] += pp[(ty + 16 * j) * TN + tx + 16 * i];
+  }
+  simple_epilogue<EPI>(a, a.g[st.gi], st.n0, st.m0, tx, ty, acc);
+}
+
 template <typename TW, int EPI>
 hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
   TileStarts tb = {};
@@ -101,7 +165,18 @@ hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
     tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + TM - 1) / TM : 0);
   const int m_tiles = tb.t[kMaxGroups];
   if (m_tiles == 0) return hipSuccess;
-  k_gemm_simple<TW, EPI><<<m_tiles * (a.n / TN), 256, 0, s>>>(a, tb, m_tiles);
+  const int tiles = m_tiles * (a.n / TN);
+  // k-slices when the tiles give under eight workgroups per compute unit (few tokens: the
+  // weights then stream through many more workgroups at once), at least 8 k-steps each
+  int splits = 1;
+  if (a.part != nullptr && a.cus > 0 && tiles < 8 * a.cus) {
+    splits = min(16, min((8 * a.cus + tiles - 1) / tiles, (a.k / TK) / 8));
+    const long long room = (long long)a.part_tiles * gemm_part_floats / (TM * TN);
+    while (splits > 1 && (long long)splits * tiles > room) --splits;
+    if (splits < 2) splits = 1;
+  }
+  k_gemm_simple<TW, EPI><<<tiles * splits, 256, 0, s>>>(a, tb, m_tiles, splits);
+  if (splits > 1) k_gemm_simple_reduce<EPI><<<tiles, 256, 0, s>>>(a, tb, m_tiles, splits);
   return hipGetLastError();
 }
 
