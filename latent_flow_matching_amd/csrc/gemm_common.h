@@ -61,6 +61,14 @@ __device__ __forceinline__ int vt_col(int u) {
   return ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
 }
 
+// Keeps accumulator v in its AGPRs up to this point, so that it is moved to VGPRs where it is
+// used: left alone, the compiler reads every accumulator out at the start of an epilogue and
+// spills.  PIN false (accumulators already rescaled in VGPRs by the caller) does nothing.
+template <bool PIN>
+__device__ __forceinline__ void keep_in_agpr(f32x4 &v) {
+  if constexpr (PIN) asm volatile("" : "+a"(v)::"memory");
+}
+
 // Fused part of linear1's epilogue for a wave whose 128 features are one Q, K or V head
 // (a.vt != nullptr).  Lane (r16, q4) holds dims 16 i + 4 q4 + {0..3} of token 16 j + r16.
 //   Q, K: RMSNorm over the head's 128 dims ("FLUX.3 Image Klein in Diffusers", "Entkoppelte
@@ -73,7 +81,7 @@ __device__ __forceinline__ int vt_col(int u) {
 //   then out as 16-byte chunks; chunks that hold tokens outside the half or the group are
 //   written element by element, so tiles that share a chunk write disjoint bytes.  The
 //   caller has passed a workgroup barrier after the main loop's last LDS reads.
-template <typename T, int BM, int WN, int WM>
+template <typename T, int BM, int WN, int WM, bool PIN>
 __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const GemmGroup &grp,
                                                    int n0, int m0, int wn, int wm, int lane,
                                                    f32x4 (&acc)[BN / WN / 16][BM / WM / 16],
@@ -97,6 +105,8 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
     char *tq = smem + wave * (128 * 256);
 #pragma unroll
     for (int j = 0; j < TS; ++j) {
+#pragma unroll
+      for (int i = 0; i < FS; ++i) keep_in_agpr<PIN>(acc[i][j]);
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < FS; ++i)
@@ -200,6 +210,8 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
       const int c = t0 + 16 * jj + r16 - g0;
       const int col = (c & ~31) + vt_col(c & 31);
 #pragma unroll
+      for (int i = 0; i < FS; ++i) keep_in_agpr<PIN>(acc[i][4 * hf + jj]);
+#pragma unroll
       for (int i = 0; i < FS; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -262,7 +274,7 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
 // Epilogue: lane owns token (lane & 15) and features 4 (lane >> 4) + {0..3} of every 16x16
 // sub-tile.  smem: the workgroup's LDS (at least 4 x kVtLds bytes), used by the fused
 // Q / K / V epilogue, which every wave of a workgroup takes or none does.
-template <typename T, int BM, int WN, int WM, int EPI>
+template <typename T, int BM, int WN, int WM, int EPI, bool PIN = true>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp, int n0, int m0,
                                          int wn, int wm, int lane,
                                          f32x4 (&acc)[BN / WN / 16][BM / WM / 16], char *smem) {
@@ -273,7 +285,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
   if constexpr (EPI == EPI_QKV_SWIGLU) {
     if (a.vt != nullptr && n0 < a.split) {
       __syncthreads();  // every wave's last fragment reads are done before LDS is reused
-      epilogue_qkv_heads<T, BM, WN, WM>(a, grp, n0, m0, wn, wm, lane, acc, smem);
+      epilogue_qkv_heads<T, BM, WN, WM, PIN>(a, grp, n0, m0, wn, wm, lane, acc, smem);
       return;
     }
   }
@@ -290,21 +302,36 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
 #pragma unroll
       for (int i = 0; i < FS; ++i)
         g[i] = *reinterpret_cast<const f32x4 *>(a.gate[seg0] + fbase + i * 16);
+      // the x rows of RB token sub-tiles are loaded before any of them is stored, so their
+      // loads share one round trip
+      constexpr int RB = PIN ? 2 : 1;
 #pragma unroll
-      for (int j = 0; j < TS; ++j) {
-        const int m = mw + j * 16 + r16;
-        if (m >= grp.rows) continue;
-        float *xr = a.x + (size_t)(grp.out_row0 + m) * a.ldres + fbase;
-        f32x4 xv[FS];
+      for (int j0 = 0; j0 < TS; j0 += RB) {
+        f32x4 xv[RB][FS];
 #pragma unroll
-        for (int i = 0; i < FS; ++i) xv[i] = *reinterpret_cast<const f32x4 *>(xr + i * 16);
+        for (int jj = 0; jj < RB && j0 + jj < TS; ++jj) {
+          const int m = mw + (j0 + jj) * 16 + r16;
+          const float *xr = a.x + (size_t)(grp.out_row0 + min(m, grp.rows - 1)) * a.ldres + fbase;
 #pragma unroll
-        for (int i = 0; i < FS; ++i) {
-          xv[i].x += g[i].x * acc[i][j][0];
-          xv[i].y += g[i].y * acc[i][j][1];
-          xv[i].z += g[i].z * acc[i][j][2];
-          xv[i].w += g[i].w * acc[i][j][3];
-          *reinterpret_cast<f32x4 *>(xr + i * 16) = xv[i];
+          for (int i = 0; i < FS; ++i) xv[jj][i] = *reinterpret_cast<const f32x4 *>(xr + i * 16);
+        }
+#pragma unroll
+        for (int jj = 0; jj < RB && j0 + jj < TS; ++jj) {
+          const int j = j0 + jj, m = mw + j * 16 + r16;
+          if (m >= grp.rows) continue;
+          float *xr = a.x + (size_t)(grp.out_row0 + m) * a.ldres + fbase;
+          // the accumulators leave their AGPRs here, not all at once at the epilogue's start
+#pragma unroll
+          for (int i = 0; i < FS; ++i) keep_in_agpr<PIN>(acc[i][j]);
+#pragma unroll
+          for (int i = 0; i < FS; ++i) {
+            f32x4 v = xv[jj][i];
+            v.x += g[i].x * acc[i][j][0];
+            v.y += g[i].y * acc[i][j][1];
+            v.z += g[i].z * acc[i][j][2];
+            v.w += g[i].w * acc[i][j][3];
+            *reinterpret_cast<f32x4 *>(xr + i * 16) = v;
+          }
         }
       }
       return;
@@ -315,6 +342,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const GemmGroup &grp
     const int m = m0 + wm * WTM + j * 16 + r16;  // row inside the group
     if (m >= grp.rows) continue;
     const int tok = grp.out_row0 + m;
+#pragma unroll
+    for (int i = 0; i < FS; ++i) keep_in_agpr<PIN>(acc[i][j]);
     if constexpr (EPI == EPI_RESID) {
       const int seg = segment_of(tok, a.b1, a.b2, a.per);
       const float *gate = a.gate[seg];

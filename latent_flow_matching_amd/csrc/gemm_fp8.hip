@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
     return;
   }
   static_assert(2 * STAGE >= 4 * kVtLds, "LDS for the fused V transpose");
-  epilogue<f16, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc, smem);
+  epilogue<f16, BM, WN, WM, EPI, false>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
 template <int EPI>
