@@ -1,13 +1,16 @@
-// fp32-accumulating kernels without MFMA:
-//   * gemm_simple: LDS-tiled FMA GEMM with fp32 activations and fp32 or bf16 weights.  It
-//     runs every GEMM of the fp32 compute path and, in both paths, the two small
-//     projections with 128-wide latents (img_in, final.out), whose inputs are the caller's
-//     unpadded fp32 latents.  Launches with few tiles cut k into slices (a second kernel
-//     adds them in a fixed order), so that few tokens still stream the weights through
-//     the whole device.
+// The fp32 path's GEMMs and attention, and the small projections with 128-wide latents:
+//   * gemm_simple: fp32 activations times fp32, bf16 or fp16 weights, fp32 accumulation.
+//     fp32 weights (every GEMM of the fp32 compute path) run on the fp32 MFMA
+//     (k_gemm_f32m, one wave per 64 x 64 tile, operands straight into registers); 16-bit
+//     weights (img_in and final.out on the 16-bit paths, whose inputs are the caller's
+//     unpadded fp32 latents) on an LDS-tiled FMA kernel.  Launches with few tiles cut k into
+//     slices, and a second kernel adds them in a fixed order, so that few tokens still stream
+//     the weights through the whole device.
 //   * attention_f32: the fp32 path's softmax attention, one wave per (query, head), online
 //     softmax over 64-key chunks.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -23,13 +26,13 @@ struct TileStarts {
   int t[kMaxGroups + 1];
 };
 
-// The epilogue of one 64 x 64 tile: thread (tx, ty) holds features n0 + tx + 16 i of tokens
-// m0 + ty + 16 j (rows inside the group).
-template <int EPI>
+// The epilogue of one 64 x 64 tile (or of its first 16 NJ rows): thread (tx, ty) holds
+// features n0 + tx + 16 i of tokens m0 + ty + 16 j (rows inside the group).
+template <int EPI, int NJ = 4>
 __device__ __forceinline__ void simple_epilogue(const GemmArgs &a, const GemmGroup &grp, int n0,
                                                 int m0, int tx, int ty, const float (&acc)[4][4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int m = m0 + ty + 16 * j;
     if (m >= grp.rows) continue;
     const int tok = grp.out_row0 + m;
@@ -141,21 +144,144 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, 
   simple_epilogue<EPI>(a, grp, n0, m0, tx, ty, acc);
 }
 
+// Sum of the k-slices of a tile's partials in slice order, and the epilogue: workgroup
+// (tile, r) takes the tile's rows 16 r .. 16 r + 15.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_simple_reduce(GemmArgs a, TileStarts tb,
                                                             int m_tiles_total, int splits) {
-  const int lt = blockIdx.x, tiles = gridDim.x;
+  const int lt = blockIdx.x, tiles = gridDim.x, r = blockIdx.y;
   const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
   for (int s = 0; s < splits; ++s) {
-    const float *pp = a.part + ((size_t)s * tiles + lt) * (TM * TN);
+    const float *pp = a.part + ((size_t)s * tiles + lt) * (TM * TN) + (16 * r + ty) * TN + tx;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] += pp[(ty + 16 * j) * TN + tx + 16 * i];
+    for (int i = 0; i < 4; ++i) acc[i][0] += pp[16 * i];
   }
-  simple_epilogue<EPI>(a, a.g[st.gi], st.n0, st.m0, tx, ty, acc);
+  simple_epilogue<EPI, 1>(a, a.g[st.gi], st.n0, st.m0 + 16 * r, tx, ty, acc);
+}
+
+// fp32 weights: v_mfma_f32_16x16x4_f32, one wave per 64 x 64 tile, operands straight from
+// global memory into registers (no LDS).  For each 16-wide chunk of k, lane (c, q) (c = lane %
+// 16, q = lane / 16) loads k0 + 4q .. k0 + 4q + 3 of weight row 16 fb + c and of token row
+// 16 tb + c; MFMA step s takes component s, so lane group q stands for k = k0 + 4q + s in both
+// operands and the four steps cover the chunk once.  Lane (c, q) then holds features
+// n0 + 16 fb + 4q + {0..3} of token m0 + 16 tb + c.  Two chunks are in flight while the
+// previous one multiplies.
+template <int EPI>
+__device__ __forceinline__ void mfma32_epilogue(const GemmArgs &a, const GemmGroup &grp, int n0,
+                                                int m0, int lane, const f32x4 (&acc)[4][4]) {
+  const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int m = m0 + 16 * tb + c;
+    if (m >= grp.rows) continue;
+    const int tok = grp.out_row0 + m;
+    if constexpr (EPI == EPI_STORE_F32) {
+      float *o = a.out + (size_t)tok * a.ldo + n0 + 4 * q;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        f32x4 *op = reinterpret_cast<f32x4 *>(o + 16 * fb);
+        f32x4 v = acc[fb][tb];
+        if (a.accumulate == 1) v = *op + a.alpha * v;
+        else if (a.accumulate == 2) v = a.alpha * v;
+        *op = v;
+      }
+    } else if constexpr (EPI == EPI_RESID) {
+      const float *gate = a.gate[segment_of(tok, a.b1, a.b2, a.per)] + n0 + 4 * q;
+      float *xr = a.x + (size_t)tok * a.ldres + n0 + 4 * q;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        f32x4 *xp = reinterpret_cast<f32x4 *>(xr + 16 * fb);
+        *xp = *xp + *reinterpret_cast<const f32x4 *>(gate + 16 * fb) * acc[fb][tb];
+      }
+    } else {
+      if (n0 < a.split) {
+        float *o = reinterpret_cast<float *>(a.qkv) + (size_t)tok * a.ldq + n0 + 4 * q;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) *reinterpret_cast<f32x4 *>(o + 16 * fb) = acc[fb][tb];
+      } else {
+        // 64-row tile = gate rows of features [32c, 32c+32) then their up rows
+        float *o = reinterpret_cast<float *>(a.cat) + (size_t)tok * a.ldc + a.cat_off +
+                   (n0 - a.split) / 2 + 4 * q;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu(acc[fb][tb][e]) * acc[fb + 2][tb][e];
+          *reinterpret_cast<f32x4 *>(o + 16 * fb) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(64) void k_gemm_f32m(GemmArgs a, TileStarts tb, int m_tiles_total,
+                                                  int splits) {
+  const int lt = blockIdx.x / splits, slice = blockIdx.x - lt * splits;
+  const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
+  const GemmGroup grp = a.g[st.gi];
+  const int lane = threadIdx.x, c = lane & 15, q = lane >> 4;
+  const int LW = a.ldw > 0 ? a.ldw : a.k;
+  const float *W = reinterpret_cast<const float *>(grp.w) + (size_t)st.n0 * LW;
+  const float *X = reinterpret_cast<const float *>(grp.x) + (size_t)st.m0 * a.ldx;
+  // descriptors over the tile's 64 weight rows and its token rows up to the group's end: rows
+  // past it read as zero (the range check includes the scalar offset)
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)W, (short)0, (int)min((long long)TN * LW * 4, 0x7FFFFFFFll), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)X, (short)0, (int)min((long long)(grp.rows - st.m0) * a.ldx * 4, 0x7FFFFFFFll),
+      0x00020000);
+  const int vo_w = (c * LW + 4 * q) * 4, vo_x = (c * a.ldx + 4 * q) * 4;
+  const int kc_all = a.k / TK;
+  const int kc0 = (int)((long long)kc_all * slice / splits);
+  const int kc1 = (int)((long long)kc_all * (slice + 1) / splits);
+  f32x4 w0[4], x0[4], w1[4], x1[4];
+  auto load = [&](int kc, f32x4 (&w)[4], f32x4 (&x)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      w[b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_w, vo_w, (16 * b * LW + kc * TK) * 4, 0));
+      x[b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_x, vo_x, (16 * b * a.ldx + kc * TK) * 4, 0));
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const f32x4 (&w)[4], const f32x4 (&x)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int tb2 = 0; tb2 < 4; ++tb2)
+          acc[fb][tb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[fb][s], x[tb2][s], acc[fb][tb2], 0, 0, 0);
+  };
+  // chunks past the slice's end are clamped to its last one (repeated loads, never used)
+  int kc = kc0;
+  load(kc, w0, x0);
+  load(min(kc + 1, kc1 - 1), w1, x1);
+  for (; kc + 2 <= kc1; kc += 2) {
+    mma(w0, x0);
+    load(min(kc + 2, kc1 - 1), w0, x0);
+    mma(w1, x1);
+    load(min(kc + 3, kc1 - 1), w1, x1);
+  }
+  if (kc < kc1) mma(w0, x0);
+  if (splits > 1) {  // partial tile [slice][tile][m][n], as k_gemm_simple_reduce reads it
+    float *pp = a.part + ((size_t)slice * (gridDim.x / splits) + lt) * (TM * TN);
+#pragma unroll
+    for (int tb2 = 0; tb2 < 4; ++tb2)
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+        *reinterpret_cast<f32x4 *>(pp + (16 * tb2 + c) * TN + 16 * fb + 4 * q) = acc[fb][tb2];
+    return;
+  }
+  mfma32_epilogue<EPI>(a, grp, st.n0, st.m0, lane, acc);
 }
 
 template <typename TW, int EPI>
@@ -176,16 +302,57 @@ hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
     if (splits < 2) splits = 1;
   }
   k_gemm_simple<TW, EPI><<<tiles * splits, 256, 0, s>>>(a, tb, m_tiles, splits);
-  if (splits > 1) k_gemm_simple_reduce<EPI><<<tiles, 256, 0, s>>>(a, tb, m_tiles, splits);
+  if (splits > 1) k_gemm_simple_reduce<EPI><<<dim3(tiles, TM / 16), 256, 0, s>>>(a, tb, m_tiles, splits);
+  return hipGetLastError();
+}
+
+// fp32 weights on the fp32 MFMA: one 64-thread wave per tile and k-slice.  k is cut into as
+// many slices as keep every wave resident at once (the occupancy the runtime reports for the
+// kernel, times the compute units): one more wave than fits would start a second round that
+// takes as long as the first.  At most 32 slices (their partials cost HBM traffic), at least
+// 8 chunks of 16 k each.
+template <int EPI>
+hipError_t launch_f32m(const GemmArgs &a, hipStream_t s) {
+  TileStarts tb = {};
+  for (int i = 0; i < kMaxGroups; ++i)
+    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + TM - 1) / TM : 0);
+  const int m_tiles = tb.t[kMaxGroups];
+  if (m_tiles == 0) return hipSuccess;
+  const int tiles = m_tiles * (a.n / TN);
+  static int per_cu = 0;  // resident waves per compute unit
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_f32m<EPI>, 64, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  int splits = 1;
+  const int slots = per_cu * a.cus;
+  if (a.part != nullptr && a.cus > 0 && 2 * tiles <= slots) {
+    splits = min(32, min(slots / tiles, (a.k / TK) / 8));
+    const long long room = (long long)a.part_tiles * gemm_part_floats / (TM * TN);
+    while (splits > 1 && (long long)splits * tiles > room) --splits;
+    if (splits < 2) splits = 1;
+  }
+  k_gemm_f32m<EPI><<<tiles * splits, 64, 0, s>>>(a, tb, m_tiles, splits);
+  if (splits > 1) k_gemm_simple_reduce<EPI><<<dim3(tiles, TM / 16), 256, 0, s>>>(a, tb, m_tiles, splits);
   return hipGetLastError();
 }
 
 template <typename TW>
 hipError_t dispatch_simple(const GemmArgs &a, int epi, hipStream_t s) {
-  switch (epi) {
-    case EPI_STORE_F32: return launch_simple<TW, EPI_STORE_F32>(a, s);
-    case EPI_QKV_SWIGLU: return launch_simple<TW, EPI_QKV_SWIGLU>(a, s);
-    case EPI_RESID: return launch_simple<TW, EPI_RESID>(a, s);
+  if constexpr (std::is_same<TW, float>::value) {
+    switch (epi) {
+      case EPI_STORE_F32: return launch_f32m<EPI_STORE_F32>(a, s);
+      case EPI_QKV_SWIGLU: return launch_f32m<EPI_QKV_SWIGLU>(a, s);
+      case EPI_RESID: return launch_f32m<EPI_RESID>(a, s);
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE_F32: return launch_simple<TW, EPI_STORE_F32>(a, s);
+      case EPI_QKV_SWIGLU: return launch_simple<TW, EPI_QKV_SWIGLU>(a, s);
+      case EPI_RESID: return launch_simple<TW, EPI_RESID>(a, s);
+    }
   }
   return hipErrorInvalidValue;
 }
