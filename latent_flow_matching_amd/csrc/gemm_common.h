@@ -88,7 +88,8 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
                                                    char *smem) {
   constexpr int WTN = BN / WN, WTM = BM / WM;
   constexpr int FS = WTN / 16, TS = WTM / 16;
-  static_assert(WTN == 128 && WTM % 64 == 0, "one head per wave, token halves of 64");
+  static_assert(WTN == 128 && WTM % 16 == 0 && WTM >= 64 && WTM <= 128,
+                "one head per wave, at most two token halves of up to 64");
   const int r16 = lane & 15, q4 = lane >> 4;
   const int dm = a.split / 3;
   const int fw = n0 + wn * WTN;  // the wave's first feature
@@ -102,7 +103,7 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
     // are this lane's 32 and those of lanes +16, +32, +48), and the scaled values as fp16
     // into the wave's LDS tile [128 tokens][128 dims], 16-byte chunk c of token t at slot
     // c ^ (t & 15) so that the 16 tokens of one write land on distinct banks.
-    char *tq = smem + wave * (128 * 256);
+    char *tq = smem + wave * (WTM * 256);
 #pragma unroll
     for (int j = 0; j < TS; ++j) {
 #pragma unroll
@@ -175,12 +176,13 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
       for (int k0 = 0; k0 < NT4; k0 += KB) {
         f16x8 hv[KB];
 #pragma unroll
-        for (int k = 0; k < KB; ++k) {
+        for (int k = 0; k < KB && k0 + k < NT4; ++k) {
           const int t = tl + 4 * (k0 + k);
           hv[k] = *reinterpret_cast<const f16x8 *>(tq + t * 256 + ((c ^ (t & 15)) << 4));
         }
 #pragma unroll
-        for (int k = 0; k < KB; ++k) dst[(k0 + k) * step] = rotate(hv[k], w0, w1, pv[k0 + k]);
+        for (int k = 0; k < KB && k0 + k < NT4; ++k)
+          dst[(k0 + k) * step] = rotate(hv[k], w0, w1, pv[k0 + k]);
       }
     } else {
 #pragma unroll 1
@@ -202,11 +204,13 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
   const int tw0 = grp.out_row0 + mw;        // the wave's first token
   const int gend = grp.out_row0 + grp.rows;  // the group's end
 #pragma unroll
-  for (int hf = 0; hf < WTM / 64; ++hf) {
+  for (int hf = 0; hf < (WTM + 63) / 64; ++hf) {
+    constexpr int HL0 = 64;
+    const int hl = min(HL0, WTM - 64 * hf);  // tokens of this half (48 for the second of 112)
     const int t0 = tw0 + 64 * hf, g0 = t0 & ~31;
     if (t0 >= gend) break;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < 4 && 16 * jj < WTM - 64 * hf; ++jj) {
       const int c = t0 + 16 * jj + r16 - g0;
       const int col = (c & ~31) + vt_col(c & 31);
 #pragma unroll
@@ -221,7 +225,7 @@ __device__ __forceinline__ void epilogue_qkv_heads(const GemmArgs &a, const Gemm
     // (a wave's LDS operations complete in order: its reads below see its writes above)
     // Lane (ch = lane % 16, of which 12 are used) copies chunk ch of dim rows lane / 16 + 4k:
     // whether that chunk lies wholly in this half is the same for every row.
-    const int t1 = min(t0 + 64, gend);
+    const int t1 = min(t0 + hl, gend);
     const int ch = lane & 15, dl = lane >> 4;
     const int ta = g0 + (ch >> 2) * 32 + (ch & 3) * 4;  // tokens ta.., ta + 16.. of the chunk
     const bool any = ch < 12 && ta + 19 >= t0 && ta < t1;
@@ -427,11 +431,12 @@ struct TileBounds {
 };
 
 // Sum of the k-slices of one partial tile (slice order fixed) and the tile's epilogue.  Grid:
-// (tiles, 64 sub-tiles); 256 threads = the GEMM's 4 waves x 64 lanes, same accumulator layout.
-template <int EPI>
+// (tiles, sub-tiles per wave); 256 threads = the GEMM's 4 waves x 64 lanes, same accumulator
+// layout (BM token rows per tile: 8 or 7 sub-tiles of 16 per wave).
+template <int EPI, int BM>
 __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, TileBounds tb, int m_tiles_total,
                                                      int total_tiles, int splits) {
-  constexpr int BM = 256, WTN = 128, WTM = 128, TS = 8;
+  constexpr int WTN = 128, WTM = BM / 2, FS = WTN / 16, TS = WTM / 16;
   const int lid = blockIdx.x, sub = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
@@ -453,8 +458,8 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, TileBounds tb, 
   const int m = m0 + wm * WTM + j * 16 + (lane & 15);
   if (m >= grp.rows) return;
   const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.part) +
-                    ((size_t)lid * 4 + wave) * (64 * 64) + sub * 64 + lane;
-  const size_t slice_stride = (size_t)total_tiles * 4 * 64 * 64;
+                    ((size_t)lid * 4 + wave) * (FS * TS * 64) + sub * 64 + lane;
+  const size_t slice_stride = (size_t)total_tiles * 4 * FS * TS * 64;
   f32x4 v = pp[0];
   for (int s = 1; s < splits; ++s) v += pp[s * slice_stride];
   const int tok = grp.out_row0 + m;

@@ -223,7 +223,7 @@ hipError_t launch8(const GemmArgs &a, hipStream_t s) {
   k_gemm8<EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
   if (splits > 1) {
     if constexpr (EPI != EPI_QKV_SWIGLU)
-      k_gemm_reduce<EPI><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);
+      k_gemm_reduce<EPI, 256><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);
   }
   return hipGetLastError();
 }

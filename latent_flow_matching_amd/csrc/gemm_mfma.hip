@@ -243,6 +243,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a, TileBounds tb, int m_t
     return;
   }
   static_assert(2 * STAGE >= 4 * kVtLds, "LDS for the fused V transpose");
+  static_assert(2 * STAGE >= 4 * WTM * 256, "LDS for the fused Q / K normalisation");
   epilogue<T, BM, WN, WM, EPI>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
@@ -254,40 +255,54 @@ int tile_bounds(const GemmArgs &a, int bm, TileBounds *tb) {
   return tb->t[kMaxGroups];
 }
 
-template <typename T, int EPI>
-hipError_t launch(const GemmArgs &a, hipStream_t s) {
+// A launch plan for tile height bm: token tiles, tiles, k-slices.
+struct Plan {
   TileBounds tb;
-  const int m_tiles = tile_bounds(a, 256, &tb);
-  if (m_tiles == 0) return hipSuccess;
-  const int total = m_tiles * (a.n / BN);
+  int m_tiles, total, splits;
+};
+template <int EPI>
+Plan make_plan(const GemmArgs &a, int bm) {
+  Plan p;
+  p.m_tiles = tile_bounds(a, bm, &p.tb);
+  p.total = p.m_tiles * (a.n / BN);
   // k-slices: only for tiles that fill under half of the compute units, with at least 8
   // k-tiles per slice
-  int splits = 1;
-  if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * total <= a.split_grid) {
-    splits = min(8, min(a.split_grid / total, (a.k / BK) / 8));
-    if (splits < 2 || (long long)splits * total > a.part_tiles) splits = 1;
+  p.splits = 1;
+  if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * p.total <= a.split_grid) {
+    p.splits = min(8, min(a.split_grid / p.total, (a.k / BK) / 8));
+    if (p.splits < 2 || (long long)p.splits * p.total > a.part_tiles) p.splits = 1;
   }
-  if constexpr (EPI == EPI_RESID) {
-    // 224-row tiles when the rounds of tiles over the compute units times the tile height
-    // (the time, up to the tiles' own efficiency) come out lower
-    if (splits == 1 && a.cus > 0) {
-      TileBounds tb7;
-      const int m7 = tile_bounds(a, 224, &tb7), total7 = m7 * (a.n / BN);
-      const long long t256 = (long long)((total + a.cus - 1) / a.cus) * 256;
-      const long long t224 = (long long)((total7 + a.cus - 1) / a.cus) * 224;
-      if (t224 < t256) {
-        k_gemm<T, EPI, 224><<<(total7 + 7) / 8 * 8, 256, 0, s>>>(a, tb7, m7, total7, 1);
-        return hipGetLastError();
-      }
+  return p;
+}
+
+template <typename T, int EPI, int BM>
+hipError_t run_plan(const GemmArgs &a, const Plan &p, hipStream_t s) {
+  const int grid = (p.total * p.splits + 7) / 8 * 8;
+  k_gemm<T, EPI, BM><<<grid, 256, 0, s>>>(a, p.tb, p.m_tiles, p.total, p.splits);
+  if constexpr (EPI != EPI_QKV_SWIGLU)
+    if (p.splits > 1)
+      k_gemm_reduce<EPI, BM><<<dim3(p.total, BM / 4), 256, 0, s>>>(a, p.tb, p.m_tiles, p.total, p.splits);
+  return hipGetLastError();
+}
+
+template <typename T, int EPI>
+hipError_t launch(const GemmArgs &a, hipStream_t s) {
+  const Plan p256 = make_plan<EPI>(a, 256);
+  if (p256.m_tiles == 0) return hipSuccess;
+  // 224-row tiles when the rounds of workgroups over the compute units, times the rows and
+  // k each workgroup takes, come out at least 5% lower (linear2 at 4608 tokens: 216 tiles of
+  // 256 rows against 252 of 224 on 256 compute units; linear1 of a single block at 1536
+  // tokens: 648 tiles, 3 rounds, against 756, 3 rounds)
+  if constexpr (EPI != EPI_STORE_F32) {
+    if (a.cus > 0) {
+      const Plan p224 = make_plan<EPI>(a, 224);
+      auto cost = [&](const Plan &p, int bm) {
+        return (double)((p.total * p.splits + a.cus - 1) / a.cus) * bm / p.splits;
+      };
+      if (20 * cost(p224, 224) < 19 * cost(p256, 256)) return run_plan<T, EPI, 224>(a, p224, s);
     }
   }
-  const int grid = (total * splits + 7) / 8 * 8;
-  k_gemm<T, EPI, 256><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
-  if (splits > 1) {
-    if constexpr (EPI != EPI_QKV_SWIGLU)
-      k_gemm_reduce<EPI><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);
-  }
-  return hipGetLastError();
+  return run_plan<T, EPI, 256>(a, p256, s);
 }
 
 }  // namespace
