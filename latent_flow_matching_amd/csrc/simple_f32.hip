@@ -319,13 +319,13 @@ hipError_t launch_f32m(const GemmArgs &a, hipStream_t s) {
   const int m_tiles = tb.t[kMaxGroups];
   if (m_tiles == 0) return hipSuccess;
   const int tiles = m_tiles * (a.n / TN);
-  static int per_cu = 0;  // resident waves per compute unit
-  if (per_cu == 0) {
+  // resident waves per compute unit (initialised once, thread-safely)
+  static const int per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_f32m<EPI>, 64, 0) != hipSuccess || n < 1)
       n = 1;
-    per_cu = n;
-  }
+    return n;
+  }();
   int splits = 1;
   const int slots = per_cu * a.cus;
   if (a.part != nullptr && a.cus > 0 && 2 * tiles <= slots) {
