@@ -269,7 +269,7 @@ Plan make_plan(const GemmArgs &a, int bm) {
   // k-tiles per slice
   p.splits = 1;
   if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * p.total <= a.split_grid) {
-    p.splits = min(8, min(a.split_grid / p.total, (a.k / BK) / 8));
+    p.splits = min(16, min(a.split_grid / p.total, (a.k / BK) / 8));
     if (p.splits < 2 || (long long)p.splits * p.total > a.part_tiles) p.splits = 1;
   }
   return p;
