@@ -64,17 +64,19 @@ __device__ __forceinline__ void simple_epilogue(const GemmArgs &a, const GemmGro
   }
 }
 
-// Tile coordinates of workgroup tile `lt` (feature tile major, then the groups' token tiles).
+// Tile coordinates of workgroup tile `lt` (feature tile major, then the groups' token tiles of
+// tm rows).
 struct SimpleTile {
   int gi, n0, m0;
 };
-__device__ __forceinline__ SimpleTile simple_tile(const TileStarts &tb, int m_tiles_total, int lt) {
+__device__ __forceinline__ SimpleTile simple_tile(const TileStarts &tb, int m_tiles_total, int lt,
+                                                  int tm = TM) {
   const int tile_n = lt / m_tiles_total;
   const int mt = lt - tile_n * m_tiles_total;
   int gi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxGroups; ++i) gi += mt >= tb.t[i];
-  return SimpleTile{gi, tile_n * TN, (mt - tb.t[gi]) * TM};
+  return SimpleTile{gi, tile_n * TN, (mt - tb.t[gi]) * tm};
 }
 
 // k-slices: workgroup (tile, slice) takes the slice's TK-steps [kt0, kt1) of the tile's k;
@@ -145,12 +147,13 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a, TileStarts tb, 
 }
 
 // Sum of the k-slices of a tile's partials in slice order, and the epilogue: workgroup
-// (tile, r) takes the tile's rows 16 r .. 16 r + 15.
+// (tile, r) takes the tile's rows 16 r .. 16 r + 15 (tiles of tm rows, partials laid out as
+// 64 x 64).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_simple_reduce(GemmArgs a, TileStarts tb,
-                                                            int m_tiles_total, int splits) {
+                                                            int m_tiles_total, int splits, int tm) {
   const int lt = blockIdx.x, tiles = gridDim.x, r = blockIdx.y;
-  const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
+  const SimpleTile st = simple_tile(tb, m_tiles_total, lt, tm);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
   for (int s = 0; s < splits; ++s) {
@@ -167,13 +170,14 @@ __global__ __launch_bounds__(256) void k_gemm_simple_reduce(GemmArgs a, TileStar
 // 16 tb + c; MFMA step s takes component s, so lane group q stands for k = k0 + 4q + s in both
 // operands and the four steps cover the chunk once.  Lane (c, q) then holds features
 // n0 + 16 fb + 4q + {0..3} of token m0 + 16 tb + c.  Two chunks are in flight while the
-// previous one multiplies.
-template <int EPI>
+// previous one multiplies.  A tile has TB blocks of 16 token rows (up to 64): groups of at
+// most 48 rows, such as 32 + 16 tokens, do not multiply padding.
+template <int EPI, int TB>
 __device__ __forceinline__ void mfma32_epilogue(const GemmArgs &a, const GemmGroup &grp, int n0,
-                                                int m0, int lane, const f32x4 (&acc)[4][4]) {
+                                                int m0, int lane, const f32x4 (&acc)[4][TB]) {
   const int c = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     const int m = m0 + 16 * tb + c;
     if (m >= grp.rows) continue;
     const int tok = grp.out_row0 + m;
@@ -216,11 +220,11 @@ __device__ __forceinline__ void mfma32_epilogue(const GemmArgs &a, const GemmGro
   }
 }
 
-template <int EPI>
+template <int EPI, int TB>
 __global__ __launch_bounds__(64) void k_gemm_f32m(GemmArgs a, TileStarts tb, int m_tiles_total,
                                                   int splits) {
   const int lt = blockIdx.x / splits, slice = blockIdx.x - lt * splits;
-  const SimpleTile st = simple_tile(tb, m_tiles_total, lt);
+  const SimpleTile st = simple_tile(tb, m_tiles_total, lt, 16 * TB);
   const GemmGroup grp = a.g[st.gi];
   const int lane = threadIdx.x, c = lane & 15, q = lane >> 4;
   const int LW = a.ldw > 0 ? a.ldw : a.k;
@@ -237,28 +241,29 @@ __global__ __launch_bounds__(64) void k_gemm_f32m(GemmArgs a, TileStarts tb, int
   const int kc_all = a.k / TK;
   const int kc0 = (int)((long long)kc_all * slice / splits);
   const int kc1 = (int)((long long)kc_all * (slice + 1) / splits);
-  f32x4 w0[4], x0[4], w1[4], x1[4];
-  auto load = [&](int kc, f32x4 (&w)[4], f32x4 (&x)[4]) {
+  f32x4 w0[4], x0[TB], w1[4], x1[TB];
+  auto load = [&](int kc, f32x4 (&w)[4], f32x4 (&x)[TB]) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < 4; ++b)
       w[b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rs_w, vo_w, (16 * b * LW + kc * TK) * 4, 0));
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
       x[b] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rs_x, vo_x, (16 * b * a.ldx + kc * TK) * 4, 0));
-    }
   };
-  f32x4 acc[4][4];
+  f32x4 acc[4][TB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const f32x4 (&w)[4], const f32x4 (&x)[4]) {
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const f32x4 (&w)[4], const f32x4 (&x)[TB]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int tb2 = 0; tb2 < 4; ++tb2)
+        for (int tb2 = 0; tb2 < TB; ++tb2)
           acc[fb][tb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[fb][s], x[tb2][s], acc[fb][tb2], 0, 0, 0);
   };
   // chunks past the slice's end are clamped to its last one (repeated loads, never used)
@@ -275,13 +280,13 @@ __global__ __launch_bounds__(64) void k_gemm_f32m(GemmArgs a, TileStarts tb, int
   if (splits > 1) {  // partial tile [slice][tile][m][n], as k_gemm_simple_reduce reads it
     float *pp = a.part + ((size_t)slice * (gridDim.x / splits) + lt) * (TM * TN);
 #pragma unroll
-    for (int tb2 = 0; tb2 < 4; ++tb2)
+    for (int tb2 = 0; tb2 < TB; ++tb2)
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb)
         *reinterpret_cast<f32x4 *>(pp + (16 * tb2 + c) * TN + 16 * fb + 4 * q) = acc[fb][tb2];
     return;
   }
-  mfma32_epilogue<EPI>(a, grp, st.n0, st.m0, lane, acc);
+  mfma32_epilogue<EPI, TB>(a, grp, st.n0, st.m0, lane, acc);
 }
 
 template <typename TW, int EPI>
@@ -302,7 +307,8 @@ hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
     if (splits < 2) splits = 1;
   }
   k_gemm_simple<TW, EPI><<<tiles * splits, 256, 0, s>>>(a, tb, m_tiles, splits);
-  if (splits > 1) k_gemm_simple_reduce<EPI><<<dim3(tiles, TM / 16), 256, 0, s>>>(a, tb, m_tiles, splits);
+  if (splits > 1)
+    k_gemm_simple_reduce<EPI><<<dim3(tiles, TM / 16), 256, 0, s>>>(a, tb, m_tiles, splits, TM);
   return hipGetLastError();
 }
 
@@ -311,18 +317,18 @@ hipError_t launch_simple(const GemmArgs &a, hipStream_t s) {
 // kernel, times the compute units): one more wave than fits would start a second round that
 // takes as long as the first.  At most 32 slices (their partials cost HBM traffic), at least
 // 8 chunks of 16 k each.
-template <int EPI>
-hipError_t launch_f32m(const GemmArgs &a, hipStream_t s) {
+template <int EPI, int TB>
+hipError_t run_f32m(const GemmArgs &a, hipStream_t s) {
   TileStarts tb = {};
   for (int i = 0; i < kMaxGroups; ++i)
-    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + TM - 1) / TM : 0);
+    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + 16 * TB - 1) / (16 * TB) : 0);
   const int m_tiles = tb.t[kMaxGroups];
   if (m_tiles == 0) return hipSuccess;
   const int tiles = m_tiles * (a.n / TN);
   // resident waves per compute unit (initialised once, thread-safely)
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_f32m<EPI>, 64, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_f32m<EPI, TB>, 64, 0) != hipSuccess || n < 1)
       n = 1;
     return n;
   }();
@@ -334,9 +340,26 @@ hipError_t launch_f32m(const GemmArgs &a, hipStream_t s) {
     while (splits > 1 && (long long)splits * tiles > room) --splits;
     if (splits < 2) splits = 1;
   }
-  k_gemm_f32m<EPI><<<tiles * splits, 64, 0, s>>>(a, tb, m_tiles, splits);
-  if (splits > 1) k_gemm_simple_reduce<EPI><<<dim3(tiles, TM / 16), 256, 0, s>>>(a, tb, m_tiles, splits);
+  k_gemm_f32m<EPI, TB><<<tiles * splits, 64, 0, s>>>(a, tb, m_tiles, splits);
+  if (splits > 1)
+    k_gemm_simple_reduce<EPI><<<dim3(tiles, TB), 256, 0, s>>>(a, tb, m_tiles, splits, 16 * TB);
   return hipGetLastError();
+}
+
+// Token rows per tile: the fewest 16-row blocks that keep the number of token tiles (each of
+// which streams the weights once) what 64-row tiles give.
+template <int EPI>
+hipError_t launch_f32m(const GemmArgs &a, hipStream_t s) {
+  auto tiles_of = [&](int rows_per_tile) {
+    int t = 0;
+    for (int i = 0; i < a.ng; ++i) t += (a.g[i].rows + rows_per_tile - 1) / rows_per_tile;
+    return t;
+  };
+  const int t64 = tiles_of(64);
+  if (tiles_of(16) == t64) return run_f32m<EPI, 1>(a, s);
+  if (tiles_of(32) == t64) return run_f32m<EPI, 2>(a, s);
+  if (tiles_of(48) == t64) return run_f32m<EPI, 3>(a, s);
+  return run_f32m<EPI, 4>(a, s);
 }
 
 template <typename TW>
