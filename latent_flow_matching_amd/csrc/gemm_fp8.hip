@@ -38,14 +38,16 @@ __device__ __forceinline__ f32x4 mma8(const i32x8 &a, const i32x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int EPI>
+template <int EPI, int BM>
 __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_tiles_total,
                                                int total_tiles, int splits) {
-  constexpr int BM = 256, WN = 2, WM = 2, NT = 256;
-  constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128
-  constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 sub-tiles of 16 x 16
-  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 16-byte loads per thread
-  constexpr int STAGE = (BN + BM) * BK8;       // 64 KB
+  constexpr int WN = 2, WM = 2, NT = 256;
+  constexpr int WTN = BN / WN, WTM = BM / WM;  // 128 x 128 (or 128 x 112)
+  constexpr int FS = WTN / 16, TS = WTM / 16;  // 8 x 8 (or 8 x 7) sub-tiles of 16 x 16
+  constexpr int LA = BN * 8 / NT, LB = BM * 8 / NT;  // 8 + 8 (or 8 + 7) 16-byte loads per thread
+  constexpr int STAGE = (BN + BM) * BK8;       // 64 KB (or 60 KB)
+  constexpr int MEND = 8 + 2 * (LA + LB);     // the LDS writes and global loads sit at m in [8, MEND)
+  static_assert(BM % 32 == 0 && MEND < (FS - 1) * TS, "tile shape");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int per = gridDim.x >> 3;
@@ -158,16 +160,16 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
     lds_sync();  // every wave is done reading the other stage (tile kt-1)
 #pragma unroll
     for (int m = 0; m < FS * TS; ++m) {
-      const int i = m >> 3, j = m & 7;
+      const int i = m / TS, j = m % TS;
       acc[i][j] = mma8(fr[i], fr[FS + j], acc[i][j]);
       if (j == 0 && i < FS - 1) read_frag(cur, i + 1);
-      if (m >= 8 && m < 40) {
+      if (m >= 8 && m < MEND) {
         const int r = (m - 8) >> 1;
         if ((m & 1) == 0) write_one(cur ^ 1, r);
         else gload_one(nk, r);
       }
-      if (m == 39) lds_sync();  // tile kt+1 written by every wave
-      if (m == 40) read_frag(cur ^ 1, 0);            // its weight fragment 0 (free since row 0)
+      if (m == MEND - 1) lds_sync();  // tile kt+1 written by every wave
+      if (m == MEND) read_frag(cur ^ 1, 0);            // its weight fragment 0 (free since row 0)
       if (i == FS - 1) read_frag(cur ^ 1, FS + j);   // its token fragment j, just freed
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -199,33 +201,60 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmArgs a, TileBounds tb, int m_
     return;
   }
   static_assert(2 * STAGE >= 4 * kVtLds, "LDS for the fused V transpose");
+  static_assert(2 * STAGE >= 4 * WTM * 256, "LDS for the fused Q / K normalisation");
   epilogue<f16, BM, WN, WM, EPI, false>(a, grp, n0, m0, wn, wm, lane, acc, smem);
 }
 
+// A launch plan for tile height bm: token tiles, tiles, k-slices.
+struct Plan8 {
+  TileBounds tb;
+  int m_tiles, total, splits;
+};
 template <int EPI>
-hipError_t launch8(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 256;
-  TileBounds tb = {};
+Plan8 make_plan8(const GemmArgs &a, int bm) {
+  Plan8 p;
+  p.tb = TileBounds{};
   for (int i = 0; i < kMaxGroups; ++i)
-    tb.t[i + 1] = tb.t[i] + (i < a.ng ? (a.g[i].rows + BM - 1) / BM : 0);
-  const int m_tiles = tb.t[kMaxGroups];
-  if (m_tiles == 0) return hipSuccess;
-  const int total = m_tiles * (a.n / BN);
+    p.tb.t[i + 1] = p.tb.t[i] + (i < a.ng ? (a.g[i].rows + bm - 1) / bm : 0);
+  p.m_tiles = p.tb.t[kMaxGroups];
+  p.total = p.m_tiles * (a.n / BN);
   // k-slices: only for tiles that fill under half of the compute units, with at least 8
   // k-tiles per slice
-  int splits = 1;
-  if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * total <= a.split_grid) {
-    splits = min(8, min(a.split_grid / total, (a.k / BK8) / 8));
-    splits = min(splits, a.part_tiles / total);  // as many partial tiles as the workspace holds
-    if (splits < 2) splits = 1;
+  p.splits = 1;
+  if (EPI != EPI_QKV_SWIGLU && a.part != nullptr && a.split_grid > 0 && 2 * p.total <= a.split_grid) {
+    p.splits = min(8, min(a.split_grid / p.total, (a.k / BK8) / 8));
+    p.splits = min(p.splits, a.part_tiles / p.total);  // as many partial tiles as the workspace holds
+    if (p.splits < 2) p.splits = 1;
   }
-  const int grid = (total * splits + 7) / 8 * 8;
-  k_gemm8<EPI><<<grid, 256, 0, s>>>(a, tb, m_tiles, total, splits);
-  if (splits > 1) {
-    if constexpr (EPI != EPI_QKV_SWIGLU)
-      k_gemm_reduce<EPI, 256><<<dim3(total, 64), 256, 0, s>>>(a, tb, m_tiles, total, splits);
-  }
+  return p;
+}
+
+template <int EPI, int BM>
+hipError_t run_plan8(const GemmArgs &a, const Plan8 &p, hipStream_t s) {
+  const int grid = (p.total * p.splits + 7) / 8 * 8;
+  k_gemm8<EPI, BM><<<grid, 256, 0, s>>>(a, p.tb, p.m_tiles, p.total, p.splits);
+  if constexpr (EPI != EPI_QKV_SWIGLU)
+    if (p.splits > 1)
+      k_gemm_reduce<EPI, BM><<<dim3(p.total, BM / 4), 256, 0, s>>>(a, p.tb, p.m_tiles, p.total, p.splits);
   return hipGetLastError();
+}
+
+// linear2: 224-row tiles when the rounds of workgroups over the compute units, times the rows
+// and k each workgroup takes, come out at least 5% lower (the 16-bit GEMM's rule)
+template <int EPI>
+hipError_t launch8(const GemmArgs &a, hipStream_t s) {
+  const Plan8 p256 = make_plan8<EPI>(a, 256);
+  if (p256.m_tiles == 0) return hipSuccess;
+  if constexpr (EPI == EPI_RESID) {
+    if (a.cus > 0) {
+      const Plan8 p224 = make_plan8<EPI>(a, 224);
+      auto cost = [&](const Plan8 &p, int bm) {
+        return (double)((p.total * p.splits + a.cus - 1) / a.cus) * bm / p.splits;
+      };
+      if (20 * cost(p224, 224) < 19 * cost(p256, 256)) return run_plan8<EPI, 224>(a, p224, s);
+    }
+  }
+  return run_plan8<EPI, 256>(a, p256, s);
 }
 
 }  // namespace

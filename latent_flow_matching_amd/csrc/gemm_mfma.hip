@@ -289,11 +289,12 @@ template <typename T, int EPI>
 hipError_t launch(const GemmArgs &a, hipStream_t s) {
   const Plan p256 = make_plan<EPI>(a, 256);
   if (p256.m_tiles == 0) return hipSuccess;
-  // 224-row tiles when the rounds of workgroups over the compute units, times the rows and
-  // k each workgroup takes, come out at least 5% lower (linear2 at 4608 tokens: 216 tiles of
-  // 256 rows against 252 of 224 on 256 compute units; linear1 of a single block at 1536
-  // tokens: 648 tiles, 3 rounds, against 756, 3 rounds)
-  if constexpr (EPI != EPI_STORE_F32) {
+  // linear2: 224-row tiles when the rounds of workgroups over the compute units, times the
+  // rows and k each workgroup takes, come out at least 5% lower (at 4608 tokens: 216 tiles of
+  // 256 rows against 252 of 224 on 256 compute units).  Not linear1: at 1536 tokens its 648
+  // tiles of 256 rows (3 rounds, the last half full) beat 756 of 224 (3 full rounds), 239
+  // against 253 us: a half-empty round runs at a higher clock under the power limit.
+  if constexpr (EPI == EPI_RESID) {
     if (a.cus > 0) {
       const Plan p224 = make_plan<EPI>(a, 224);
       auto cost = [&](const Plan &p, int bm) {
