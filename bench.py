@@ -34,14 +34,16 @@ GEMM_SOURCES = {"f16": ("gemm_mfma.hip", "gemm_common.h"), "bf16": ("gemm_mfma.h
                 "fp8": ("gemm_fp8.hip", "gemm_common.h")}
 COPY_BYTES = 1 << 30          # copy-calibration: 1 GiB read + 1 GiB written per launch
 # rocprofv3 kernel names of the library's launches, by the classes the library's profiler uses
-# (patterns match the mangled names rocprofv3 prints: the epilogue is the template argument
-# after the operand type, followed by the token-tile height on the 16-bit GEMM)
-KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8)?I.*Li1E(?:Li\d+E)?EEv|k_gemm8<1>"),
-                  ("linear2", r"k_gemm(?:_v3|_mfma|8)?I.*Li2E(?:Li\d+E)?EEv|k_gemm8<2>"),
+# (patterns match the mangled or demangled names rocprofv3 prints: the epilogue is the template
+# argument after the operand type, followed by the token-tile height)
+KERNEL_CLASSES = [("linear1", r"k_gemm(?:_v3|_mfma|8|_f32m)?I.*Li1E(?:Li\d+E)?EEv|k_gemm8<1(?:, \d+)?>"),
+                  ("linear2", r"k_gemm(?:_v3|_mfma|8|_f32m)?I.*Li2E(?:Li\d+E)?EEv|k_gemm8<2(?:, \d+)?>"
+                              r"|k_gemm_reduceILi2E|k_gemm_reduce<2(?:, \d+)?>"),
                   ("fp8_quant", r"k_quant_rows"),
                   ("attention", r"k_attn_"), ("qk_norm_rope", r"k_qk_norm_rope"),
                   ("ln_modulate", r"k_ln_modulate"),
-                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8)?I.*Li0E(?:Li\d+E)?EEv|k_to_half"),
+                  ("final/embed", r"k_gemm_simple|k_gemm(?:_v3|_mfma|8|_f32m)?I.*Li0E(?:Li\d+E)?EEv"
+                                  r"|k_gemm8<0(?:, \d+)?>|k_gemm_reduceILi0E|k_gemm_reduce<0(?:, \d+)?>|k_to_half"),
                   ("conditioning", r"k_gemv|k_timestep_embed"), ("euler noise", r"k_philox")]
 
 
