@@ -28,6 +28,18 @@ def test_several_gpus_refused_with_a_message():
     ("_ZN3dit12_GLOBAL__N_16k_gemmIDF16_Li0EEEvNS_8GemmArgsENS0_10TileBoundsEiii", "final/embed"),
     ("void dit::(anonymous namespace)::k_gemm8<1>(dit::GemmArgs, dit::TileBounds, int)", "linear1"),
     ("void dit::(anonymous namespace)::k_gemm8<2>(dit::GemmArgs, dit::TileBounds, int)", "linear2"),
+    # tile height after the epilogue (16-bit and FP8 GEMMs), token blocks (fp32 MFMA GEMM)
+    ("_ZN3dit12_GLOBAL__N_16k_gemmIDF16_Li1ELi256EEEvNS_8GemmArgsENS0_10TileBoundsEiii", "linear1"),
+    ("_ZN3dit12_GLOBAL__N_16k_gemmIDF16bLi2ELi224EEEvNS_8GemmArgsENS0_10TileBoundsEiii", "linear2"),
+    ("void dit::(anonymous namespace)::k_gemm8<1, 256>(dit::GemmArgs, dit::(anonymous", "linear1"),
+    ("void dit::(anonymous namespace)::k_gemm8<2, 224>(dit::GemmArgs, dit::(anonymous", "linear2"),
+    ("void dit::(anonymous namespace)::k_gemm_reduce<2, 224>(dit::GemmArgs, dit::(anon", "linear2"),
+    ("_ZN3dit12_GLOBAL__N_113k_gemm_reduceILi0ELi256EEEvNS_8GemmArgsENS0_10TileBoundsEiii",
+     "final/embed"),
+    ("_ZN3dit12_GLOBAL__N_111k_gemm_f32mILi1ELi3EEEvNS_8GemmArgsENS0_10TileStartsEii", "linear1"),
+    ("_ZN3dit12_GLOBAL__N_111k_gemm_f32mILi2ELi4EEEvNS_8GemmArgsENS0_10TileStartsEii", "linear2"),
+    ("_ZN3dit12_GLOBAL__N_113k_gemm_simpleIDF16bLi0EEEvNS_8GemmArgsENS0_10TileStartsEii",
+     "final/embed"),
     ("_ZN3dit12_GLOBAL__N_19k_attn_ppIDF16_EEvNS_8AttnArgsENS0_8AttnPlanE", "attention"),
     ("_ZN3dit6k_gemvIDF16_Lb1EEEvPfPKT_iiPKfii", "conditioning"),
     ("__amd_rocclr_fillBufferAligned", None),
