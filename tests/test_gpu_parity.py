@@ -157,6 +157,18 @@ def test_block_tiny_ragged(cfg, b):
     assert err <= tol(cfg) and derr <= tol_update(cfg)
 
 
+@pytest.mark.parametrize("cfg", F32, ids=["flux2_f32", "flux3_f32"])
+@pytest.mark.parametrize("segs", [(12, (3, 3), None), (20, (5, 5), (2, 4))],
+                         ids=["16_and_32_row_tiles", "32_and_48_row_tiles"])
+def test_block_f32_short_segments(cfg, segs):
+    """fp32 blocks whose row groups are all short, so the fp32 GEMM takes token tiles of 16,
+    32 or 48 rows (the fewest 16-row blocks that keep the tile count), every element."""
+    n_txt, grid, ref = segs
+    for b in (0, 1):
+        err, derr = run_block(cfg, b, n_txt, grid, ref)
+        assert err <= tol(cfg) and derr <= tol_update(cfg)
+
+
 @pytest.mark.parametrize("cfg", [TINY2, TINY3] + C16,
                          ids=["flux2_f16", "flux3_f16", "flux2_bf16", "flux3_bf16"])
 def test_fused_qk_norm_rope_and_v_transpose(cfg):
